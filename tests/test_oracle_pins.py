@@ -1,0 +1,479 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Each test checks the oracle against something other than itself: numbers the
+pages print (fixtures under tests/golden/, each with its citation), closed
+forms, special cases that reduce to a textbook routine, and brute force with
+exact rational arithmetic on tiny inputs.  Together they are chosen so that a
+plausible slip in the oracle (a dropped abs, a wrong qmax, reciprocal-multiply
+instead of division, round-half-away instead of half-even, swapped nibbles, a
+wrong offset, scales applied along the wrong axis, a transposed operand)
+fails at least one of them.
+"""
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from int8_int4_dequant_amd import inputs
+
+
+def _golden(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+# ------------------------------------------------------------ exact helpers
+
+
+def f32(x):
+    return np.float32(x)
+
+
+def fl32_of_fraction(fr):
+    """Round an exact rational to the nearest fp32 (ties to even).
+
+    float(Fraction) is the correctly rounded binary64 value; rounding that to
+    binary32 is again correct for quotients and products of binary32 numbers
+    because binary64 carries more than 2*24+2 bits (double rounding is then
+    innocuous)."""
+    return np.float32(float(fr))
+
+
+def exact_codes(values, bits):
+    """Codes of one group computed with exact rationals: scale = fl32(max/qmax)
+    (1 if zero), code = clip(round_half_even(fl32(w / scale)))."""
+    qmax = 2 ** (bits - 1) - 1
+    vals = [Fraction(float(np.float32(v))) for v in values]
+    m = max(abs(v) for v in vals)
+    s = fl32_of_fraction(m / qmax)
+    if s == 0:
+        s = np.float32(1.0)
+    S = Fraction(float(s))
+    codes = []
+    for v in vals:
+        r = Fraction(float(fl32_of_fraction(v / S)))
+        c = round(r)  # Python rounds Fractions half to even
+        codes.append(max(-qmax, min(qmax, c)))
+    return s, codes
+
+
+def pack_bytes_by_hand(codes, bits):
+    """Pure-Python packing written from the format's description."""
+    if bits == 8:
+        return bytes((c + 256) % 256 for c in codes)
+    out = []
+    for i in range(0, len(codes), 2):
+        lo = codes[i] + 8
+        hi = codes[i + 1] + 8
+        out.append(lo | (hi << 4))
+    return bytes(out)
+
+
+def decode_by_hand(payload, bits, count):
+    """Pure-Python decoding of a payload into signed codes."""
+    b = bytes(np.asarray(payload, np.uint8).tobytes())
+    if bits == 8:
+        codes = [v - 256 if v >= 128 else v for v in b]
+    else:
+        codes = []
+        for v in b:
+            codes.append((v & 15) - 8)
+            codes.append((v >> 4) - 8)
+    assert len(codes) == count
+    return codes
+
+
+# ------------------------------------------- Chapter 23 worked example (P2)
+
+
+def chapter23_quantise_fp64(ws, bits):
+    """The per-tensor special case in binary64, as the Chapter 23 script's
+    ``quantise`` states it (scale from max|w|, Python round, clip)."""
+    qmax = 2 ** (bits - 1) - 1
+    scale = max(abs(w) for w in ws) / qmax
+    codes = [max(-qmax - 1, min(qmax, round(w / scale))) for w in ws]
+    return scale, codes, [c * scale for c in codes]
+
+
+def _errors(ws, deq):
+    e = [abs(float(a) - float(b)) for a, b in zip(ws, deq)]
+    return max(e), math.sqrt(sum(v * v for v in e) / len(e))
+
+
+def _oracle_tensor(ws, bits, group=None):
+    w = np.array(ws, np.float32)
+    rec = oracle.quantize_pack(w, bits, group or w.size)
+    return rec, oracle.unpack(rec)
+
+
+def test_chapter23_steps_printed(golden_dir):
+    g = _golden(golden_dir, "chapter23_worked_example.json")
+    ws = g["weights"]
+    r8, _ = _oracle_tensor(ws, 8)
+    r4, _ = _oracle_tensor(ws, 4)
+    assert f"{float(r8['scales'][0]):.6f}" == g["printed"]["step_int8"]
+    assert f"{float(r4['scales'][0]):.6f}" == g["printed"]["step_int4"]
+    # the bit patterns follow from fp32 division of fl32(0.51) by qmax
+    assert r8["scales"][0] == fl32_of_fraction(Fraction(float(f32(0.51))) / 127)
+    assert r4["scales"][0] == fl32_of_fraction(Fraction(float(f32(0.51))) / 7)
+
+
+def test_chapter23_codes_and_bytes_exact(golden_dir):
+    g = _golden(golden_dir, "chapter23_worked_example.json")
+    ws = g["weights"]
+    for bits in (8, 4):
+        rec, _ = _oracle_tensor(ws, bits)
+        s, codes = exact_codes(ws, bits)
+        assert rec["scales"][0] == s
+        assert rec["q"].tolist() == codes
+        assert rec["payload"].tobytes() == pack_bytes_by_hand(codes, bits)
+        # the fp64 script of the page picks the same codes
+        assert chapter23_quantise_fp64(ws, bits)[1] == codes
+    # the bytes written out once by hand from the format description
+    assert _oracle_tensor(ws, 8)[0]["payload"].tobytes().hex() == "1e9052ec7fc911a4"
+    assert _oracle_tensor(ws, 4)[0]["payload"].tobytes().hex() == "2a7d5f39"
+
+
+def test_chapter23_rms_ratio(golden_dir):
+    g = _golden(golden_dir, "chapter23_worked_example.json")
+    ws = g["weights"]
+    _, d8 = _oracle_tensor(ws, 8)
+    _, d4 = _oracle_tensor(ws, 4)
+    mx8, r8 = _errors(np.float32(ws), d8)
+    mx4, r4 = _errors(np.float32(ws), d4)
+    assert f"{r4 / r8:.1f}" == g["printed"]["rms_ratio_int4_over_int8"]
+
+
+def test_chapter23_outlier(golden_dir):
+    g = _golden(golden_dir, "chapter23_worked_example.json")
+    ws = g["weights"]
+    out = ws + [g["outlier_value"]]
+    rc, _ = _oracle_tensor(ws, 8)
+    ro, d = _oracle_tensor(out, 8)
+    ratio = float(ro["scales"][0]) / float(rc["scales"][0])
+    assert f"{ratio:.1f}" == g["printed"]["outlier_scale_coarsening"]
+    w32 = np.float32(out)
+    small = [100 * abs(float(a) - float(b)) / abs(float(a))
+             for a, b in zip(w32, d) if abs(float(a)) <= 1]
+    assert f"{max(small):.2f}" == g["printed"]["outlier_worst_small_weight_error_percent"]
+    self_err = 100 * abs(float(w32[-1]) - float(d[-1])) / float(w32[-1])
+    assert f"{self_err:.2f}" == g["printed"]["outlier_self_error_percent"]
+
+
+def test_chapter23_two_scales(golden_dir):
+    g = _golden(golden_dir, "chapter23_worked_example.json")
+    ws = g["weights"]
+    out = ws + [g["outlier_value"]]
+    _, d_all = _oracle_tensor(out, 8)
+    _, rms_all = _errors(np.float32(out), d_all)
+    sq, n = 0.0, 0
+    for part in (ws, [g["outlier_value"]]):
+        _, d = _oracle_tensor(part, 8)
+        sq += sum((float(a) - float(b)) ** 2 for a, b in zip(np.float32(part), d))
+        n += len(part)
+    rms_grouped = math.sqrt(sq / n)
+    assert f"{rms_all / rms_grouped:.0f}" == g["printed"]["two_scales_rms_improvement"]
+
+
+def test_bits_per_weight(golden_dir):
+    g = _golden(golden_dir, "chapter23_worked_example.json")
+    # fp16 scale per 64 weights: the page's 4.25 bits
+    assert f"{oracle.bits_per_weight(4, 64, scale_bytes=2):.2f}" == \
+        g["printed"]["int4_bits_with_fp16_scale_per_64"]
+    # this build stores fp32 scales: 4 + 32/group
+    assert oracle.bits_per_weight(4, 128) == 4.25
+    assert oracle.bits_per_weight(4, 32) == 5.0
+    assert oracle.bits_per_weight(8, 4096) == 8 + 32 / 4096
+    # measured on real records
+    for bits, group in ((4, 32), (4, 128), (8, 64)):
+        rec = oracle.quantize_pack(np.ones((4, 256), np.float32), bits, group)
+        total = 8 * (rec["payload"].nbytes + rec["scales"].nbytes) / (4 * 256)
+        assert total == oracle.bits_per_weight(bits, group)
+
+
+def test_memory_table(golden_dir):
+    g = _golden(golden_dir, "chapter23_worked_example.json")
+    params = 7_000_000_000
+    for name, bits in (("int8", 8), ("int4", 4)):
+        gb = oracle.payload_bytes(bits, params, 1) / 1e9
+        assert f"{gb:.1f}" == g["memory_table_7b_gb"][name]
+    for name, b in g["bytes_per_param"].items():
+        assert f"{params * b / 1e9:.1f}" == g["memory_table_7b_gb"][name]
+
+
+def test_smallem_sizes(golden_dir):
+    g = _golden(golden_dir, "smallem_sizes.json")
+    p = g["params_70b"]
+    assert oracle.payload_bytes(4, p, 1) / 1e9 == g["gb_4bit"]
+    assert p * 2 / 1e9 == g["gb_16bit"]
+    # 24-bit integer words: 3 int8 or 6 int4 codes per 4-byte word
+    assert f"{4 / 3:.2f}" == g["f32_word_bytes_per_weight"]["int8"]
+    assert f"{4 / 6:.2f}" == g["f32_word_bytes_per_weight"]["int4"]
+    # 4-byte scales: g64 -> g32 grows int4 weights by ~9 % in word storage
+    sb = g["scale_bytes"]
+    grow = (4 / 6 + sb / 32) / (4 / 6 + sb / 64) - 1
+    assert round(100 * grow) == g["g32_vs_g64_growth_percent"]
+    # with nibble packing the same change costs more (1/8 more bits)
+    grow_nib = oracle.bits_per_weight(4, 32) / oracle.bits_per_weight(4, 64) - 1
+    assert abs(grow_nib - (5.0 / 4.5 - 1)) < 1e-12
+
+
+# ------------------------------------------------ the P1 script's own checks
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_p1_zero_and_linspace_groups(bits):
+    zeros = np.zeros((2, 32), np.float32)
+    lin = np.linspace(-3, 3, 64, dtype=np.float32).reshape(2, 32)
+    for w in (zeros, lin):
+        rec = oracle.quantize_pack(w, bits, 32)
+        assert rec["payload"].nbytes == w.size * bits // 8
+        expected = rec["q"].reshape(-1, 32).astype(np.float32) * rec["scales"][:, None]
+        np.testing.assert_array_equal(oracle.unpack(rec), expected.reshape(w.shape))
+        # brute force: codes and scales from exact rationals, row by row
+        for r in range(2):
+            s, codes = exact_codes(w[r], bits)
+            assert rec["scales"][r] == s
+            assert rec["q"][32 * r:32 * (r + 1)].tolist() == codes
+    # closed forms for the linspace rows: max |w| = 3 in row 0
+    qmax = 2 ** (bits - 1) - 1
+    rec = oracle.quantize_pack(lin, bits, 32)
+    assert rec["scales"][0] == np.float32(3.0) / np.float32(qmax)
+    if bits == 8:
+        assert rec["q"][:4].tolist() == [-127, -123, -119, -115]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_zero_group(bits):
+    rec = oracle.quantize_pack(np.zeros((3, 64), np.float32), bits, 32)
+    assert np.all(rec["scales"] == 1.0)
+    assert np.all(rec["q"] == 0)
+    assert set(rec["payload"].tolist()) == ({0x88} if bits == 4 else {0x00})
+    assert np.all(oracle.unpack(rec) == 0)
+
+
+def test_equal_weight_error_unequal_output_error():
+    # the P1 script's checks(): x = diag(100, 1), errors e1 = [.1, 0] and
+    # e2 = [0, .1] have equal mean squared weight error but output squared
+    # errors 100 and 0.01 -- which is why tolerances are stated per output
+    # against sum |x * w_hat| and not against weight error.
+    x = np.diag([100.0, 1.0])
+    e1 = np.array([[0.1, 0.0]])
+    e2 = np.array([[0.0, 0.1]])
+    assert np.mean(e1 * e1) == pytest.approx(0.005)
+    assert np.mean(e2 * e2) == pytest.approx(0.005)
+    assert np.sum((e1 @ x) ** 2) == pytest.approx(100.0)
+    assert np.sum((e2 @ x) ** 2) == pytest.approx(0.01)
+    # error_base scales with the activation the weight meets
+    rec = oracle.quantize_pack(np.array([[1.0, 1.0]], np.float32), 8, 2)
+    b = oracle.error_base(rec, np.array([[100.0, 0.0], [0.0, 1.0]], np.float32))
+    assert b[0, 0] == pytest.approx(100.0) and b[1, 0] == pytest.approx(1.0)
+
+
+# --------------------------------------------- P4 mean relative error pin
+
+
+def test_row_quantization_mean_relative_error(golden_dir):
+    g = _golden(golden_dir, "arabic_row_quantization.json")
+    rng = np.random.default_rng(g["seed"])
+    W = rng.normal(scale=g["sigma"], size=tuple(g["shape"])).astype(np.float32)
+    errs = {}
+    for bits in (8, 4):
+        rec = oracle.quantize_pack(W, bits, W.shape[1])
+        restored = oracle.unpack(rec)
+        errs[bits] = float(np.abs(W - restored).mean() / np.abs(W).mean())
+    assert errs[8] < g["int8_mean_relative_error_below"]
+    assert round(100 * errs[4]) == g["int4_mean_relative_error_percent_rounded"]
+
+
+# ------------------------------------------------- rounding special cases
+
+
+def test_ties_to_even_int4():
+    w = inputs.tie_vector()
+    rec = oracle.quantize_pack(w, 4, 8)
+    assert rec["scales"][0] == 1.0
+    assert rec["q"].tolist() == [7, 2, -2, 4, 0, 0, 2, 6]
+    assert rec["payload"].tobytes().hex() == "afc688ea"
+
+
+def test_ties_to_even_int8():
+    w = np.array([127, 2.5, -2.5, 3.5, -0.5, 0.5, 1.5, 6.5], np.float32)
+    rec = oracle.quantize_pack(w, 8, 8)
+    assert rec["scales"][0] == 1.0
+    assert rec["q"].tolist() == [127, 2, -2, 4, 0, 0, 2, 6]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_near_ties_match_exact_rationals(bits):
+    w = inputs.near_tie_matrix(seed=11 + bits, bits=bits, rows=48, group=32)
+    rec = oracle.quantize_pack(w, bits, 32)
+    for r in range(w.shape[0]):
+        s, codes = exact_codes(w[r], bits)
+        assert rec["scales"][r] == s, r
+        assert rec["q"][32 * r:32 * (r + 1)].tolist() == codes, r
+
+
+def test_near_ties_separate_division_from_reciprocal():
+    # The sweep is sharp enough to tell fp32 division from multiplication by
+    # a rounded reciprocal: some codes differ between the two.
+    diffs = 0
+    for bits in (4, 8):
+        w = inputs.near_tie_matrix(seed=11 + bits, bits=bits, rows=48, group=32)
+        rec = oracle.quantize_pack(w, bits, 32)
+        qmax = 2 ** (bits - 1) - 1
+        s = rec["scales"][:, None]
+        recip = (np.float32(1.0) / s).astype(np.float32)
+        alt = np.clip(np.rint((w * recip).astype(np.float32)), -qmax, qmax)
+        diffs += int(np.sum(alt.reshape(-1) != rec["q"]))
+    assert diffs > 0
+
+
+def test_subnormal_group():
+    w = inputs.subnormal_matrix(seed=5, rows=8, group=32)
+    assert np.any(np.abs(w) < np.finfo(np.float32).tiny)
+    for bits in (4, 8):
+        rec = oracle.quantize_pack(w, bits, 32)
+        for r in range(w.shape[0]):
+            s, codes = exact_codes(w[r], bits)
+            assert rec["scales"][r] == s
+            assert rec["q"][32 * r:32 * (r + 1)].tolist() == codes
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_group_of_one(bits):
+    w = np.array([0.3, -2.0, 0.0, 1e-30, -7.5, 6.0], np.float32)
+    rec = oracle.quantize_pack(w, bits, 1)
+    qmax = 2 ** (bits - 1) - 1
+    assert rec["q"].tolist() == [qmax, -qmax, 0, qmax, -qmax, qmax]
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_per_tensor_is_chapter23_quantise(bits):
+    w = inputs.weight(21, 16, 24, 0.3)
+    rec = oracle.quantize_pack(w, bits, w.size)
+    assert rec["scales"].shape == (1,)
+    _, codes, _ = chapter23_quantise_fp64([float(v) for v in w.reshape(-1)], bits)
+    assert rec["q"].tolist() == codes
+
+
+# ------------------------------------------------------- invariants
+
+
+@pytest.mark.parametrize("bits,group", [(4, 32), (4, 128), (8, 32), (8, 256)])
+def test_half_step_bound_and_code_range(bits, group):
+    w = inputs.weight(3, 64, 256, 0.02)
+    rec = oracle.quantize_pack(w, bits, group)
+    qmax = 2 ** (bits - 1) - 1
+    q = rec["q"].reshape(-1, group)
+    s = rec["scales"].astype(np.float64)[:, None]
+    assert np.all(np.abs(q) <= qmax)
+    # the element holding max |w| of a group maps to +-qmax exactly
+    idx = np.argmax(np.abs(w.reshape(-1, group)), axis=1)
+    assert np.all(np.abs(q[np.arange(q.shape[0]), idx]) == qmax)
+    # error at most half a step (plus the fp32 rounding of q*S)
+    err = np.abs(w.reshape(-1, group).astype(np.float64)
+                 - oracle.unpack(rec).reshape(-1, group).astype(np.float64))
+    assert np.all(err <= s * 0.5 * (1 + 2 ** -20))
+    if bits == 4:
+        nib = np.concatenate([rec["payload"] & 15, rec["payload"] >> 4])
+        assert np.all(nib != 0)  # code -8 never occurs
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_unpack_decodes_like_hand_decoder(bits):
+    w = inputs.weight(4, 8, 64, 0.1)
+    rec = oracle.quantize_pack(w, bits, 16)
+    codes = decode_by_hand(rec["payload"], bits, w.size)
+    assert codes == rec["q"].tolist()
+    scales = rec["scales"].tolist()
+    exp = [np.float32(float(c) * scales[i // 16]) for i, c in enumerate(codes)]
+    np.testing.assert_array_equal(oracle.unpack(rec).reshape(-1), np.array(exp, np.float32))
+
+
+def test_argument_errors():
+    with pytest.raises(ValueError):
+        oracle.quantize_pack(np.ones(8, np.float32), 3, 4)
+    with pytest.raises(ValueError):
+        oracle.quantize_pack(np.ones(8, np.float32), 8, 3)
+    with pytest.raises(ValueError):
+        oracle.quantize_pack(np.ones(3, np.float32), 4, 1)
+
+
+# ------------------------------------------- matmul reference: brute force
+
+
+def _exact_dot(x_row, w_row):
+    return sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(x_row, w_row))
+
+
+@pytest.mark.parametrize("bits,n,k,group,m", [(4, 5, 12, 4, 3), (8, 7, 16, 8, 2),
+                                               (4, 3, 64, 32, 1), (8, 9, 6, 6, 4)])
+def test_gemv_bruteforce_exact(bits, n, k, group, m):
+    w = inputs.weight(7, n, k, 0.5)
+    x = inputs.activations(8, m, k)
+    rec = oracle.quantize_pack(w, bits, group)
+    y = oracle.gemv_ref(rec, x)
+    B = oracle.error_base(rec, x)
+    assert y.shape == (m, n)
+    # w_hat from the hand decoder and exact products q * S rounded to fp32
+    codes = decode_by_hand(rec["payload"], bits, n * k)
+    sc = rec["scales"].tolist()
+    w_hat = [[np.float32(float(codes[r * k + c]) * sc[(r * k + c) // group])
+              for c in range(k)] for r in range(n)]
+    for i in range(m):
+        for j in range(n):
+            exact = _exact_dot(x[i], w_hat[j])
+            babs = sum(abs(Fraction(float(a)) * Fraction(float(b)))
+                       for a, b in zip(x[i], w_hat[j]))
+            assert abs(Fraction(float(y[i, j])) - exact) <= Fraction(k, 2 ** 52) * babs
+            assert abs(float(B[i, j]) - float(babs)) <= 1e-12 * float(babs) + 1e-300
+
+
+def test_gemm_bf16_decode_and_rounding(golden_dir):
+    g = _golden(golden_dir, "float_formats_bf16.json")
+    for d in g["decoded"]:
+        v = oracle.bf16_bits_to_f32(np.array([int(d["bits"], 16)], np.uint16))
+        assert float(v[0]) == d["value"]
+    for d in g["rounded"]:
+        bits = inputs.bf16_round_bits(np.array([d["fp32"]], np.float32))
+        assert float(oracle.bf16_bits_to_f32(bits)[0]) == d["bf16_value"]
+
+
+def test_gemm_ref_is_gemv_ref_on_bf16_values():
+    w = inputs.weight(9, 6, 32, 0.2)
+    xb = inputs.bf16_activations(10, 3, 32)
+    rec = oracle.quantize_pack(w, 4, 16)
+    y = oracle.gemm_ref(rec, xb)
+    codes = decode_by_hand(rec["payload"], 4, w.size)
+    sc = rec["scales"].tolist()
+    xf = [[Fraction(float(np.uint32(int(b) << 16).view(np.float32))) for b in row] for row in xb]
+    for i in range(3):
+        for j in range(6):
+            exact = sum(xf[i][c] * Fraction(float(np.float32(codes[j * 32 + c] * sc[(j * 32 + c) // 16])))
+                        for c in range(32))
+            assert abs(Fraction(float(y[i, j])) - exact) <= Fraction(32, 2 ** 52) * sum(
+                abs(xf[i][c]) * abs(Fraction(float(np.float32(codes[j * 32 + c] * sc[(j * 32 + c) // 16]))))
+                for c in range(32))
+
+
+def test_codes_path_equals_dequantized_path():
+    # The two QuantizedMatmul forms agree up to summation order at the row
+    # counts the Smallem tests use (1, 9, 40, 300): here the dequantized path
+    # is unpack + a plain fp64 loop order, the codes path is gemv_ref.
+    w = inputs.weight(12, 24, 64, 0.1)
+    rec = oracle.quantize_pack(w, 4, 32)
+    w_hat = oracle.unpack(rec).astype(np.float64)
+    for m in (1, 9, 40, 300):
+        x = inputs.activations(13 + m, m, 64)
+        y = oracle.gemv_ref(rec, x)
+        B = oracle.error_base(rec, x)
+        y2 = np.zeros((m, 24))
+        for c in range(64):
+            y2 += np.outer(x[:, c].astype(np.float64), w_hat[:, c])
+        assert np.all(np.abs(y - y2) <= 64 * 2 ** -52 * B)
