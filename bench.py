@@ -1,0 +1,295 @@
+"""Benchmark of the quantization hot path on one MI355X.
+
+A step is one pass of the whole path over the 7B-shaped linear stack (32
+layers x q, k, v, o, gate, up, down = 224 matrices, 6,476,005,376 fp32
+weights resident in HBM): quantize and pack every matrix to int4 with group
+32 (qw_quantize_pack), then one M = 1 dequantizing GEMV through every matrix
+(qw_gemv, which unpacks the codes in registers).  `value` is the step's
+algorithmic HBM bytes divided by the step time.
+
+In the same run the prefill GEMM (qw_gemm: 2048 tokens through a 70B-style
+MLP weight of 28672 x 8192, int4 group 128, bf16 matrix cores) is timed on
+its own and reported under "prefill_gemm", and the CPU oracle is timed on a
+bounded sample of the stack under "cpu_baseline".
+
+Prints ONE JSON line.  `--gpus N` with N > 1 exits: this build runs on one
+GPU.
+"""
+
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "int4/int8 dequant-GEMV weight GB/s (% HBM peak); prefill GEMM TFLOPS"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--gemm-reps", type=int, default=20)
+    ap.add_argument("--no-gemm", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layers", type=int, default=32, help="layers of the stack (default: all 32)")
+    ap.add_argument("--cpu-sample-worker", action="store_true", help=argparse.SUPPRESS)
+    return ap.parse_args()
+
+
+# ---------------------------------------------------------------- CPU leg
+
+
+def cpu_sample_worker():
+    """Runs in a child process with one BLAS / OpenMP thread: the oracle on
+    layer 0 of the stack (7 matrices), quantize + pack then the M = 1 GEMV."""
+    import numpy as np
+
+    import oracle
+    from int8_int4_dequant_amd import inputs
+
+    total_bytes = 0
+    elapsed = 0.0
+    weights = 0
+    for slot, (tag, n, k) in enumerate(inputs.C4_SLOTS):
+        w = inputs.c4_weight(0, slot)
+        x = inputs.c4_x(k)
+        t0 = time.perf_counter()
+        rec = oracle.quantize_pack(w, 4, 32)
+        oracle.gemv_ref(rec, x)
+        elapsed += time.perf_counter() - t0
+        total_bytes += step_bytes_matrix(n, k)
+        weights += n * k
+    print(json.dumps(dict(seconds=elapsed, bytes=total_bytes, weights=weights)))
+
+
+def cpu_baseline():
+    env = dict(os.environ)
+    for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "VECLIB_MAXIMUM_THREADS"):
+        env[v] = "1"
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-sample-worker"],
+                       capture_output=True, text=True, env=env, timeout=900)
+    if r.returncode != 0:
+        log(r.stderr[-2000:])
+        return None
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    return {"value": round(d["bytes"] / d["seconds"] / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"layer 0 of the stack (7 matrices, {d['weights']} weights): oracle "
+                      f"quantize_pack + fp64 GEMV, {d['seconds']:.2f} s, one thread"}
+
+
+# ------------------------------------------------------------ accounting
+
+
+def quant_bytes(n, k, bits=4, group=32):
+    return n * k * 4 + n * k * bits // 8 + 4 * (n * k // group)
+
+
+def gemv_bytes(n, k, m=1, bits=4, group=32):
+    return n * k * bits // 8 + 4 * (n * k // group) + 4 * m * k + 4 * m * n
+
+
+def step_bytes_matrix(n, k):
+    return quant_bytes(n, k) + gemv_bytes(n, k)
+
+
+# ----------------------------------------------------------------- main
+
+
+def main():
+    args = parse()
+    if args.cpu_sample_worker:
+        cpu_sample_worker()
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the quantization path has no multi-GPU mode in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from int8_int4_dequant_amd import inputs, qw
+
+    qw.lib()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    L = qw.lib()
+
+    # ---- setup: the stack's fp32 weights resident in HBM, outputs allocated
+    mats = [m for m in inputs.c4_matrices() if m[0] < args.layers]
+    W, P, S, Y = [], [], [], []
+    xs = {k: torch.from_numpy(inputs.c4_x(k)).to(dev) for k in (4096, 11008)}
+    t0 = time.time()
+
+    def upload(i, layer, tag, w):
+        n, k = w.shape
+        W.append(torch.from_numpy(w).to(dev))
+        P.append(torch.empty(n * k // 2, dtype=torch.uint8, device=dev))
+        S.append(torch.empty(n * k // 32, dtype=torch.float32, device=dev))
+        Y.append(torch.empty((1, n), dtype=torch.float32, device=dev))
+
+    if args.layers == 32:
+        inputs.c4_weights_parallel(upload)
+    else:
+        for i, (layer, tag, n, k, seed) in enumerate(mats):
+            upload(i, layer, tag, inputs.weight(seed, n, k, inputs.C4["sigma"]))
+    torch.cuda.synchronize()
+    log(f"setup: {len(W)} matrices uploaded in {time.time() - t0:.1f} s")
+
+    shapes = [(m[2], m[3]) for m in mats]
+    qbytes = sum(quant_bytes(n, k) for n, k in shapes)
+    gbytes = sum(gemv_bytes(n, k) for n, k in shapes)
+    weights = sum(n * k for n, k in shapes)
+
+    def run_step(ev=None):
+        for i, (n, k) in enumerate(shapes):
+            if ev is not None:
+                ev[0][i].record(stream)
+            st = L.qw_quantize_pack(4, 32, n, k, W[i].data_ptr(), P[i].data_ptr(),
+                                    S[i].data_ptr(), sptr)
+            if ev is not None:
+                ev[1][i].record(stream)
+            if st:
+                raise RuntimeError(f"qw_quantize_pack failed: {st}")
+        for i, (n, k) in enumerate(shapes):
+            if ev is not None:
+                ev[2][i].record(stream)
+            st = L.qw_gemv(4, 32, n, k, P[i].data_ptr(), S[i].data_ptr(), 1,
+                           xs[k].data_ptr(), Y[i].data_ptr(), sptr)
+            if ev is not None:
+                ev[3][i].record(stream)
+            if st:
+                raise RuntimeError(f"qw_gemv failed: {st}")
+
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, per-launch HIP events on the launch stream
+    evs = [[[torch.cuda.Event(enable_timing=True) for _ in shapes] for _ in range(4)]
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(args.steps):
+        run_step(evs[s])
+    torch.cuda.synchronize()
+    t_total = time.perf_counter() - t_start
+
+    q_ms = sum(evs[s][0][i].elapsed_time(evs[s][1][i]) for s in range(args.steps) for i in range(len(shapes)))
+    g_ms = sum(evs[s][2][i].elapsed_time(evs[s][3][i]) for s in range(args.steps) for i in range(len(shapes)))
+    launches = args.steps * len(shapes)
+    q_avg_us = 1e3 * q_ms / launches
+    g_avg_us = 1e3 * g_ms / launches
+    q_gbs = qbytes * args.steps / (q_ms * 1e-3) / 1e9
+    g_gbs = gbytes * args.steps / (g_ms * 1e-3) / 1e9
+    ms_per_step = 1e3 * t_total / args.steps
+    value = (qbytes + gbytes) / (ms_per_step * 1e-3) / 1e9
+    log(f"step {ms_per_step:.3f} ms; quantize {q_gbs:.0f} GB/s (avg {q_avg_us:.1f} us/launch); "
+        f"gemv {g_gbs:.0f} GB/s (avg {g_avg_us:.2f} us/launch)")
+
+    dominant = "quantize_pack" if q_ms >= g_ms else "gemv"
+    if dominant == "quantize_pack":
+        ach, per_launch = q_gbs, qbytes / len(shapes)
+    else:
+        ach, per_launch = g_gbs, gbytes / len(shapes)
+    roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "kernel": f"qw_{dominant} (int4 g32, 224 launches per step)",
+                "algorithmic_bytes_per_launch": round(per_launch),
+                "avg_launch_us": round(q_avg_us if dominant == "quantize_pack" else g_avg_us, 3)}
+    parts = {
+        "quantize_pack": {"GB/s": round(q_gbs, 1), "frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4),
+                          "avg_launch_us": round(q_avg_us, 3), "bytes_per_step": qbytes},
+        "decode_gemv_m1": {"GB/s": round(g_gbs, 1), "frac_hbm": round(g_gbs / HBM_PEAK_GBS, 4),
+                           "avg_launch_us": round(g_avg_us, 3), "bytes_per_step": gbytes,
+                           "pass_us_kernel_sum": round(1e3 * g_ms / args.steps, 1)},
+    }
+
+    # free the stack before the GEMM leg
+    del W, P, S, Y
+    torch.cuda.empty_cache()
+
+    gemm = None
+    if not args.no_gemm:
+        gemm = bench_gemm(args, L, stream)
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline()
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded N(0,0.02) fp32 weights in place of trained 7B layers)",
+        "config": {"workload": "c4: 7B-shaped linear stack, 32 layers x (4 x 4096x4096 + 2 x "
+                               "11008x4096 + 4096x11008), int4 group 32; step = quantize+pack "
+                               "all + one M=1 GEMV pass",
+                   "layers": args.layers, "matrices": len(shapes), "weights": weights,
+                   "bits": 4, "group": 32, "m": 1, "bytes_per_step": qbytes + gbytes},
+        "roofline": roofline, "parts": parts, "prefill_gemm": gemm, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_gemm(args, L, stream):
+    import numpy as np
+    import torch
+
+    from int8_int4_dequant_amd import inputs
+
+    dev = torch.device("cuda:0")
+    c = inputs.C5
+    n, k, m = c["n"], c["k"], c["m"]
+    w = torch.from_numpy(inputs.c5_weight()).to(dev)
+    p = torch.empty(n * k // 2, dtype=torch.uint8, device=dev)
+    s = torch.empty(n * k // 128, dtype=torch.float32, device=dev)
+    st = L.qw_quantize_pack(4, 128, n, k, w.data_ptr(), p.data_ptr(), s.data_ptr(), stream.cuda_stream)
+    assert st == 0, st
+    del w
+    x = torch.from_numpy(inputs.c5_x_bf16().view(np.int16)).to(dev)
+    y = torch.empty((m, n), dtype=torch.float32, device=dev)
+    sp = stream.cuda_stream
+
+    def run():
+        r = L.qw_gemm(4, 128, n, k, p.data_ptr(), s.data_ptr(), m, x.data_ptr(), y.data_ptr(), sp)
+        if r:
+            raise RuntimeError(f"qw_gemm failed: {r}")
+
+    for _ in range(3):
+        run()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.gemm_reps)]
+    for a, b in ev:
+        a.record(stream)
+        run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    times = sorted(a.elapsed_time(b) for a, b in ev)
+    med = times[len(times) // 2]
+    flops = 2.0 * m * n * k
+    tf = flops / (med * 1e-3) / 1e12
+    log(f"gemm: median {med * 1e3:.1f} us, {tf:.1f} TFLOP/s ({tf / BF16_PEAK_TFLOPS:.1%} of bf16 peak)")
+    return {"workload": "c5: M=2048 bf16 x (28672 x 8192) int4 group 128, fp32 accumulate",
+            "median_us": round(med * 1e3, 2), "p90_us": round(times[int(0.9 * (len(times) - 1))] * 1e3, 2),
+            "TFLOP/s": round(tf, 2),
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None}}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,144 @@
+/*
+ * qw.h -- C ABI of libqw: symmetric round-to-nearest group quantization of
+ * linear-layer weights and the weight-only dequantizing matmul, for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Formats (page "量化推理：INT8/INT4 的体积、困惑度与速度为什么不同步",
+ * script functions `pack` and `unpack`; page "Huit bits, puis quatre",
+ * section "Arrondir"):
+ *
+ *   weight    fp32 [n][k], row-major.  Row i is output channel i; k is the
+ *             reduction axis and is contiguous.
+ *   groups    consecutive runs of `group` elements in that storage order
+ *             (so with k % group == 0 a group lies inside one row).
+ *   scale     one fp32 per group: S = max|w| / qmax computed as an IEEE
+ *             fp32 division, qmax = 2^(bits-1) - 1 (127 or 7); S = 1 for an
+ *             all-zero group.
+ *   code      q = clip(round_half_even(fl32(w / S)), -qmax, +qmax), where
+ *             w / S is an IEEE fp32 division.
+ *   payload   int8: one two's-complement byte per weight, storage order.
+ *             int4: n*k/2 bytes; byte i = (q[2i] + 8) | (q[2i+1] + 8) << 4
+ *             (element 2i in the low nibble).
+ *   w_hat     fl32(float(q) * S) -- the dequantized weight.
+ *
+ * Matmul (page "Huit bits, puis quatre", section "Ranger des entiers dans
+ * des f32", the QuantizedMatmul paragraph: generation products read the
+ * codes, large evaluation products use the dequantized weights; both are
+ * the same product up to summation order):
+ *
+ *   y[m][i] = sum_j x[m][j] * w_hat[i][j]
+ *
+ *   qw_gemv : decode-time product, fp32 activations, fp32 arithmetic,
+ *             1 <= m <= 8.  Error <= 1e-5 * sum_j |x[m][j] * w_hat[i][j]|.
+ *   qw_gemm : prefill product, bf16 activations; the weights are dequantized
+ *             to bf16 (round to nearest even of w_hat) and multiplied on the
+ *             matrix cores with fp32 accumulation; m >= 1.
+ *             Error <= 8e-3 * sum_j |x[m][j] * w_hat[i][j]|.
+ *
+ * Conventions shared by every entry point:
+ *   - All buffers are DEVICE pointers owned by the caller.  The library never
+ *     allocates, frees or synchronizes; it keeps no state besides cached
+ *     device properties and is safe to call from several threads.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls return
+ *     once the work is enqueued; results are valid after the stream has
+ *     synchronized.
+ *   - Buffers must not overlap.  Inputs must be finite (NaN / Inf give
+ *     unspecified codes and outputs).
+ *   - Any pointer alignment is accepted; 16-byte aligned buffers (as every
+ *     hipMalloc / torch allocation is) take the fast kernels.
+ *   - Empty work (n*k == 0, or m == 0) is valid and enqueues nothing, except
+ *     that a product with k == 0 writes zeros to y.  Pointers may then be
+ *     NULL.
+ *   - Errors are returned as negative status codes and never abort; on error
+ *     nothing is enqueued (QW_EHIP: a launch failed; its HIP error text is
+ *     available from qw_last_error()).
+ */
+#ifndef QW_H
+#define QW_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum qw_status {
+    QW_OK = 0,
+    QW_EBITS = -1,   /* bits is not 4 or 8                                   */
+    QW_EGROUP = -2,  /* group < 1, or group does not divide n*k              */
+    QW_ESHAPE = -3,  /* n < 0, k < 0, n*k overflows, or int4 with odd n*k     */
+    QW_EM = -4,      /* m out of range (gemv: 0..8, gemm: >= 0)              */
+    QW_ENULL = -5,   /* a required pointer is NULL                           */
+    QW_EHIP = -6,    /* a HIP launch failed                                  */
+    QW_ECOUNT = -7   /* batched call: count < 0 or a descriptor is invalid   */
+};
+
+/* Bytes of packed codes for an n x k matrix: n*k*bits/8 (-1 if invalid). */
+int64_t qw_payload_bytes(int bits, int64_t n, int64_t k);
+
+/* Number of fp32 scales for an n x k matrix: n*k/group (-1 if invalid). */
+int64_t qw_num_scales(int64_t group, int64_t n, int64_t k);
+
+/* Static text for a status code. */
+const char* qw_status_string(int status);
+
+/* Text of the last HIP error seen by this thread (empty if none). */
+const char* qw_last_error(void);
+
+/*
+ * Quantize and pack (one pass over the weight).
+ *   w        fp32 [n][k]                       (read)
+ *   payload  uint8 [qw_payload_bytes(bits,n,k)] (written)
+ *   scales   fp32 [qw_num_scales(group,n,k)]   (written)
+ * group must divide n*k; int4 needs n*k even.  Codes, scales and payload are
+ * bit-identical to the definitions above.
+ */
+int qw_quantize_pack(int bits, int64_t group, int64_t n, int64_t k,
+                     const float* w, uint8_t* payload, float* scales,
+                     void* stream);
+
+/*
+ * Unpack: w_out[i][j] = fl32(float(q) * S), bit-identical.
+ *   payload, scales as written by qw_quantize_pack   (read)
+ *   w_out    fp32 [n][k]                             (written)
+ */
+int qw_unpack(int bits, int64_t group, int64_t n, int64_t k,
+              const uint8_t* payload, const float* scales, float* w_out,
+              void* stream);
+
+/*
+ * Dequantizing GEMV (decode), fp32:
+ *   x  fp32 [m][k]  (read),   y  fp32 [m][n]  (written),   0 <= m <= 8.
+ * Any group dividing n*k is accepted; groups with k % group == 0 and
+ * group % 32 == 0 (int4) / group % 16 == 0 (int8), or group % k == 0, take
+ * the streaming kernel.
+ */
+int qw_gemv(int bits, int64_t group, int64_t n, int64_t k,
+            const uint8_t* payload, const float* scales,
+            int64_t m, const float* x, float* y, void* stream);
+
+/*
+ * Dequantizing GEMM (prefill), bf16 matrix cores, fp32 accumulate:
+ *   x_bf16  bf16 bit patterns [m][k]  (read),   y  fp32 [m][n]  (written).
+ * Any group dividing n*k is accepted; k % 64 == 0 with k % group == 0 and
+ * group % 32 == 0 (or group % k == 0) takes the MFMA kernel.
+ */
+int qw_gemm(int bits, int64_t group, int64_t n, int64_t k,
+            const uint8_t* payload, const float* scales,
+            int64_t m, const uint16_t* x_bf16, float* y, void* stream);
+
+/*
+ * Diagnostic: which kernel family a call with these arguments would take
+ * (1 = streaming/tiled fast kernel, 2 = block-per-group kernel, 3 = generic
+ * kernel) or a negative status for invalid arguments.  `op`: 0 quantize_pack
+ * (a = w, b = payload), 1 unpack (a = payload, b = w_out), 2 gemv (a =
+ * payload, b = x), 3 gemm (a = payload, b = x_bf16).  Enqueues nothing.
+ */
+int qw_debug_path(int op, int bits, int64_t group, int64_t n, int64_t k,
+                  const void* a, const void* b);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QW_H */

@@ -1,0 +1,62 @@
+"""Build libqw.so (the HIP kernels and the C ABI) in-tree for gfx950.
+
+Every source is compiled by hipcc for gfx950 only, without fast-math and
+without denormal flushing (bit-exact quantization needs IEEE fp32 division,
+round-half-even and preserved fp32 subnormals), and with packed-fp32
+instructions disabled.
+"""
+
+import concurrent.futures as cf
+import os
+import subprocess
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(HERE, "_build")
+LIB = os.path.join(HERE, "libqw.so")
+SOURCES = ["qw_api.hip", "quantize.hip", "gemv.hip", "gemm.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-fno-fast-math", "-fno-gpu-flush-denormals-to-zero",
+    "-Wall", "-Wno-unused-function",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    # hipcc's host pass warns that it does not know the packed-fp32 feature
+    err = "\n".join(l for l in r.stderr.splitlines()
+                    if "packed-fp32-ops" not in l and l.strip())
+    if r.returncode != 0:
+        raise RuntimeError(f"command failed ({r.returncode}): {' '.join(cmd)}\n{err}")
+    return err
+
+
+def build(verbose=False, save_temps=False):
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    jobs = []
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+        for src in SOURCES:
+            obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+            objs.append(obj)
+            extra = ["--save-temps"] if save_temps else []
+            cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+            jobs.append(ex.submit(_run, cmd))
+        for j in jobs:
+            msg = j.result()
+            if verbose and msg:
+                print(msg)
+    tmp = LIB + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,132 @@
+// C ABI of libqw (declared in include/qw.h): argument validation and
+// dispatch to the HIP kernels.  No allocation, no synchronization.
+#include <string.h>
+
+#include "../../include/qw.h"
+#include "qw_internal.h"
+
+namespace {
+
+thread_local char g_last_error[256] = {0};
+
+int record(hipError_t e) {
+  if (e == hipSuccess) return QW_OK;
+  strncpy(g_last_error, hipGetErrorString(e), sizeof(g_last_error) - 1);
+  g_last_error[sizeof(g_last_error) - 1] = 0;
+  return QW_EHIP;
+}
+
+bool mul_overflows(int64_t a, int64_t b) {
+  return a != 0 && b > INT64_MAX / 4 / a;  // keep headroom for byte counts
+}
+
+// Validates bits / group / shape; fills `mt` on success.
+int check_mat(int bits, int64_t group, int64_t n, int64_t k, qw::Mat* mt) {
+  if (bits != 4 && bits != 8) return QW_EBITS;
+  if (n < 0 || k < 0 || mul_overflows(n, k)) return QW_ESHAPE;
+  if (group < 1) return QW_EGROUP;
+  const int64_t count = n * k;
+  if (count % group != 0) return QW_EGROUP;
+  if (bits == 4 && count % 2 != 0) return QW_ESHAPE;
+  mt->bits = bits;
+  mt->group = group;
+  mt->n = n;
+  mt->k = k;
+  return QW_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t qw_payload_bytes(int bits, int64_t n, int64_t k) {
+  if ((bits != 4 && bits != 8) || n < 0 || k < 0 || mul_overflows(n, k)) return -1;
+  if (bits == 4 && (n * k) % 2 != 0) return -1;
+  return n * k * bits / 8;
+}
+
+int64_t qw_num_scales(int64_t group, int64_t n, int64_t k) {
+  if (group < 1 || n < 0 || k < 0 || mul_overflows(n, k) || (n * k) % group != 0) return -1;
+  return n * k / group;
+}
+
+const char* qw_status_string(int status) {
+  switch (status) {
+    case QW_OK: return "ok";
+    case QW_EBITS: return "bits must be 4 or 8";
+    case QW_EGROUP: return "group must be >= 1 and divide n*k";
+    case QW_ESHAPE: return "invalid shape (negative, overflowing, or odd element count for int4)";
+    case QW_EM: return "m out of range";
+    case QW_ENULL: return "required pointer is NULL";
+    case QW_EHIP: return "HIP launch failed (see qw_last_error)";
+    case QW_ECOUNT: return "invalid batch count or descriptor";
+    default: return "unknown status";
+  }
+}
+
+const char* qw_last_error(void) { return g_last_error; }
+
+int qw_quantize_pack(int bits, int64_t group, int64_t n, int64_t k, const float* w,
+                     uint8_t* payload, float* scales, void* stream) {
+  qw::Mat mt;
+  int st = check_mat(bits, group, n, k, &mt);
+  if (st != QW_OK) return st;
+  if (n * k == 0) return QW_OK;
+  if (!w || !payload || !scales) return QW_ENULL;
+  return record(qw::launch_quantize_pack(mt, w, payload, scales, (hipStream_t)stream));
+}
+
+int qw_unpack(int bits, int64_t group, int64_t n, int64_t k, const uint8_t* payload,
+              const float* scales, float* w_out, void* stream) {
+  qw::Mat mt;
+  int st = check_mat(bits, group, n, k, &mt);
+  if (st != QW_OK) return st;
+  if (n * k == 0) return QW_OK;
+  if (!payload || !scales || !w_out) return QW_ENULL;
+  return record(qw::launch_unpack(mt, payload, scales, w_out, (hipStream_t)stream));
+}
+
+int qw_gemv(int bits, int64_t group, int64_t n, int64_t k, const uint8_t* payload,
+            const float* scales, int64_t m, const float* x, float* y, void* stream) {
+  qw::Mat mt;
+  int st = check_mat(bits, group, n, k, &mt);
+  if (st != QW_OK) return st;
+  if (m < 0 || m > 8) return QW_EM;
+  if (m == 0 || n == 0) return QW_OK;
+  if (!y) return QW_ENULL;
+  if (k == 0) return record(qw::launch_fill_zero(y, m * n, (hipStream_t)stream));
+  if (!payload || !scales || !x) return QW_ENULL;
+  return record(qw::launch_gemv(mt, payload, scales, (int)m, x, y, (hipStream_t)stream));
+}
+
+int qw_gemm(int bits, int64_t group, int64_t n, int64_t k, const uint8_t* payload,
+            const float* scales, int64_t m, const uint16_t* x_bf16, float* y, void* stream) {
+  qw::Mat mt;
+  int st = check_mat(bits, group, n, k, &mt);
+  if (st != QW_OK) return st;
+  if (m < 0 || mul_overflows(m, n) || mul_overflows(m, k)) return QW_EM;
+  if (m == 0 || n == 0) return QW_OK;
+  if (!y) return QW_ENULL;
+  if (k == 0) return record(qw::launch_fill_zero(y, m * n, (hipStream_t)stream));
+  if (!payload || !scales || !x_bf16) return QW_ENULL;
+  return record(qw::launch_gemm(mt, payload, scales, m, x_bf16, y, (hipStream_t)stream));
+}
+
+// Which kernel family a call with these arguments would take (1 = fast,
+// 2 = block, 3 = generic; negative = invalid arguments).  Used by the tests
+// to make sure every family is exercised.
+int qw_debug_path(int op, int bits, int64_t group, int64_t n, int64_t k, const void* a,
+                  const void* b) {
+  qw::Mat mt;
+  int st = check_mat(bits, group, n, k, &mt);
+  if (st != QW_OK) return st;
+  switch (op) {
+    case 0: return qw::quantize_path(mt, (const float*)a, (const uint8_t*)b);
+    case 1: return qw::unpack_path(mt, (const uint8_t*)a, (const float*)b);
+    case 2: return qw::gemv_path(mt, (const uint8_t*)a, (const float*)b);
+    case 3: return qw::gemm_path(mt, (const uint8_t*)a, (const uint16_t*)b);
+    default: return QW_ECOUNT;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,40 @@
+// Internal interfaces between the C ABI (qw_api.hip) and the kernel files.
+// Not installed; the public interface is include/qw.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qw {
+
+// Problem description after validation by the C ABI.
+struct Mat {
+  int bits;        // 4 or 8
+  int64_t group;   // elements per scale, divides n*k
+  int64_t n, k;    // rows (output channels), row length (reduction axis)
+};
+
+inline bool aligned(const void* p, uintptr_t a) {
+  return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+// Each launcher enqueues on `stream` and returns hipSuccess or the launch
+// error.  Shapes are already validated and non-empty.
+hipError_t launch_quantize_pack(const Mat& mt, const float* w, uint8_t* payload,
+                                float* scales, hipStream_t stream);
+hipError_t launch_unpack(const Mat& mt, const uint8_t* payload,
+                         const float* scales, float* w_out, hipStream_t stream);
+hipError_t launch_gemv(const Mat& mt, const uint8_t* payload, const float* scales,
+                       int m, const float* x, float* y, hipStream_t stream);
+hipError_t launch_gemm(const Mat& mt, const uint8_t* payload, const float* scales,
+                       int64_t m, const uint16_t* x, float* y, hipStream_t stream);
+hipError_t launch_fill_zero(float* y, int64_t count, hipStream_t stream);
+
+// Which kernel family a call takes (exposed for tests through qw_debug_path).
+enum Path { PATH_NONE = 0, PATH_FAST = 1, PATH_BLOCK = 2, PATH_GENERIC = 3 };
+int quantize_path(const Mat& mt, const float* w, const uint8_t* payload);
+int unpack_path(const Mat& mt, const uint8_t* payload, const float* w_out);
+int gemv_path(const Mat& mt, const uint8_t* payload, const float* x);
+int gemm_path(const Mat& mt, const uint8_t* payload, const uint16_t* x);
+
+}  // namespace qw

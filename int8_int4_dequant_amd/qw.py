@@ -1,0 +1,194 @@
+"""Thin Python binding of libqw (include/qw.h).
+
+Argument marshalling only: every step of quantization, unpacking and the
+products runs in the HIP kernels of libqw.so.  PyTorch provides device
+memory and the current HIP stream.  If the library has not been built this
+module raises; there is no CPU fallback.
+
+Low-level functions carry the C names (``qw_quantize_pack``, ``qw_unpack``,
+``qw_gemv``, ``qw_gemm``) and take preallocated tensors; the convenience
+layer (``quantize_pack``, ``unpack``, ``gemv``, ``gemm``) allocates outputs
+and returns a record shaped like the pages' ``pack`` result:
+``{bits, group, shape, payload, scales}``.
+"""
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqw.so")
+
+QW_OK = 0
+STATUS_NAMES = {0: "QW_OK", -1: "QW_EBITS", -2: "QW_EGROUP", -3: "QW_ESHAPE", -4: "QW_EM",
+                -5: "QW_ENULL", -6: "QW_EHIP", -7: "QW_ECOUNT"}
+
+#: symbols declared in include/qw.h
+EXPORTS = ["qw_payload_bytes", "qw_num_scales", "qw_status_string", "qw_last_error",
+           "qw_quantize_pack", "qw_unpack", "qw_gemv", "qw_gemm", "qw_debug_path"]
+
+_lib = None
+
+
+class QwError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        msg = f"{what}: {STATUS_NAMES.get(status, status)} ({_text(status)})"
+        if status == -6:
+            msg += f": {_lib.qw_last_error().decode()}"
+        super().__init__(msg)
+
+
+def _text(status):
+    return _lib.qw_status_string(status).decode() if _lib else str(status)
+
+
+def lib():
+    """Load libqw.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built; run __graft_entry__.build() first")
+    L = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p
+    L.qw_payload_bytes.argtypes = [i32, i64, i64]
+    L.qw_payload_bytes.restype = i64
+    L.qw_num_scales.argtypes = [i64, i64, i64]
+    L.qw_num_scales.restype = i64
+    L.qw_status_string.argtypes = [i32]
+    L.qw_status_string.restype = ctypes.c_char_p
+    L.qw_last_error.argtypes = []
+    L.qw_last_error.restype = ctypes.c_char_p
+    L.qw_quantize_pack.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp]
+    L.qw_quantize_pack.restype = i32
+    L.qw_unpack.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp]
+    L.qw_unpack.restype = i32
+    L.qw_gemv.argtypes = [i32, i64, i64, i64, vp, vp, i64, vp, vp, vp]
+    L.qw_gemv.restype = i32
+    L.qw_gemm.argtypes = [i32, i64, i64, i64, vp, vp, i64, vp, vp, vp]
+    L.qw_gemm.restype = i32
+    L.qw_debug_path.argtypes = [i32, i32, i64, i64, i64, vp, vp]
+    L.qw_debug_path.restype = i32
+    _lib = L
+    return L
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        return t  # raw integer address
+    if t.numel() and not t.is_cuda:
+        raise ValueError("libqw takes device tensors")
+    return t.data_ptr() if t.numel() else None
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _check(status, what):
+    if status != QW_OK:
+        raise QwError(status, what)
+
+
+# ------------------------------------------------------------ C-name layer
+
+
+def qw_payload_bytes(bits, n, k):
+    return lib().qw_payload_bytes(bits, n, k)
+
+
+def qw_num_scales(group, n, k):
+    return lib().qw_num_scales(group, n, k)
+
+
+def qw_quantize_pack(bits, group, n, k, w, payload, scales, stream=None):
+    return lib().qw_quantize_pack(bits, group, n, k, _ptr(w), _ptr(payload), _ptr(scales),
+                                  _stream(stream))
+
+
+def qw_unpack(bits, group, n, k, payload, scales, w_out, stream=None):
+    return lib().qw_unpack(bits, group, n, k, _ptr(payload), _ptr(scales), _ptr(w_out),
+                           _stream(stream))
+
+
+def qw_gemv(bits, group, n, k, payload, scales, m, x, y, stream=None):
+    return lib().qw_gemv(bits, group, n, k, _ptr(payload), _ptr(scales), m, _ptr(x), _ptr(y),
+                         _stream(stream))
+
+
+def qw_gemm(bits, group, n, k, payload, scales, m, x_bf16, y, stream=None):
+    return lib().qw_gemm(bits, group, n, k, _ptr(payload), _ptr(scales), m, _ptr(x_bf16),
+                         _ptr(y), _stream(stream))
+
+
+def qw_debug_path(op, bits, group, n, k, a=None, b=None):
+    return lib().qw_debug_path(op, bits, group, n, k, _ptr(a), _ptr(b))
+
+
+# -------------------------------------------------------- convenience layer
+
+
+def _nk(shape):
+    if len(shape) != 2:
+        raise ValueError("weights are 2-D [n][k]")
+    return int(shape[0]), int(shape[1])
+
+
+def quantize_pack(w, bits, group, stream=None):
+    """Quantize a contiguous fp32 device tensor [n][k]; returns a record
+    ``{bits, group, shape, payload (uint8), scales (float32)}``."""
+    if w.dtype != torch.float32 or not w.is_contiguous():
+        raise ValueError("w must be a contiguous float32 tensor")
+    n, k = _nk(w.shape)
+    nb = lib().qw_payload_bytes(bits, n, k)
+    ns = lib().qw_num_scales(group, n, k)
+    if nb < 0 or ns < 0:
+        _check(QW_EBITS if bits not in (4, 8) else -2 if ns < 0 else -3, "quantize_pack")
+    payload = torch.empty(nb, dtype=torch.uint8, device=w.device)
+    scales = torch.empty(ns, dtype=torch.float32, device=w.device)
+    _check(qw_quantize_pack(bits, group, n, k, w, payload, scales, stream), "qw_quantize_pack")
+    return dict(bits=bits, group=group, shape=[n, k], payload=payload, scales=scales)
+
+
+def unpack(rec, out=None, stream=None):
+    n, k = _nk(rec["shape"])
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.float32, device=rec["payload"].device)
+    _check(qw_unpack(rec["bits"], rec["group"], n, k, rec["payload"], rec["scales"], out,
+                     stream), "qw_unpack")
+    return out
+
+
+def gemv(rec, x, out=None, stream=None):
+    """fp32 x [m][k] (m <= 8) times the quantized weight; returns y [m][n]."""
+    n, k = _nk(rec["shape"])
+    if x.dtype != torch.float32 or not x.is_contiguous() or x.dim() != 2 or x.shape[1] != k:
+        raise ValueError("x must be a contiguous float32 [m][k] tensor")
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _check(qw_gemv(rec["bits"], rec["group"], n, k, rec["payload"], rec["scales"], m, x, out,
+                   stream), "qw_gemv")
+    return out
+
+
+def gemm(rec, x_bf16, out=None, stream=None):
+    """bf16 x [m][k] (torch.bfloat16, or int16/uint16 bit patterns) times the
+    quantized weight on the matrix cores; returns fp32 y [m][n]."""
+    n, k = _nk(rec["shape"])
+    if x_bf16.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise ValueError("x must hold bf16 values or bit patterns")
+    if not x_bf16.is_contiguous() or x_bf16.dim() != 2 or x_bf16.shape[1] != k:
+        raise ValueError("x must be a contiguous [m][k] tensor")
+    m = x_bf16.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=x_bf16.device)
+    _check(qw_gemm(rec["bits"], rec["group"], n, k, rec["payload"], rec["scales"], m, x_bf16,
+                   out, stream), "qw_gemm")
+    return out

@@ -1,0 +1,106 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, computes sizes, and rejects invalid arguments before it
+touches a GPU.  No compute call is made here."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from int8_int4_dequant_amd import qw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "qw.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(qw_[a-z_]+)\s*\(", txt)))
+
+
+def test_header_lists_the_boundary():
+    fns = header_functions()
+    for name in ("qw_quantize_pack", "qw_unpack", "qw_gemv", "qw_gemm"):
+        assert name in fns
+    assert sorted(qw.EXPORTS) == fns
+
+
+def test_library_exports_every_declared_symbol():
+    L = qw.lib()
+    raw = ctypes.CDLL(qw.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(L, name), name
+        assert ctypes.cast(getattr(raw, name), ctypes.c_void_p).value
+
+
+def test_sizes():
+    L = qw.lib()
+    assert L.qw_payload_bytes(4, 11008, 4096) == 11008 * 4096 // 2
+    assert L.qw_payload_bytes(8, 4096, 4096) == 4096 * 4096
+    assert L.qw_payload_bytes(4, 3, 3) == -1
+    assert L.qw_payload_bytes(5, 4, 4) == -1
+    assert L.qw_num_scales(128, 11008, 4096) == 11008 * 32
+    assert L.qw_num_scales(3, 4, 4) == -1
+    assert L.qw_num_scales(0, 4, 4) == -1
+    # the 7B stack of 224 matrices at int4 group 32
+    total_p = total_s = 0
+    for n, k in [(4096, 4096)] * 4 + [(11008, 4096)] * 2 + [(4096, 11008)]:
+        total_p += L.qw_payload_bytes(4, n, k)
+        total_s += 4 * L.qw_num_scales(32, n, k)
+    assert 32 * total_p == 3_238_002_688
+    assert 32 * total_s == 809_500_672
+
+
+def test_status_strings():
+    L = qw.lib()
+    for st in range(-7, 1):
+        assert L.qw_status_string(st)
+    assert L.qw_status_string(0) == b"ok"
+
+
+def _q(bits, group, n, k, w=None, p=None, s=None):
+    return qw.lib().qw_quantize_pack(bits, group, n, k, w, p, s, None)
+
+
+def test_validation_before_any_launch():
+    L = qw.lib()
+    assert _q(3, 32, 4, 32) == -1
+    assert _q(8, 0, 4, 32) == -2
+    assert _q(8, 33, 4, 32) == -2
+    assert _q(4, 1, 3, 3) == -3
+    assert _q(8, 32, -1, 32) == -3
+    assert _q(8, 32, 4, 32) == -5          # null pointers with real work
+    assert _q(8, 32, 0, 32) == 0           # empty: nothing to do
+    assert _q(8, 32, 4, 0) == 0
+    assert L.qw_unpack(8, 32, 4, 32, None, None, None, None) == -5
+    assert L.qw_gemv(8, 32, 4, 32, None, None, 9, None, None, None) == -4
+    assert L.qw_gemv(8, 32, 4, 32, None, None, -1, None, None, None) == -4
+    assert L.qw_gemv(8, 32, 4, 32, None, None, 0, None, None, None) == 0
+    assert L.qw_gemv(8, 32, 4, 32, None, None, 1, None, None, None) == -5
+    assert L.qw_gemm(8, 32, 4, 32, None, None, -1, None, None, None) == -4
+    assert L.qw_gemm(4, 32, 4, 32, None, None, 0, None, None, None) == 0
+    assert L.qw_gemm(4, 32, 4, 32, None, None, 5, None, None, None) == -5
+
+
+@pytest.mark.parametrize("bits,group,n,k,al,expect", [
+    (4, 32, 64, 256, 16, 1), (8, 128, 64, 256, 16, 1), (8, 512, 4, 512, 16, 1),
+    (8, 4096, 8, 4096, 16, 2), (4, 11008, 4, 11008, 16, 2), (4, 1024, 4, 1024, 16, 2),
+    (4, 3, 4, 6, 16, 3), (8, 1, 4, 8, 16, 3), (4, 4096 * 16, 16, 4096, 16, 3),
+    (4, 32, 64, 256, 4, 3),
+])
+def test_quantize_dispatch(bits, group, n, k, al, expect):
+    base = 1 << 20
+    assert qw.lib().qw_debug_path(0, bits, group, n, k, base + (al % 16), base) == expect
+
+
+@pytest.mark.parametrize("op,bits,group,n,k,expect", [
+    (2, 4, 128, 4096, 11008, 1), (2, 8, 4096, 4096, 4096, 1), (2, 4, 32, 11008, 4096, 1),
+    (2, 4, 16, 64, 256, 3), (2, 4, 32, 8, 48, 3), (2, 4, 4096 * 8, 8, 4096, 1),
+    (2, 4, 3, 8, 48, 3),
+    (3, 4, 128, 28672, 8192, 1), (3, 8, 32, 64, 256, 1), (3, 4, 16, 64, 256, 3),
+    (3, 4, 32, 64, 96, 3),
+])
+def test_product_dispatch(op, bits, group, n, k, expect):
+    base = 1 << 20
+    assert qw.lib().qw_debug_path(op, bits, group, n, k, base, base) == expect

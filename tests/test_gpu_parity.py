@@ -1,0 +1,304 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Bars: payload, scales and unpacked weights bit-identical; GEMV outputs within
+1e-5 * sum|x * w_hat| and GEMM outputs within 8e-3 * sum|x * w_hat| per
+element.  Small cases compare every element; the full-size workloads compare
+every byte of the quantization where the oracle is quick enough, otherwise
+sampled rows (groups never cross rows there, so a row's payload depends on
+that row only), in the same launch configuration the benchmark times.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from int8_int4_dequant_amd import inputs, qw
+
+pytestmark = pytest.mark.gpu
+
+GEMV_TOL = 1e-5
+GEMM_TOL = 8e-3
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda")
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def same_bits(a, b):
+    a = np.ascontiguousarray(a)
+    b = np.ascontiguousarray(b)
+    return a.shape == b.shape and np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
+def quant_both(w, bits, group):
+    ref = oracle.quantize_pack(w, bits, group)
+    rec = qw.quantize_pack(dev(w), bits, group)
+    assert same_bits(host(rec["scales"]), ref["scales"]), "scales differ"
+    assert same_bits(host(rec["payload"]), ref["payload"]), "payload differs"
+    return ref, rec
+
+
+def check_unpack(ref, rec):
+    assert same_bits(host(qw.unpack(rec)), oracle.unpack(ref)), "unpack differs"
+
+
+def check_gemv(ref, rec, x):
+    y = host(qw.gemv(rec, dev(x)))
+    yr = oracle.gemv_ref(ref, x)
+    B = oracle.error_base(ref, x)
+    err = np.abs(y.astype(np.float64) - yr)
+    assert np.all(err <= GEMV_TOL * B), f"gemv max err/B = {np.max(err / np.maximum(B, 1e-300))}"
+    return y
+
+
+def check_gemm(ref, rec, xb):
+    y = host(qw.gemm(rec, dev(xb.view(np.int16))))
+    yr = oracle.gemm_ref(ref, xb)
+    B = oracle.error_base(ref, oracle.bf16_bits_to_f32(xb))
+    err = np.abs(y.astype(np.float64) - yr)
+    assert np.all(err <= GEMM_TOL * B), f"gemm max err/B = {np.max(err / np.maximum(B, 1e-300))}"
+    return y
+
+
+# ------------------------------------------------------------ small cases
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_tiny_config(bits):
+    w, x = inputs.c1_weight(), inputs.c1_x()
+    ref, rec = quant_both(w, bits, 32)
+    check_unpack(ref, rec)
+    check_gemv(ref, rec, x)
+
+
+def test_worked_example_on_gpu():
+    w = np.array([[0.12, -0.45, 0.33, -0.08, 0.51, -0.22, 0.07, -0.37]], np.float32)
+    for bits, hexp in ((8, "1e9052ec7fc911a4"), (4, "2a7d5f39")):
+        ref, rec = quant_both(w, bits, 8)
+        assert host(rec["payload"]).tobytes().hex() == hexp
+        check_unpack(ref, rec)
+
+
+def test_ties_on_gpu():
+    w = inputs.tie_vector().reshape(1, 8)
+    ref, rec = quant_both(w, 4, 8)
+    assert host(rec["payload"]).tobytes().hex() == "afc688ea"
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("group", [32, 128])
+def test_near_ties(bits, group):
+    w = inputs.near_tie_matrix(seed=100 + bits + group, bits=bits, rows=512, group=group)
+    ref, rec = quant_both(w.reshape(64, -1), bits, group)
+    check_unpack(ref, rec)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_subnormal_and_zero_groups(bits):
+    w = np.concatenate([inputs.subnormal_matrix(3, 16, 64),
+                        np.zeros((4, 64), np.float32),
+                        inputs.weight(4, 12, 64, 1e-3)], axis=0)
+    w[18, 5] = np.float32(1e-45)  # smallest subnormal alone in a group
+    for group in (32, 64):
+        ref, rec = quant_both(w, bits, group)
+        check_unpack(ref, rec)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+@pytest.mark.parametrize("group,n,k", [
+    (8, 16, 64), (16, 16, 64), (64, 8, 256), (256, 8, 512), (512, 6, 1024),  # subgroup
+    (1024, 6, 2048), (4096, 4, 4096), (11008, 3, 11008), (2048, 5, 6144),   # block
+    (1, 4, 16), (6, 4, 48), (24, 5, 48), (4 * 64, 4, 64), (3 * 96, 3, 96),   # generic
+])
+def test_group_families(bits, group, n, k):
+    w = inputs.weight(group + n + k, n, k, 0.3)
+    ref, rec = quant_both(w, bits, group)
+    check_unpack(ref, rec)
+    if group % k == 0 or k % group == 0:
+        x = inputs.activations(7, 3, k)
+        check_gemv(ref, rec, x)
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_per_tensor_group(bits):
+    w = inputs.weight(31, 24, 256, 0.2)
+    ref, rec = quant_both(w, bits, w.size)
+    check_unpack(ref, rec)
+    check_gemv(ref, rec, inputs.activations(8, 2, 256))
+    check_gemm(ref, rec, inputs.bf16_activations(9, 5, 256))
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_unaligned_pointers_take_generic_kernels(bits):
+    n, k, group = 24, 128, 32
+    w = inputs.weight(5, n, k, 0.1)
+    ref = oracle.quantize_pack(w, bits, group)
+    wd = torch.empty(n * k + 1, dtype=torch.float32, device="cuda")
+    wd[1:] = dev(w).reshape(-1)
+    nb = n * k * bits // 8
+    pd = torch.zeros(nb + 1, dtype=torch.uint8, device="cuda")
+    sd = torch.zeros(n * k // group + 1, dtype=torch.float32, device="cuda")
+    assert qw.qw_debug_path(0, bits, group, n, k, wd[1:], pd[1:]) == 3
+    assert qw.qw_quantize_pack(bits, group, n, k, wd[1:], pd[1:], sd[1:]) == 0
+    assert same_bits(host(pd[1:]), ref["payload"])
+    assert same_bits(host(sd[1:]), ref["scales"])
+    out = torch.zeros(n * k + 1, dtype=torch.float32, device="cuda")
+    assert qw.qw_unpack(bits, group, n, k, pd[1:], sd[1:], out[1:]) == 0
+    assert same_bits(host(out[1:]), oracle.unpack(ref).reshape(-1))
+    x = inputs.activations(6, 2, k)
+    xd = torch.zeros(2 * k + 1, dtype=torch.float32, device="cuda")
+    xd[1:] = dev(x).reshape(-1)
+    y = torch.zeros(2 * n, dtype=torch.float32, device="cuda")
+    assert qw.qw_gemv(bits, group, n, k, pd[1:], sd[1:], 2, xd[1:], y) == 0
+    B = oracle.error_base(ref, x)
+    assert np.all(np.abs(host(y).reshape(2, n) - oracle.gemv_ref(ref, x)) <= GEMV_TOL * B)
+
+
+# ------------------------------------------------------------------- GEMV
+
+
+@pytest.mark.parametrize("bits,group", [(4, 32), (4, 128), (8, 16), (8, 4096 // 4)])
+@pytest.mark.parametrize("n,k", [(13, 4096), (77, 11008), (200, 1024), (8, 32 * 3)])
+def test_gemv_shapes_all_m(bits, group, n, k):
+    if k % group:
+        pytest.skip("group does not divide k")
+    w = inputs.weight(n * 7 + k, n, k, 0.02)
+    ref, rec = quant_both(w, bits, group)
+    for m in range(1, 9):
+        check_gemv(ref, rec, inputs.activations(m * 13 + n, m, k))
+
+
+def test_gemv_k_zero_and_empty():
+    rec = dict(bits=4, group=32, shape=[5, 0],
+               payload=torch.empty(0, dtype=torch.uint8, device="cuda"),
+               scales=torch.empty(0, dtype=torch.float32, device="cuda"))
+    y = torch.full((3, 5), 7.0, device="cuda")
+    x = torch.empty((3, 0), dtype=torch.float32, device="cuda")
+    assert qw.qw_gemv(4, 32, 5, 0, rec["payload"], rec["scales"], 3, x, y) == 0
+    assert np.all(host(y) == 0)
+    w = np.zeros((0, 64), np.float32)
+    rec = qw.quantize_pack(dev(w), 4, 32)
+    assert rec["payload"].numel() == 0 and rec["scales"].numel() == 0
+
+
+def test_gemv_deterministic():
+    w = inputs.weight(1, 300, 4096, 0.02)
+    rec = qw.quantize_pack(dev(w), 4, 128)
+    x = dev(inputs.activations(2, 4, 4096))
+    y1 = host(qw.gemv(rec, x))
+    y2 = host(qw.gemv(rec, x))
+    assert same_bits(y1, y2)
+
+
+# ------------------------------------------------------------------- GEMM
+
+
+@pytest.mark.parametrize("bits,group", [(4, 128), (4, 32), (8, 64), (8, 128)])
+@pytest.mark.parametrize("m,n,k", [(1, 256, 512), (9, 300, 256), (40, 77, 1024),
+                                   (300, 520, 512), (257, 2048, 128)])
+def test_gemm_shapes(bits, group, m, n, k):
+    w = inputs.weight(m + n + k, n, k, 0.015)
+    ref, rec = quant_both(w, bits, group)
+    check_gemm(ref, rec, inputs.bf16_activations(m * 3 + 1, m, k))
+
+
+def test_gemm_generic_shape():
+    w = inputs.weight(3, 33, 96, 0.1)
+    ref, rec = quant_both(w, 4, 16)
+    assert qw.qw_debug_path(3, 4, 16, 33, 96, rec["payload"], rec["payload"]) == 3
+    check_gemm(ref, rec, inputs.bf16_activations(4, 7, 96))
+
+
+def test_codes_path_agrees_with_dequantized_path():
+    # rows 1, 9, 40, 300 as in the Smallem tests: the GEMM (dequantized
+    # operand) and, at one row, the GEMV (codes) against unpack + fp64.
+    w = inputs.weight(77, 256, 1024, 0.02)
+    ref, rec = quant_both(w, 4, 32)
+    w_hat = host(qw.unpack(rec)).astype(np.float64)
+    for m in (1, 9, 40, 300):
+        xb = inputs.bf16_activations(500 + m, m, 1024)
+        xf = oracle.bf16_bits_to_f32(xb).astype(np.float64)
+        y = host(qw.gemm(rec, dev(xb.view(np.int16))))
+        B = np.abs(xf) @ np.abs(w_hat).T
+        assert np.all(np.abs(y - xf @ w_hat.T) <= GEMM_TOL * B)
+        if m == 1:
+            yv = host(qw.gemv(rec, dev(xf.astype(np.float32))))
+            assert np.all(np.abs(yv - xf @ w_hat.T) <= GEMV_TOL * B)
+
+
+def test_gemm_deterministic():
+    w = inputs.weight(9, 512, 1024, 0.02)
+    rec = qw.quantize_pack(dev(w), 4, 128)
+    xb = dev(inputs.bf16_activations(3, 300, 1024).view(np.int16))
+    assert same_bits(host(qw.gemm(rec, xb)), host(qw.gemm(rec, xb)))
+
+
+# ------------------------------------------------------ full-size configs
+
+
+def test_config2_int8_per_channel():
+    w, x = inputs.c2_weight(), inputs.c2_x()
+    ref, rec = quant_both(w, 8, 4096)
+    check_unpack(ref, rec)
+    check_gemv(ref, rec, x)
+
+
+@pytest.mark.parametrize("j", [0, 1])
+def test_config3_int4_g128(j):
+    w = inputs.c3_weight(j)
+    ref, rec = quant_both(w, 4, 128)
+    for m in (1, 4, 8):
+        check_gemv(ref, rec, inputs.c3_x(j, m))
+
+
+def _rows_check(rec, w, bits, group, rows, x=None, y=None):
+    """Oracle on selected rows only (groups lie inside rows)."""
+    n, k = w.shape
+    ref = oracle.quantize_pack(w[rows], bits, group)
+    pb = k * bits // 8
+    payload = host(rec["payload"]).reshape(n, pb)[rows]
+    scales = host(rec["scales"]).reshape(n, k // group)[rows]
+    assert same_bits(payload.reshape(-1), ref["payload"])
+    assert same_bits(scales.reshape(-1), ref["scales"])
+    if x is not None:
+        yr = oracle.gemv_ref(ref, x)
+        B = oracle.error_base(ref, x)
+        assert np.all(np.abs(y[:, rows] - yr) <= GEMV_TOL * B)
+
+
+@pytest.mark.parametrize("layer", [0, 31])
+def test_config4_layers_sampled(layer):
+    rng = np.random.default_rng(layer)
+    for slot, (tag, n, k) in enumerate(inputs.C4_SLOTS):
+        w = inputs.c4_weight(layer, slot)
+        rec = qw.quantize_pack(dev(w), 4, 32)
+        x = inputs.c4_x(k)
+        y = host(qw.gemv(rec, dev(x)))
+        rows = np.sort(rng.choice(n, size=96, replace=False))
+        rows[0], rows[-1] = 0, n - 1
+        _rows_check(rec, w, 4, 32, rows, x, y)
+
+
+def test_config5_gemm_sampled():
+    w = inputs.c5_weight()
+    n, k = w.shape
+    rec = qw.quantize_pack(dev(w), 4, 128)
+    rng = np.random.default_rng(5)
+    rows = np.sort(rng.choice(n, size=64, replace=False))
+    rows[0], rows[-1] = 0, n - 1
+    _rows_check(rec, w, 4, 128, rows)
+    xb = inputs.c5_x_bf16()
+    y = host(qw.gemm(rec, dev(xb.view(np.int16))))
+    ms = np.sort(rng.choice(xb.shape[0], size=48, replace=False))
+    ms[0], ms[-1] = 0, xb.shape[0] - 1
+    ref = oracle.quantize_pack(w[rows], 4, 128)
+    yr = oracle.gemm_ref(ref, xb[ms])
+    B = oracle.error_base(ref, oracle.bf16_bits_to_f32(xb[ms]))
+    got = y[np.ix_(ms, rows)]
+    assert np.all(np.abs(got - yr) <= GEMM_TOL * B)
