@@ -142,6 +142,8 @@ def main():
         P.append(torch.empty(n * k // 2, dtype=torch.uint8, device=dev))
         S.append(torch.empty(n * k // 32, dtype=torch.float32, device=dev))
         Y.append(torch.empty((1, n), dtype=torch.float32, device=dev))
+        if (i + 1) % 28 == 0:
+            log(f"setup: {i + 1} matrices resident ({time.time() - t0:.1f} s)")
 
     if args.layers == 32:
         inputs.c4_weights_parallel(upload)
@@ -156,23 +158,42 @@ def main():
     gbytes = sum(gemv_bytes(n, k) for n, k in shapes)
     weights = sum(n * k for n, k in shapes)
 
+    # quantize/pack every matrix, then the decode pass: one batched call each
+    # (a few large launches instead of one per matrix)
+    qdescs, nq = qw.make_quant_descs(
+        (4, 32, n, k, W[i], P[i], S[i]) for i, (n, k) in enumerate(shapes))
+    descs, ndesc = qw.make_gemv_descs(
+        (4, 32, n, k, P[i], S[i], xs[k], Y[i]) for i, (n, k) in enumerate(shapes))
+    quant_launches = (nq + 63) // 64
+    gemv_launches = (ndesc + 31) // 32
+
     def run_step(ev=None):
+        if ev is not None:
+            ev[0][0].record(stream)
+        st = L.qw_quantize_pack_batched(nq, qdescs, sptr)
+        if ev is not None:
+            ev[1][0].record(stream)
+        if st:
+            raise RuntimeError(f"qw_quantize_pack_batched failed: {st}")
+        if ev is not None:
+            ev[2][0].record(stream)
+        st = L.qw_gemv_batched(ndesc, descs, 1, sptr)
+        if ev is not None:
+            ev[3][0].record(stream)
+        if st:
+            raise RuntimeError(f"qw_gemv_batched failed: {st}")
+
+    def single_quant_pass():
         for i, (n, k) in enumerate(shapes):
-            if ev is not None:
-                ev[0][i].record(stream)
             st = L.qw_quantize_pack(4, 32, n, k, W[i].data_ptr(), P[i].data_ptr(),
                                     S[i].data_ptr(), sptr)
-            if ev is not None:
-                ev[1][i].record(stream)
             if st:
                 raise RuntimeError(f"qw_quantize_pack failed: {st}")
+
+    def single_gemv_pass():
         for i, (n, k) in enumerate(shapes):
-            if ev is not None:
-                ev[2][i].record(stream)
             st = L.qw_gemv(4, 32, n, k, P[i].data_ptr(), S[i].data_ptr(), 1,
                            xs[k].data_ptr(), Y[i].data_ptr(), sptr)
-            if ev is not None:
-                ev[3][i].record(stream)
             if st:
                 raise RuntimeError(f"qw_gemv failed: {st}")
 
@@ -181,8 +202,7 @@ def main():
     torch.cuda.synchronize()
 
     # ---- timed region: K steps, per-launch HIP events on the launch stream
-    evs = [[[torch.cuda.Event(enable_timing=True) for _ in shapes] for _ in range(4)]
-           for _ in range(args.steps)]
+    evs = [[[torch.cuda.Event(enable_timing=True)] for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for s in range(args.steps):
@@ -190,34 +210,59 @@ def main():
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
 
-    q_ms = sum(evs[s][0][i].elapsed_time(evs[s][1][i]) for s in range(args.steps) for i in range(len(shapes)))
-    g_ms = sum(evs[s][2][i].elapsed_time(evs[s][3][i]) for s in range(args.steps) for i in range(len(shapes)))
-    launches = args.steps * len(shapes)
-    q_avg_us = 1e3 * q_ms / launches
-    g_avg_us = 1e3 * g_ms / launches
+    q_ms = sum(evs[s][0][0].elapsed_time(evs[s][1][0]) for s in range(args.steps))
+    g_ms = sum(evs[s][2][0].elapsed_time(evs[s][3][0]) for s in range(args.steps))
+    q_avg_us = 1e3 * q_ms / (args.steps * quant_launches)
+    g_avg_us = 1e3 * g_ms / (args.steps * gemv_launches)
+
+    # for comparison (not part of the step): the same passes as one launch per matrix
+    def timed(fn):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        fn()
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / args.steps
+
+    single_us = timed(single_gemv_pass)
+    single_q_us = timed(single_quant_pass)
     q_gbs = qbytes * args.steps / (q_ms * 1e-3) / 1e9
     g_gbs = gbytes * args.steps / (g_ms * 1e-3) / 1e9
     ms_per_step = 1e3 * t_total / args.steps
     value = (qbytes + gbytes) / (ms_per_step * 1e-3) / 1e9
-    log(f"step {ms_per_step:.3f} ms; quantize {q_gbs:.0f} GB/s (avg {q_avg_us:.1f} us/launch); "
-        f"gemv {g_gbs:.0f} GB/s (avg {g_avg_us:.2f} us/launch)")
+    log(f"step {ms_per_step:.3f} ms; quantize {q_gbs:.0f} GB/s ({quant_launches} launches, avg "
+        f"{q_avg_us:.1f} us); one quantize launch per matrix: {single_q_us:.1f} us; "
+        f"gemv pass {g_gbs:.0f} GB/s ({1e3 * g_ms / args.steps:.1f} us, {gemv_launches} launches); "
+        f"one launch per matrix: {single_us:.1f} us")
 
     dominant = "quantize_pack" if q_ms >= g_ms else "gemv"
     if dominant == "quantize_pack":
-        ach, per_launch = q_gbs, qbytes / len(shapes)
+        ach, per_launch = q_gbs, qbytes / quant_launches
     else:
-        ach, per_launch = g_gbs, gbytes / len(shapes)
+        ach, per_launch = g_gbs, gbytes / gemv_launches
     roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
-                "kernel": f"qw_{dominant} (int4 g32, 224 launches per step)",
+                "kernel": ("qw_quantize_pack_batched" if dominant == "quantize_pack"
+                           else "qw_gemv_batched") + " (int4 g32, 224 matrices per step)",
                 "algorithmic_bytes_per_launch": round(per_launch),
                 "avg_launch_us": round(q_avg_us if dominant == "quantize_pack" else g_avg_us, 3)}
     parts = {
         "quantize_pack": {"GB/s": round(q_gbs, 1), "frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4),
-                          "avg_launch_us": round(q_avg_us, 3), "bytes_per_step": qbytes},
+                          "entry": "qw_quantize_pack_batched", "launches_per_pass": quant_launches,
+                          "avg_launch_us": round(q_avg_us, 3), "bytes_per_step": qbytes,
+                          "pass_us": round(1e3 * q_ms / args.steps, 1)},
+        "quantize_pack_one_launch_per_matrix": {
+            "pass_us": round(single_q_us, 1),
+            "GB/s": round(qbytes / (single_q_us * 1e-6) / 1e9, 1)},
         "decode_gemv_m1": {"GB/s": round(g_gbs, 1), "frac_hbm": round(g_gbs / HBM_PEAK_GBS, 4),
+                           "entry": "qw_gemv_batched", "launches_per_pass": gemv_launches,
                            "avg_launch_us": round(g_avg_us, 3), "bytes_per_step": gbytes,
-                           "pass_us_kernel_sum": round(1e3 * g_ms / args.steps, 1)},
+                           "pass_us": round(1e3 * g_ms / args.steps, 1)},
+        "decode_gemv_m1_one_launch_per_matrix": {
+            "pass_us": round(single_us, 1),
+            "GB/s": round(gbytes / (single_us * 1e-6) / 1e9, 1)},
     }
 
     # free the stack before the GEMM leg

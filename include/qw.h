@@ -98,6 +98,32 @@ int qw_quantize_pack(int bits, int64_t group, int64_t n, int64_t k,
                      void* stream);
 
 /*
+ * One matrix of a batched quantize/pack (see qw_quantize_pack_batched); the
+ * fields mean what the qw_quantize_pack arguments of the same names mean.
+ */
+typedef struct qw_quant_desc {
+    const float* w;      /* fp32 [n][k] */
+    uint8_t* payload;    /* qw_payload_bytes(bits, n, k) bytes */
+    float* scales;       /* qw_num_scales(group, n, k) floats */
+    int64_t n;
+    int64_t k;
+    int64_t group;
+    int32_t bits;
+    int32_t reserved;    /* must be 0 */
+} qw_quant_desc;
+
+/*
+ * Batched quantize/pack: `count` independent matrices (for instance every
+ * linear layer of a model at load time), each exactly as qw_quantize_pack
+ * would produce it, enqueued as a few large launches instead of one per
+ * matrix.  `descs` is a HOST array read before the call returns; outputs
+ * must not overlap each other or any input.  Every entry is validated
+ * first; on any invalid entry nothing is enqueued and its status (or
+ * QW_ECOUNT for count < 0 / reserved != 0) is returned.
+ */
+int qw_quantize_pack_batched(int count, const qw_quant_desc* descs, void* stream);
+
+/*
  * Unpack: w_out[i][j] = fl32(float(q) * S), bit-identical.
  *   payload, scales as written by qw_quantize_pack   (read)
  *   w_out    fp32 [n][k]                             (written)
@@ -109,13 +135,43 @@ int qw_unpack(int bits, int64_t group, int64_t n, int64_t k,
 /*
  * Dequantizing GEMV (decode), fp32:
  *   x  fp32 [m][k]  (read),   y  fp32 [m][n]  (written),   0 <= m <= 8.
- * Any group dividing n*k is accepted; groups with k % group == 0 and
- * group % 32 == 0 (int4) / group % 16 == 0 (int8), or group % k == 0, take
- * the streaming kernel.
+ * Any group dividing n*k is accepted; with k % 8 == 0 and either
+ * k % group == 0 with group % 8 == 0, or group % k == 0, the streaming
+ * kernel runs.
  */
 int qw_gemv(int bits, int64_t group, int64_t n, int64_t k,
             const uint8_t* payload, const float* scales,
             int64_t m, const float* x, float* y, void* stream);
+
+/*
+ * One matrix of a batched GEMV (see qw_gemv_batched).  Same meaning as the
+ * qw_gemv arguments of the same names; pointers are device pointers.
+ */
+typedef struct qw_gemv_desc {
+    const uint8_t* payload;
+    const float* scales;
+    const float* x;      /* fp32 [m][k] */
+    float* y;            /* fp32 [m][n] */
+    int64_t n;
+    int64_t k;
+    int64_t group;
+    int32_t bits;
+    int32_t reserved;    /* must be 0 */
+} qw_gemv_desc;
+
+/*
+ * Batched dequantizing GEMV: `count` independent products y_i = x_i * W_i^T
+ * with a common m (0 <= m <= 8), each exactly as qw_gemv would compute it,
+ * enqueued as a few launches that stream the weights back to back instead
+ * of one launch per matrix (the fixed cost of many short kernels is what
+ * dominates a decode step otherwise -- page "Huit bits, puis quatre",
+ * section "La vitesse").  `descs` is a HOST array of `count` entries, read
+ * before the call returns.  No y_i may overlap another y_i or any input.
+ * Every entry is validated first; on any invalid entry nothing is enqueued
+ * and the entry's status (or QW_ECOUNT for count < 0 / reserved != 0) is
+ * returned.
+ */
+int qw_gemv_batched(int count, const qw_gemv_desc* descs, int64_t m, void* stream);
 
 /*
  * Dequantizing GEMM (prefill), bf16 matrix cores, fp32 accumulate:

@@ -10,23 +10,29 @@
 // 32 int4 or 16 int8 codes.)
 //
 // Design (HBM-bound for M <= ~4; fp32-FMA bound beyond):
-//   * A block of W waves owns R consecutive output rows.  Its 64*W lanes
-//     split every row into 16-byte chunks (lane t takes chunks t, t+64W, ...),
-//     so each payload load instruction is a fully coalesced 1 KiB run.
-//   * Per chunk a lane loads the R rows' 16 bytes (R loads in flight), the
-//     matching x values (shared by all R rows) and one scale per row.
+//   * One wave per work item = R consecutive rows of one matrix over the
+//     whole row; the waves of a block are independent (no LDS, no barrier),
+//     so a launch over many matrices (qw_gemv_batched) streams the weights.
+//   * Lane l takes the 8-code chunks l, l+64, ... of each of its R rows:
+//     every payload load instruction (4 B int4 / 8 B int8 per lane) is a
+//     contiguous run across the wave, the chunk's 8 x values (two 16-byte
+//     loads, also contiguous across the wave) serve all R rows, and the
+//     group of a chunk is tracked incrementally, without a division.
+//     (Measured alternatives -- 16-byte payload chunks with 128-byte x
+//     slices per lane, x staged in LDS, persistent prefetching waves -- were
+//     slower on gfx950: per-lane 128-byte x slices touch 64 cache lines per
+//     load instruction.)  Generic kernel for any other group or alignment.
 //   * int4 decode: two masks split a dword into low and high nibbles as
 //     bytes 0x0u; v_cvt_pk_f32_fp8 turns two such bytes into u * 2^-9
-//     exactly (an OCP e4m3 byte 0x0u has value u * 2^-9 for u < 16), and
-//     subtracting 8 * 2^-9 gives q * 2^-9 exactly.  int8 decode: one
-//     sign-extending byte conversion per code.
-//   * fp32 FMAs accumulate x * q per chunk; the chunk sum is scaled by S
-//     (and 2^9 for int4) into the row accumulator.  Every product and the
-//     scaling are exact or singly rounded, so the error is within
-//     (chain length) * 2^-24 * sum|x * w_hat| -- well inside 1e-5 of it.
+//     exactly (an OCP e4m3 byte 0x0u has value u * 2^-9 for u < 16) and one
+//     fma gives q = u - 8 exactly.  int8 decode: one sign-extending byte
+//     conversion per code.
+//   * fp32 FMAs accumulate x * q over a chunk (8 terms, one group); the chunk
+//     sum times the group's scale is added to the row accumulator.  Every
+//     product is exact or singly rounded, so the error stays within
+//     (chain length) * 2^-24 * sum|x * w_hat| -- far inside 1e-5 of it.
 //   * The R*M partial sums per lane are reduced across the wave with a
-//     butterfly reduce-scatter (each step halves the values a lane holds),
-//     then across the W waves through LDS.
+//     butterfly reduce-scatter (each step halves the values a lane holds).
 #include "qw_internal.h"
 
 namespace qw {
@@ -114,7 +120,9 @@ constexpr int pow2_at_least(int v) {
 
 // ------------------------------------------------------------ decode helpers
 
-// 8 int4 codes of one dword, in element order, as q * 2^-9 (exact).
+// 8 int4 codes of one dword, in element order, as exact floats q.  An OCP
+// e4m3 byte 0x0u has the value u * 2^-9 for u < 16, so one conversion turns
+// two nibble bytes into u * 2^-9; u * 2^-9 * 512 - 8 = q is exact in an fma.
 __device__ __forceinline__ void decode8_int4(uint32_t w, float (&q)[8]) {
   const uint32_t lo = w & 0x0F0F0F0Fu;         // elements 0, 2, 4, 6 as bytes 0x0u
   const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // elements 1, 3, 5, 7
@@ -122,9 +130,10 @@ __device__ __forceinline__ void decode8_int4(uint32_t w, float (&q)[8]) {
   const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
   const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
   const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
-  constexpr float off = 8.0f / 512.0f;  // the +8 offset in units of 2^-9
-  q[0] = a.x - off; q[2] = a.y - off; q[4] = b.x - off; q[6] = b.y - off;
-  q[1] = c.x - off; q[3] = c.y - off; q[5] = d.x - off; q[7] = d.y - off;
+  q[0] = __builtin_fmaf(a.x, 512.0f, -8.0f); q[2] = __builtin_fmaf(a.y, 512.0f, -8.0f);
+  q[4] = __builtin_fmaf(b.x, 512.0f, -8.0f); q[6] = __builtin_fmaf(b.y, 512.0f, -8.0f);
+  q[1] = __builtin_fmaf(c.x, 512.0f, -8.0f); q[3] = __builtin_fmaf(c.y, 512.0f, -8.0f);
+  q[5] = __builtin_fmaf(d.x, 512.0f, -8.0f); q[7] = __builtin_fmaf(d.y, 512.0f, -8.0f);
 }
 
 // 4 int8 codes of one dword, in element order, exact.
@@ -135,125 +144,142 @@ __device__ __forceinline__ void decode4_int8(uint32_t w, float (&q)[4]) {
   q[3] = (float)((int)w >> 24);
 }
 
-// ------------------------------------------------------------------ kernel
+// ------------------------------------------------------------------ kernels
 
-struct GemvArgs {
+// One matrix of a (possibly batched) call, validated on the host.
+struct GemvDesc {
   const uint8_t* payload;
   const float* scales;
   const float* x;
   float* y;
-  int n;             // rows
-  int k;             // row length (elements)
-  int nchunks;       // 16-byte chunks per row
-  int row_stride_b;  // bytes per payload row (= k * bits / 8)
   int64_t group;
-  int per_row_groups;  // 1: k % group == 0 ; 0: group % k == 0
-  int64_t groups_per_row;  // k / group when per_row_groups
-  FastDiv cpg;         // chunks per group (per_row_groups only)
+  FastDiv cpg;         // 8-code chunks per group (per-row groups)
+  int n;               // rows
+  int k;               // row length (elements)
+  int row_stride_b;    // payload bytes per row (= k * bits / 8)
+  int per_row;         // 1: k % group == 0 ; 0: group % k == 0
+  int gpr;             // groups per row when per_row
 };
 
+constexpr int GEMV_NB = 32;  // matrices per launch (descriptors travel as kernel arguments)
+
+struct GemvBatch {
+  int item0[GEMV_NB];  // first work item of each matrix (contiguous: one scalar load)
+  GemvDesc d[GEMV_NB];
+  int count;           // descriptors in use
+  int items;           // total work items
+};
+
+// The matrix work item `item` belongs to: compares against all item0 values
+// (kept together at the start of the kernel arguments, loaded by a few
+// scalar loads) and reads that descriptor in place from the kernel-argument
+// segment (indexing the by-value parameter would copy it to memory).
+__device__ __forceinline__ int find_desc(const GemvBatch& b, int item) {
+  typedef const __attribute__((address_space(4))) GemvBatch* KArg;
+  const KArg kb = (KArg)__builtin_amdgcn_kernarg_segment_ptr();
+  int di = 0;
+#pragma unroll
+  for (int i = 1; i < GEMV_NB; ++i) di += (i < b.count && item >= kb->item0[i]) ? 1 : 0;
+  return di;
+}
+
+__device__ __forceinline__ GemvDesc load_desc(int di) {
+  typedef const __attribute__((address_space(4))) GemvBatch* KArg;
+  const KArg kb = (KArg)__builtin_amdgcn_kernarg_segment_ptr();
+  const auto& d = kb->d[di];
+  return GemvDesc{d.payload, d.scales, d.x, d.y, d.group,
+                  {d.cpg.mul, d.cpg.shift, d.cpg.is_pow2, d.cpg.d},
+                  d.n, d.k, d.row_stride_b, d.per_row, d.gpr};
+}
+
+// Streaming kernel: 8-code chunks (4-byte int4 / 8-byte int8 payload loads
+// per lane and row, two 16-byte x loads per lane), any group that is a
+// multiple of 8 codes (or spans whole rows).
 template <int BITS, int M, int R>
-__global__ __launch_bounds__(256) void gemv_kernel(GemvArgs a) {
-  constexpr int CPC = BITS == 4 ? 32 : 16;  // codes per 16-byte chunk
+__global__ __launch_bounds__(256) void gemv8_kernel(const GemvBatch b) {
   constexpr int V = pow2_at_least(R * M);
-  __shared__ float red[4][V];
+  constexpr int PW = BITS == 4 ? 1 : 2;     // payload dwords per 8-code chunk
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (item >= b.items) return;
+  const int di = find_desc(b, item);
+  const GemvDesc a = load_desc(di);
+  typedef const __attribute__((address_space(4))) GemvBatch* KArg;
+  const int row0 = (item - ((KArg)__builtin_amdgcn_kernarg_segment_ptr())->item0[di]) * R;
+  const int nch = a.k / 8;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int nthreads = blockDim.x;
-  const int row0 = blockIdx.x * R;
-
-  int64_t rowoff[R];   // byte offset of each row's payload
-  int64_t sbase[R];    // scale index of the row's first group
+  const uint32_t* prow[R];
+  const float* srow[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int row = min(row0 + r, a.n - 1);
-    rowoff[r] = (int64_t)row * a.row_stride_b;
-    sbase[r] = a.per_row_groups ? (int64_t)row * a.groups_per_row
-                                : ((int64_t)row * a.k) / a.group;
+    prow[r] = reinterpret_cast<const uint32_t*>(a.payload + (int64_t)row * a.row_stride_b);
+    srow[r] = a.scales + (a.per_row ? (int64_t)row * a.gpr : ((int64_t)row * a.k) / a.group);
   }
-
   float acc[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.0f;
 
-  for (int c = tid; c < a.nchunks; c += nthreads) {
-    uint4 p[R];
+  // the group of chunk c, tracked without a division: chunk l of a lane
+  // starts at group gl = l / cpg, and each step of 64 chunks advances the
+  // group by 64 / cpg (+1 when the remainder wraps)
+  const uint32_t cpg = a.per_row ? a.cpg.d : 0u;
+  uint32_t gc = 0, rem = 0, step_g = 0, step_r = 0;
+  if (cpg) {
+    gc = fastdiv((uint32_t)lane, a.cpg);
+    rem = (uint32_t)lane - gc * cpg;
+    step_g = fastdiv(64u, a.cpg);
+    step_r = 64u - step_g * cpg;
+  }
+  for (int c = lane; c < nch; c += 64) {
+    uint32_t p[R][PW];
     float s[R];
-    const int gc = a.per_row_groups ? (int)fastdiv((uint32_t)c, a.cpg) : 0;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      p[r] = ldnt(reinterpret_cast<const uint4*>(a.payload + rowoff[r]) + c);
-      s[r] = a.scales[sbase[r] + gc];
+#pragma unroll
+      for (int i = 0; i < PW; ++i) p[r][i] = __builtin_nontemporal_load(prow[r] + PW * c + i);
+      s[r] = srow[r][gc];
     }
-    float part[R][M];
+    float xv[M][8];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int m = 0; m < M; ++m) {
+      const float4* xp = reinterpret_cast<const float4*>(a.x + (int64_t)m * a.k) + 2 * c;
+      const float4 x0 = xp[0], x1 = xp[1];
+      xv[m][0] = x0.x; xv[m][1] = x0.y; xv[m][2] = x0.z; xv[m][3] = x0.w;
+      xv[m][4] = x1.x; xv[m][5] = x1.y; xv[m][6] = x1.z; xv[m][7] = x1.w;
+    }
 #pragma unroll
-      for (int m = 0; m < M; ++m) part[r][m] = 0.0f;
-
-    const float* xc = a.x + (int64_t)c * CPC;
+    for (int r = 0; r < R; ++r) {
+      float q[8];
+      if constexpr (BITS == 4) {
+        decode8_int4(p[r][0], q);
+      } else {
+        float q0[4], q1[4];
+        decode4_int8(p[r][0], q0);
+        decode4_int8(p[r][PW - 1], q1);
 #pragma unroll
-    for (int d = 0; d < 4; ++d) {
-      constexpr int E = BITS == 4 ? 8 : 4;  // codes per dword
-      float xv[M][E];
+        for (int e = 0; e < 4; ++e) { q[e] = q0[e]; q[4 + e] = q1[e]; }
+      }
 #pragma unroll
       for (int m = 0; m < M; ++m) {
-        const float4* xp = reinterpret_cast<const float4*>(xc + (int64_t)m * a.k + d * E);
-        const float4 x0 = xp[0];
-        xv[m][0] = x0.x; xv[m][1] = x0.y; xv[m][2] = x0.z; xv[m][3] = x0.w;
-        if constexpr (E == 8) {
-          const float4 x1 = xp[1];
-          xv[m][4] = x1.x; xv[m][5] = x1.y; xv[m][6] = x1.z; xv[m][7] = x1.w;
-        }
-      }
+        float part = 0.0f;
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const uint32_t w = d == 0 ? p[r].x : d == 1 ? p[r].y : d == 2 ? p[r].z : p[r].w;
-        float q[E];
-        if (BITS == 4) {
-          float q8[8];
-          decode8_int4(w, q8);
-#pragma unroll
-          for (int e = 0; e < E; ++e) q[e] = q8[e];
-        } else {
-          float q4[4];
-          decode4_int8(w, q4);
-#pragma unroll
-          for (int e = 0; e < E; ++e) q[e] = q4[e];
-        }
-#pragma unroll
-        for (int m = 0; m < M; ++m)
-#pragma unroll
-          for (int e = 0; e < E; ++e) part[r][m] = __builtin_fmaf(xv[m][e], q[e], part[r][m]);
+        for (int e = 0; e < 8; ++e) part = __builtin_fmaf(xv[m][e], q[e], part);
+        acc[r * M + m] = __builtin_fmaf(part, s[r], acc[r * M + m]);
       }
     }
-    constexpr float unit = BITS == 4 ? 512.0f : 1.0f;  // undo the 2^-9 of the int4 decode
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-      for (int m = 0; m < M; ++m)
-        acc[r * M + m] = __builtin_fmaf(part[r][m] * unit, s[r], acc[r * M + m]);
+    if (cpg) {
+      gc += step_g;
+      rem += step_r;
+      if (rem >= cpg) { rem -= cpg; ++gc; }
+    }
   }
 
   wave_reduce_scatter<V>(acc, lane);
   const int idx = scatter_index<V>(lane);
-  const int nw = nthreads >> 6;
-  if (nw == 1) {
-    if ((lane & (64 / V - 1)) == 0 && idx < R * M) {
-      const int r = idx / M, m = idx % M;
-      if (row0 + r < a.n) a.y[(int64_t)m * a.n + row0 + r] = acc[0];
-    }
-    return;
-  }
-  if ((lane & (64 / V - 1)) == 0) red[wave][idx] = acc[0];
-  __syncthreads();
-  if (tid < R * M) {
-    float t = red[0][tid];
-    for (int w = 1; w < nw; ++w) t += red[w][tid];
-    const int r = tid / M, m = tid % M;
-    if (row0 + r < a.n) a.y[(int64_t)m * a.n + row0 + r] = t;
+  if ((lane & (64 / V - 1)) == 0 && idx < R * M) {
+    const int r = idx / M, m = idx % M;
+    if (row0 + r < a.n) a.y[(int64_t)m * a.n + row0 + r] = acc[0];
   }
 }
 
@@ -287,60 +313,77 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(
   if (lane == 0) y[mm * n + row] = sum;
 }
 
+// Rows per wave: as many as the registers allow (x reused across more rows,
+// fewer reductions); fewer for a lone small matrix so every SIMD gets waves.
+template <int M>
+constexpr int rows_big() { return M <= 4 ? 8 : 4; }
+constexpr int kRowsSmall = 2;
+
+// Launches `count` descriptors (same bits, m), GEMV_NB per launch, R rows per
+// work item.
+template <int BITS, int M, int R>
+hipError_t launch_group(const GemvDesc* ds, int count, hipStream_t st) {
+  for (int base = 0; base < count; base += GEMV_NB) {
+    GemvBatch b{};
+    b.count = count - base < GEMV_NB ? count - base : GEMV_NB;
+    int items = 0;
+    for (int i = 0; i < b.count; ++i) {
+      b.d[i] = ds[base + i];
+      b.item0[i] = items;
+      items += (b.d[i].n + R - 1) / R;
+    }
+    b.items = items;
+    gemv8_kernel<BITS, M, R><<<(unsigned)((items + 3) / 4), 256, 0, st>>>(b);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 template <int BITS, int M>
-hipError_t launch_fast(const GemvArgs& a, hipStream_t st) {
-  constexpr int R = M <= 4 ? 8 : 4;
-  const int w4 = (a.nchunks + 63) / 64;
-  const int waves = w4 < 4 ? w4 : 4;
-  const unsigned grid = (unsigned)((a.n + R - 1) / R);
-  gemv_kernel<BITS, M, R><<<grid, 64 * waves, 0, st>>>(a);
-  return hipGetLastError();
+hipError_t launch_m(const GemvDesc* ds, int count, hipStream_t st) {
+  int64_t rows = 0;
+  for (int i = 0; i < count; ++i) rows += ds[i].n;
+  // big items when they still give about two waves per SIMD (2048 items)
+  constexpr int RB = rows_big<M>();
+  return rows / RB >= 2048 ? launch_group<BITS, M, RB>(ds, count, st)
+                           : launch_group<BITS, M, kRowsSmall>(ds, count, st);
 }
 
 template <int BITS>
-hipError_t launch_fast_bits(const GemvArgs& a, int m, hipStream_t st) {
+hipError_t launch_bits(const GemvDesc* ds, int count, int m, hipStream_t st) {
   switch (m) {
-    case 1: return launch_fast<BITS, 1>(a, st);
-    case 2: return launch_fast<BITS, 2>(a, st);
-    case 3: return launch_fast<BITS, 3>(a, st);
-    case 4: return launch_fast<BITS, 4>(a, st);
-    case 5: return launch_fast<BITS, 5>(a, st);
-    case 6: return launch_fast<BITS, 6>(a, st);
-    case 7: return launch_fast<BITS, 7>(a, st);
-    default: return launch_fast<BITS, 8>(a, st);
+    case 1: return launch_m<BITS, 1>(ds, count, st);
+    case 2: return launch_m<BITS, 2>(ds, count, st);
+    case 3: return launch_m<BITS, 3>(ds, count, st);
+    case 4: return launch_m<BITS, 4>(ds, count, st);
+    case 5: return launch_m<BITS, 5>(ds, count, st);
+    case 6: return launch_m<BITS, 6>(ds, count, st);
+    case 7: return launch_m<BITS, 7>(ds, count, st);
+    default: return launch_m<BITS, 8>(ds, count, st);
   }
 }
 
-}  // namespace
-
-int gemv_path(const Mat& mt, const uint8_t* payload, const float* x) {
-  const int cpc = mt.bits == 4 ? 32 : 16;
-  const bool shape_ok = mt.k % cpc == 0 && mt.n < (1ll << 31) && mt.k < (1ll << 31) &&
-                        (int64_t)mt.k * mt.bits / 8 < (1ll << 31);
-  const bool group_ok = (mt.k % mt.group == 0 && mt.group % cpc == 0) || (mt.group % mt.k == 0);
-  if (shape_ok && group_ok && aligned(payload, 16) && aligned(x, 16)) return PATH_FAST;
-  return PATH_GENERIC;
+GemvDesc make_desc(const Mat& mt, const uint8_t* payload, const float* scales, const float* x,
+                   float* y) {
+  GemvDesc d{};
+  const int cpc = 8;  // codes per chunk
+  d.payload = payload;
+  d.scales = scales;
+  d.x = x;
+  d.y = y;
+  d.n = (int)mt.n;
+  d.k = (int)mt.k;
+  d.row_stride_b = (int)(mt.k * mt.bits / 8);
+  d.group = mt.group;
+  d.per_row = mt.k % mt.group == 0 ? 1 : 0;
+  d.gpr = d.per_row ? (int)(mt.k / mt.group) : 0;
+  d.cpg = make_fastdiv(d.per_row ? (uint32_t)(mt.group / cpc) : 1u);
+  return d;
 }
 
-hipError_t launch_gemv(const Mat& mt, const uint8_t* payload, const float* scales, int m,
-                       const float* x, float* y, hipStream_t st) {
-  if (gemv_path(mt, payload, x) == PATH_FAST) {
-    GemvArgs a{};
-    const int cpc = mt.bits == 4 ? 32 : 16;
-    a.payload = payload;
-    a.scales = scales;
-    a.x = x;
-    a.y = y;
-    a.n = (int)mt.n;
-    a.k = (int)mt.k;
-    a.row_stride_b = (int)(mt.k * mt.bits / 8);
-    a.nchunks = a.row_stride_b / 16;
-    a.group = mt.group;
-    a.per_row_groups = mt.k % mt.group == 0 ? 1 : 0;
-    a.groups_per_row = a.per_row_groups ? mt.k / mt.group : 0;
-    a.cpg = make_fastdiv(a.per_row_groups ? (uint32_t)(mt.group / cpc) : 1u);
-    return mt.bits == 4 ? launch_fast_bits<4>(a, m, st) : launch_fast_bits<8>(a, m, st);
-  }
+hipError_t launch_generic(const Mat& mt, const uint8_t* payload, const float* scales, int m,
+                          const float* x, float* y, hipStream_t st) {
   const int64_t waves = mt.n * m;
   const unsigned grid = (unsigned)((waves + 3) / 4);
   if (mt.bits == 4)
@@ -348,6 +391,55 @@ hipError_t launch_gemv(const Mat& mt, const uint8_t* payload, const float* scale
   else
     gemv_generic_kernel<8><<<grid, 256, 0, st>>>(payload, scales, x, y, mt.n, mt.k, m, mt.group);
   return hipGetLastError();
+}
+
+}  // namespace
+
+int gemv_path(const Mat& mt, const uint8_t* payload, const float* x) {
+  const int cpc = 8;  // codes per chunk
+  const bool shape_ok = mt.k % cpc == 0 && mt.n < (1ll << 30) && mt.k < (1ll << 30) &&
+                        (int64_t)mt.k * mt.bits / 8 < (1ll << 31);
+  const bool group_ok = (mt.k % mt.group == 0 && mt.group % cpc == 0) || (mt.group % mt.k == 0);
+  if (shape_ok && group_ok && aligned(payload, mt.bits == 4 ? 4 : 8) && aligned(x, 16))
+    return PATH_FAST;
+  return PATH_GENERIC;
+}
+
+hipError_t launch_gemv(const Mat& mt, const uint8_t* payload, const float* scales, int m,
+                       const float* x, float* y, hipStream_t st) {
+  if (gemv_path(mt, payload, x) == PATH_FAST) {
+    const GemvDesc d = make_desc(mt, payload, scales, x, y);
+    return mt.bits == 4 ? launch_bits<4>(&d, 1, m, st) : launch_bits<8>(&d, 1, m, st);
+  }
+  return launch_generic(mt, payload, scales, m, x, y, st);
+}
+
+hipError_t launch_gemv_batched(const Mat* mts, const uint8_t* const* payloads,
+                               const float* const* scales, int m, const float* const* xs,
+                               float* const* ys, int count, hipStream_t st) {
+  // fast-path matrices, grouped by bit width, go out GEMV_NB per launch;
+  // the others take the generic kernel one by one.
+  for (int bits = 4; bits <= 8; bits += 4) {
+    GemvDesc ds[GEMV_NB];
+    int nd = 0;
+    for (int i = 0; i <= count; ++i) {
+      const bool flush = (i == count) || nd == GEMV_NB;
+      if (flush && nd) {
+        hipError_t e = bits == 4 ? launch_bits<4>(ds, nd, m, st) : launch_bits<8>(ds, nd, m, st);
+        if (e != hipSuccess) return e;
+        nd = 0;
+      }
+      if (i == count) break;
+      if (mts[i].bits != bits || mts[i].n * mts[i].k == 0) continue;
+      if (gemv_path(mts[i], payloads[i], xs[i]) == PATH_FAST) {
+        ds[nd++] = make_desc(mts[i], payloads[i], scales[i], xs[i], ys[i]);
+      } else {
+        hipError_t e = launch_generic(mts[i], payloads[i], scales[i], m, xs[i], ys[i], st);
+        if (e != hipSuccess) return e;
+      }
+    }
+  }
+  return hipSuccess;
 }
 
 __global__ void fill_zero_kernel(float* y, int64_t count) {

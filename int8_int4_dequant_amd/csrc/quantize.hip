@@ -16,21 +16,24 @@
 // build never enables fast-math or denormal flushing.
 //
 // Kernel families:
-//   subgroup  group = 8*L, L in {1,2,...,64}: each lane owns 8 consecutive
-//             weights (two 16-byte loads); the L lanes of a group reduce
-//             max|w| with cross-lane shuffles.  One pass, fully coalesced.
-//   block     group % 8 == 0 and group <= 256*8*QB_J: one 256-thread block
-//             per group; weights stay in registers between the max and the
-//             code pass.
+//   subgroup  group a power of two in [8, 1024]: each lane owns 16
+//             consecutive weights (four 16-byte loads; 8 for group 8); the
+//             lanes of a group reduce max|w| with cross-lane shuffles.  One
+//             pass, fully coalesced.
+//   block     group % 4 == 0 and group <= 16384: one 256-thread block per
+//             group; weights stay in registers between the max and the code
+//             pass.
 //   generic   any group dividing n*k, any alignment: a scale kernel (one
 //             thread or one block per group) then a code kernel (one thread
 //             per payload byte).
 #include "qw_internal.h"
 
+#include <vector>
+
 namespace qw {
 namespace {
 
-constexpr int QB_J = 8;  // chunks of 8 weights per thread in the block kernel
+constexpr int QB_J = 16;  // float4 vectors per thread in the block kernel (group <= 16384)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -62,88 +65,180 @@ __device__ __forceinline__ float scale_of(float m) {
   return s == 0.0f ? 1.0f : s;
 }
 
-// Pack 8 consecutive codes and store them at chunk index `c`.
-template <int BITS>
-__device__ __forceinline__ void store_chunk(uint8_t* payload, uint64_t c, const int (&q)[8]) {
-  if (BITS == 4) {
-    uint32_t v = 0;
+// Rounded quotients rint(fl32(w[e] / s)) for the NE values of one lane,
+// all in one group (scale s), returned as exact small integers in fp32.
+//
+// Shortcut: with R = fl32(1/s) and t = fl32(w * R), |t - fl32(w / s)| <=
+// (3u + u^2) |w / s| < 3 * 2^-24 * 128 < 2^-15 (u = 2^-24, |w / s| <= qmax
+// up to one ulp), provided 1/s is a normal number.  rint is constant
+// between half-integers, so wherever t is farther than 2^-15 from a
+// half-integer rint(t) equals rint(fl32(w / s)) exactly.  Otherwise (a
+// near-tie, about 6e-5 of random codes) or when s is extreme, every value of
+// the lane is recomputed with the IEEE division.  Both paths are exact.
+template <int NE>
+__device__ __forceinline__ void rounded_quotients(const float (&w)[NE], float s, float (&r)[NE]) {
+  // t must be the rounded product, and t - rint(t) a separate (exact)
+  // subtraction: no contraction into an fma here.
+#pragma clang fp contract(off)
+  bool fast = s >= 0x1p-125f && s <= 0x1p+125f;
+  if (fast) {
+    const float rs = 1.0f / s;
+    float dmax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v |= (uint32_t)((q[i] + 8) & 15) << (4 * i);
-    reinterpret_cast<uint32_t*>(payload)[c] = v;
-  } else {
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lo |= (uint32_t)(q[i] & 255) << (8 * i);
-      hi |= (uint32_t)(q[4 + i] & 255) << (8 * i);
+    for (int e = 0; e < NE; ++e) {
+      const float t = w[e] * rs;
+      const float rt = rintf(t);
+      dmax = fmaxf(dmax, fabsf(t - rt));  // exact: t and rint(t) are close
+      r[e] = rt;
     }
-    reinterpret_cast<uint2*>(payload)[c] = make_uint2(lo, hi);
+    fast = dmax < 0.5f - 0x1p-15f;
   }
-}
-
-__device__ __forceinline__ float absmax8(const float4& a, const float4& b) {
-  float m = fmaxf(fmaxf(fabsf(a.x), fabsf(a.y)), fmaxf(fabsf(a.z), fabsf(a.w)));
-  return fmaxf(m, fmaxf(fmaxf(fabsf(b.x), fabsf(b.y)), fmaxf(fabsf(b.z), fabsf(b.w))));
-}
-
-template <int BITS>
-__device__ __forceinline__ void quantize8(const float4& a, const float4& b, float s, int (&q)[8]) {
-  q[0] = code_of<BITS>(a.x, s); q[1] = code_of<BITS>(a.y, s);
-  q[2] = code_of<BITS>(a.z, s); q[3] = code_of<BITS>(a.w, s);
-  q[4] = code_of<BITS>(b.x, s); q[5] = code_of<BITS>(b.y, s);
-  q[6] = code_of<BITS>(b.z, s); q[7] = code_of<BITS>(b.w, s);
+  if (!fast) {
+#pragma unroll
+    for (int e = 0; e < NE; ++e) r[e] = rintf(w[e] / s);
+  }
 }
 
 // ---------------------------------------------------------------- subgroup
 
-template <int BITS, int L>
+// Packs 4 rounded quotients (element order): int4 -> 16 bits, int8 -> 32 bits.
+// The quotients already lie in [-qmax, qmax] for finite inputs (|w / s|
+// exceeds qmax by at most one ulp), so no clip is needed; the masks keep
+// garbage from non-finite inputs inside its own field.  Adding 2^23 + 8
+// (int4) or 2^23 + 256 (int8) puts q + 8, resp. q mod 256, in the low
+// mantissa bits.
+__device__ __forceinline__ uint32_t pack4_int4(const float* r) {
+  uint32_t v = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v |= (__float_as_uint(r[i] + 8388616.0f) & 15u) << (4 * i);
+  return v;
+}
+__device__ __forceinline__ uint32_t pack4_int8(const float* r) {
+  uint32_t v = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v |= (__float_as_uint(r[i] + 8388864.0f) & 255u) << (8 * i);
+  return v;
+}
+
+constexpr int QV = 4;  // float4 vectors per lane in the subgroup kernel
+
+// A wave owns 64*QV consecutive float4 vectors; its j-th load instruction
+// reads vectors [base + 64j, base + 64j + 64) -- one fully coalesced 1 KiB
+// run per instruction.  A group of G vectors (G = group / 4, a power of two
+// from 2 to 256) is G consecutive lanes of one instruction (G <= 64) or the
+// same lane across 2 or 4 instructions (G = 128, 256); max|w| is reduced
+// with cross-lane shuffles.  Each lane then writes 2 (int4) or 4 (int8)
+// payload bytes per vector, again contiguous across the wave.
+template <int BITS, int G>
+__device__ __forceinline__ void quant_subgroup_body(
+    const float* __restrict__ w, uint8_t* __restrict__ payload,
+    float* __restrict__ scales, uint64_t nvec, uint64_t block) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t base = (block * 4 + (threadIdx.x >> 6)) * (64 * QV);
+  float v[QV][4];
+  float m[QV];
+#pragma unroll
+  for (int j = 0; j < QV; ++j) {
+    const uint64_t idx = base + lane + 64 * j;
+    float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (idx < nvec) f = ldnt(reinterpret_cast<const float4*>(w) + idx);
+    v[j][0] = f.x; v[j][1] = f.y; v[j][2] = f.z; v[j][3] = f.w;
+    m[j] = fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w)));
+  }
+  // Groups are aligned to G vectors and never straddle the end of the data
+  // (nvec is a multiple of G), so inactive lanes only meet inactive lanes.
+  if constexpr (G <= 64) {
+#pragma unroll
+    for (int j = 0; j < QV; ++j)
+#pragma unroll
+      for (int off = G / 2; off >= 1; off >>= 1) m[j] = fmaxf(m[j], __shfl_xor(m[j], off));
+  } else {
+    constexpr int J = G / 64;  // instructions per group: 2 or 4
+#pragma unroll
+    for (int j0 = 0; j0 < QV; j0 += J) {
+      float t = m[j0];
+#pragma unroll
+      for (int j = 1; j < J; ++j) t = fmaxf(t, m[j0 + j]);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) t = fmaxf(t, __shfl_xor(t, off));
+#pragma unroll
+      for (int j = 0; j < J; ++j) m[j0 + j] = t;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < QV; ++j) {
+    const uint64_t idx = base + lane + 64 * j;
+    if (idx >= nvec) continue;
+    const float s = scale_of<BITS>(m[j]);
+    if (idx % G == 0) scales[idx / G] = s;
+    float r[4];
+    rounded_quotients<4>(v[j], s, r);
+    if constexpr (BITS == 4)
+      reinterpret_cast<uint16_t*>(payload)[idx] = (uint16_t)pack4_int4(r);
+    else
+      reinterpret_cast<uint32_t*>(payload)[idx] = pack4_int8(r);
+  }
+}
+
+template <int BITS, int G>
 __global__ __launch_bounds__(256) void quant_subgroup_kernel(
     const float* __restrict__ w, uint8_t* __restrict__ payload,
-    float* __restrict__ scales, uint64_t nchunks) {
-  const uint64_t t = (uint64_t)blockIdx.x * 256u + threadIdx.x;
-  const bool active = t < nchunks;
-  float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
-  if (active) {
-    const float4* p = reinterpret_cast<const float4*>(w) + 2 * t;
-    a = ldnt(p);
-    b = ldnt(p + 1);
-  }
-  float m = absmax8(a, b);
-  // Groups never straddle the active / inactive boundary (nchunks is a
-  // multiple of L), so inactive lanes only meet inactive lanes here.
-#pragma unroll
-  for (int off = L / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  const float s = scale_of<BITS>(m);
-  if (!active) return;
-  if ((t & (L - 1)) == 0) scales[t / L] = s;
-  int q[8];
-  quantize8<BITS>(a, b, s, q);
-  store_chunk<BITS>(payload, t, q);
+    float* __restrict__ scales, uint64_t nvec) {
+  quant_subgroup_body<BITS, G>(w, payload, scales, nvec, blockIdx.x);
+}
+
+// Several matrices of the same bits and group in one launch: the matrices'
+// descriptors travel in the kernel arguments; block b finds its matrix by a
+// wave-uniform search and quantizes that matrix's block (b - first block).
+struct QuantDesc {
+  const float* w;
+  uint8_t* payload;
+  float* scales;
+  uint64_t nvec;    // float4 vectors of the matrix
+  uint32_t block0;  // first block of the matrix in the launch
+  uint32_t pad;
+};
+constexpr int QUANT_NB = 64;
+struct QuantBatch {
+  QuantDesc d[QUANT_NB];
+  int count;
+  int blocks;
+};
+
+template <int BITS, int G>
+__global__ __launch_bounds__(256) void quant_subgroup_batched_kernel(const QuantBatch b) {
+  typedef const __attribute__((address_space(4))) QuantBatch* KArg;
+  const KArg kb = (KArg)__builtin_amdgcn_kernarg_segment_ptr();
+  const uint32_t blk = blockIdx.x;
+  int di = 0;
+  for (int i = 1; i < b.count; ++i)
+    if (blk >= kb->d[i].block0) di = i;
+  quant_subgroup_body<BITS, G>(kb->d[di].w, kb->d[di].payload, kb->d[di].scales, kb->d[di].nvec,
+                               blk - kb->d[di].block0);
 }
 
 // ------------------------------------------------------------------- block
 
+// One 256-thread block per group (group % 4 == 0, group <= 4 * 256 * QB_J):
+// thread t owns vectors t, t + 256, ... of the group (coalesced loads), all
+// held in registers between the block-wide max and the code pass.
 template <int BITS>
 __global__ __launch_bounds__(256) void quant_block_kernel(
     const float* __restrict__ w, uint8_t* __restrict__ payload,
-    float* __restrict__ scales, int cpg /* chunks of 8 per group */) {
+    float* __restrict__ scales, int vpg /* float4 vectors per group */) {
   __shared__ float red[4];
   const uint64_t g = blockIdx.x;
-  const uint64_t base = g * (uint64_t)cpg;  // first chunk of this group
+  const uint64_t base = g * (uint64_t)vpg;  // first vector of this group
   const int tid = threadIdx.x;
-  float4 a[QB_J], b[QB_J];
+  float v[QB_J][4];
   float m = 0.0f;
 #pragma unroll
   for (int j = 0; j < QB_J; ++j) {
     const int c = tid + 256 * j;
-    a[j] = make_float4(0.f, 0.f, 0.f, 0.f);
-    b[j] = a[j];
-    if (c < cpg) {
-      const float4* p = reinterpret_cast<const float4*>(w) + 2 * (base + c);
-      a[j] = ldnt(p);
-      b[j] = ldnt(p + 1);
-    }
-    m = fmaxf(m, absmax8(a[j], b[j]));
+    float4 f = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (c < vpg) f = ldnt(reinterpret_cast<const float4*>(w) + base + c);
+    v[j][0] = f.x; v[j][1] = f.y; v[j][2] = f.z; v[j][3] = f.w;
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
   }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
@@ -155,10 +250,13 @@ __global__ __launch_bounds__(256) void quant_block_kernel(
 #pragma unroll
   for (int j = 0; j < QB_J; ++j) {
     const int c = tid + 256 * j;
-    if (c < cpg) {
-      int q[8];
-      quantize8<BITS>(a[j], b[j], s, q);
-      store_chunk<BITS>(payload, base + c, q);
+    if (c < vpg) {
+      float r[4];
+      rounded_quotients<4>(v[j], s, r);
+      if constexpr (BITS == 4)
+        reinterpret_cast<uint16_t*>(payload)[base + c] = (uint16_t)pack4_int4(r);
+      else
+        reinterpret_cast<uint32_t*>(payload)[base + c] = pack4_int8(r);
     }
   }
 }
@@ -219,30 +317,32 @@ __device__ __forceinline__ int nibble_or_byte(uint32_t v, int i) {
   return BITS == 4 ? (int)((v >> (4 * i)) & 15u) - 8 : (int)(int8_t)(v >> (8 * i));
 }
 
-// One thread per chunk of 8 weights; group % 8 == 0.
+// Unpack, group % 4 == 0: lane handles QV output vectors of 4 weights at
+// wave-contiguous positions (coalesced 2- or 4-byte payload loads, 16-byte
+// streaming stores).
 template <int BITS>
-__global__ __launch_bounds__(256) void unpack_chunk_kernel(
+__global__ __launch_bounds__(256) void unpack_vec_kernel(
     const uint8_t* __restrict__ payload, const float* __restrict__ scales,
-    float* __restrict__ out, uint64_t nchunks, uint64_t cpg) {
-  const uint64_t t = (uint64_t)blockIdx.x * 256u + threadIdx.x;
-  if (t >= nchunks) return;
-  const float s = scales[t / cpg];
-  float v[8];
-  if (BITS == 4) {
-    const uint32_t p = reinterpret_cast<const uint32_t*>(payload)[t];
+    float* __restrict__ out, uint64_t nvec, uint64_t vpg /* vectors per group */) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t base = ((uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 * QV);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = (float)nibble_or_byte<4>(p, i) * s;
-  } else {
-    const uint2 p = reinterpret_cast<const uint2*>(payload)[t];
+  for (int j = 0; j < QV; ++j) {
+    const uint64_t idx = base + lane + 64 * j;
+    if (idx >= nvec) continue;
+    const float s = scales[idx / vpg];
+    float v[4];
+    if constexpr (BITS == 4) {
+      const uint32_t p = reinterpret_cast<const uint16_t*>(payload)[idx];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[i] = (float)nibble_or_byte<8>(p.x, i) * s;
-      v[4 + i] = (float)nibble_or_byte<8>(p.y, i) * s;
+      for (int i = 0; i < 4; ++i) v[i] = (float)((int)((p >> (4 * i)) & 15u) - 8) * s;
+    } else {
+      const uint32_t p = reinterpret_cast<const uint32_t*>(payload)[idx];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = (float)(int)(int8_t)(p >> (8 * i)) * s;
     }
+    stnt(reinterpret_cast<float4*>(out) + idx, make_float4(v[0], v[1], v[2], v[3]));
   }
-  float4* o = reinterpret_cast<float4*>(out) + 2 * t;
-  stnt(o, make_float4(v[0], v[1], v[2], v[3]));
-  stnt(o + 1, make_float4(v[4], v[5], v[6], v[7]));
 }
 
 // One thread per weight; any group and alignment.
@@ -271,20 +371,21 @@ hipError_t quantize_bits(const Mat& mt, const float* w, uint8_t* payload, float*
   const uint64_t group = (uint64_t)mt.group;
   const int path = quantize_path(mt, w, payload);
   if (path == PATH_FAST) {
-    const uint64_t nchunks = count / 8;
-    const unsigned grid = blocks_for(nchunks);
-    switch (group / 8) {
-      case 1: quant_subgroup_kernel<BITS, 1><<<grid, 256, 0, st>>>(w, payload, scales, nchunks); break;
-      case 2: quant_subgroup_kernel<BITS, 2><<<grid, 256, 0, st>>>(w, payload, scales, nchunks); break;
-      case 4: quant_subgroup_kernel<BITS, 4><<<grid, 256, 0, st>>>(w, payload, scales, nchunks); break;
-      case 8: quant_subgroup_kernel<BITS, 8><<<grid, 256, 0, st>>>(w, payload, scales, nchunks); break;
-      case 16: quant_subgroup_kernel<BITS, 16><<<grid, 256, 0, st>>>(w, payload, scales, nchunks); break;
-      case 32: quant_subgroup_kernel<BITS, 32><<<grid, 256, 0, st>>>(w, payload, scales, nchunks); break;
-      default: quant_subgroup_kernel<BITS, 64><<<grid, 256, 0, st>>>(w, payload, scales, nchunks); break;
+    const uint64_t nvec = count / 4;
+    const unsigned grid = (unsigned)((nvec + 4 * 64 * QV - 1) / (4 * 64 * QV));
+    switch (group / 4) {
+      case 2: quant_subgroup_kernel<BITS, 2><<<grid, 256, 0, st>>>(w, payload, scales, nvec); break;
+      case 4: quant_subgroup_kernel<BITS, 4><<<grid, 256, 0, st>>>(w, payload, scales, nvec); break;
+      case 8: quant_subgroup_kernel<BITS, 8><<<grid, 256, 0, st>>>(w, payload, scales, nvec); break;
+      case 16: quant_subgroup_kernel<BITS, 16><<<grid, 256, 0, st>>>(w, payload, scales, nvec); break;
+      case 32: quant_subgroup_kernel<BITS, 32><<<grid, 256, 0, st>>>(w, payload, scales, nvec); break;
+      case 64: quant_subgroup_kernel<BITS, 64><<<grid, 256, 0, st>>>(w, payload, scales, nvec); break;
+      case 128: quant_subgroup_kernel<BITS, 128><<<grid, 256, 0, st>>>(w, payload, scales, nvec); break;
+      default: quant_subgroup_kernel<BITS, 256><<<grid, 256, 0, st>>>(w, payload, scales, nvec); break;
     }
   } else if (path == PATH_BLOCK) {
     const uint64_t ngroups = count / group;
-    quant_block_kernel<BITS><<<(unsigned)ngroups, 256, 0, st>>>(w, payload, scales, (int)(group / 8));
+    quant_block_kernel<BITS><<<(unsigned)ngroups, 256, 0, st>>>(w, payload, scales, (int)(group / 4));
   } else {
     const uint64_t ngroups = count / group;
     if (group <= 64)
@@ -303,8 +404,9 @@ hipError_t unpack_bits(const Mat& mt, const uint8_t* payload, const float* scale
   const uint64_t count = (uint64_t)mt.n * (uint64_t)mt.k;
   const uint64_t group = (uint64_t)mt.group;
   if (unpack_path(mt, payload, out) == PATH_FAST) {
-    const uint64_t nchunks = count / 8;
-    unpack_chunk_kernel<BITS><<<blocks_for(nchunks), 256, 0, st>>>(payload, scales, out, nchunks, group / 8);
+    const uint64_t nvec = count / 4;
+    const unsigned grid = (unsigned)((nvec + 4 * 64 * QV - 1) / (4 * 64 * QV));
+    unpack_vec_kernel<BITS><<<grid, 256, 0, st>>>(payload, scales, out, nvec, group / 4);
   } else {
     unpack_generic_kernel<BITS><<<blocks_for(count), 256, 0, st>>>(payload, scales, out, count, group);
   }
@@ -317,19 +419,19 @@ int quantize_path(const Mat& mt, const float* w, const uint8_t* payload) {
   const uint64_t count = (uint64_t)mt.n * (uint64_t)mt.k;
   const uint64_t group = (uint64_t)mt.group;
   const bool al = aligned(w, 16) && aligned(payload, mt.bits == 4 ? 4 : 8);
-  const uint64_t blocks_needed = (count / 8 + 255) / 256;
-  if (al && group % 8 == 0 && group <= 512 && ((group / 8) & (group / 8 - 1)) == 0 &&
-      blocks_needed < (1ull << 31))
+  const uint64_t blocks_needed = (count / 4 + 1023) / 1024;
+  const bool pow2 = (group & (group - 1)) == 0;
+  if (al && pow2 && group >= 8 && group <= 1024 && blocks_needed < (1ull << 31))
     return PATH_FAST;
-  if (al && group % 8 == 0 && group <= 256u * 8u * QB_J && count / group < (1ull << 31))
+  if (al && group % 4 == 0 && group <= 256u * 4u * QB_J && count / group < (1ull << 31))
     return PATH_BLOCK;
   return PATH_GENERIC;
 }
 
 int unpack_path(const Mat& mt, const uint8_t* payload, const float* w_out) {
   const uint64_t count = (uint64_t)mt.n * (uint64_t)mt.k;
-  const bool al = aligned(w_out, 16) && aligned(payload, mt.bits == 4 ? 4 : 8);
-  if (al && mt.group % 8 == 0 && (count / 8 + 255) / 256 < (1ull << 31)) return PATH_FAST;
+  const bool al = aligned(w_out, 16) && aligned(payload, mt.bits == 4 ? 2 : 4);
+  if (al && mt.group % 4 == 0 && (count / 4 + 1023) / 1024 < (1ull << 31)) return PATH_FAST;
   return PATH_GENERIC;
 }
 
@@ -337,6 +439,81 @@ hipError_t launch_quantize_pack(const Mat& mt, const float* w, uint8_t* payload,
                                 hipStream_t st) {
   return mt.bits == 4 ? quantize_bits<4>(mt, w, payload, scales, st)
                       : quantize_bits<8>(mt, w, payload, scales, st);
+}
+
+namespace {
+
+template <int BITS, int G>
+hipError_t launch_quant_batch(const QuantBatch& b, hipStream_t st) {
+  quant_subgroup_batched_kernel<BITS, G><<<b.blocks, 256, 0, st>>>(b);
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_quant_batch_g(const QuantBatch& b, int64_t group, hipStream_t st) {
+  switch (group / 4) {
+    case 2: return launch_quant_batch<BITS, 2>(b, st);
+    case 4: return launch_quant_batch<BITS, 4>(b, st);
+    case 8: return launch_quant_batch<BITS, 8>(b, st);
+    case 16: return launch_quant_batch<BITS, 16>(b, st);
+    case 32: return launch_quant_batch<BITS, 32>(b, st);
+    case 64: return launch_quant_batch<BITS, 64>(b, st);
+    case 128: return launch_quant_batch<BITS, 128>(b, st);
+    default: return launch_quant_batch<BITS, 256>(b, st);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize_pack_batched(const Mat* mts, const float* const* ws,
+                                        uint8_t* const* payloads, float* const* scales,
+                                        int count, hipStream_t st) {
+  // Matrices that take the subgroup kernel are bucketed by (bits, group) and
+  // launched QUANT_NB at a time; any other matrix is launched on its own.
+  struct Bucket {
+    int bits;
+    int64_t group;
+    std::vector<int> idx;
+  };
+  std::vector<Bucket> buckets;
+  for (int i = 0; i < count; ++i) {
+    if (mts[i].n * mts[i].k == 0) continue;
+    if (quantize_path(mts[i], ws[i], payloads[i]) != PATH_FAST) {
+      hipError_t e = launch_quantize_pack(mts[i], ws[i], payloads[i], scales[i], st);
+      if (e != hipSuccess) return e;
+      continue;
+    }
+    Bucket* bk = nullptr;
+    for (auto& b : buckets)
+      if (b.bits == mts[i].bits && b.group == mts[i].group) bk = &b;
+    if (!bk) {
+      buckets.push_back(Bucket{mts[i].bits, mts[i].group, {}});
+      bk = &buckets.back();
+    }
+    bk->idx.push_back(i);
+  }
+  for (const auto& bk : buckets) {
+    for (size_t base = 0; base < bk.idx.size(); base += QUANT_NB) {
+      QuantBatch b{};
+      uint64_t blocks = 0;
+      for (size_t j = base; j < bk.idx.size() && j < base + QUANT_NB; ++j) {
+        const int i = bk.idx[j];
+        QuantDesc& d = b.d[b.count++];
+        d.w = ws[i];
+        d.payload = payloads[i];
+        d.scales = scales[i];
+        d.nvec = (uint64_t)(mts[i].n * mts[i].k) / 4;
+        d.block0 = (uint32_t)blocks;
+        blocks += (d.nvec + 4 * 64 * QV - 1) / (4 * 64 * QV);
+      }
+      if (blocks >= (1ull << 31)) return hipErrorInvalidValue;
+      b.blocks = (int)blocks;
+      hipError_t e = bk.bits == 4 ? launch_quant_batch_g<4>(b, bk.group, st)
+                                  : launch_quant_batch_g<8>(b, bk.group, st);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_unpack(const Mat& mt, const uint8_t* payload, const float* scales, float* w_out,

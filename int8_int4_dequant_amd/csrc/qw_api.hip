@@ -76,6 +76,40 @@ int qw_quantize_pack(int bits, int64_t group, int64_t n, int64_t k, const float*
   return record(qw::launch_quantize_pack(mt, w, payload, scales, (hipStream_t)stream));
 }
 
+int qw_quantize_pack_batched(int count, const qw_quant_desc* descs, void* stream) {
+  if (count < 0) return QW_ECOUNT;
+  if (count == 0) return QW_OK;
+  if (!descs) return QW_ENULL;
+  for (int i = 0; i < count; ++i) {
+    const qw_quant_desc& d = descs[i];
+    if (d.reserved != 0) return QW_ECOUNT;
+    qw::Mat mt;
+    int st = check_mat(d.bits, d.group, d.n, d.k, &mt);
+    if (st != QW_OK) return st;
+    if (d.n * d.k > 0 && (!d.w || !d.payload || !d.scales)) return QW_ENULL;
+  }
+  const int kChunk = 256;
+  qw::Mat mts[kChunk];
+  const float* ws[kChunk];
+  uint8_t* ps[kChunk];
+  float* ss[kChunk];
+  for (int base = 0; base < count; base += kChunk) {
+    int nb = 0;
+    for (int i = base; i < count && i < base + kChunk; ++i) {
+      const qw_quant_desc& d = descs[i];
+      if (d.n * d.k == 0) continue;
+      check_mat(d.bits, d.group, d.n, d.k, &mts[nb]);
+      ws[nb] = d.w;
+      ps[nb] = d.payload;
+      ss[nb] = d.scales;
+      ++nb;
+    }
+    int st = record(qw::launch_quantize_pack_batched(mts, ws, ps, ss, nb, (hipStream_t)stream));
+    if (st != QW_OK) return st;
+  }
+  return QW_OK;
+}
+
 int qw_unpack(int bits, int64_t group, int64_t n, int64_t k, const uint8_t* payload,
               const float* scales, float* w_out, void* stream) {
   qw::Mat mt;
@@ -97,6 +131,52 @@ int qw_gemv(int bits, int64_t group, int64_t n, int64_t k, const uint8_t* payloa
   if (k == 0) return record(qw::launch_fill_zero(y, m * n, (hipStream_t)stream));
   if (!payload || !scales || !x) return QW_ENULL;
   return record(qw::launch_gemv(mt, payload, scales, (int)m, x, y, (hipStream_t)stream));
+}
+
+int qw_gemv_batched(int count, const qw_gemv_desc* descs, int64_t m, void* stream) {
+  if (count < 0) return QW_ECOUNT;
+  if (count == 0) return QW_OK;
+  if (!descs) return QW_ENULL;
+  if (m < 0 || m > 8) return QW_EM;
+  if (m == 0) return QW_OK;
+  // validate everything before enqueuing anything
+  for (int i = 0; i < count; ++i) {
+    const qw_gemv_desc& d = descs[i];
+    if (d.reserved != 0) return QW_ECOUNT;
+    qw::Mat mt;
+    int st = check_mat(d.bits, d.group, d.n, d.k, &mt);
+    if (st != QW_OK) return st;
+    if (d.n == 0) continue;
+    if (!d.y) return QW_ENULL;
+    if (d.k > 0 && (!d.payload || !d.scales || !d.x)) return QW_ENULL;
+  }
+  const int kChunk = 256;
+  qw::Mat mts[kChunk];
+  const uint8_t* ps[kChunk];
+  const float* ss[kChunk];
+  const float* xs[kChunk];
+  float* ys[kChunk];
+  for (int base = 0; base < count; base += kChunk) {
+    int nb = 0;
+    for (int i = base; i < count && i < base + kChunk; ++i) {
+      const qw_gemv_desc& d = descs[i];
+      if (d.n == 0) continue;
+      if (d.k == 0) {
+        int st = record(qw::launch_fill_zero(d.y, m * d.n, (hipStream_t)stream));
+        if (st != QW_OK) return st;
+        continue;
+      }
+      check_mat(d.bits, d.group, d.n, d.k, &mts[nb]);
+      ps[nb] = d.payload;
+      ss[nb] = d.scales;
+      xs[nb] = d.x;
+      ys[nb] = d.y;
+      ++nb;
+    }
+    int st = record(qw::launch_gemv_batched(mts, ps, ss, (int)m, xs, ys, nb, (hipStream_t)stream));
+    if (st != QW_OK) return st;
+  }
+  return QW_OK;
 }
 
 int qw_gemm(int bits, int64_t group, int64_t n, int64_t k, const uint8_t* payload,

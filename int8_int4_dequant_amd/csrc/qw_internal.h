@@ -22,10 +22,16 @@ inline bool aligned(const void* p, uintptr_t a) {
 // error.  Shapes are already validated and non-empty.
 hipError_t launch_quantize_pack(const Mat& mt, const float* w, uint8_t* payload,
                                 float* scales, hipStream_t stream);
+hipError_t launch_quantize_pack_batched(const Mat* mts, const float* const* ws,
+                                        uint8_t* const* payloads, float* const* scales,
+                                        int count, hipStream_t stream);
 hipError_t launch_unpack(const Mat& mt, const uint8_t* payload,
                          const float* scales, float* w_out, hipStream_t stream);
 hipError_t launch_gemv(const Mat& mt, const uint8_t* payload, const float* scales,
                        int m, const float* x, float* y, hipStream_t stream);
+hipError_t launch_gemv_batched(const Mat* mts, const uint8_t* const* payloads,
+                               const float* const* scales, int m, const float* const* xs,
+                               float* const* ys, int count, hipStream_t stream);
 hipError_t launch_gemm(const Mat& mt, const uint8_t* payload, const float* scales,
                        int64_t m, const uint16_t* x, float* y, hipStream_t stream);
 hipError_t launch_fill_zero(float* y, int64_t count, hipStream_t stream);

@@ -26,7 +26,23 @@ STATUS_NAMES = {0: "QW_OK", -1: "QW_EBITS", -2: "QW_EGROUP", -3: "QW_ESHAPE", -4
 
 #: symbols declared in include/qw.h
 EXPORTS = ["qw_payload_bytes", "qw_num_scales", "qw_status_string", "qw_last_error",
-           "qw_quantize_pack", "qw_unpack", "qw_gemv", "qw_gemm", "qw_debug_path"]
+           "qw_quantize_pack", "qw_quantize_pack_batched", "qw_unpack", "qw_gemv",
+           "qw_gemv_batched", "qw_gemm", "qw_debug_path"]
+
+
+class QwQuantDesc(ctypes.Structure):
+    """Mirror of `qw_quant_desc` in include/qw.h."""
+    _fields_ = [("w", ctypes.c_void_p), ("payload", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("n", ctypes.c_int64), ("k", ctypes.c_int64), ("group", ctypes.c_int64),
+                ("bits", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class QwGemvDesc(ctypes.Structure):
+    """Mirror of `qw_gemv_desc` in include/qw.h."""
+    _fields_ = [("payload", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("n", ctypes.c_int64), ("k", ctypes.c_int64), ("group", ctypes.c_int64),
+                ("bits", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 _lib = None
 
@@ -63,10 +79,14 @@ def lib():
     L.qw_last_error.restype = ctypes.c_char_p
     L.qw_quantize_pack.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp]
     L.qw_quantize_pack.restype = i32
+    L.qw_quantize_pack_batched.argtypes = [i32, ctypes.POINTER(QwQuantDesc), vp]
+    L.qw_quantize_pack_batched.restype = i32
     L.qw_unpack.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp]
     L.qw_unpack.restype = i32
     L.qw_gemv.argtypes = [i32, i64, i64, i64, vp, vp, i64, vp, vp, vp]
     L.qw_gemv.restype = i32
+    L.qw_gemv_batched.argtypes = [i32, ctypes.POINTER(QwGemvDesc), i64, vp]
+    L.qw_gemv_batched.restype = i32
     L.qw_gemm.argtypes = [i32, i64, i64, i64, vp, vp, i64, vp, vp, vp]
     L.qw_gemm.restype = i32
     L.qw_debug_path.argtypes = [i32, i32, i64, i64, i64, vp, vp]
@@ -112,6 +132,20 @@ def qw_quantize_pack(bits, group, n, k, w, payload, scales, stream=None):
                                   _stream(stream))
 
 
+def make_quant_descs(items):
+    """items: iterable of (bits, group, n, k, w, payload, scales); returns a
+    ctypes array for qw_quantize_pack_batched and its length."""
+    items = list(items)
+    arr = (QwQuantDesc * max(1, len(items)))()
+    for i, (bits, group, n, k, w, payload, scales) in enumerate(items):
+        arr[i] = QwQuantDesc(_ptr(w), _ptr(payload), _ptr(scales), n, k, group, bits, 0)
+    return arr, len(items)
+
+
+def qw_quantize_pack_batched(count, descs, stream=None):
+    return lib().qw_quantize_pack_batched(count, descs, _stream(stream))
+
+
 def qw_unpack(bits, group, n, k, payload, scales, w_out, stream=None):
     return lib().qw_unpack(bits, group, n, k, _ptr(payload), _ptr(scales), _ptr(w_out),
                            _stream(stream))
@@ -120,6 +154,21 @@ def qw_unpack(bits, group, n, k, payload, scales, w_out, stream=None):
 def qw_gemv(bits, group, n, k, payload, scales, m, x, y, stream=None):
     return lib().qw_gemv(bits, group, n, k, _ptr(payload), _ptr(scales), m, _ptr(x), _ptr(y),
                          _stream(stream))
+
+
+def make_gemv_descs(items):
+    """items: iterable of (bits, group, n, k, payload, scales, x, y) with
+    device tensors (or raw addresses); returns a ctypes array for
+    qw_gemv_batched."""
+    items = list(items)
+    arr = (QwGemvDesc * max(1, len(items)))()
+    for i, (bits, group, n, k, payload, scales, x, y) in enumerate(items):
+        arr[i] = QwGemvDesc(_ptr(payload), _ptr(scales), _ptr(x), _ptr(y), n, k, group, bits, 0)
+    return arr, len(items)
+
+
+def qw_gemv_batched(count, descs, m, stream=None):
+    return lib().qw_gemv_batched(count, descs, m, _stream(stream))
 
 
 def qw_gemm(bits, group, n, k, payload, scales, m, x_bf16, y, stream=None):
@@ -156,6 +205,26 @@ def quantize_pack(w, bits, group, stream=None):
     return dict(bits=bits, group=group, shape=[n, k], payload=payload, scales=scales)
 
 
+def quantize_pack_batched(ws, bits, group, stream=None):
+    """Quantize a list of contiguous fp32 [n][k] device tensors (same bits
+    and group) in a few launches; returns their records."""
+    recs = []
+    for w in ws:
+        if w.dtype != torch.float32 or not w.is_contiguous():
+            raise ValueError("each w must be a contiguous float32 tensor")
+        n, k = _nk(w.shape)
+        nb, ns = lib().qw_payload_bytes(bits, n, k), lib().qw_num_scales(group, n, k)
+        if nb < 0 or ns < 0:
+            _check(-1 if bits not in (4, 8) else -2 if ns < 0 else -3, "quantize_pack_batched")
+        recs.append(dict(bits=bits, group=group, shape=[n, k],
+                         payload=torch.empty(nb, dtype=torch.uint8, device=w.device),
+                         scales=torch.empty(ns, dtype=torch.float32, device=w.device)))
+    arr, cnt = make_quant_descs((bits, group, r["shape"][0], r["shape"][1], w, r["payload"],
+                                 r["scales"]) for w, r in zip(ws, recs))
+    _check(qw_quantize_pack_batched(cnt, arr, stream), "qw_quantize_pack_batched")
+    return recs
+
+
 def unpack(rec, out=None, stream=None):
     n, k = _nk(rec["shape"])
     if out is None:
@@ -176,6 +245,21 @@ def gemv(rec, x, out=None, stream=None):
     _check(qw_gemv(rec["bits"], rec["group"], n, k, rec["payload"], rec["scales"], m, x, out,
                    stream), "qw_gemv")
     return out
+
+
+def gemv_batched(recs, xs, outs=None, stream=None):
+    """Independent GEMVs (common m) in a few launches; returns the list of y."""
+    m = xs[0].shape[0]
+    if outs is None:
+        outs = [torch.empty((m, r["shape"][0]), dtype=torch.float32, device=x.device)
+                for r, x in zip(recs, xs)]
+    for r, x in zip(recs, xs):
+        if x.dtype != torch.float32 or not x.is_contiguous() or x.shape != (m, r["shape"][1]):
+            raise ValueError("each x must be a contiguous float32 [m][k] tensor")
+    arr, cnt = make_gemv_descs((r["bits"], r["group"], r["shape"][0], r["shape"][1], r["payload"],
+                                r["scales"], x, y) for r, x, y in zip(recs, xs, outs))
+    _check(qw_gemv_batched(cnt, arr, m, stream), "qw_gemv_batched")
+    return outs
 
 
 def gemm(rec, x_bf16, out=None, stream=None):

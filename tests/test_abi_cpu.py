@@ -85,7 +85,8 @@ def test_validation_before_any_launch():
 
 @pytest.mark.parametrize("bits,group,n,k,al,expect", [
     (4, 32, 64, 256, 16, 1), (8, 128, 64, 256, 16, 1), (8, 512, 4, 512, 16, 1),
-    (8, 4096, 8, 4096, 16, 2), (4, 11008, 4, 11008, 16, 2), (4, 1024, 4, 1024, 16, 2),
+    (8, 4096, 8, 4096, 16, 2), (4, 11008, 4, 11008, 16, 2), (4, 1024, 4, 1024, 16, 1),
+    (4, 2048, 4, 2048, 16, 2),
     (4, 3, 4, 6, 16, 3), (8, 1, 4, 8, 16, 3), (4, 4096 * 16, 16, 4096, 16, 3),
     (4, 32, 64, 256, 4, 3),
 ])
@@ -96,7 +97,7 @@ def test_quantize_dispatch(bits, group, n, k, al, expect):
 
 @pytest.mark.parametrize("op,bits,group,n,k,expect", [
     (2, 4, 128, 4096, 11008, 1), (2, 8, 4096, 4096, 4096, 1), (2, 4, 32, 11008, 4096, 1),
-    (2, 4, 16, 64, 256, 3), (2, 4, 32, 8, 48, 3), (2, 4, 4096 * 8, 8, 4096, 1),
+    (2, 4, 16, 64, 256, 1), (2, 4, 8, 64, 256, 1), (2, 4, 4, 64, 256, 3), (2, 4, 32, 8, 48, 3), (2, 4, 4096 * 8, 8, 4096, 1),
     (2, 4, 3, 8, 48, 3),
     (3, 4, 128, 28672, 8192, 1), (3, 8, 32, 64, 256, 1), (3, 4, 16, 64, 256, 3),
     (3, 4, 32, 64, 96, 3),

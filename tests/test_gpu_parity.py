@@ -105,6 +105,7 @@ def test_subnormal_and_zero_groups(bits):
                         np.zeros((4, 64), np.float32),
                         inputs.weight(4, 12, 64, 1e-3)], axis=0)
     w[18, 5] = np.float32(1e-45)  # smallest subnormal alone in a group
+    w[0, 32:64] = np.linspace(-3.3e38, 3.3e38, 32, dtype=np.float32)  # scale > 2^125 at int4
     for group in (32, 64):
         ref, rec = quant_both(w, bits, group)
         check_unpack(ref, rec)
@@ -272,17 +273,100 @@ def _rows_check(rec, w, bits, group, rows, x=None, y=None):
         assert np.all(np.abs(y[:, rows] - yr) <= GEMV_TOL * B)
 
 
-@pytest.mark.parametrize("layer", [0, 31])
-def test_config4_layers_sampled(layer):
-    rng = np.random.default_rng(layer)
-    for slot, (tag, n, k) in enumerate(inputs.C4_SLOTS):
-        w = inputs.c4_weight(layer, slot)
-        rec = qw.quantize_pack(dev(w), 4, 32)
-        x = inputs.c4_x(k)
-        y = host(qw.gemv(rec, dev(x)))
+def test_config4_layers_sampled():
+    # layers 0 and 31 of the 7B stack: per-matrix quantize, then the decode
+    # GEMVs as one batched call (the launch configuration of the benchmark)
+    # and as single calls; sampled rows against the oracle.
+    rng = np.random.default_rng(4)
+    ws, xs = [], []
+    for layer in (0, 31):
+        for slot, (tag, n, k) in enumerate(inputs.C4_SLOTS):
+            ws.append(inputs.c4_weight(layer, slot))
+            xs.append(dev(inputs.c4_x(k)))
+    recs = qw.quantize_pack_batched([dev(w) for w in ws], 4, 32)
+    ys = [host(y) for y in qw.gemv_batched(recs, xs)]
+    for w, rec, x, y in zip(ws, recs, xs, ys):
+        n, k = w.shape
         rows = np.sort(rng.choice(n, size=96, replace=False))
         rows[0], rows[-1] = 0, n - 1
-        _rows_check(rec, w, 4, 32, rows, x, y)
+        _rows_check(rec, w, 4, 32, rows, host(x), y)
+        y1 = host(qw.gemv(rec, x))
+        _rows_check(rec, w, 4, 32, rows, host(x), y1)
+
+
+@pytest.mark.parametrize("m", [1, 3, 8])
+def test_gemv_batched_mixed(m):
+    # mixed bit widths, groups, shapes, a generic-path matrix, an empty one
+    # and one with k == 0; more than one launch's worth of matrices.
+    specs = []
+    for i in range(40):
+        bits = 4 if i % 3 else 8
+        n = [5, 64, 300, 1000][i % 4]
+        k = [128, 256, 4096, 96][(i // 4) % 4]
+        group = [32, k, 32 * k, 16][i % 4] if bits == 4 else [16, k, 64, 32][i % 4]
+        if (n * k) % group:
+            group = k
+        specs.append((bits, group, n, k))
+    specs += [(4, 6, 8, 24), (8, 32, 0, 64), (4, 32, 7, 0)]
+    refs, recs, xs, xds = [], [], [], []
+    for j, (bits, group, n, k) in enumerate(specs):
+        w = inputs.weight(900 + j, n, k, 0.05)
+        ref = oracle.quantize_pack(w, bits, group)
+        rec = qw.quantize_pack(dev(w), bits, group) if n * k else dict(
+            bits=bits, group=group, shape=[n, k],
+            payload=torch.empty(0, dtype=torch.uint8, device="cuda"),
+            scales=torch.empty(0, dtype=torch.float32, device="cuda"))
+        x = inputs.activations(950 + j, m, k)
+        refs.append(ref); recs.append(rec); xs.append(x); xds.append(dev(x))
+    ys = qw.gemv_batched(recs, xds)
+    for ref, x, y in zip(refs, xs, ys):
+        yr = oracle.gemv_ref(ref, x)
+        B = oracle.error_base(ref, x)
+        assert np.all(np.abs(host(y) - yr) <= GEMV_TOL * B)
+
+
+def test_quantize_pack_batched_mixed():
+    # several (bits, group) classes, a generic-path group, an empty matrix and
+    # more matrices than one launch holds; every output bit-identical
+    specs = [(4, 32, 64, 256)] * 70 + [(8, 128, 33, 512), (4, 4096, 4, 4096), (8, 6, 5, 12),
+                                       (4, 32, 0, 64), (4, 1024, 2, 2048), (8, 8, 3, 8)]
+    ws = [inputs.weight(700 + j, n, k, 0.05) for j, (b, g, n, k) in enumerate(specs)]
+    recs = []
+    for (bits, group, n, k), w in zip(specs, ws):
+        nb, ns = n * k * bits // 8, n * k // group
+        recs.append(dict(bits=bits, group=group, shape=[n, k],
+                         payload=torch.full((nb,), 0x5A, dtype=torch.uint8, device="cuda"),
+                         scales=torch.full((ns,), -1.0, dtype=torch.float32, device="cuda")))
+    wd = [dev(w) for w in ws]
+    arr, cnt = qw.make_quant_descs((r["bits"], r["group"], r["shape"][0], r["shape"][1], w,
+                                    r["payload"], r["scales"]) for r, w in zip(recs, wd))
+    assert qw.qw_quantize_pack_batched(cnt, arr) == 0
+    for (bits, group, n, k), w, rec in zip(specs, ws, recs):
+        ref = oracle.quantize_pack(w, bits, group)
+        assert same_bits(host(rec["payload"]), ref["payload"])
+        assert same_bits(host(rec["scales"]), ref["scales"])
+    # the convenience wrapper takes the same path
+    recs2 = qw.quantize_pack_batched(wd[:70], 4, 32)
+    for w, rec in zip(ws[:70], recs2):
+        ref = oracle.quantize_pack(w, 4, 32)
+        assert same_bits(host(rec["payload"]), ref["payload"])
+
+
+def test_quantize_pack_batched_validation():
+    arr, cnt = qw.make_quant_descs([(4, 32, 64, 256, None, None, None)])
+    assert qw.qw_quantize_pack_batched(cnt, arr) == -5
+    arr, cnt = qw.make_quant_descs([(4, 33, 64, 256, None, None, None)])
+    assert qw.qw_quantize_pack_batched(cnt, arr) == -2
+    assert qw.qw_quantize_pack_batched(-2, arr) == -7
+
+
+def test_gemv_batched_validation():
+    arr, cnt = qw.make_gemv_descs([(4, 32, 64, 128, None, None, None, None)])
+    assert qw.qw_gemv_batched(cnt, arr, 1) == -5
+    arr, cnt = qw.make_gemv_descs([(5, 32, 64, 128, None, None, None, None)])
+    assert qw.qw_gemv_batched(cnt, arr, 1) == -1
+    assert qw.qw_gemv_batched(-1, arr, 1) == -7
+    assert qw.qw_gemv_batched(1, arr, 9) == -4
 
 
 def test_config5_gemm_sampled():
