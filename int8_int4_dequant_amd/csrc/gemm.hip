@@ -15,8 +15,8 @@
 //   * wave w owns columns [64w, 64w+64) of the tile and all 256 rows: 8 x 2
 //     accumulators of 32x32 fp32 (256 accumulation registers per lane).
 //   * X tile (256 x 64 bf16 = 32 KiB) is staged through LDS, double
-//     buffered, with a 16-byte-chunk XOR swizzle so that the fragment reads
-//     (32 consecutive rows, same k) hit distinct banks.
+//     buffered, rows padded to 144 bytes so that the fragment reads (16
+//     consecutive rows per phase, same k) hit distinct banks.
 //   * Weight fragments come straight from global memory: within one MFMA the
 //     k-slots are a free permutation shared by A and B, so lane group g
 //     (lanes 32g..32g+31) takes the contiguous k range [32g, 32g+32) of the
@@ -35,8 +35,13 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 256, BN = 256, BK = 64;
+// LDS row stride of the X tile: 128 bytes of data + 16 bytes of padding, so
+// that 16 consecutive rows (one 16-lane phase of a ds_read_b128) start 36
+// dwords apart and cover 16 distinct 4-bank groups of the 64 banks.
+constexpr int XS = BK * 2 + 16;
 
 struct GemmArgs {
   const uint16_t* x;
@@ -49,7 +54,11 @@ struct GemmArgs {
   int64_t group;
   int per_row_groups;   // 1: k % group == 0 ; 0: group % k == 0
   int64_t groups_per_row;
-  int group_shift;      // log2(group) when per_row_groups and group is a power of two, else -1
+  // Scale index within a row, kk / group for kk < 2^31 and group >= 2, without a
+  // division: t = umulhi(kk, gdiv_mul), q = (t + ((kk - t) >> 1)) >> (gdiv_shift - 1)
+  // (Granlund and Montgomery, "Division by invariant integers using
+  // multiplication", 1994).  gmask is 0 when a whole row shares one scale.
+  uint32_t gdiv_mul, gdiv_shift, gmask;
   int tiles_m, tiles_n;
   int xcd_map;          // 1: XCD-aware block order
 };
@@ -61,7 +70,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 }
 
 // 8 int4 codes (one dword, element order) -> bf16(fl32(q * s)), packed in 4 dwords.
-__device__ __forceinline__ uint4 dequant8_int4(uint32_t w, float s) {
+__device__ __forceinline__ u32x4 dequant8_int4(uint32_t w, float s) {
   const uint32_t lo = w & 0x0F0F0F0Fu;
   const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;
   const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);  // e0, e2  (u * 2^-9)
@@ -77,12 +86,12 @@ __device__ __forceinline__ uint4 dequant8_int4(uint32_t w, float s) {
   const float q3 = __builtin_fmaf(c.y, 512.0f, -8.0f) * s;
   const float q5 = __builtin_fmaf(d.x, 512.0f, -8.0f) * s;
   const float q7 = __builtin_fmaf(d.y, 512.0f, -8.0f) * s;
-  return make_uint4(pack_bf16x2(q0, q1), pack_bf16x2(q2, q3), pack_bf16x2(q4, q5),
-                    pack_bf16x2(q6, q7));
+  return u32x4{pack_bf16x2(q0, q1), pack_bf16x2(q2, q3), pack_bf16x2(q4, q5),
+               pack_bf16x2(q6, q7)};
 }
 
 // 8 int8 codes (two dwords, element order) -> 4 dwords of bf16 pairs.
-__device__ __forceinline__ uint4 dequant8_int8(uint32_t w0, uint32_t w1, float s) {
+__device__ __forceinline__ u32x4 dequant8_int8(uint32_t w0, uint32_t w1, float s) {
   const float q0 = (float)(int)(int8_t)(w0) * s;
   const float q1 = (float)(int)(int8_t)(w0 >> 8) * s;
   const float q2 = (float)(int)(int8_t)(w0 >> 16) * s;
@@ -91,20 +100,45 @@ __device__ __forceinline__ uint4 dequant8_int8(uint32_t w0, uint32_t w1, float s
   const float q5 = (float)(int)(int8_t)(w1 >> 8) * s;
   const float q6 = (float)(int)(int8_t)(w1 >> 16) * s;
   const float q7 = (float)((int)w1 >> 24) * s;
-  return make_uint4(pack_bf16x2(q0, q1), pack_bf16x2(q2, q3), pack_bf16x2(q4, q5),
-                    pack_bf16x2(q6, q7));
+  return u32x4{pack_bf16x2(q0, q1), pack_bf16x2(q2, q3), pack_bf16x2(q4, q5),
+               pack_bf16x2(q6, q7)};
+}
+
+// Workgroup barrier for LDS hand-off only: wait for this wave's LDS
+// accesses, then s_barrier.  (__syncthreads also waits for every
+// outstanding global load, which would drain the prefetch pipeline below.)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt untouched
+  __builtin_amdgcn_s_barrier();
 }
 
 template <int BITS>
 struct BRegs {
   // raw payload of the lane's 32 codes for one N block
-  uint4 p[BITS == 4 ? 1 : 2];
+  u32x4 p[BITS == 4 ? 1 : 2];
   float s;
 };
 
+// Software pipeline.  A k-step (BK = 64) is four sub-steps of k = 16; one
+// sub-step is 16 MFMAs per wave (8 row blocks x 2 column blocks).  Per
+// k-step ks, with the X tile double-buffered in LDS (buffer ks&1), the A
+// fragments double-buffered in registers and the dequantized B fragments of
+// two k-steps in registers:
+//   sub-step 0: store X(ks+1) (loaded one k-step ago) into LDS buffer
+//               (ks+1)&1, issue the loads of X(ks+2);
+//   sub-step 1: dequantize the first column block of W(ks+1);
+//   sub-step 2: dequantize the second one, issue the loads of W(ks+3) into
+//               the registers just freed, then the k-step's only barrier;
+//   sub-step 3: (after the barrier) read A(ks+1, sub-step 0).
+// Every sub-step also reads the next sub-step's A fragments from LDS while
+// its MFMAs run.  A buffer is rewritten (sub-step 0 of step ks+2) only after
+// the barrier of step ks+1, which every wave reaches after its last read of
+// it (sub-step 2 of step ks), so one barrier per k-step suffices.  Loads past
+// the last k-step re-read the last one (their results are never used), so
+// the loop body has no branches and the compiler's wait counts stay exact.
 template <int BITS>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][BM * BK * 2];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BM * XS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -127,59 +161,78 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   }
   const int64_t m0 = (int64_t)tm * BM;
   const int n0 = tn * BN;
+  const int nk = a.k / BK;
+  const int klast = (nk - 1) * BK;
 
   // ---- per-lane weight rows (two 32-column blocks per wave)
-  int nrow[2];
   bool nvalid[2];
-  int64_t prow[2], srow[2];
+  const uint8_t* prow[2];
+  const float* srow[2];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int nn = n0 + 64 * wave + 32 * nb + l32;
     nvalid[nb] = nn < a.n;
-    nrow[nb] = nvalid[nb] ? nn : a.n - 1;
-    prow[nb] = (int64_t)nrow[nb] * a.row_stride_b;
-    srow[nb] = a.per_row_groups ? (int64_t)nrow[nb] * a.groups_per_row
-                                : ((int64_t)nrow[nb] * a.k) / a.group;
+    const int row = nvalid[nb] ? nn : a.n - 1;
+    prow[nb] = a.payload + (int64_t)row * a.row_stride_b + 16 * g * (BITS / 4);
+    srow[nb] = a.scales + (a.per_row_groups ? (int64_t)row * a.groups_per_row
+                                            : ((int64_t)row * a.k) / a.group);
   }
-
-  // ---- X tile loader: 2048 16-byte chunks, 8 per thread
-  uint4 xa[8];
-  auto load_x = [&](int k0) {
+  // ---- per-thread X chunks: chunk i = tile row (tid>>3) + 32*i, 16-byte column tid&7.
+  // Rows past the end of X (last M tile only) re-read row m-1; their outputs are never
+  // stored.
+  const uint16_t* xrow[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int id = tid + 256 * i;
-      const int row = id >> 3, kc = id & 7;
-      const int64_t mm = m0 + row;
-      if (mm < a.m)
-        xa[i] = *reinterpret_cast<const uint4*>(a.x + mm * a.k + k0 + kc * 8);
-      else
-        xa[i] = make_uint4(0u, 0u, 0u, 0u);
-    }
-  };
-  auto store_x = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int id = tid + 256 * i;
-      const int row = id >> 3, kc = id & 7;
-      *reinterpret_cast<uint4*>(&lds[buf][row * 128 + ((kc ^ (row & 7)) << 4)]) = xa[i];
-    }
-  };
+  for (int i = 0; i < 8; ++i) {
+    const int64_t mm = m0 + (tid >> 3) + 32 * i;
+    xrow[i] = a.x + (mm < a.m ? mm : a.m - 1) * a.k + (tid & 7) * 8;
+  }
+  const int wr_off = (tid >> 3) * XS + (tid & 7) * 16;   // + i * 32 * XS
+  const int rd_off = l32 * XS + g * 64;                  // + mb * 32 * XS + s * 16
 
-  BRegs<BITS> br[2];
-  auto load_w = [&](int k0) {
-    const int kk = k0 + 32 * g;  // first code of this lane's range
-    int64_t gi;
-    if (a.per_row_groups)
-      gi = a.group_shift >= 0 ? (int64_t)(kk >> a.group_shift) : (int64_t)kk / a.group;
-    else
-      gi = 0;
+  auto load_x = [&](u32x4 (&xa)[8], int k0) __attribute__((always_inline)) {
+    k0 = k0 < klast ? k0 : klast;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xa[i] = *reinterpret_cast<const u32x4*>(xrow[i] + k0);
+  };
+  auto store_x = [&](const u32x4 (&xv)[8], int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<u32x4*>(&lds[buf * (BM * XS) + wr_off + i * 32 * XS]) = xv[i];
+  };
+  auto load_w = [&](BRegs<BITS> (&br)[2], int k0) __attribute__((always_inline)) {
+    k0 = k0 < klast ? k0 : klast;
+    const uint32_t kk = (uint32_t)(k0 + 32 * g);  // first code of this lane's range
+    const uint32_t t = __umulhi(kk, a.gdiv_mul);
+    const uint32_t gi = ((t + ((kk - t) >> 1)) >> (a.gdiv_shift - 1)) & a.gmask;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      const uint8_t* src = a.payload + prow[nb] + (int64_t)kk * BITS / 8;
-      br[nb].p[0] = *reinterpret_cast<const uint4*>(src);
-      if (BITS == 8) br[nb].p[BITS == 8 ? 1 : 0] = *reinterpret_cast<const uint4*>(src + 16);
-      br[nb].s = a.scales[srow[nb] + gi];
+      const uint8_t* src = prow[nb] + (int64_t)k0 * BITS / 8;
+      br[nb].p[0] = *reinterpret_cast<const u32x4*>(src);
+      if constexpr (BITS == 8) br[nb].p[1] = *reinterpret_cast<const u32x4*>(src + 16);
+      br[nb].s = srow[nb][gi];
     }
+  };
+  auto dequant_nb = [&](const BRegs<BITS>& br, u32x4 (&bq)[4]) __attribute__((always_inline)) {
+    const float s = br.s;
+    if constexpr (BITS == 4) {
+      const u32x4 p = br.p[0];
+      bq[0] = dequant8_int4(p.x, s);
+      bq[1] = dequant8_int4(p.y, s);
+      bq[2] = dequant8_int4(p.z, s);
+      bq[3] = dequant8_int4(p.w, s);
+    } else {
+      const u32x4 p0 = br.p[0], p1 = br.p[1];
+      bq[0] = dequant8_int8(p0.x, p0.y, s);
+      bq[1] = dequant8_int8(p0.z, p0.w, s);
+      bq[2] = dequant8_int8(p1.x, p1.y, s);
+      bq[3] = dequant8_int8(p1.z, p1.w, s);
+    }
+  };
+  auto read_a = [&](u32x4 (&af)[8], int buf, int s) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+      af[mb] = *reinterpret_cast<const u32x4*>(
+          &lds[buf * (BM * XS) + rd_off + mb * 32 * XS + s * 16]);
   };
 
   f32x16 acc[8][2];
@@ -190,56 +243,63 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nk = a.k / BK;
-  load_x(0);
-  load_w(0);
-  store_x(0);
-  __syncthreads();
+  auto mfma16 = [&](const u32x4 (&af)[8], const u32x4 (&bq)[2][4], int s)
+      __attribute__((always_inline)) {
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, af[mb]), __builtin_bit_cast(bf16x8, bq[nb][s]),
+            acc[mb][nb], 0, 0, 0);
+  };
 
-  for (int ks = 0; ks < nk; ++ks) {
-    const int buf = ks & 1;
-    // dequantize this step's weight fragments: bq[nb][s] = 8 bf16 of k = 32g + 8s ..
-    uint4 bq[2][4];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const float s = br[nb].s;
-      if (BITS == 4) {
-        const uint4 p = br[nb].p[0];
-        bq[nb][0] = dequant8_int4(p.x, s);
-        bq[nb][1] = dequant8_int4(p.y, s);
-        bq[nb][2] = dequant8_int4(p.z, s);
-        bq[nb][3] = dequant8_int4(p.w, s);
-      } else {
-        const uint4 p0 = br[nb].p[0], p1 = br[nb].p[BITS == 8 ? 1 : 0];
-        bq[nb][0] = dequant8_int8(p0.x, p0.y, s);
-        bq[nb][1] = dequant8_int8(p0.z, p0.w, s);
-        bq[nb][2] = dequant8_int8(p1.x, p1.y, s);
-        bq[nb][3] = dequant8_int8(p1.z, p1.w, s);
-      }
-    }
-    if (ks + 1 < nk) {
-      load_x((ks + 1) * BK);
-      load_w((ks + 1) * BK);
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-#pragma unroll
-      for (int mb = 0; mb < 8; ++mb) {
-        const int row = mb * 32 + l32;
-        const int kc = 4 * g + s;
-        const uint4 av = *reinterpret_cast<const uint4*>(&lds[buf][row * 128 + ((kc ^ (row & 7)) << 4)]);
-        const bf16x8 af = __builtin_bit_cast(bf16x8, av);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              af, __builtin_bit_cast(bf16x8, bq[nb][s]), acc[mb][nb], 0, 0, 0);
-      }
-    }
-    if (ks + 1 < nk) {
-      store_x(buf ^ 1);
-      __syncthreads();
-    }
+  // ---- prologue: X(0) in LDS buffer 0, X(1) in flight, B(0) dequantized, W(1) and
+  // W(2) in flight, A(0, sub-step 0) in registers.
+  u32x4 xa[8];
+  BRegs<BITS> brE[2], brO[2];   // raw W of even / odd k-steps
+  u32x4 bqE[2][4], bqO[2][4];   // dequantized B of even / odd k-steps
+  u32x4 af0[8], af1[8];
+  load_x(xa, 0);
+  load_w(brE, 0);
+  load_w(brO, BK);
+  store_x(xa, 0);
+  load_x(xa, BK);
+  dequant_nb(brE[0], bqE[0]);
+  dequant_nb(brE[1], bqE[1]);
+  load_w(brE, 2 * BK);
+  lds_barrier();
+  read_a(af0, 0, 0);
+
+  // One k-step.  bq_cur = B(ks); br_nxt = W(ks+1), refilled with W(ks+3); bq_nxt <- B(ks+1).
+  auto kstep = [&](int ks, const u32x4 (&bq_cur)[2][4], BRegs<BITS> (&br_nxt)[2],
+                   u32x4 (&bq_nxt)[2][4]) __attribute__((always_inline)) {
+    const int cur = ks & 1, nxt = cur ^ 1;
+    // sub-step 0
+    store_x(xa, nxt);
+    load_x(xa, (ks + 2) * BK);
+    read_a(af1, cur, 1);
+    mfma16(af0, bq_cur, 0);
+    // sub-step 1
+    read_a(af0, cur, 2);
+    dequant_nb(br_nxt[0], bq_nxt[0]);
+    mfma16(af1, bq_cur, 1);
+    // sub-step 2
+    read_a(af1, cur, 3);
+    dequant_nb(br_nxt[1], bq_nxt[1]);
+    load_w(br_nxt, (ks + 3) * BK);
+    mfma16(af0, bq_cur, 2);
+    lds_barrier();
+    // sub-step 3
+    read_a(af0, nxt, 0);
+    mfma16(af1, bq_cur, 3);
+  };
+  int ks = 0;
+  for (; ks + 1 < nk; ks += 2) {
+    kstep(ks, bqE, brO, bqO);
+    kstep(ks + 1, bqO, brE, bqE);
   }
+  if (ks < nk) kstep(ks, bqE, brO, bqO);
 
   // ---- epilogue: D[i][j] of a 32x32 block sits in lane j + 32*((i/4)%2), register 4*(i/8) + i%4
 #pragma unroll
@@ -310,11 +370,18 @@ hipError_t launch_gemm(const Mat& mt, const uint8_t* payload, const float* scale
     a.group = mt.group;
     a.per_row_groups = mt.k % mt.group == 0 ? 1 : 0;
     a.groups_per_row = a.per_row_groups ? mt.k / mt.group : 0;
-    a.group_shift = -1;
-    if (a.per_row_groups && (mt.group & (mt.group - 1)) == 0) {
-      int sh = 0;
-      while ((1ll << sh) < mt.group) ++sh;
-      a.group_shift = sh;
+    if (a.per_row_groups) {
+      // group >= 32 here, so l = ceil(log2 group) >= 5
+      const uint32_t d = (uint32_t)mt.group;
+      uint32_t l = 0;
+      while ((1ull << l) < d) ++l;
+      a.gdiv_mul = (uint32_t)((((1ull << (32 + l)) / d) + 1) & 0xffffffffu);
+      a.gdiv_shift = l;
+      a.gmask = 0xffffffffu;
+    } else {
+      a.gdiv_mul = 0;
+      a.gdiv_shift = 1;
+      a.gmask = 0;
     }
     const int64_t tm = (m + BM - 1) / BM;
     const int64_t tn = (mt.n + BN - 1) / BN;
