@@ -60,8 +60,27 @@ struct GemmArgs {
   // multiplication", 1994).  gmask is 0 when a whole row shares one scale.
   uint32_t gdiv_mul, gdiv_shift, gmask;
   int tiles_m, tiles_n;
-  int xcd_map;          // 1: XCD-aware block order
+  int xcd_map;          // 1: XCD-aware tile order
+  // Tiles [0, full_tiles) take one block each.  Every later tile takes two
+  // blocks, one per half of the k-steps (the first nk_lo steps, then the
+  // rest), which add their partial sums into Y (zeroed beforehand).
+  int full_tiles;
+  int nk_lo;
 };
+
+// Tile index -> (tile row, tile column).  With the XCD-aware order, tiles
+// t, t+8, t+16, ... (dispatched to one XCD) walk all M tiles of one N tile,
+// so that XCD's L2 keeps the weight tile while the M tiles reuse it.
+__device__ __forceinline__ void tile_coords(const GemmArgs& a, int t, int& tm, int& tn) {
+  if (a.xcd_map) {
+    const int xcd = t & 7, j = t >> 3;
+    tm = j % a.tiles_m;
+    tn = xcd + 8 * (j / a.tiles_m);
+  } else {
+    tm = t % a.tiles_m;
+    tn = t / a.tiles_m;
+  }
+}
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -112,6 +131,37 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
+// Scheduling patterns (group masks: 0x002 VALU, 0x008 MFMA, 0x020 global
+// load, 0x100 LDS read, 0x200 LDS write).
+// Sub-step with the X hand-off: 8 A reads, then MFMAs interleaved with the
+// 8 LDS stores of X and the 8 global loads that refill its registers.
+__device__ __forceinline__ void sched_substep_x() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+  }
+}
+// Sub-step with NV VALU instructions after each MFMA and NG global loads at the end.
+template <int NV, int NG>
+__device__ __forceinline__ void sched_substep() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+  }
+  if constexpr (NG > 0) __builtin_amdgcn_sched_group_barrier(0x020, NG, 0);
+}
+
 template <int BITS>
 struct BRegs {
   // raw payload of the lane's 32 codes for one N block
@@ -146,23 +196,32 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   const int g = lane >> 5;    // lane group: k range [32g, 32g+32) of a step
   const int l32 = lane & 31;
 
-  // ---- block -> tile (XCD-aware when the tile grid allows it)
-  int tm, tn;
+  // ---- block -> tile and k-step range
+  int t, kbeg, kend;
+  bool split;
   {
     const int b = blockIdx.x;
-    if (a.xcd_map) {
-      const int xcd = b & 7, j = b >> 3;
-      tm = j % a.tiles_m;
-      tn = xcd + 8 * (j / a.tiles_m);
+    const int nk = a.k / BK;
+    if (b < a.full_tiles) {
+      t = b;
+      kbeg = 0;
+      kend = nk;
+      split = false;
     } else {
-      tm = b % a.tiles_m;
-      tn = b / a.tiles_m;
+      const int i = b - a.full_tiles;
+      t = a.full_tiles + (i >> 1);
+      kbeg = (i & 1) ? a.nk_lo : 0;
+      kend = (i & 1) ? nk : a.nk_lo;
+      split = true;
     }
   }
+  int tm, tn;
+  tile_coords(a, t, tm, tn);
   const int64_t m0 = (int64_t)tm * BM;
   const int n0 = tn * BN;
-  const int nk = a.k / BK;
-  const int klast = (nk - 1) * BK;
+  const int nsteps = kend - kbeg;
+  const int kfirst = kbeg * BK;
+  const int klast = (kend - 1) * BK;
 
   // ---- per-lane weight rows (two 32-column blocks per wave)
   bool nvalid[2];
@@ -260,46 +319,55 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
   BRegs<BITS> brE[2], brO[2];   // raw W of even / odd k-steps
   u32x4 bqE[2][4], bqO[2][4];   // dequantized B of even / odd k-steps
   u32x4 af0[8], af1[8];
-  load_x(xa, 0);
-  load_w(brE, 0);
-  load_w(brO, BK);
+  load_x(xa, kfirst);
+  load_w(brE, kfirst);
+  load_w(brO, kfirst + BK);
   store_x(xa, 0);
-  load_x(xa, BK);
+  load_x(xa, kfirst + BK);
   dequant_nb(brE[0], bqE[0]);
   dequant_nb(brE[1], bqE[1]);
-  load_w(brE, 2 * BK);
+  load_w(brE, kfirst + 2 * BK);
   lds_barrier();
   read_a(af0, 0, 0);
 
-  // One k-step.  bq_cur = B(ks); br_nxt = W(ks+1), refilled with W(ks+3); bq_nxt <- B(ks+1).
-  auto kstep = [&](int ks, const u32x4 (&bq_cur)[2][4], BRegs<BITS> (&br_nxt)[2],
+  // One k-step (i = local step number).  bq_cur = B(i); br_nxt = W(i+1), refilled with
+  // W(i+3); bq_nxt <- B(i+1).
+  auto kstep = [&](int i, const u32x4 (&bq_cur)[2][4], BRegs<BITS> (&br_nxt)[2],
                    u32x4 (&bq_nxt)[2][4]) __attribute__((always_inline)) {
-    const int cur = ks & 1, nxt = cur ^ 1;
+    const int cur = i & 1, nxt = cur ^ 1;
     // sub-step 0
-    store_x(xa, nxt);
-    load_x(xa, (ks + 2) * BK);
     read_a(af1, cur, 1);
+    store_x(xa, nxt);
+    load_x(xa, kfirst + (i + 2) * BK);
     mfma16(af0, bq_cur, 0);
+    sched_substep_x();
+    __builtin_amdgcn_sched_barrier(0);
     // sub-step 1
     read_a(af0, cur, 2);
     dequant_nb(br_nxt[0], bq_nxt[0]);
     mfma16(af1, bq_cur, 1);
+    sched_substep<8, 0>();
+    __builtin_amdgcn_sched_barrier(0);
     // sub-step 2
     read_a(af1, cur, 3);
     dequant_nb(br_nxt[1], bq_nxt[1]);
-    load_w(br_nxt, (ks + 3) * BK);
+    load_w(br_nxt, kfirst + (i + 3) * BK);
     mfma16(af0, bq_cur, 2);
+    sched_substep<8, 6>();
+    __builtin_amdgcn_sched_barrier(0);
     lds_barrier();
     // sub-step 3
     read_a(af0, nxt, 0);
     mfma16(af1, bq_cur, 3);
+    sched_substep<2, 0>();
+    __builtin_amdgcn_sched_barrier(0);
   };
-  int ks = 0;
-  for (; ks + 1 < nk; ks += 2) {
-    kstep(ks, bqE, brO, bqO);
-    kstep(ks + 1, bqO, brE, bqE);
+  int i = 0;
+  for (; i + 1 < nsteps; i += 2) {
+    kstep(i, bqE, brO, bqO);
+    kstep(i + 1, bqO, brE, bqE);
   }
-  if (ks < nk) kstep(ks, bqE, brO, bqO);
+  if (i < nsteps) kstep(i, bqE, brO, bqO);
 
   // ---- epilogue: D[i][j] of a 32x32 block sits in lane j + 32*((i/4)%2), register 4*(i/8) + i%4
 #pragma unroll
@@ -311,9 +379,28 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t mm = m0 + mb * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (mm < a.m) a.y[mm * a.n + nn] = acc[mb][nb][r];
+        if (mm < a.m) {
+          if (split)
+            unsafeAtomicAdd(&a.y[mm * a.n + nn], acc[mb][nb][r]);
+          else
+            a.y[mm * a.n + nn] = acc[mb][nb][r];
+        }
       }
     }
+}
+
+// Zeroes the output tiles that two blocks accumulate into: block (tile
+// t = full_tiles + blockIdx.x / 16, 16-row slab blockIdx.x % 16).
+__global__ __launch_bounds__(256) void gemm_zero_split_tiles(GemmArgs a) {
+  const int t = a.full_tiles + (int)(blockIdx.x >> 4);
+  int tm, tn;
+  tile_coords(a, t, tm, tn);
+  const int nn = tn * BN + (int)threadIdx.x;
+  if (nn >= a.n) return;
+  const int64_t r0 = (int64_t)tm * BM + 16 * (blockIdx.x & 15);
+#pragma unroll 4
+  for (int r = 0; r < 16; ++r)
+    if (r0 + r < a.m) a.y[(r0 + r) * a.n + nn] = 0.0f;
 }
 
 // ---------------------------------------------------------- generic kernel
@@ -355,6 +442,21 @@ int gemm_path(const Mat& mt, const uint8_t* payload, const uint16_t* x) {
   return PATH_GENERIC;
 }
 
+// Compute units of the current device (cached per device).
+static int compute_units() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 hipError_t launch_gemm(const Mat& mt, const uint8_t* payload, const float* scales, int64_t m,
                        const uint16_t* x, float* y, hipStream_t st) {
   if (gemm_path(mt, payload, x) == PATH_FAST) {
@@ -389,7 +491,23 @@ hipError_t launch_gemm(const Mat& mt, const uint8_t* payload, const float* scale
     a.tiles_m = (int)tm;
     a.tiles_n = (int)tn;
     a.xcd_map = (tn % 8 == 0) ? 1 : 0;
-    const unsigned grid = (unsigned)(tm * tn);
+    // One block per compute unit at a time (the block holds all of a CU's
+    // registers).  If the last round of tiles would leave at least half the
+    // compute units idle, split each of its tiles in two along K.
+    const int tiles = (int)(tm * tn);
+    const int nk = (int)(mt.k / BK);
+    const int cus = compute_units();
+    const int rem = tiles - ((tiles - 1) / cus) * cus;  // tiles in the last round
+    a.full_tiles = tiles;
+    a.nk_lo = 0;
+    if (nk >= 2 && 2 * rem <= cus) {
+      a.full_tiles = tiles - rem;
+      a.nk_lo = nk / 2;
+      gemm_zero_split_tiles<<<(unsigned)rem * 16, 256, 0, st>>>(a);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    const unsigned grid = (unsigned)(a.full_tiles + 2 * (tiles - a.full_tiles));
     if (mt.bits == 4)
       gemm_kernel<4><<<grid, 256, 0, st>>>(a);
     else

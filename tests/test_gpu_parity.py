@@ -233,6 +233,35 @@ def test_codes_path_agrees_with_dequantized_path():
             assert np.all(np.abs(yv - xf @ w_hat.T) <= GEMV_TOL * B)
 
 
+# The tiled kernel runs one 256 x 256 output tile per block.  When the last
+# round of tiles would leave at least half the compute units idle, those
+# tiles are split in two along K and both halves add into Y (zeroed first).
+# Shapes: every tile split (small), every tile whole (140 tiles), and 256
+# whole tiles followed by 100 split ones; k = 192 gives halves of one and two
+# k-steps.
+@pytest.mark.parametrize("bits,group,m,n,k", [
+    (4, 64, 300, 520, 192),
+    (4, 128, 64, 256 * 140, 128),
+    (8, 128, 300, 256 * 178 - 40, 128),
+])
+def test_gemm_split_tail(bits, group, m, n, k):
+    w = inputs.weight(n + k, n, k, 0.02)
+    ref, rec = quant_both(w, bits, group)
+    check_gemm(ref, rec, inputs.bf16_activations(m + 7, m, k))
+
+
+def test_gemm_ignores_stale_output():
+    # the split tiles accumulate into Y: stale contents (NaN) must not leak
+    w = inputs.weight(21, 300, 512, 0.02)
+    ref, rec = quant_both(w, 4, 32)
+    xb = inputs.bf16_activations(22, 40, 512)
+    out = torch.full((40, 300), float("nan"), dtype=torch.float32, device="cuda")
+    y = host(qw.gemm(rec, dev(xb.view(np.int16)), out=out))
+    yr = oracle.gemm_ref(ref, xb)
+    B = oracle.error_base(ref, oracle.bf16_bits_to_f32(xb))
+    assert np.all(np.abs(y - yr) <= GEMM_TOL * B)
+
+
 def test_gemm_deterministic():
     w = inputs.weight(9, 512, 1024, 0.02)
     rec = qw.quantize_pack(dev(w), 4, 128)
