@@ -16,10 +16,11 @@
 // build never enables fast-math or denormal flushing.
 //
 // Kernel families:
-//   subgroup  group a power of two in [8, 1024]: each lane owns 16
-//             consecutive weights (four 16-byte loads; 8 for group 8); the
-//             lanes of a group reduce max|w| with cross-lane shuffles.  One
-//             pass, fully coalesced.
+//   subgroup  group a power of two in [8, 1024]: a wave owns 256
+//             consecutive float4 vectors, each load instruction reading a
+//             contiguous 1 KiB run; a group is consecutive lanes of one
+//             instruction (or whole instructions for group >= 512) and its
+//             max|w| is reduced with cross-lane shuffles.  One pass.
 //   block     group % 4 == 0 and group <= 16384: one 256-thread block per
 //             group; weights stay in registers between the max and the code
 //             pass.
