@@ -164,8 +164,8 @@ def main():
         (4, 32, n, k, W[i], P[i], S[i]) for i, (n, k) in enumerate(shapes))
     descs, ndesc = qw.make_gemv_descs(
         (4, 32, n, k, P[i], S[i], xs[k], Y[i]) for i, (n, k) in enumerate(shapes))
-    quant_launches = (nq + 63) // 64
-    gemv_launches = (ndesc + 31) // 32
+    quant_launches = (nq + qw.BATCH_PER_LAUNCH - 1) // qw.BATCH_PER_LAUNCH
+    gemv_launches = (ndesc + qw.BATCH_PER_LAUNCH - 1) // qw.BATCH_PER_LAUNCH
 
     def run_step(ev=None):
         if ev is not None:

@@ -73,6 +73,10 @@ enum qw_status {
     QW_ECOUNT = -7   /* batched call: count < 0 or a descriptor is invalid   */
 };
 
+/* Largest number of matrices the batched calls put into one kernel launch
+ * (their descriptors travel as kernel arguments). */
+#define QW_BATCH_PER_LAUNCH 256
+
 /* Bytes of packed codes for an n x k matrix: n*k*bits/8 (-1 if invalid). */
 int64_t qw_payload_bytes(int bits, int64_t n, int64_t k);
 
@@ -116,7 +120,9 @@ typedef struct qw_quant_desc {
  * Batched quantize/pack: `count` independent matrices (for instance every
  * linear layer of a model at load time), each exactly as qw_quantize_pack
  * would produce it, enqueued as a few large launches instead of one per
- * matrix.  `descs` is a HOST array read before the call returns; outputs
+ * matrix (matrices of the same bits and group share a launch, up to
+ * QW_BATCH_PER_LAUNCH of them).  `descs` is a HOST array read before the
+ * call returns; outputs
  * must not overlap each other or any input.  Every entry is validated
  * first; on any invalid entry nothing is enqueued and its status (or
  * QW_ECOUNT for count < 0 / reserved != 0) is returned.
@@ -162,8 +168,9 @@ typedef struct qw_gemv_desc {
 /*
  * Batched dequantizing GEMV: `count` independent products y_i = x_i * W_i^T
  * with a common m (0 <= m <= 8), each exactly as qw_gemv would compute it,
- * enqueued as a few launches that stream the weights back to back instead
- * of one launch per matrix (the fixed cost of many short kernels is what
+ * enqueued as a few launches (up to QW_BATCH_PER_LAUNCH matrices of one bit
+ * width each) that stream the weights back to back instead of one launch
+ * per matrix (the fixed cost of many short kernels is what
  * dominates a decode step otherwise -- page "Huit bits, puis quatre",
  * section "La vitesse").  `descs` is a HOST array of `count` entries, read
  * before the call returns.  No y_i may overlap another y_i or any input.

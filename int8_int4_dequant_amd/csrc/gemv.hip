@@ -93,11 +93,14 @@ __device__ __forceinline__ void wave_reduce_scatter(float (&v)[V], int lane) {
   for (int s = 0; s < LOGV; ++s) {
     const int o = 32 >> s;
     const int h = V >> (s + 1);
-    const bool up = (lane & o) != 0;
+    // lane-dependent choice by bit masks: a select between two array
+    // elements can otherwise become a dynamically indexed (scratch) load
+    const uint32_t up = (lane & o) ? 0xffffffffu : 0u;
 #pragma unroll
     for (int i = 0; i < h; ++i) {
-      const float send = up ? v[i] : v[i + h];
-      const float keep = up ? v[i + h] : v[i];
+      const uint32_t lo = __float_as_uint(v[i]), hi = __float_as_uint(v[i + h]);
+      const float send = __uint_as_float((lo & up) | (hi & ~up));
+      const float keep = __uint_as_float((hi & up) | (lo & ~up));
       v[i] = keep + __shfl_xor(send, o);
     }
   }
@@ -161,30 +164,39 @@ struct GemvDesc {
   int gpr;             // groups per row when per_row
 };
 
-constexpr int GEMV_NB = 32;  // matrices per launch (descriptors travel as kernel arguments)
+// Matrices per launch: the descriptors travel as kernel arguments (up to
+// ~21 KB for a whole model's decode pass in one launch; a single matrix
+// launches with a one-entry table).
+constexpr int GEMV_NB = QW_BATCH_PER_LAUNCH;
 
+template <int NB>
 struct GemvBatch {
-  int item0[GEMV_NB];  // first work item of each matrix (contiguous: one scalar load)
-  GemvDesc d[GEMV_NB];
+  int item0[NB];       // first work item of each matrix, ascending
+  GemvDesc d[NB];
   int count;           // descriptors in use
   int items;           // total work items
 };
 
-// The matrix work item `item` belongs to: compares against all item0 values
-// (kept together at the start of the kernel arguments, loaded by a few
-// scalar loads) and reads that descriptor in place from the kernel-argument
-// segment (indexing the by-value parameter would copy it to memory).
-__device__ __forceinline__ int find_desc(const GemvBatch& b, int item) {
-  typedef const __attribute__((address_space(4))) GemvBatch* KArg;
+// The matrix work item `item` belongs to: a binary search over item0
+// (ascending, item0[0] = 0), read in place from the kernel-argument segment
+// with scalar loads (indexing the by-value parameter would copy it to
+// memory).  Wave-uniform.
+template <int NB>
+__device__ __forceinline__ int find_desc(const GemvBatch<NB>& b, int item) {
+  if constexpr (NB == 1) return 0;
+  typedef const __attribute__((address_space(4))) GemvBatch<NB>* KArg;
   const KArg kb = (KArg)__builtin_amdgcn_kernarg_segment_ptr();
-  int di = 0;
-#pragma unroll
-  for (int i = 1; i < GEMV_NB; ++i) di += (i < b.count && item >= kb->item0[i]) ? 1 : 0;
-  return di;
+  int lo = 0, hi = b.count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (kb->item0[mid] <= item) lo = mid; else hi = mid - 1;
+  }
+  return lo;
 }
 
+template <int NB>
 __device__ __forceinline__ GemvDesc load_desc(int di) {
-  typedef const __attribute__((address_space(4))) GemvBatch* KArg;
+  typedef const __attribute__((address_space(4))) GemvBatch<NB>* KArg;
   const KArg kb = (KArg)__builtin_amdgcn_kernarg_segment_ptr();
   const auto& d = kb->d[di];
   return GemvDesc{d.payload, d.scales, d.x, d.y, d.group,
@@ -195,16 +207,16 @@ __device__ __forceinline__ GemvDesc load_desc(int di) {
 // Streaming kernel: 8-code chunks (4-byte int4 / 8-byte int8 payload loads
 // per lane and row, two 16-byte x loads per lane), any group that is a
 // multiple of 8 codes (or spans whole rows).
-template <int BITS, int M, int R>
-__global__ __launch_bounds__(256) void gemv8_kernel(const GemvBatch b) {
+template <int BITS, int M, int R, int NB>
+__global__ __launch_bounds__(256) void gemv8_kernel(const GemvBatch<NB> b) {
   constexpr int V = pow2_at_least(R * M);
   constexpr int PW = BITS == 4 ? 1 : 2;     // payload dwords per 8-code chunk
   const int lane = threadIdx.x & 63;
   const int item = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (item >= b.items) return;
   const int di = find_desc(b, item);
-  const GemvDesc a = load_desc(di);
-  typedef const __attribute__((address_space(4))) GemvBatch* KArg;
+  const GemvDesc a = load_desc<NB>(di);
+  typedef const __attribute__((address_space(4))) GemvBatch<NB>* KArg;
   const int row0 = (item - ((KArg)__builtin_amdgcn_kernarg_segment_ptr())->item0[di]) * R;
   const int nch = a.k / 8;
 
@@ -321,11 +333,11 @@ constexpr int kRowsSmall = 2;
 
 // Launches `count` descriptors (same bits, m), GEMV_NB per launch, R rows per
 // work item.
-template <int BITS, int M, int R>
+template <int BITS, int M, int R, int NB>
 hipError_t launch_group(const GemvDesc* ds, int count, hipStream_t st) {
-  for (int base = 0; base < count; base += GEMV_NB) {
-    GemvBatch b{};
-    b.count = count - base < GEMV_NB ? count - base : GEMV_NB;
+  for (int base = 0; base < count; base += NB) {
+    GemvBatch<NB> b{};
+    b.count = count - base < NB ? count - base : NB;
     int items = 0;
     for (int i = 0; i < b.count; ++i) {
       b.d[i] = ds[base + i];
@@ -333,7 +345,7 @@ hipError_t launch_group(const GemvDesc* ds, int count, hipStream_t st) {
       items += (b.d[i].n + R - 1) / R;
     }
     b.items = items;
-    gemv8_kernel<BITS, M, R><<<(unsigned)((items + 3) / 4), 256, 0, st>>>(b);
+    gemv8_kernel<BITS, M, R, NB><<<(unsigned)((items + 3) / 4), 256, 0, st>>>(b);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -346,8 +358,11 @@ hipError_t launch_m(const GemvDesc* ds, int count, hipStream_t st) {
   for (int i = 0; i < count; ++i) rows += ds[i].n;
   // big items when they still give about two waves per SIMD (2048 items)
   constexpr int RB = rows_big<M>();
-  return rows / RB >= 2048 ? launch_group<BITS, M, RB>(ds, count, st)
-                           : launch_group<BITS, M, kRowsSmall>(ds, count, st);
+  if (count == 1)
+    return rows / RB >= 2048 ? launch_group<BITS, M, RB, 1>(ds, count, st)
+                             : launch_group<BITS, M, kRowsSmall, 1>(ds, count, st);
+  return rows / RB >= 2048 ? launch_group<BITS, M, RB, GEMV_NB>(ds, count, st)
+                           : launch_group<BITS, M, kRowsSmall, GEMV_NB>(ds, count, st);
 }
 
 template <int BITS>

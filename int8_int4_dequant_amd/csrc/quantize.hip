@@ -189,18 +189,19 @@ __global__ __launch_bounds__(256) void quant_subgroup_kernel(
 }
 
 // Several matrices of the same bits and group in one launch: the matrices'
-// descriptors travel in the kernel arguments; block b finds its matrix by a
-// wave-uniform search and quantizes that matrix's block (b - first block).
+// descriptors travel in the kernel arguments (a whole model's linear layers
+// fit one launch); block b finds its matrix by a wave-uniform binary search
+// over the first-block table and quantizes that matrix's block (b - first
+// block).
 struct QuantDesc {
   const float* w;
   uint8_t* payload;
   float* scales;
   uint64_t nvec;    // float4 vectors of the matrix
-  uint32_t block0;  // first block of the matrix in the launch
-  uint32_t pad;
 };
-constexpr int QUANT_NB = 64;
+constexpr int QUANT_NB = QW_BATCH_PER_LAUNCH;
 struct QuantBatch {
+  uint32_t block0[QUANT_NB];  // first block of each matrix, ascending, block0[0] = 0
   QuantDesc d[QUANT_NB];
   int count;
   int blocks;
@@ -211,11 +212,13 @@ __global__ __launch_bounds__(256) void quant_subgroup_batched_kernel(const Quant
   typedef const __attribute__((address_space(4))) QuantBatch* KArg;
   const KArg kb = (KArg)__builtin_amdgcn_kernarg_segment_ptr();
   const uint32_t blk = blockIdx.x;
-  int di = 0;
-  for (int i = 1; i < b.count; ++i)
-    if (blk >= kb->d[i].block0) di = i;
-  quant_subgroup_body<BITS, G>(kb->d[di].w, kb->d[di].payload, kb->d[di].scales, kb->d[di].nvec,
-                               blk - kb->d[di].block0);
+  int lo = 0, hi = b.count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (kb->block0[mid] <= blk) lo = mid; else hi = mid - 1;
+  }
+  quant_subgroup_body<BITS, G>(kb->d[lo].w, kb->d[lo].payload, kb->d[lo].scales, kb->d[lo].nvec,
+                               blk - kb->block0[lo]);
 }
 
 // ------------------------------------------------------------------- block
@@ -493,21 +496,27 @@ hipError_t launch_quantize_pack_batched(const Mat* mts, const float* const* ws,
     }
     bk->idx.push_back(i);
   }
+  // a launch takes up to QUANT_NB matrices and fewer than 2^31 blocks
+  const uint64_t kMaxBlocks = (1ull << 31) - 1;
   for (const auto& bk : buckets) {
-    for (size_t base = 0; base < bk.idx.size(); base += QUANT_NB) {
+    size_t j = 0;
+    while (j < bk.idx.size()) {
       QuantBatch b{};
       uint64_t blocks = 0;
-      for (size_t j = base; j < bk.idx.size() && j < base + QUANT_NB; ++j) {
+      for (; j < bk.idx.size() && b.count < QUANT_NB; ++j) {
         const int i = bk.idx[j];
+        const uint64_t nvec = (uint64_t)(mts[i].n * mts[i].k) / 4;
+        const uint64_t nblk = (nvec + 4 * 64 * QV - 1) / (4 * 64 * QV);
+        if (nblk > kMaxBlocks) return hipErrorInvalidValue;
+        if (blocks + nblk > kMaxBlocks) break;  // next launch
+        b.block0[b.count] = (uint32_t)blocks;
         QuantDesc& d = b.d[b.count++];
         d.w = ws[i];
         d.payload = payloads[i];
         d.scales = scales[i];
-        d.nvec = (uint64_t)(mts[i].n * mts[i].k) / 4;
-        d.block0 = (uint32_t)blocks;
-        blocks += (d.nvec + 4 * 64 * QV - 1) / (4 * 64 * QV);
+        d.nvec = nvec;
+        blocks += nblk;
       }
-      if (blocks >= (1ull << 31)) return hipErrorInvalidValue;
       b.blocks = (int)blocks;
       hipError_t e = bk.bits == 4 ? launch_quant_batch_g<4>(b, bk.group, st)
                                   : launch_quant_batch_g<8>(b, bk.group, st);

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/qw.h"
+
 namespace qw {
 
 // Problem description after validation by the C ABI.

@@ -20,6 +20,9 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqw.so")
 
+#: matrices per kernel launch in the batched calls (QW_BATCH_PER_LAUNCH in qw.h)
+BATCH_PER_LAUNCH = 256
+
 QW_OK = 0
 STATUS_NAMES = {0: "QW_OK", -1: "QW_EBITS", -2: "QW_EGROUP", -3: "QW_ESHAPE", -4: "QW_EM",
                 -5: "QW_ENULL", -6: "QW_EHIP", -7: "QW_ECOUNT"}

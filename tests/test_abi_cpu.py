@@ -34,6 +34,12 @@ def test_library_exports_every_declared_symbol():
         assert ctypes.cast(getattr(raw, name), ctypes.c_void_p).value
 
 
+def test_batch_capacity_matches_header():
+    txt = open(os.path.join(ROOT, "include", "qw.h")).read()
+    m = re.search(r"#define QW_BATCH_PER_LAUNCH (\d+)", txt)
+    assert m and int(m.group(1)) == qw.BATCH_PER_LAUNCH
+
+
 def test_sizes():
     L = qw.lib()
     assert L.qw_payload_bytes(4, 11008, 4096) == 11008 * 4096 // 2

@@ -326,7 +326,7 @@ def test_config4_layers_sampled():
 @pytest.mark.parametrize("m", [1, 3, 8])
 def test_gemv_batched_mixed(m):
     # mixed bit widths, groups, shapes, a generic-path matrix, an empty one
-    # and one with k == 0; more than one launch's worth of matrices.
+    # and one with k == 0; more than one launch's worth of int4 matrices.
     specs = []
     for i in range(40):
         bits = 4 if i % 3 else 8
@@ -337,6 +337,8 @@ def test_gemv_batched_mixed(m):
             group = k
         specs.append((bits, group, n, k))
     specs += [(4, 6, 8, 24), (8, 32, 0, 64), (4, 32, 7, 0)]
+    # and more matrices than one launch holds (QW_BATCH_PER_LAUNCH)
+    specs += [(4, 32, 1 + i % 9, 64) for i in range(qw.BATCH_PER_LAUNCH + 20)]
     refs, recs, xs, xds = [], [], [], []
     for j, (bits, group, n, k) in enumerate(specs):
         w = inputs.weight(900 + j, n, k, 0.05)
@@ -357,8 +359,9 @@ def test_gemv_batched_mixed(m):
 def test_quantize_pack_batched_mixed():
     # several (bits, group) classes, a generic-path group, an empty matrix and
     # more matrices than one launch holds; every output bit-identical
-    specs = [(4, 32, 64, 256)] * 70 + [(8, 128, 33, 512), (4, 4096, 4, 4096), (8, 6, 5, 12),
-                                       (4, 32, 0, 64), (4, 1024, 2, 2048), (8, 8, 3, 8)]
+    nmany = qw.BATCH_PER_LAUNCH + 14
+    specs = [(4, 32, 16, 256)] * nmany + [(8, 128, 33, 512), (4, 4096, 4, 4096), (8, 6, 5, 12),
+                                          (4, 32, 0, 64), (4, 1024, 2, 2048), (8, 8, 3, 8)]
     ws = [inputs.weight(700 + j, n, k, 0.05) for j, (b, g, n, k) in enumerate(specs)]
     recs = []
     for (bits, group, n, k), w in zip(specs, ws):
@@ -375,8 +378,8 @@ def test_quantize_pack_batched_mixed():
         assert same_bits(host(rec["payload"]), ref["payload"])
         assert same_bits(host(rec["scales"]), ref["scales"])
     # the convenience wrapper takes the same path
-    recs2 = qw.quantize_pack_batched(wd[:70], 4, 32)
-    for w, rec in zip(ws[:70], recs2):
+    recs2 = qw.quantize_pack_batched(wd[:nmany], 4, 32)
+    for w, rec in zip(ws[:nmany], recs2):
         ref = oracle.quantize_pack(w, 4, 32)
         assert same_bits(host(rec["payload"]), ref["payload"])
 
