@@ -14,6 +14,13 @@ bounded sample of the stack under "cpu_baseline".
 
 Prints ONE JSON line.  `--gpus N` with N > 1 exits: this build runs on one
 GPU.
+
+HBM traffic ("roofline.traffic"): two rocprofv3 counter runs of this script
+with `--calib-copy-mib 1024` (FETCH_SIZE, then WRITE_SIZE) are reduced by
+`--pmc-summary FETCH_DIR WRITE_DIR` into profiles/pmc_traffic_c4_c5.md; each
+counter is scaled by what it reads for a plain device copy of known size.
+The benchmark reports that traffic only while the kernel sources still hash
+to the values recorded there (null otherwise).
 """
 
 import argparse
@@ -44,8 +51,84 @@ def parse():
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=32, help="layers of the stack (default: all 32)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="after the timed steps, copy a buffer of this many MiB on the device "
+                         "(the known-size kernel that calibrates the HBM byte counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the traffic summary of two rocprofv3 --pmc runs and exit")
     ap.add_argument("--cpu-sample-worker", action="store_true", help=argparse.SUPPRESS)
     return ap.parse_args()
+
+
+# ------------------------------------------------------- HBM traffic (PMC)
+
+CSRC = os.path.join(ROOT, "int8_int4_dequant_amd", "csrc")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_c4_c5.md")
+# kernel-name fragment -> (label, source file whose hash pins the measurement)
+PMC_KERNELS = {
+    "quant_subgroup_batched_kernel": ("quantize_pack_batched", "quantize.hip"),
+    "gemv8_kernel<4, 1, 8, 256>": ("gemv_batched_m1", "gemv.hip"),
+    "gemm_kernel<4>": ("gemm", "gemm.hip"),
+}
+COPY_KERNEL = "neg_kernel"  # the calibration copy (torch.neg over a known-size buffer)
+
+
+def source_hashes():
+    import hashlib
+    out = {}
+    for f in sorted({v[1] for v in PMC_KERNELS.values()} | {"qw_internal.h"}):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            out[f] = hashlib.sha256(fh.read()).hexdigest()[:16]
+    return out
+
+
+def pmc_means(d, counter):
+    """Mean counter value (KiB per dispatch) per kernel-name fragment."""
+    import csv
+    import glob
+    sums, cnt = {}, {}
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            for frag in list(PMC_KERNELS) + [COPY_KERNEL]:
+                if frag in r["Kernel_Name"]:
+                    sums[frag] = sums.get(frag, 0.0) + float(r["Counter_Value"])
+                    cnt[frag] = cnt.get(frag, 0) + 1
+    return {k: sums[k] / cnt[k] for k in sums}, cnt
+
+
+def pmc_summary(fetch_dir, write_dir, copy_mib):
+    f, fc = pmc_means(fetch_dir, "FETCH_SIZE")
+    w, wc = pmc_means(write_dir, "WRITE_SIZE")
+    copy_kib = copy_mib * 1024.0
+    ff = copy_kib / f[COPY_KERNEL]   # true KiB per counted KiB
+    wf = copy_kib / w[COPY_KERNEL]
+    kernels = {}
+    for frag, (label, _) in PMC_KERNELS.items():
+        if frag in f and frag in w:
+            kernels[label] = {"fetch_kib_raw": round(f[frag], 1), "write_kib_raw": round(w[frag], 1),
+                              "dispatches": [fc[frag], wc[frag]],
+                              "traffic_bytes": round((f[frag] * ff + w[frag] * wf) * 1024)}
+    return {"copy_mib": copy_mib, "copy_fetch_kib_raw": round(f[COPY_KERNEL], 1),
+            "copy_write_kib_raw": round(w[COPY_KERNEL], 1),
+            "fetch_factor": round(ff, 4), "write_factor": round(wf, 4),
+            "kernels": kernels, "source_sha256": source_hashes()}
+
+
+def measured_traffic(label):
+    """HBM bytes per launch of `label` from the committed counter summary, or
+    None when the summary is missing or the kernel sources changed since."""
+    try:
+        txt = open(TRAFFIC_FILE).read()
+        blob = json.loads(txt.split("```json")[1].split("```")[0])
+    except (OSError, IndexError, ValueError):
+        return None
+    if blob.get("source_sha256") != source_hashes():
+        return None
+    k = blob.get("kernels", {}).get(label)
+    return None if k is None else k["traffic_bytes"]
 
 
 # ---------------------------------------------------------------- CPU leg
@@ -112,6 +195,10 @@ def main():
     args = parse()
     if args.cpu_sample_worker:
         cpu_sample_worker()
+        return
+    if args.pmc_summary:
+        print("```json\n" + json.dumps(pmc_summary(*args.pmc_summary, copy_mib=1024), indent=1)
+              + "\n```")
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
@@ -242,8 +329,10 @@ def main():
         ach, per_launch = q_gbs, qbytes / quant_launches
     else:
         ach, per_launch = g_gbs, gbytes / gemv_launches
+    traffic = measured_traffic("quantize_pack_batched" if dominant == "quantize_pack"
+                               else "gemv_batched_m1")
     roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "kernel": ("qw_quantize_pack_batched" if dominant == "quantize_pack"
                            else "qw_gemv_batched") + " (int4 g32, 224 matrices per step)",
                 "algorithmic_bytes_per_launch": round(per_launch),
@@ -259,11 +348,24 @@ def main():
         "decode_gemv_m1": {"GB/s": round(g_gbs, 1), "frac_hbm": round(g_gbs / HBM_PEAK_GBS, 4),
                            "entry": "qw_gemv_batched", "launches_per_pass": gemv_launches,
                            "avg_launch_us": round(g_avg_us, 3), "bytes_per_step": gbytes,
+                           "traffic_per_launch": measured_traffic("gemv_batched_m1"),
                            "pass_us": round(1e3 * g_ms / args.steps, 1)},
         "decode_gemv_m1_one_launch_per_matrix": {
             "pass_us": round(single_us, 1),
             "GB/s": round(gbytes / (single_us * 1e-6) / 1e9, 1)},
     }
+
+    if args.calib_copy_mib:
+        # known-size device copy (outside the timed region) for the byte counters
+        # (an elementwise negation: fully coalesced 16-byte loads and stores per
+        # lane like the kernels measured, N bytes read and N bytes written)
+        nf = (args.calib_copy_mib << 20) // 4
+        src = torch.empty(nf, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     # free the stack before the GEMM leg
     del W, P, S, Y
@@ -333,7 +435,9 @@ def bench_gemm(args, L, stream):
             "median_us": round(med * 1e3, 2), "p90_us": round(times[int(0.9 * (len(times) - 1))] * 1e3, 2),
             "TFLOP/s": round(tf, 2),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4), "traffic": None}}
+                         "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                         "traffic": measured_traffic("gemm"),
+                         "algorithmic_bytes": n * k // 2 + n * k // 128 * 4 + m * k * 2 + m * n * 4}}
 
 
 if __name__ == "__main__":
