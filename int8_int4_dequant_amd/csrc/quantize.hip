@@ -128,14 +128,21 @@ constexpr int QV = 4;  // float4 vectors per lane in the subgroup kernel
 // run per instruction.  A group of G vectors (G = group / 4, a power of two
 // from 2 to 256) is G consecutive lanes of one instruction (G <= 64) or the
 // same lane across 2 or 4 instructions (G = 128, 256); max|w| is reduced
-// with cross-lane shuffles.  Each lane then writes 2 (int4) or 4 (int8)
-// payload bytes per vector, again contiguous across the wave.
+// with cross-lane shuffles.  The wave's payload (2 or 4 bytes per vector)
+// and scales are assembled in LDS and written with one wide non-temporal
+// store per lane (8 or 16 payload bytes, 4 or 8 scale bytes): stores of 2
+// bytes per lane were the slowest part of the kernel.
 template <int BITS, int G>
 __device__ __forceinline__ void quant_subgroup_body(
     const float* __restrict__ w, uint8_t* __restrict__ payload,
     float* __restrict__ scales, uint64_t nvec, uint64_t block) {
+  constexpr int PB = BITS / 2;               // payload bytes per vector (2 or 4)
+  constexpr int NS = 64 * QV / G;            // scales per wave (1 .. 128)
+  __shared__ __attribute__((aligned(16))) uint8_t stage_p[4][64 * QV * PB];
+  __shared__ __attribute__((aligned(16))) float stage_s[4][NS];
   const int lane = threadIdx.x & 63;
-  const uint64_t base = (block * 4 + (threadIdx.x >> 6)) * (64 * QV);
+  const int wv = threadIdx.x >> 6;
+  const uint64_t base = (block * 4 + wv) * (64 * QV);
   float v[QV][4];
   float m[QV];
 #pragma unroll
@@ -166,18 +173,50 @@ __device__ __forceinline__ void quant_subgroup_body(
       for (int j = 0; j < J; ++j) m[j0 + j] = t;
     }
   }
+  // codes and scales into this wave's LDS stage (wave-private: LDS accesses
+  // of one wave complete in order, no barrier needed)
 #pragma unroll
   for (int j = 0; j < QV; ++j) {
-    const uint64_t idx = base + lane + 64 * j;
-    if (idx >= nvec) continue;
+    const int vi = lane + 64 * j;  // vector index within the wave
     const float s = scale_of<BITS>(m[j]);
-    if (idx % G == 0) scales[idx / G] = s;
+    if (vi % G == 0) stage_s[wv][vi / G] = s;
     float r[4];
     rounded_quotients<4>(v[j], s, r);
     if constexpr (BITS == 4)
-      reinterpret_cast<uint16_t*>(payload)[idx] = (uint16_t)pack4_int4(r);
+      reinterpret_cast<uint16_t*>(stage_p[wv])[vi] = (uint16_t)pack4_int4(r);
     else
-      reinterpret_cast<uint32_t*>(payload)[idx] = pack4_int8(r);
+      reinterpret_cast<uint32_t*>(stage_p[wv])[vi] = pack4_int8(r);
+  }
+  // lane L writes vectors [QV*L, QV*L + QV) of the wave: QV * PB contiguous bytes
+  const uint64_t v0 = base + (uint64_t)QV * lane;
+  if (v0 + QV <= nvec) {
+    if constexpr (QV * PB == 8) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      __builtin_nontemporal_store(reinterpret_cast<const u32x2*>(stage_p[wv])[lane],
+                                  reinterpret_cast<u32x2*>(payload + v0 * PB));
+    } else {
+      static_assert(QV * PB == 16, "QV * PB must be 8 or 16");
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      __builtin_nontemporal_store(reinterpret_cast<const u32x4*>(stage_p[wv])[lane],
+                                  reinterpret_cast<u32x4*>(payload + v0 * PB));
+    }
+  } else {
+    for (int i = 0; i < QV && v0 + i < nvec; ++i)
+      for (int bb = 0; bb < PB; ++bb)
+        payload[(v0 + i) * PB + bb] = stage_p[wv][(QV * lane + i) * PB + bb];
+  }
+  // scales of the wave's groups: NS contiguous floats, one or two per lane
+  const uint64_t g0 = base / G;
+  const uint64_t ngr = (nvec - (base < nvec ? base : nvec)) / G;  // groups of this wave with data
+  if constexpr (NS <= 64) {
+    if (lane < NS && (uint64_t)lane < ngr)
+      __builtin_nontemporal_store(stage_s[wv][lane], scales + g0 + lane);
+  } else {
+#pragma unroll
+    for (int i = 0; i < NS / 64; ++i) {
+      const int gi = (NS / 64) * lane + i;
+      if ((uint64_t)gi < ngr) __builtin_nontemporal_store(stage_s[wv][gi], scales + g0 + gi);
+    }
   }
 }
 
