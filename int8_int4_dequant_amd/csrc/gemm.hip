@@ -383,7 +383,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs a) {
           if (split)
             unsafeAtomicAdd(&a.y[mm * a.n + nn], acc[mb][nb][r]);
           else
-            a.y[mm * a.n + nn] = acc[mb][nb][r];
+            __builtin_nontemporal_store(acc[mb][nb][r], &a.y[mm * a.n + nn]);
         }
       }
     }
