@@ -7,7 +7,10 @@ weights resident in HBM): quantize and pack every matrix to int4 with group
 (qw_gemv, which unpacks the codes in registers).  `value` is the step's
 algorithmic HBM bytes divided by the step time.
 
-In the same run the prefill GEMM (qw_gemm: 2048 tokens through a 70B-style
+In the same run the single-matrix decode GEMVs (4096 x 4096 int8 with one
+scale per output channel at M = 1; the 7B MLP up and down matrices at int4
+group 128 for M = 1, 4, 8) are timed over rotating weight copies and
+reported under "decode_gemv_configs"; the prefill GEMM (qw_gemm: 2048 tokens through a 70B-style
 MLP weight of 28672 x 8192, int4 group 128, bf16 matrix cores) is timed on
 its own and reported under "prefill_gemm", and the CPU oracle is timed on a
 bounded sample of the stack under "cpu_baseline".
@@ -371,6 +374,8 @@ def main():
     del W, P, S, Y
     torch.cuda.empty_cache()
 
+    gemv_cfgs = bench_gemv_configs(args, L, stream)
+
     gemm = None
     if not args.no_gemm:
         gemm = bench_gemm(args, L, stream)
@@ -387,9 +392,74 @@ def main():
                                "all + one M=1 GEMV pass",
                    "layers": args.layers, "matrices": len(shapes), "weights": weights,
                    "bits": 4, "group": 32, "m": 1, "bytes_per_step": qbytes + gbytes},
-        "roofline": roofline, "parts": parts, "prefill_gemm": gemm, "cpu_baseline": cpu,
+        "roofline": roofline, "parts": parts, "decode_gemv_configs": gemv_cfgs,
+        "prefill_gemm": gemm, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_gemv_configs(args, L, stream):
+    """The single-matrix decode GEMVs of the other workloads: c2 (int8, one
+    scale per output channel, M = 1) and c3 (int4 group 128, MLP up and down,
+    M = 1, 4, 8).  Each is timed over rotating copies of its packed weight
+    totalling >= 1 GiB, so the 256 MB Infinity Cache cannot serve repeats."""
+    import numpy as np
+    import torch
+
+    from int8_int4_dequant_amd import inputs
+
+    dev = torch.device("cuda:0")
+    sp = stream.cuda_stream
+    out = {}
+
+    def one(tag, w, bits, group, ms, xs_of):
+        n, k = w.shape
+        wd = torch.from_numpy(w).to(dev)
+        p0 = torch.empty(n * k * bits // 8, dtype=torch.uint8, device=dev)
+        s0 = torch.empty(n * k // group, dtype=torch.float32, device=dev)
+        st = L.qw_quantize_pack(bits, group, n, k, wd.data_ptr(), p0.data_ptr(), s0.data_ptr(), sp)
+        assert st == 0, st
+        del wd
+        wbytes = p0.numel() + 4 * s0.numel()
+        copies = max(2, -(-(1 << 30) // wbytes))
+        ps = [p0] + [p0.clone() for _ in range(copies - 1)]
+        ss = [s0] + [s0.clone() for _ in range(copies - 1)]
+        for m in ms:
+            x = torch.from_numpy(xs_of(m)).to(dev)
+            y = torch.empty((m, n), dtype=torch.float32, device=dev)
+
+            def rnd():
+                for c in range(copies):
+                    r = L.qw_gemv(bits, group, n, k, ps[c].data_ptr(), ss[c].data_ptr(), m,
+                                  x.data_ptr(), y.data_ptr(), sp)
+                    if r:
+                        raise RuntimeError(f"qw_gemv failed: {r}")
+            rnd()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            reps = 3
+            for _ in range(reps):
+                rnd()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us = 1e3 * e0.elapsed_time(e1) / (reps * copies)
+            nbytes = wbytes + 4 * m * k + 4 * m * n
+            gbs = nbytes / (us * 1e-6) / 1e9
+            flops = 2.0 * m * n * k
+            out[f"{tag}_m{m}"] = {"shape_nk": [n, k], "bits": bits, "group": group, "m": m,
+                                  "us_per_call": round(us, 2), "GB/s": round(gbs, 1),
+                                  "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                                  "TFLOP/s": round(flops / (us * 1e-6) / 1e12, 3),
+                                  "rotating_copies": copies}
+            log(f"gemv {tag} m={m}: {us:.2f} us/call, {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.1%})")
+        del ps, ss
+        torch.cuda.empty_cache()
+
+    one("c2_int8_per_channel_4096x4096", inputs.c2_weight(), 8, 4096, [1], lambda m: inputs.c2_x())
+    for j, mat in enumerate(inputs.C3["mats"]):
+        one(f"c3_int4_g128_{mat['tag']}_{mat['n']}x{mat['k']}", inputs.c3_weight(j), 4, 128,
+            inputs.C3["ms"], lambda m, j=j: inputs.c3_x(j, m))
+    return out
 
 
 def bench_gemm(args, L, stream):

@@ -295,6 +295,101 @@ __global__ __launch_bounds__(256) void gemv8_kernel(const GemvBatch<NB> b) {
   }
 }
 
+// Split-K kernel for one matrix with few rows per wave of the GPU: a block's
+// 4 waves share R rows and each takes a quarter of the row's 8-code chunks
+// (lane l of wave w: chunks q*w + l, q*w + l + 64, ... below q*(w+1)); the
+// four partial sums meet in LDS and are added in wave order (deterministic).
+// Four times the waves of gemv8_kernel for the same rows, so a single decode
+// matrix still fills the GPU.
+template <int BITS, int M, int R>
+__global__ __launch_bounds__(256) void gemv8_split_kernel(const GemvDesc a) {
+  constexpr int V = pow2_at_least(R * M);
+  constexpr int PW = BITS == 4 ? 1 : 2;     // payload dwords per 8-code chunk
+  __shared__ float part_lds[4][R * M];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row0 = blockIdx.x * R;
+  const int nch = a.k / 8;
+  const int q = (nch + 3) >> 2;              // chunks per wave
+  const int cbeg = wave * q;
+  const int cend = min(nch, cbeg + q);
+
+  const uint32_t* prow[R];
+  const float* srow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int row = min(row0 + r, a.n - 1);
+    prow[r] = reinterpret_cast<const uint32_t*>(a.payload + (int64_t)row * a.row_stride_b);
+    srow[r] = a.scales + (a.per_row ? (int64_t)row * a.gpr : ((int64_t)row * a.k) / a.group);
+  }
+  float acc[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) acc[i] = 0.0f;
+
+  const uint32_t cpg = a.per_row ? a.cpg.d : 0u;
+  uint32_t gc = 0, rem = 0, step_g = 0, step_r = 0;
+  if (cpg) {
+    const uint32_t c0 = (uint32_t)(cbeg + lane);
+    gc = fastdiv(c0, a.cpg);
+    rem = c0 - gc * cpg;
+    step_g = fastdiv(64u, a.cpg);
+    step_r = 64u - step_g * cpg;
+  }
+  for (int c = cbeg + lane; c < cend; c += 64) {
+    uint32_t p[R][PW];
+    float s[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+      for (int i = 0; i < PW; ++i) p[r][i] = __builtin_nontemporal_load(prow[r] + PW * c + i);
+      s[r] = srow[r][gc];
+    }
+    float xv[M][8];
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const float4* xp = reinterpret_cast<const float4*>(a.x + (int64_t)m * a.k) + 2 * c;
+      const float4 x0 = xp[0], x1 = xp[1];
+      xv[m][0] = x0.x; xv[m][1] = x0.y; xv[m][2] = x0.z; xv[m][3] = x0.w;
+      xv[m][4] = x1.x; xv[m][5] = x1.y; xv[m][6] = x1.z; xv[m][7] = x1.w;
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float q8[8];
+      if constexpr (BITS == 4) {
+        decode8_int4(p[r][0], q8);
+      } else {
+        float q0[4], q1[4];
+        decode4_int8(p[r][0], q0);
+        decode4_int8(p[r][PW - 1], q1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { q8[e] = q0[e]; q8[4 + e] = q1[e]; }
+      }
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float part = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part = __builtin_fmaf(xv[m][e], q8[e], part);
+        acc[r * M + m] = __builtin_fmaf(part, s[r], acc[r * M + m]);
+      }
+    }
+    if (cpg) {
+      gc += step_g;
+      rem += step_r;
+      if (rem >= cpg) { rem -= cpg; ++gc; }
+    }
+  }
+
+  wave_reduce_scatter<V>(acc, lane);
+  const int idx = scatter_index<V>(lane);
+  if ((lane & (64 / V - 1)) == 0 && idx < R * M) part_lds[wave][idx] = acc[0];
+  __syncthreads();
+  if (wave == 0 && lane < R * M) {
+    const float v = ((part_lds[0][lane] + part_lds[1][lane]) + part_lds[2][lane]) + part_lds[3][lane];
+    const int r = lane / M, m = lane % M;
+    if (row0 + r < a.n) a.y[(int64_t)m * a.n + row0 + r] = v;
+  }
+}
+
 // --------------------------------------------------------- generic kernel
 
 // One wave per (row, m); any group dividing n*k and any alignment.
@@ -326,10 +421,12 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(
 }
 
 // Rows per wave: as many as the registers allow (x reused across more rows,
-// fewer reductions); fewer for a lone small matrix so every SIMD gets waves.
+// fewer reductions); fewer when the matrices have too few rows to give every
+// SIMD waves (a lone such matrix takes the split-K kernel instead).
 template <int M>
 constexpr int rows_big() { return M <= 4 ? 8 : 4; }
 constexpr int kRowsSmall = 2;
+constexpr int kRowsSplit = 4;  // rows per block of the split-K kernel
 
 // Launches `count` descriptors (same bits, m), GEMV_NB per launch, R rows per
 // work item.
@@ -358,9 +455,13 @@ hipError_t launch_m(const GemvDesc* ds, int count, hipStream_t st) {
   for (int i = 0; i < count; ++i) rows += ds[i].n;
   // big items when they still give about two waves per SIMD (2048 items)
   constexpr int RB = rows_big<M>();
-  if (count == 1)
-    return rows / RB >= 2048 ? launch_group<BITS, M, RB, 1>(ds, count, st)
-                             : launch_group<BITS, M, kRowsSmall, 1>(ds, count, st);
+  if (count == 1) {
+    if (rows / RB >= 2048) return launch_group<BITS, M, RB, 1>(ds, count, st);
+    // a lone matrix with fewer rows: split K over the 4 waves of a block
+    gemv8_split_kernel<BITS, M, kRowsSplit><<<(unsigned)((ds[0].n + kRowsSplit - 1) / kRowsSplit),
+                                              256, 0, st>>>(ds[0]);
+    return hipGetLastError();
+  }
   return rows / RB >= 2048 ? launch_group<BITS, M, RB, GEMV_NB>(ds, count, st)
                            : launch_group<BITS, M, kRowsSmall, GEMV_NB>(ds, count, st);
 }
