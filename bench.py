@@ -318,6 +318,19 @@ def main():
 
     single_us = timed(single_gemv_pass)
     single_q_us = timed(single_quant_pass)
+
+    # unpack (a5 on its own): every matrix back to fp32, one call per matrix
+    wout = torch.empty(max(n * k for n, k in shapes), dtype=torch.float32, device=dev)
+
+    def unpack_pass():
+        for i, (n, k) in enumerate(shapes):
+            st = L.qw_unpack(4, 32, n, k, P[i].data_ptr(), S[i].data_ptr(), wout.data_ptr(), sptr)
+            if st:
+                raise RuntimeError(f"qw_unpack failed: {st}")
+
+    unpack_us = timed(unpack_pass)
+    ubytes = sum(n * k * 4 + n * k // 2 + 4 * (n * k // 32) for n, k in shapes)
+    del wout
     q_gbs = qbytes * args.steps / (q_ms * 1e-3) / 1e9
     g_gbs = gbytes * args.steps / (g_ms * 1e-3) / 1e9
     ms_per_step = 1e3 * t_total / args.steps
@@ -325,7 +338,8 @@ def main():
     log(f"step {ms_per_step:.3f} ms; quantize {q_gbs:.0f} GB/s ({quant_launches} launches, avg "
         f"{q_avg_us:.1f} us); one quantize launch per matrix: {single_q_us:.1f} us; "
         f"gemv pass {g_gbs:.0f} GB/s ({1e3 * g_ms / args.steps:.1f} us, {gemv_launches} launches); "
-        f"one launch per matrix: {single_us:.1f} us")
+        f"one launch per matrix: {single_us:.1f} us; unpack pass {unpack_us:.1f} us "
+        f"({ubytes / (unpack_us * 1e-6) / 1e9:.0f} GB/s)")
 
     dominant = "quantize_pack" if q_ms >= g_ms else "gemv"
     if dominant == "quantize_pack":
@@ -353,6 +367,10 @@ def main():
                            "avg_launch_us": round(g_avg_us, 3), "bytes_per_step": gbytes,
                            "traffic_per_launch": measured_traffic("gemv_batched_m1"),
                            "pass_us": round(1e3 * g_ms / args.steps, 1)},
+        "unpack": {"GB/s": round(ubytes / (unpack_us * 1e-6) / 1e9, 1),
+                   "frac_hbm": round(ubytes / (unpack_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                   "entry": "qw_unpack", "launches_per_pass": len(shapes),
+                   "pass_us": round(unpack_us, 1), "bytes_per_pass": ubytes},
         "decode_gemv_m1_one_launch_per_matrix": {
             "pass_us": round(single_us, 1),
             "GB/s": round(gbytes / (single_us * 1e-6) / 1e9, 1)},

@@ -360,27 +360,52 @@ __device__ __forceinline__ int nibble_or_byte(uint32_t v, int i) {
   return BITS == 4 ? (int)((v >> (4 * i)) & 15u) - 8 : (int)(int8_t)(v >> (8 * i));
 }
 
-// Unpack, group % 4 == 0: lane handles QV output vectors of 4 weights at
-// wave-contiguous positions (coalesced 2- or 4-byte payload loads, 16-byte
-// streaming stores).
+// Unpack, vector kernel: a wave owns 64*QV consecutive float4 outputs.  Its
+// payload (2 or 4 bytes per vector) is read with one contiguous 8- or
+// 16-byte load per lane and redistributed through LDS, so that lane l then
+// produces vectors l, l + 64, ... and every output store instruction is a
+// contiguous 1 KiB run (non-temporal).  The scale of vector v is
+// scales[v >> vshift] (groups of a power-of-two number of vectors), else
+// scales[v / vpg].
 template <int BITS>
 __global__ __launch_bounds__(256) void unpack_vec_kernel(
     const uint8_t* __restrict__ payload, const float* __restrict__ scales,
-    float* __restrict__ out, uint64_t nvec, uint64_t vpg /* vectors per group */) {
+    float* __restrict__ out, uint64_t nvec, uint64_t vpg /* vectors per group */, int vshift) {
+  constexpr int PB = BITS / 2;  // payload bytes per vector
+  __shared__ __attribute__((aligned(16))) uint8_t stage[4][64 * QV * PB];
   const int lane = threadIdx.x & 63;
-  const uint64_t base = ((uint64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * (64 * QV);
+  const int wv = threadIdx.x >> 6;
+  const uint64_t base = ((uint64_t)blockIdx.x * 4 + wv) * (64 * QV);
+  const uint64_t v0 = base + (uint64_t)QV * lane;  // first vector of this lane's load
+  if (v0 + QV <= nvec) {
+    if constexpr (QV * PB == 8) {
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      reinterpret_cast<u32x2*>(stage[wv])[lane] =
+          __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(payload + v0 * PB));
+    } else {
+      static_assert(QV * PB == 16, "QV * PB must be 8 or 16");
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      reinterpret_cast<u32x4*>(stage[wv])[lane] =
+          __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(payload + v0 * PB));
+    }
+  } else {
+    for (int i = 0; i < QV * PB && v0 * PB + i < nvec * PB; ++i)
+      stage[wv][QV * PB * lane + i] = payload[v0 * PB + i];
+  }
+  // (the wave's own LDS writes above complete before its reads below)
 #pragma unroll
   for (int j = 0; j < QV; ++j) {
-    const uint64_t idx = base + lane + 64 * j;
+    const int vi = lane + 64 * j;
+    const uint64_t idx = base + vi;
     if (idx >= nvec) continue;
-    const float s = scales[idx / vpg];
+    const float s = scales[vshift >= 0 ? (idx >> vshift) : idx / vpg];
     float v[4];
     if constexpr (BITS == 4) {
-      const uint32_t p = reinterpret_cast<const uint16_t*>(payload)[idx];
+      const uint32_t p = reinterpret_cast<const uint16_t*>(stage[wv])[vi];
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = (float)((int)((p >> (4 * i)) & 15u) - 8) * s;
     } else {
-      const uint32_t p = reinterpret_cast<const uint32_t*>(payload)[idx];
+      const uint32_t p = reinterpret_cast<const uint32_t*>(stage[wv])[vi];
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = (float)(int)(int8_t)(p >> (8 * i)) * s;
     }
@@ -449,7 +474,13 @@ hipError_t unpack_bits(const Mat& mt, const uint8_t* payload, const float* scale
   if (unpack_path(mt, payload, out) == PATH_FAST) {
     const uint64_t nvec = count / 4;
     const unsigned grid = (unsigned)((nvec + 4 * 64 * QV - 1) / (4 * 64 * QV));
-    unpack_vec_kernel<BITS><<<grid, 256, 0, st>>>(payload, scales, out, nvec, group / 4);
+    const uint64_t vpg = group / 4;
+    int vshift = -1;
+    if ((vpg & (vpg - 1)) == 0) {
+      vshift = 0;
+      while ((1ull << vshift) < vpg) ++vshift;
+    }
+    unpack_vec_kernel<BITS><<<grid, 256, 0, st>>>(payload, scales, out, nvec, vpg, vshift);
   } else {
     unpack_generic_kernel<BITS><<<blocks_for(count), 256, 0, st>>>(payload, scales, out, count, group);
   }
@@ -473,7 +504,7 @@ int quantize_path(const Mat& mt, const float* w, const uint8_t* payload) {
 
 int unpack_path(const Mat& mt, const uint8_t* payload, const float* w_out) {
   const uint64_t count = (uint64_t)mt.n * (uint64_t)mt.k;
-  const bool al = aligned(w_out, 16) && aligned(payload, mt.bits == 4 ? 2 : 4);
+  const bool al = aligned(w_out, 16) && aligned(payload, mt.bits == 4 ? 8 : 16);
   if (al && mt.group % 4 == 0 && (count / 4 + 1023) / 1024 < (1ull << 31)) return PATH_FAST;
   return PATH_GENERIC;
 }
