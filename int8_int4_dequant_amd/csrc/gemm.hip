@@ -38,6 +38,9 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 256, BN = 256, BK = 64;
+// Rows of X up to which the small-M kernel runs (measured: it beats the
+// 256-row tiles up to M = 32 on the 7B and 70B MLP shapes, loses from 64).
+constexpr int kSmallMaxM = 32;
 // LDS row stride of the X tile: 128 bytes of data + 16 bytes of padding, so
 // that 16 consecutive rows (one 16-lane phase of a ds_read_b128) start 36
 // dwords apart and cover 16 distinct 4-bank groups of the 64 banks.
@@ -403,6 +406,160 @@ __global__ __launch_bounds__(256) void gemm_zero_split_tiles(GemmArgs a) {
     if (r0 + r < a.m) a.y[(r0 + r) * a.n + nn] = 0.0f;
 }
 
+// ------------------------------------------------------------ small-M kernel
+
+// GEMM for few rows of X (decode batches, short prompts): an output tile of
+// 32*MB rows x 32*NBW columns per block, its K split over the block's 4
+// waves (contiguous quarters of the k-steps).  A wave reads its A fragments
+// straight from global memory (X is small and cache-resident), dequantizes
+// its own weights once (the same register recipe as the large kernel) and
+// keeps 32*MB x 32*NBW fp32 accumulators; the four partial tiles meet in LDS
+// and are added in wave order (deterministic).  The work is bound by
+// streaming and dequantizing the weights, not by the matrix cores, so the
+// tile is small enough to give every compute unit blocks.
+template <int BITS, int MB, int NBW>
+__global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
+  constexpr int TILE = 32 * MB * 32 * NBW;  // outputs per block
+  __shared__ float red[3][TILE];            // partial tiles of waves 1..3
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int l32 = lane & 31;
+  const int tm = blockIdx.x % a.tiles_m;
+  const int tn = blockIdx.x / a.tiles_m;
+  const int64_t m0 = (int64_t)tm * 32 * MB;
+  const int n0 = tn * 32 * NBW;
+  const int nk = a.k / BK;
+  const int q = (nk + 3) >> 2;
+  const int ks0 = min(nk, wave * q);
+  const int ks1 = min(nk, ks0 + q);
+
+  // weights: lane's row for column block nb, k range [32g, 32g+32) of a step
+  const uint8_t* prow[NBW];
+  const float* srow[NBW];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) {
+    const int nn = min(n0 + 32 * nb + l32, a.n - 1);
+    prow[nb] = a.payload + (int64_t)nn * a.row_stride_b + 16 * g * (BITS / 4);
+    srow[nb] = a.scales + (a.per_row_groups ? (int64_t)nn * a.groups_per_row
+                                            : ((int64_t)nn * a.k) / a.group);
+  }
+  // X rows of the lane's A fragments (rows past M re-read row M-1)
+  const uint16_t* xrow[MB];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int64_t mm = m0 + 32 * mb + l32;
+    xrow[mb] = a.x + (mm < a.m ? mm : a.m - 1) * a.k + 32 * g;
+  }
+  // last k-step a load may touch (idle waves, ks0 == nk, still issue the prologue loads)
+  const int klast = min(nk - 1, max(ks0, ks1 - 1)) * BK;
+
+  auto load_w = [&](BRegs<BITS> (&br)[NBW], int k0) __attribute__((always_inline)) {
+    k0 = k0 < klast ? k0 : klast;
+    const uint32_t kk = (uint32_t)(k0 + 32 * g);
+    const uint32_t t = __umulhi(kk, a.gdiv_mul);
+    const uint32_t gi = ((t + ((kk - t) >> 1)) >> (a.gdiv_shift - 1)) & a.gmask;
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) {
+      const uint8_t* src = prow[nb] + (int64_t)k0 * BITS / 8;
+      br[nb].p[0] = *reinterpret_cast<const u32x4*>(src);
+      if constexpr (BITS == 8) br[nb].p[1] = *reinterpret_cast<const u32x4*>(src + 16);
+      br[nb].s = srow[nb][gi];
+    }
+  };
+  auto load_a = [&](u32x4 (&af)[MB][4], int k0) __attribute__((always_inline)) {
+    k0 = k0 < klast ? k0 : klast;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s) af[mb][s] = *reinterpret_cast<const u32x4*>(xrow[mb] + k0 + 8 * s);
+  };
+  auto dequant = [&](const BRegs<BITS>& br, u32x4 (&bq)[4]) __attribute__((always_inline)) {
+    const float sc = br.s;
+    if constexpr (BITS == 4) {
+      const u32x4 p = br.p[0];
+      bq[0] = dequant8_int4(p.x, sc);
+      bq[1] = dequant8_int4(p.y, sc);
+      bq[2] = dequant8_int4(p.z, sc);
+      bq[3] = dequant8_int4(p.w, sc);
+    } else {
+      const u32x4 p0 = br.p[0], p1 = br.p[1];
+      bq[0] = dequant8_int8(p0.x, p0.y, sc);
+      bq[1] = dequant8_int8(p0.z, p0.w, sc);
+      bq[2] = dequant8_int8(p1.x, p1.y, sc);
+      bq[3] = dequant8_int8(p1.z, p1.w, sc);
+    }
+  };
+
+  f32x16 acc[MB][NBW];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NBW; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // k-step ks: weights loaded two steps ahead, A fragments one step ahead
+  BRegs<BITS> brE[NBW], brO[NBW];
+  u32x4 afE[MB][4], afO[MB][4];
+  load_w(brE, ks0 * BK);
+  load_w(brO, (ks0 + 1) * BK);
+  load_a(afE, ks0 * BK);
+  auto kstep = [&](int ks, BRegs<BITS> (&br)[NBW], const u32x4 (&af)[MB][4],
+                   u32x4 (&af_nxt)[MB][4]) __attribute__((always_inline)) {
+    u32x4 bq[NBW][4];
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) dequant(br[nb], bq[nb]);
+    load_w(br, (ks + 2) * BK);
+    load_a(af_nxt, (ks + 1) * BK);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8, af[mb][s]), __builtin_bit_cast(bf16x8, bq[nb][s]),
+              acc[mb][nb], 0, 0, 0);
+  };
+  int ks = ks0;
+  for (; ks + 1 < ks1; ks += 2) {
+    kstep(ks, brE, afE, afO);
+    kstep(ks + 1, brO, afO, afE);
+  }
+  if (ks < ks1) kstep(ks, brE, afE, afO);
+
+  // ---- partial tiles of waves 1..3 into LDS (register layout), then every
+  // thread adds the four partials of its outputs in wave order and stores
+  if (wave > 0) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          red[wave - 1][((mb * NBW + nb) * 16 + r) * 64 + lane] = acc[mb][nb][r];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) {
+        const int nn = n0 + 32 * nb + l32;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int e = ((mb * NBW + nb) * 16 + r) * 64 + lane;
+          const float v = ((acc[mb][nb][r] + red[0][e]) + red[1][e]) + red[2][e];
+          // D[i][j] of a 32x32 block: lane j + 32*((i/4)%2), register 4*(i/8) + i%4
+          const int64_t mm = m0 + 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3);
+          if (mm < a.m && nn < a.n) __builtin_nontemporal_store(v, &a.y[mm * a.n + nn]);
+        }
+      }
+  }
+}
+
 // ---------------------------------------------------------- generic kernel
 
 // One thread per output; any shape, group and alignment (slow; for shapes
@@ -484,6 +641,27 @@ hipError_t launch_gemm(const Mat& mt, const uint8_t* payload, const float* scale
       a.gdiv_mul = 0;
       a.gdiv_shift = 1;
       a.gmask = 0;
+    }
+    if (m <= kSmallMaxM) {
+      // few rows: the small-M kernel, tile 32 x 32*NBW, K split over the block's waves
+      const int cus = compute_units();
+      const int64_t tms = (m + 31) / 32;
+      // two column blocks per wave (half the A-fragment reads per weight) when that
+      // still gives every compute unit a block
+      const int nbw = tms * ((mt.n + 63) / 64) >= cus ? 2 : 1;
+      const int64_t tns = (mt.n + 32 * nbw - 1) / (32 * nbw);
+      if (tms * tns >= (1ll << 31)) return hipErrorInvalidValue;
+      a.tiles_m = (int)tms;
+      a.tiles_n = (int)tns;
+      const unsigned grid = (unsigned)(tms * tns);
+#define QW_SMALL(B, NBv) gemm_small_kernel<B, 1, NBv><<<grid, 256, 0, st>>>(a)
+      if (mt.bits == 4) {
+        if (nbw == 1) QW_SMALL(4, 1); else QW_SMALL(4, 2);
+      } else {
+        if (nbw == 1) QW_SMALL(8, 1); else QW_SMALL(8, 2);
+      }
+#undef QW_SMALL
+      return hipGetLastError();
     }
     const int64_t tm = (m + BM - 1) / BM;
     const int64_t tn = (mt.n + BN - 1) / BN;

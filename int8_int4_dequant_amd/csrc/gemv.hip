@@ -426,7 +426,7 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(
 template <int M>
 constexpr int rows_big() { return M <= 4 ? 8 : 4; }
 constexpr int kRowsSmall = 2;
-constexpr int kRowsSplit = 4;  // rows per block of the split-K kernel
+constexpr int kRowsSplit = 4;  // rows per block of the split-K kernel (8 for m >= 4)
 
 // Launches `count` descriptors (same bits, m), GEMV_NB per launch, R rows per
 // work item.
@@ -458,8 +458,8 @@ hipError_t launch_m(const GemvDesc* ds, int count, hipStream_t st) {
   if (count == 1) {
     if (rows / RB >= 2048) return launch_group<BITS, M, RB, 1>(ds, count, st);
     // a lone matrix with fewer rows: split K over the 4 waves of a block
-    gemv8_split_kernel<BITS, M, kRowsSplit><<<(unsigned)((ds[0].n + kRowsSplit - 1) / kRowsSplit),
-                                              256, 0, st>>>(ds[0]);
+    constexpr int RS = M >= 4 ? 2 * kRowsSplit : kRowsSplit;  // x reused over more rows
+    gemv8_split_kernel<BITS, M, RS><<<(unsigned)((ds[0].n + RS - 1) / RS), 256, 0, st>>>(ds[0]);
     return hipGetLastError();
   }
   return rows / RB >= 2048 ? launch_group<BITS, M, RB, GEMV_NB>(ds, count, st)

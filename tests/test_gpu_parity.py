@@ -266,6 +266,21 @@ def test_gemm_split_tail(bits, group, m, n, k):
     check_gemm(ref, rec, inputs.bf16_activations(m + 7, m, k))
 
 
+# Up to 32 rows of X the small-M kernel runs: a 32-row tile of 32 or 64
+# columns per block, K split over the block's four waves (some idle when
+# k / 64 < 4), partial tiles added in LDS.  Ragged columns, per-tensor
+# groups, int8, and a width that selects 64-column tiles (n >= 16384).
+@pytest.mark.parametrize("bits,group,m,n,k", [
+    (4, 128, 1, 300, 512), (4, 32, 2, 77, 64), (8, 64, 17, 130, 192), (4, 32, 31, 96, 128),
+    (8, 128, 32, 257, 1024), (4, 96 * 2, 5, 40, 96 * 2), (4, 256, 3, 16448, 256),
+    (4, 1024 * 3, 7, 3, 1024),
+])
+def test_gemm_small_m(bits, group, m, n, k):
+    w = inputs.weight(m + n + k + 5, n, k, 0.02)
+    ref, rec = quant_both(w, bits, group)
+    check_gemm(ref, rec, inputs.bf16_activations(m * 5 + 3, m, k))
+
+
 def test_gemm_ignores_stale_output():
     # the split tiles accumulate into Y: stale contents (NaN) must not leak
     w = inputs.weight(21, 300, 512, 0.02)
