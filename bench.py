@@ -67,11 +67,13 @@ def parse():
 
 CSRC = os.path.join(ROOT, "int8_int4_dequant_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_c4_c5.md")
-# kernel-name fragment -> (label, source file whose hash pins the measurement)
+# kernel-name fragment -> (label, source file whose hash pins the measurement,
+# grid size in threads or None): the benchmark's own launches -- the c5 GEMM is
+# the 262144-thread grid of gemm_kernel<4> (the M sweep launches it too)
 PMC_KERNELS = {
-    "quant_subgroup_batched_kernel": ("quantize_pack_batched", "quantize.hip"),
-    "gemv8_kernel<4, 1, 8, 256>": ("gemv_batched_m1", "gemv.hip"),
-    "gemm_kernel<4>": ("gemm", "gemm.hip"),
+    "quant_subgroup_batched_kernel": ("quantize_pack_batched", "quantize.hip", None),
+    "gemv8_kernel<4, 1, 8, 256>": ("gemv_batched_m1", "gemv.hip", None),
+    "gemm_kernel<4>": ("gemm", "gemm.hip", 262144),
 }
 COPY_KERNEL = "neg_kernel"  # the calibration copy (torch.neg over a known-size buffer)
 
@@ -96,6 +98,9 @@ def pmc_means(d, counter):
             if r["Counter_Name"] != counter:
                 continue
             for frag in list(PMC_KERNELS) + [COPY_KERNEL]:
+                grid = PMC_KERNELS[frag][2] if frag in PMC_KERNELS else None
+                if grid is not None and int(r["Grid_Size"]) != grid:
+                    continue
                 if frag in r["Kernel_Name"]:
                     sums[frag] = sums.get(frag, 0.0) + float(r["Counter_Value"])
                     cnt[frag] = cnt.get(frag, 0) + 1
@@ -109,7 +114,7 @@ def pmc_summary(fetch_dir, write_dir, copy_mib):
     ff = copy_kib / f[COPY_KERNEL]   # true KiB per counted KiB
     wf = copy_kib / w[COPY_KERNEL]
     kernels = {}
-    for frag, (label, _) in PMC_KERNELS.items():
+    for frag, (label, _, _) in PMC_KERNELS.items():
         if frag in f and frag in w:
             kernels[label] = {"fetch_kib_raw": round(f[frag], 1), "write_kib_raw": round(w[frag], 1),
                               "dispatches": [fc[frag], wc[frag]],
@@ -517,9 +522,44 @@ def bench_gemm(args, L, stream):
     times = sorted(a.elapsed_time(b) for a, b in ev)
     med = times[len(times) // 2]
     flops = 2.0 * m * n * k
+
+    # the same weight against the number of rows: qw_gemm (bf16, matrix cores)
+    # and, up to 8 rows, qw_gemv (fp32) -- where one product overtakes the other
+    sweep = {}
+    xf = torch.from_numpy(inputs.activations(7, 8, k)).to(dev)
+    yv = torch.empty((8, n), dtype=torch.float32, device=dev)
+    for mm in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024):
+        def g(mm=mm):
+            r = L.qw_gemm(4, 128, n, k, p.data_ptr(), s.data_ptr(), mm, x.data_ptr(), y.data_ptr(), sp)
+            if r:
+                raise RuntimeError(f"qw_gemm failed: {r}")
+
+        def v(mm=mm):
+            r = L.qw_gemv(4, 128, n, k, p.data_ptr(), s.data_ptr(), mm, xf.data_ptr(), yv.data_ptr(), sp)
+            if r:
+                raise RuntimeError(f"qw_gemv failed: {r}")
+
+        row = {}
+        for name, fn in (("gemm_us", g), ("gemv_us", v)):
+            if name == "gemv_us" and mm > 8:
+                continue
+            fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(5):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            row[name] = round(1e3 * e0.elapsed_time(e1) / 5, 2)
+        row["gemm_TFLOP/s"] = round(2.0 * mm * n * k / (row["gemm_us"] * 1e-6) / 1e12, 1)
+        sweep[str(mm)] = row
+    log("gemm/gemv against m: " + ", ".join(
+        f"m={k_}: {r_['gemm_us']:.0f}" + (f"/{r_['gemv_us']:.0f}" if "gemv_us" in r_ else "") + " us"
+        for k_, r_ in sweep.items()))
     tf = flops / (med * 1e-3) / 1e12
     log(f"gemm: median {med * 1e3:.1f} us, {tf:.1f} TFLOP/s ({tf / BF16_PEAK_TFLOPS:.1%} of bf16 peak)")
     return {"workload": "c5: M=2048 bf16 x (28672 x 8192) int4 group 128, fp32 accumulate",
+            "m_sweep_same_weight": sweep,
             "median_us": round(med * 1e3, 2), "p90_us": round(times[int(0.9 * (len(times) - 1))] * 1e3, 2),
             "TFLOP/s": round(tf, 2),
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
