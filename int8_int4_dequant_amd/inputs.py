@@ -186,6 +186,75 @@ def c5_x_bf16():
     return bf16_activations(C5["x_seed"], C5["m"], C5["k"])
 
 
+# ------------------------------------------------------------ GPTQ calibration
+#
+# One layer of the small model of the GPTQ section (model width 512,
+# feed-forward width 1368, so its largest matrix is 1368 x 512), with the
+# section's calibration budget of 8 batches of 16 sequences, 65,536 tokens.
+# The trained weights and real layer inputs are not available: the weights
+# are N(0, 0.02) draws, and the inputs are synthetic activations whose
+# components are correlated (a low-rank common part plus independent noise),
+# have uneven magnitudes, and include three components 2.5x larger than the
+# rest (the section's calibration statistics find three such components,
+# 112, 257 and 285, about 2.5 times the median).
+
+SMALLEM_D = 512
+SMALLEM_FFN = 1368
+CALIB_TOKENS = 65536
+#: (name, n, k, calibration input) of the layer's linear maps, stored [n][k]
+SMALLEM_LAYER = [
+    ("q", SMALLEM_D, SMALLEM_D, "attn_in"),
+    ("k", SMALLEM_D, SMALLEM_D, "attn_in"),
+    ("v", SMALLEM_D, SMALLEM_D, "attn_in"),
+    ("o", SMALLEM_D, SMALLEM_D, "o_in"),
+    ("gate", SMALLEM_FFN, SMALLEM_D, "ffn_in"),
+    ("up", SMALLEM_FFN, SMALLEM_D, "ffn_in"),
+    ("down", SMALLEM_D, SMALLEM_FFN, "down_in"),
+]
+#: calibration inputs: name -> (k, seed)
+SMALLEM_INPUTS = {
+    "attn_in": (SMALLEM_D, [6, 100]),
+    "o_in": (SMALLEM_D, [6, 101]),
+    "ffn_in": (SMALLEM_D, [6, 102]),
+    "down_in": (SMALLEM_FFN, [6, 103]),
+}
+SMALLEM_OUTLIER_COMPONENTS = (112, 257, 285)
+
+
+def calibration_activations(seed, t, k):
+    """fp32 [t][k] correlated activations from ``default_rng(seed)``:
+    x = (0.8 * z_c . F + 0.4 * z_i) * c, with z_c [t][r] and z_i [t][k]
+    N(0, 1), r = max(1, k // 16) common factors, F [r][k] N(0, 1/r), and
+    per-component magnitudes c = exp(0.5 * N(0, 1)), multiplied by 2.5 at
+    the components 112, 257 and 285 that exist."""
+    rng = np.random.default_rng(seed)
+    r = max(1, k // 16)
+    f = rng.standard_normal((r, k), dtype=np.float32)
+    f *= np.float32(1.0 / np.sqrt(r))
+    c = np.exp(0.5 * rng.standard_normal(k)).astype(np.float32)
+    for j in SMALLEM_OUTLIER_COMPONENTS:
+        if j < k:
+            c[j] *= np.float32(2.5)
+    zc = rng.standard_normal((t, r), dtype=np.float32)
+    x = zc @ f
+    x *= np.float32(0.8)
+    x += np.float32(0.4) * rng.standard_normal((t, k), dtype=np.float32)
+    x *= c[None, :]
+    return x
+
+
+def smallem_weight(slot):
+    """fp32 weight [n][k] of the layer's map number ``slot`` (q, k, v, o,
+    gate, up, down)."""
+    _, n, k, _ = SMALLEM_LAYER[slot]
+    return weight([6, slot], n, k, 0.02)
+
+
+def smallem_calibration(name, t=CALIB_TOKENS):
+    k, seed = SMALLEM_INPUTS[name]
+    return calibration_activations(seed, t, k)
+
+
 # ------------------------------------------------------------ edge cases
 
 

@@ -15,6 +15,10 @@ and without blocking, fusion or reordering, so that it can be checked by eye:
                  (page "量化推理：INT8/INT4 的体积、困惑度与速度为什么不同步",
                  script functions ``pack`` and ``unpack``; page "Huit bits,
                  puis quatre", section "Arrondir").
+* ``gptq``    -- the calibration matrix H = sum x^T x, its damping, the
+                 factor U of H^-1 = U^T U, and the column-by-column GPTQ
+                 codes in the same payload / scale format (page "Huit bits,
+                 puis quatre", section "Arrondir mieux : GPTQ").
 * ``matmul``  -- the dequantizing products y = x . w_hat^T in fp64 and the
                  per-output error base sum |x . w_hat| used for tolerances
                  (page "Huit bits, puis quatre", section "Ranger des entiers
@@ -27,6 +31,7 @@ pages print, closed forms, special cases and brute force on tiny inputs.
 from .rtn import (  # noqa: F401
     QMAX,
     quantize_pack,
+    pack_codes,
     unpack,
     codes_from_payload,
     payload_bytes,
@@ -39,3 +44,4 @@ from .matmul import (  # noqa: F401
     gemm_ref,
     error_base,
 )
+from . import gptq  # noqa: F401,E402

@@ -73,14 +73,23 @@ def quantize_pack(w, bits, group):
     q = np.clip(np.rint(r), -qmax, qmax).astype(np.int8).reshape(-1)
 
     # step 5: packing
-    if bits == 8:
-        payload = q.view(np.uint8).copy()
-    else:
-        u = (q.astype(np.int16) + 8).astype(np.uint8)  # 1..15
-        payload = (u[0::2] | (u[1::2] << 4)).astype(np.uint8)
+    payload = pack_codes(q, bits)
 
     return dict(bits=bits, group=group, shape=list(w.shape),
                 payload=payload, scales=scales.astype("<f4"), q=q)
+
+
+def pack_codes(q, bits):
+    """Pack signed codes (storage order) into the payload: int8 codes as
+    their two's-complement bytes; int4 codes offset by +8, element 2i in the
+    low nibble and element 2i+1 in the high nibble of byte i."""
+    q = np.asarray(q, dtype=np.int8).reshape(-1)
+    if bits == 8:
+        return q.view(np.uint8).copy()
+    if bits != 4:
+        raise ValueError(f"bits must be 4 or 8, got {bits}")
+    u = (q.astype(np.int16) + 8).astype(np.uint8)  # 1..15
+    return (u[0::2] | (u[1::2] << 4)).astype(np.uint8)
 
 
 def codes_from_payload(payload, bits, count):

@@ -1,0 +1,222 @@
+"""Pins of the GPTQ oracle (page "Huit bits, puis quatre", section "Arrondir
+mieux : GPTQ") against what the section and the mathematics fix.
+
+* H is checked against exact rational sums on tiny batches.
+* The factor is pinned by its defining identity: U^T U H = I, U upper
+  triangular with a positive diagonal (a Cholesky factor is unique).
+* The page's two checks: with a diagonal H the codes are exactly those of
+  plain round-to-nearest; with correlated inputs the output error drops by
+  more than 30 %.
+* The column loop is pinned by the least-squares property that defines
+  what the carried error is for: when column j is rounded, the later
+  columns of each channel hold w_F + d_F with
+  d_F = -H_FF^-1 H_FQ (w_hat_Q - w_Q), the deviation of the free columns
+  F = {j, ...} that minimises (d^T H d) once the columns Q = {0..j-1} are
+  fixed to their rounded values.  It is evaluated here with a linear solve
+  on the damped H, a route that shares nothing with the oracle's
+  inverse-then-Cholesky factor, so a transposed factor, a wrong sign, a
+  missing division by U[k, k] or a wrong index fails it.
+* The group scale is pinned to the weights at the group's first column.
+"""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import gptq as G
+from int8_int4_dequant_amd import inputs
+
+
+def _spd_h(seed, t, k):
+    x = inputs.calibration_activations(seed, t, k)
+    return G.hessian([x]), x
+
+
+# ----------------------------------------------------------------- H
+
+
+def test_hessian_matches_exact_rational_sums():
+    rng = np.random.default_rng(11)
+    b1 = rng.standard_normal((3, 4), dtype=np.float32)
+    b2 = rng.standard_normal((2, 4), dtype=np.float32)
+    h = G.hessian([b1, b2])
+    assert h.shape == (4, 4) and h.dtype == np.float64
+    rows = [list(map(float, r)) for r in np.vstack([b1, b2])]
+    for i in range(4):
+        for j in range(4):
+            exact = sum(Fraction(r[i]) * Fraction(r[j]) for r in rows)
+            bound = sum(abs(Fraction(r[i]) * Fraction(r[j])) for r in rows)
+            # five exact products summed in fp64: at most 4 roundings
+            assert abs(Fraction(h[i, j]) - exact) <= bound * Fraction(4, 2 ** 53)
+
+
+def test_hessian_accumulates_over_batches():
+    x = inputs.calibration_activations([7, 1], 96, 24)
+    whole = G.hessian([x])
+    split = G.hessian([x[:40], x[40:41], x[41:]])
+    base = np.abs(x.astype(np.float64)).T @ np.abs(x.astype(np.float64))
+    assert np.all(np.abs(whole - split) <= 96 * 2.0 ** -52 * base)
+    assert np.allclose(whole, whole.T, rtol=0, atol=0)
+
+
+def test_damping_of_a_diagonal_h():
+    d = np.array([4.0, 1.0, 0.5, 2.5])
+    hd = G.damped(np.diag(d), 0.01)
+    assert np.array_equal(hd, np.diag(d + 0.01 * 2.0))
+
+
+def test_damping_rejects_zero_h():
+    with pytest.raises(ValueError):
+        G.damped(np.zeros((3, 3)))
+
+
+# ----------------------------------------------------------------- U
+
+
+@pytest.mark.parametrize("k", [1, 2, 7, 40])
+def test_factor_identity(k):
+    h, _ = _spd_h([7, 2, k], 4 * k + 8, k)
+    hd = G.damped(h)
+    u = G.inverse_factor(hd)
+    assert np.array_equal(u, np.triu(u))
+    assert np.all(np.diag(u) > 0)
+    assert np.allclose(u.T @ u @ hd, np.eye(k), rtol=0, atol=1e-9)
+
+
+def test_factor_of_two_by_two_closed_form():
+    # H = [[a, b], [b, c]]: H^-1 = [[c, -b], [-b, a]] / det, and its upper
+    # factor is U00 = sqrt(c / det), U01 = -b / sqrt(c * det), U11 = 1/sqrt(c)
+    a, b, c = 3.0, 1.25, 2.0
+    det = a * c - b * b
+    u = G.inverse_factor(np.array([[a, b], [b, c]]))
+    want = np.array([[np.sqrt(c / det), -b / np.sqrt(c * det)],
+                     [0.0, 1.0 / np.sqrt(c)]])
+    assert np.allclose(u, want, rtol=1e-14, atol=0)
+
+
+# ----------------------------------------------------------------- page checks
+
+
+@pytest.mark.parametrize("bits,group", [(4, 32), (4, 64), (8, 64), (8, 128), (4, 128)])
+def test_diagonal_h_gives_round_to_nearest(bits, group):
+    """Independent inputs: nothing can compensate anything, GPTQ must be
+    exactly the plain quantizer."""
+    rng = np.random.default_rng([7, 3, bits, group])
+    n, k = 24, 256
+    w = inputs.weight([7, 4], n, k, 0.02)
+    h = np.diag(rng.uniform(0.1, 5.0, size=k))
+    rec = G.gptq(w, h, bits, group)
+    rtn = oracle.quantize_pack(w, bits, group)
+    assert np.array_equal(rec["payload"], rtn["payload"])
+    assert np.array_equal(rec["scales"].view(np.uint32), rtn["scales"].view(np.uint32))
+    assert np.array_equal(rec["q"], rtn["q"])
+
+
+@pytest.mark.parametrize("bits,group", [(4, 32), (4, 64), (8, 256)])
+def test_correlated_inputs_lower_the_output_error(bits, group):
+    """Correlated inputs: the output error ||X W^T - X W_hat^T|| must drop by
+    more than 30 % against plain rounding."""
+    n, k, t = 48, 256, 4096
+    x = inputs.calibration_activations([7, 5], t, k)
+    w = inputs.weight([7, 6], n, k, 0.02)
+    rec = G.gptq(w, G.hessian([x]), bits, group)
+    rtn = oracle.quantize_pack(w, bits, group)
+    xd = x.astype(np.float64)
+    e_gptq = np.linalg.norm(xd @ (oracle.unpack(rec).astype(np.float64) - w).T)
+    e_rtn = np.linalg.norm(xd @ (oracle.unpack(rtn).astype(np.float64) - w).T)
+    assert e_gptq < 0.7 * e_rtn
+
+
+# ----------------------------------------------------------------- column loop
+
+
+def _least_squares_state(hd, w_row, w_hat_row, j):
+    """Weights of the free columns F = {j..k-1} that minimise the quadratic
+    error once the columns 0..j-1 are fixed to their rounded values."""
+    if j == 0:
+        return w_row.astype(np.float64).copy()
+    q_idx = np.arange(j)
+    f_idx = np.arange(j, len(w_row))
+    d_q = w_hat_row[q_idx].astype(np.float64) - w_row[q_idx].astype(np.float64)
+    d_f = -np.linalg.solve(hd[np.ix_(f_idx, f_idx)], hd[np.ix_(f_idx, q_idx)] @ d_q)
+    return w_row[f_idx].astype(np.float64) + d_f
+
+
+@pytest.mark.parametrize("bits,group", [(4, 8), (8, 24)])
+def test_rounding_time_weights_solve_the_least_squares_problem(bits, group):
+    n, k = 5, 48
+    h, _ = _spd_h([7, 7], 256, k)
+    hd = G.damped(h)
+    w = inputs.weight([7, 8], n, k, 0.02)
+    rec = G.quantize_pack(w, G.inverse_factor(hd), bits, group)
+    w_hat = oracle.unpack(rec)
+    at = rec["w_at_quant"]
+    for r in range(n):
+        for j in range(k):
+            want = _least_squares_state(hd, w[r], w_hat[r], j)[0]
+            assert abs(at[r, j] - want) <= 1e-10 * (1.0 + abs(want)), (r, j)
+
+
+def test_two_components_closed_form():
+    """k = 2: after rounding component 0 with deviation d0, component 1
+    moves by -H01/H11 * d0."""
+    h = np.array([[2.0, 0.9], [0.9, 1.5]])
+    hd = G.damped(h)
+    w = np.array([[0.3, -0.2], [0.05, 0.07]], np.float32)
+    rec = G.quantize_pack(w, G.inverse_factor(hd), 4, 2)
+    w_hat = oracle.unpack(rec).astype(np.float64)
+    d0 = w_hat[:, 0] - w[:, 0].astype(np.float64)
+    want = w[:, 1].astype(np.float64) - hd[0, 1] / hd[1, 1] * d0
+    assert np.allclose(rec["w_at_quant"][:, 1], want, rtol=1e-14, atol=1e-16)
+
+
+def test_group_scale_is_fixed_at_the_group_first_column():
+    n, k, group, bits = 4, 64, 16, 4
+    h, _ = _spd_h([7, 9], 512, k)
+    hd = G.damped(h)
+    w = inputs.weight([7, 10], n, k, 0.02)
+    rec = G.quantize_pack(w, G.inverse_factor(hd), bits, group)
+    w_hat = oracle.unpack(rec)
+    scales = rec["scales"].reshape(n, k // group)
+    # first group: nothing has been carried yet, so it is the plain scale
+    plain = oracle.quantize_pack(w, bits, group)["scales"].reshape(n, k // group)
+    assert np.array_equal(scales[:, 0].view(np.uint32), plain[:, 0].view(np.uint32))
+    for r in range(n):
+        for g in range(1, k // group):
+            state = _least_squares_state(hd, w[r], w_hat[r], g * group)[:group]
+            want = np.float32(np.abs(state.astype(np.float32)).max()) / np.float32(7)
+            assert abs(float(scales[r, g]) - float(want)) <= 2.0 ** -21 * float(want)
+            # and the scale is not the one of the uncorrected weights
+            assert scales[r, g] != plain[r, g]
+
+
+def test_per_channel_group_and_int8():
+    n, k = 6, 40
+    h, _ = _spd_h([7, 11], 300, k)
+    w = inputs.weight([7, 12], n, k, 0.02)
+    rec = G.gptq(w, h, 8, k)
+    assert rec["payload"].size == n * k and rec["scales"].size == n
+    codes = oracle.codes_from_payload(rec["payload"], 8, n * k)
+    assert np.array_equal(codes, rec["q"].astype(np.int16))
+    assert np.abs(codes).max() <= 127
+
+
+def test_rejects_bad_arguments():
+    w = np.zeros((2, 8), np.float32)
+    u = np.eye(8)
+    with pytest.raises(ValueError):
+        G.quantize_pack(w, u, 4, 3)
+    with pytest.raises(ValueError):
+        G.quantize_pack(w, u, 5, 8)
+    with pytest.raises(ValueError):
+        G.quantize_pack(w, np.eye(4), 4, 8)
+
+
+def test_zero_weights_give_zero_codes():
+    h, _ = _spd_h([7, 13], 64, 16)
+    rec = G.gptq(np.zeros((3, 16), np.float32), h, 4, 8)
+    assert np.all(rec["q"] == 0)
+    assert np.all(rec["payload"] == 0x88)
+    assert np.all(rec["scales"] == 1.0)
