@@ -70,7 +70,9 @@ enum qw_status {
     QW_EM = -4,      /* m out of range (gemv: 0..8, gemm: >= 0)              */
     QW_ENULL = -5,   /* a required pointer is NULL                           */
     QW_EHIP = -6,    /* a HIP launch failed                                  */
-    QW_ECOUNT = -7   /* batched call: count < 0 or a descriptor is invalid   */
+    QW_ECOUNT = -7,  /* batched call: count < 0 or a descriptor is invalid   */
+    QW_EWORK = -8,   /* work buffer NULL or smaller than the size query says */
+    QW_EARG = -9     /* another argument out of range (see the entry point)  */
 };
 
 /* Largest number of matrices the batched calls put into one kernel launch
@@ -189,6 +191,83 @@ int qw_gemv_batched(int count, const qw_gemv_desc* descs, int64_t m, void* strea
 int qw_gemm(int bits, int64_t group, int64_t n, int64_t k,
             const uint8_t* payload, const float* scales,
             int64_t m, const uint16_t* x_bf16, float* y, void* stream);
+
+/*
+ * GPTQ codes (page "Huit bits, puis quatre", section "Arrondir mieux :
+ * GPTQ").  Rounding every weight to its nearest code minimises each weight's
+ * error, not the error of the layer's output X W^T on typical inputs X.
+ * GPTQ rounds the input components (columns of the [n][k] weight) one after
+ * the other and carries each rounding error onto the later components of
+ * the same output channel, weighted by how correlated their inputs are.
+ * What it needs from the inputs is H = sum x^T x over some calibration
+ * tokens; the carrying factors are the rows of U, the upper triangular
+ * factor of H^-1 = U^T U after H is damped by a fraction (the page: 1 %) of
+ * its mean diagonal.  For component c of every channel, in order:
+ *
+ *   when c starts a group: S = fl32(max |fl32(w)| over the group's
+ *                          current weights / qmax), 1 if zero
+ *   q      = clip(round_half_even(fl32(fl32(w_c) / S)), -qmax, qmax)
+ *   e      = (w_c - fl32(q * S)) / U[c][c]
+ *   w_j   -= e * U[c][j]                      for every j > c
+ *
+ * The result uses the same payload and scale format as qw_quantize_pack
+ * (so qw_unpack, qw_gemv and qw_gemm take it unchanged); with a diagonal H
+ * it is bit-identical to qw_quantize_pack.  All of H, U and the carried
+ * weights are fp64.  Three steps, each enqueued on `stream` like the other
+ * entry points; each takes a caller-owned device work buffer of at least
+ * the size its *_work_bytes query returns (contents undefined on return,
+ * not shared between calls in flight).
+ */
+
+/* Work bytes for qw_gptq_hessian (-1 if k or t is negative). */
+int64_t qw_gptq_hessian_work_bytes(int64_t k, int64_t t);
+
+/*
+ * Calibration accumulation: h += x^T x.
+ *   x  fp32 [t][k] row-major, one row per token          (read)
+ *   h  fp64 [k][k], symmetric                            (read-write)
+ * The per-layer accumulator the page's calibration adds to before each
+ * product; call once per batch.  Deterministic for given shapes.  t == 0 or
+ * k == 0 enqueues nothing.
+ */
+int qw_gptq_hessian(int64_t k, int64_t t, const float* x, double* h,
+                    void* work, int64_t work_bytes, void* stream);
+
+/* Work bytes for qw_gptq_factor (-1 if k is negative). */
+int64_t qw_gptq_factor_work_bytes(int64_t k);
+
+/*
+ * Damping and factor: u (fp64 [k][k], written) is upper triangular with
+ * zeros below the diagonal and (h + damp * mean(diag h) * I)^-1 = u^T u.
+ *   h     fp64 [k][k] symmetric (read)
+ *   damp  fraction of the mean diagonal added to it (the page uses 0.01);
+ *         finite and >= 0, else QW_EARG
+ *   info  DEVICE int32 (written, may be NULL): 0 on success; 1 if the mean
+ *         diagonal is not positive or the damped matrix is not positive
+ *         definite, in which case u is undefined.  Read it after the stream
+ *         synchronizes; the call itself does not wait.
+ */
+int qw_gptq_factor(int64_t k, const double* h, double damp, double* u, int32_t* info,
+                   void* work, int64_t work_bytes, void* stream);
+
+/* Work bytes for qw_gptq_quantize_pack (-1 if invalid). */
+int64_t qw_gptq_quantize_work_bytes(int64_t n, int64_t k);
+
+/*
+ * GPTQ codes of one weight.
+ *   w        fp32 [n][k]                        (read)
+ *   u        fp64 [k][k] from qw_gptq_factor    (read; only its upper
+ *            triangle is used)
+ *   payload  uint8 [qw_payload_bytes(bits,n,k)] (written)
+ *   scales   fp32 [qw_num_scales(group,n,k)]    (written)
+ * group must divide k (a group lies inside one output channel) and be even
+ * for int4; QW_EGROUP otherwise.  Matrices that share an input (and so an
+ * H) can be stacked along n into one call.
+ */
+int qw_gptq_quantize_pack(int bits, int64_t group, int64_t n, int64_t k,
+                          const float* w, const double* u,
+                          uint8_t* payload, float* scales,
+                          void* work, int64_t work_bytes, void* stream);
 
 /*
  * Diagnostic: which kernel family a call with these arguments would take

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libqw.so")
-SOURCES = ["qw_api.hip", "quantize.hip", "gemv.hip", "gemm.hip"]
+SOURCES = ["qw_api.hip", "quantize.hip", "gemv.hip", "gemm.hip", "gptq.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

@@ -1,0 +1,634 @@
+// GPTQ codes on the GPU (page "Huit bits, puis quatre", section "Arrondir
+// mieux : GPTQ"): the calibration matrix H = sum x^T x, its damping by a
+// fraction of the mean diagonal, the upper factor U of H^-1 = U^T U, and the
+// component-by-component rounding that carries each rounding error onto the
+// later components of the same output channel, in the payload / scale
+// format of the plain quantizer.
+//
+// Everything is fp64, as the section's host implementation is.  The dense
+// contractions (H itself, the factorization's trailing updates, the
+// triangular inverse, the carried-error updates) run on one fp64 MFMA GEMM
+// (v_mfma_f64_16x16x4f64); the sequential parts are small kernels:
+//
+//   H       X^T X over token chunks into per-chunk partial sums, then a
+//           fixed-order reduction into h (lower tiles only, mirrored), so a
+//           call is deterministic.
+//   U       With J the index reversal, JHJ = L L^T (lower Cholesky) gives
+//           H = R R^T with R = J L J upper, hence H^-1 = (R^-1)^T R^-1 and
+//           U = R^-1 = J L^-1 J.  One blocked Cholesky (64-wide diagonal
+//           blocks factored and inverted in LDS, panels as GEMMs with the
+//           block inverse, trailing updates as GEMMs on the lower tiles) and
+//           one blocked triangular inverse (diagonal block inverses, then
+//           doubling: X21 = -X22 (L21 X11) for pairs of ever larger blocks).
+//   codes   The page's column loop, blocked: a block of up to 64 components
+//           is rounded by one wave per output channel (lane j holds
+//           component j of the block; the rounding error is broadcast with
+//           readlane and carried to the later lanes at once); the carried
+//           errors of the block are then applied to every later component
+//           with one GEMM, W[:, after] -= E . U[block, after].  This is the
+//           same arithmetic in another summation order.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "qw_internal.h"
+
+namespace qw {
+namespace {
+
+typedef double d4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------ GEMM
+//
+// C(i, j) = beta * C(i, j) + alpha * sum_kk A(i, kk) * B(kk, j)
+// with A(i, kk) = a[i*a_sm + kk*a_sk], B(kk, j) = b[kk*b_sk + j*b_sn],
+// C(i, j) = c[i*c_sm + j*c_sn]; blockIdx.z selects a batch entry whose
+// operands are offset by a_sz, b_sz, c_sz elements.  Every entry reduces
+// over kred terms, except that with kred_total > 0 (consecutive chunks of
+// one long reduction) entry z reduces over min(kred, kred_total - z*kred).  64x64 tiles, 4 waves of 32x32,
+// reduction staged through LDS in steps of 16.  With `lower` set the grid
+// enumerates only the tiles (ti, tj) with ti >= tj (diagonal tiles whole).
+
+struct G64 {
+  const void* a;
+  const void* b;
+  double* c;
+  int64_t a_sm, a_sk, a_sz;
+  int64_t b_sk, b_sn, b_sz;
+  int64_t c_sm, c_sn, c_sz;
+  int64_t m, n, kred, kred_total;
+  double alpha, beta;
+  int32_t lower, tiles_n;
+};
+
+constexpr int kT = 64;     // tile edge
+constexpr int kS = 16;     // reduction step per LDS stage
+constexpr int kLd = kT + 4;
+
+template <typename T>
+__device__ inline double ld_as_double(const T* p, int64_t off) {
+  return (double)p[off];
+}
+
+template <typename TA, typename TB>
+__global__ __launch_bounds__(256) void gemm64_kernel(G64 g) {
+  __shared__ double as[2][kS][kLd];
+  __shared__ double bs[2][kS][kLd];
+
+  int64_t ti, tj;
+  if (g.lower) {
+    // linear index over the lower triangle of tiles: x = ti*(ti+1)/2 + tj
+    const int64_t x = blockIdx.x;
+    int64_t r = (int64_t)((sqrt(8.0 * (double)x + 1.0) - 1.0) * 0.5);
+    while (r * (r + 1) / 2 > x) --r;
+    while ((r + 1) * (r + 2) / 2 <= x) ++r;
+    ti = r;
+    tj = x - r * (r + 1) / 2;
+  } else {
+    ti = blockIdx.x / g.tiles_n;
+    tj = blockIdx.x % g.tiles_n;
+  }
+  const int64_t z = blockIdx.z;
+  // no __restrict__: the panel step of the factorization reads and writes
+  // the same rows
+  const TA* pa = (const TA*)g.a + z * g.a_sz;
+  const TB* pb = (const TB*)g.b + z * g.b_sz;
+  double* pc = g.c + z * g.c_sz;
+  int64_t kred = g.kred;
+  if (g.kred_total > 0 && g.kred_total - z * g.kred < kred) kred = g.kred_total - z * g.kred;
+  const int64_t i0 = ti * kT, j0 = tj * kT;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = t >> 6;
+  const int wi = wave >> 1, wj = wave & 1;
+
+  // global -> register mapping of the staged tiles (4 elements per thread)
+  const bool a_icontig = (g.a_sm == 1);
+  const bool b_jcontig = (g.b_sn == 1);
+  double ra[4], rb[4];
+
+  auto load_stage = [&](int64_t k0) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      int ii, kk;
+      if (a_icontig) { ii = t & 63; kk = (t >> 6) + 4 * r; }
+      else { kk = t & 15; ii = (t >> 4) + 16 * r; }
+      const int64_t gi = i0 + ii, gk = k0 + kk;
+      ra[r] = (gi < g.m && gk < kred) ? ld_as_double(pa, gi * g.a_sm + gk * g.a_sk) : 0.0;
+      int jj, kb;
+      if (b_jcontig) { jj = t & 63; kb = (t >> 6) + 4 * r; }
+      else { kb = t & 15; jj = (t >> 4) + 16 * r; }
+      const int64_t gj = j0 + jj, gkb = k0 + kb;
+      rb[r] = (gj < g.n && gkb < kred) ? ld_as_double(pb, gkb * g.b_sk + gj * g.b_sn) : 0.0;
+    }
+  };
+  auto store_stage = [&](int buf) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      int ii, kk;
+      if (a_icontig) { ii = t & 63; kk = (t >> 6) + 4 * r; }
+      else { kk = t & 15; ii = (t >> 4) + 16 * r; }
+      as[buf][kk][ii] = ra[r];
+      int jj, kb;
+      if (b_jcontig) { jj = t & 63; kb = (t >> 6) + 4 * r; }
+      else { kb = t & 15; jj = (t >> 4) + 16 * r; }
+      bs[buf][kb][jj] = rb[r];
+    }
+  };
+
+  d4 acc[2][2];
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj) acc[bi][bj] = (d4){0.0, 0.0, 0.0, 0.0};
+
+  const int64_t nstage = (kred + kS - 1) / kS;
+  if (nstage > 0) {
+    load_stage(0);
+    store_stage(0);
+  }
+  __syncthreads();
+  for (int64_t s = 0; s < nstage; ++s) {
+    const int buf = (int)(s & 1);
+    if (s + 1 < nstage) load_stage((s + 1) * kS);
+#pragma unroll
+    for (int ks = 0; ks < kS / 4; ++ks) {
+      const int kk = ks * 4 + (lane >> 4);
+      double fa[2], fb[2];
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi) fa[bi] = as[buf][kk][wi * 32 + bi * 16 + (lane & 15)];
+#pragma unroll
+      for (int bj = 0; bj < 2; ++bj) fb[bj] = bs[buf][kk][wj * 32 + bj * 16 + (lane & 15)];
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < 2; ++bj)
+          acc[bi][bj] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[bi], fb[bj], acc[bi][bj], 0, 0, 0);
+    }
+    if (s + 1 < nstage) store_stage(buf ^ 1);
+    __syncthreads();
+  }
+
+  // D of v_mfma_f64_16x16x4f64: register r of lane l is row 4r + l/16,
+  // column l%16 of the 16x16 block.
+#pragma unroll
+  for (int bi = 0; bi < 2; ++bi)
+#pragma unroll
+    for (int bj = 0; bj < 2; ++bj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t gi = i0 + wi * 32 + bi * 16 + 4 * r + (lane >> 4);
+        const int64_t gj = j0 + wj * 32 + bj * 16 + (lane & 15);
+        if (gi < g.m && gj < g.n) {
+          double* p = pc + gi * g.c_sm + gj * g.c_sn;
+          double v = g.alpha * acc[bi][bj][r];
+          if (g.beta != 0.0) v += g.beta * *p;
+          *p = v;
+        }
+      }
+}
+
+template <typename TA, typename TB>
+hipError_t gemm64(G64 g, int batch, hipStream_t stream) {
+  if (g.m <= 0 || g.n <= 0 || batch <= 0) return hipSuccess;
+  const int64_t tm = (g.m + kT - 1) / kT, tn = (g.n + kT - 1) / kT;
+  int64_t tiles;
+  if (g.lower) {
+    // the lower mode needs a square tile grid
+    tiles = tm * (tm + 1) / 2;
+    g.tiles_n = (int32_t)tn;
+  } else {
+    tiles = tm * tn;
+    g.tiles_n = (int32_t)tn;
+  }
+  hipLaunchKernelGGL((gemm64_kernel<TA, TB>), dim3((unsigned)tiles, 1, (unsigned)batch),
+                     dim3(256), 0, stream, g);
+  return hipGetLastError();
+}
+
+G64 g64(const void* a, int64_t a_sm, int64_t a_sk, const void* b, int64_t b_sk, int64_t b_sn,
+        double* c, int64_t c_sm, int64_t c_sn, int64_t m, int64_t n, int64_t kred,
+        double alpha, double beta) {
+  G64 g{};
+  g.a = a; g.a_sm = a_sm; g.a_sk = a_sk;
+  g.b = b; g.b_sk = b_sk; g.b_sn = b_sn;
+  g.c = c; g.c_sm = c_sm; g.c_sn = c_sn;
+  g.m = m; g.n = n; g.kred = kred; g.kred_total = 0;
+  g.alpha = alpha; g.beta = beta;
+  return g;
+}
+
+// ------------------------------------------------------------------ H
+
+constexpr int64_t kHessTargetBlocks = 512;   // enough work-groups to fill the chip
+constexpr int64_t kHessMinChunk = 256;       // tokens per partial sum, at least
+
+int64_t hessian_splits(int64_t k, int64_t t) {
+  const int64_t tm = (k + kT - 1) / kT;
+  const int64_t tiles = tm * (tm + 1) / 2;
+  int64_t s = (kHessTargetBlocks + tiles - 1) / tiles;
+  int64_t smax = t / kHessMinChunk;
+  if (smax < 1) smax = 1;
+  if (s > smax) s = smax;
+  if (s > 65535) s = 65535;
+  return s < 1 ? 1 : s;
+}
+
+// h[i][j] += sum_s part[s][max][min]: 32x32 tiles of the lower triangle,
+// mirrored through LDS so both halves of h are written coalesced.
+__global__ __launch_bounds__(256) void hess_reduce_kernel(const double* __restrict__ part,
+                                                          int64_t splits, int64_t k,
+                                                          double* __restrict__ h) {
+  __shared__ double tile[32][33];
+  const int64_t x = blockIdx.x;
+  int64_t bi = (int64_t)((sqrt(8.0 * (double)x + 1.0) - 1.0) * 0.5);
+  while (bi * (bi + 1) / 2 > x) --bi;
+  while ((bi + 1) * (bi + 2) / 2 <= x) ++bi;
+  const int64_t bj = x - bi * (bi + 1) / 2;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
+  const int64_t kk2 = k * k;
+  for (int yy = ty; yy < 32; yy += 8) {
+    const int64_t i = bi * 32 + yy, j = bj * 32 + tx;
+    double s = 0.0;
+    if (i < k && j < k && i >= j)
+      for (int64_t p = 0; p < splits; ++p) s += part[p * kk2 + i * k + j];
+    tile[yy][tx] = s;
+    if (i < k && j < k && i >= j) h[i * k + j] += s;
+  }
+  __syncthreads();
+  // mirrored half: h[j][i] += s(i, j) for i > j, read transposed from LDS
+  for (int yy = ty; yy < 32; yy += 8) {
+    const int64_t j = bj * 32 + yy, i = bi * 32 + tx;
+    if (i < k && j < k && i > j) h[j * k + i] += tile[tx][yy];
+  }
+}
+
+// ------------------------------------------------------------------ U
+
+constexpr int kNb = 64;  // diagonal block of the factorization
+
+// lam = frac * mean(diag h), summed in a fixed order; info = 0, or 1 when
+// the mean diagonal is not positive or lam is not finite.
+__global__ __launch_bounds__(256) void diag_mean_kernel(const double* __restrict__ h, int64_t k,
+                                                        double frac, double* __restrict__ lam,
+                                                        int32_t* __restrict__ info) {
+  __shared__ double red[256];
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < k; i += 256) s += h[i * k + i];
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const double mean = red[0] / (double)k;
+    const double l = frac * mean;
+    const bool ok = mean > 0.0 && l < INFINITY;
+    *lam = ok ? l : 0.0;
+    if (info) *info = ok ? 0 : 1;
+  }
+}
+
+// a[r][c] (kp x kp) = h[k-1-r][k-1-c] + lam*(r == c) on the lower triangle
+// of the reversed, damped matrix, 0 above it, identity on the padding.
+__global__ __launch_bounds__(256) void reverse_damp_kernel(const double* __restrict__ h, int64_t k,
+                                                           const double* __restrict__ lam,
+                                                           double* __restrict__ a, int64_t kp) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= kp * kp) return;
+  const int64_t r = idx / kp, c = idx % kp;
+  double v = 0.0;
+  if (r < k && c < k) {
+    if (r >= c) v = h[(k - 1 - r) * k + (k - 1 - c)] + (r == c ? *lam : 0.0);
+  } else if (r == c) {
+    v = 1.0;
+  }
+  a[idx] = v;
+}
+
+// Factor the diagonal block at (p0, p0) in place (lower L, zeros above the
+// diagonal) and write its inverse to dinv (64 x 64, lower).  One work-group;
+// column by column: the pivot, the column below it, then the rank-1 update
+// of the rest of the block and the matching elimination step of the inverse
+// (which starts as the identity and is turned into L^-1 row by row).
+__global__ __launch_bounds__(256) void potrf_diag_kernel(double* __restrict__ a, int64_t kp,
+                                                         int64_t p0, double* __restrict__ dinv,
+                                                         int32_t* __restrict__ info) {
+  __shared__ double l[kNb][kNb + 1];
+  __shared__ double y[kNb][kNb + 1];
+  const int t = threadIdx.x;
+  for (int e = t; e < kNb * kNb; e += 256) {
+    const int r = e / kNb, c = e % kNb;
+    l[r][c] = (r >= c) ? a[(p0 + r) * kp + (p0 + c)] : 0.0;
+    y[r][c] = (r == c) ? 1.0 : 0.0;
+  }
+  __syncthreads();
+  bool bad = false;
+  for (int c = 0; c < kNb; ++c) {
+    const double d = l[c][c];
+    const double piv = sqrt(d);
+    if (!(d > 0.0)) bad = true;
+    __syncthreads();
+    // column c of L, row c of L^-1
+    if (t < kNb) {
+      if (t > c) l[t][c] = l[t][c] / piv;
+      else if (t == c) l[c][c] = piv;
+    } else if (t < 2 * kNb) {
+      const int j = t - kNb;
+      y[c][j] = y[c][j] / piv;
+    }
+    __syncthreads();
+    // trailing update: l[r][s] -= l[r][c] l[s][c] (c < s <= r);
+    // elimination:     y[r][j] -= l[r][c] y[c][j] (r > c, j <= c)
+    for (int e = t; e < kNb * kNb; e += 256) {
+      const int r = e / kNb, s = e % kNb;
+      if (r > c) {
+        if (s > c && s <= r) l[r][s] -= l[r][c] * l[s][c];
+        if (s <= c) y[r][s] -= l[r][c] * y[c][s];
+      }
+    }
+    __syncthreads();
+  }
+  if (bad && t == 0 && info) *info = 1;
+  for (int e = t; e < kNb * kNb; e += 256) {
+    const int r = e / kNb, c = e % kNb;
+    a[(p0 + r) * kp + (p0 + c)] = (r >= c) ? l[r][c] : 0.0;
+    dinv[r * kNb + c] = (r >= c) ? y[r][c] : 0.0;
+  }
+}
+
+// Copy the 64 x 64 inverses back onto the diagonal blocks of a.
+__global__ __launch_bounds__(256) void put_diag_kernel(double* __restrict__ a, int64_t kp,
+                                                       const double* __restrict__ dinv) {
+  const int64_t p = blockIdx.x;
+  for (int e = threadIdx.x; e < kNb * kNb; e += 256) {
+    const int r = e / kNb, c = e % kNb;
+    a[(p * kNb + r) * kp + (p * kNb + c)] = dinv[p * kNb * kNb + e];
+  }
+}
+
+// u[i][j] = a[k-1-i][k-1-j] for i <= j, 0 below the diagonal.
+__global__ __launch_bounds__(256) void reverse_out_kernel(const double* __restrict__ a, int64_t kp,
+                                                          int64_t k, double* __restrict__ u) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= k * k) return;
+  const int64_t i = idx / k, j = idx % k;
+  u[idx] = (i <= j) ? a[(k - 1 - i) * kp + (k - 1 - j)] : 0.0;
+}
+
+// ------------------------------------------------------------------ codes
+
+__global__ __launch_bounds__(256) void to_f64_kernel(const float* __restrict__ w,
+                                                     double* __restrict__ wd, int64_t count) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx < count) wd[idx] = (double)w[idx];
+}
+
+__device__ inline double readlane_f64(double v, int lane) {
+  const uint64_t b = __double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)b, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(b >> 32), lane);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+__device__ inline float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// One block of components [k0, k0 + bsz) (bsz <= 64) for 4 output channels
+// per work-group, one per wave.  Lane j holds component k0 + j of its
+// channel.  For each component s in order: the group scale when s starts a
+// group, the code of the component (same fp32 quantizer as the plain path),
+// the carried error e = (w_s - w_hat_s) / U[s][s], and w_j -= e * U[s][j]
+// on the lanes j > s.  The codes go to the payload, the errors to e_out
+// [n][64] for the update of the later components.
+template <int BITS>
+__global__ __launch_bounds__(256) void gptq_block_kernel(
+    const double* __restrict__ wd, const double* __restrict__ u, int64_t n, int64_t k,
+    int64_t k0, int bsz, int64_t group, double* __restrict__ e_out,
+    uint8_t* __restrict__ payload, float* __restrict__ scales) {
+  __shared__ double ub[64][64];
+  const int t = threadIdx.x;
+  for (int e = t; e < 64 * 64; e += 256) {
+    const int s = e >> 6, j = e & 63;
+    ub[s][j] = (s < bsz && j < bsz) ? u[(k0 + s) * k + (k0 + j)] : 0.0;
+  }
+  __syncthreads();
+  const int lane = t & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (t >> 6);
+  if (row >= n) return;
+  constexpr float qmax = BITS == 8 ? 127.0f : 7.0f;
+  const double* wr = wd + row * k;
+  const int64_t ngroups = k / group;
+  double w = lane < bsz ? wr[k0 + lane] : 0.0;
+  float sc = 1.0f;
+  if (group > bsz) {
+    // the whole group starts at this block: its scale from the current
+    // weights of all its components (later blocks' entries are in wd)
+    if (k0 % group == 0) {
+      float m = 0.0f;
+      for (int64_t j = k0 + lane; j < k0 + group; j += 64) m = fmaxf(m, fabsf((float)wr[j]));
+      m = wave_max(m);
+      sc = m / qmax;
+      if (sc == 0.0f) sc = 1.0f;
+      if (lane == 0) scales[row * ngroups + k0 / group] = sc;
+    } else {
+      // a block inside a group: the scale was fixed at the group's start
+      sc = scales[row * ngroups + k0 / group];
+    }
+  }
+  int code = 0;
+  double ev = 0.0;
+  for (int s = 0; s < bsz; ++s) {
+    const double us = ub[s][lane];
+    if (group <= bsz && ((k0 + s) % group) == 0) {
+      const float v = (lane >= s && lane < s + group) ? fabsf((float)w) : 0.0f;
+      const float m = wave_max(v);
+      sc = m / qmax;
+      if (sc == 0.0f) sc = 1.0f;
+      if (lane == 0) scales[row * ngroups + (k0 + s) / group] = sc;
+    }
+    const double ws = readlane_f64(w, s);
+    const double uss = readlane_f64(us, s);
+    const float r = (float)ws / sc;
+    const float c = fminf(fmaxf(rintf(r), -qmax), qmax);
+    const float what = c * sc;
+    const double err = (ws - (double)what) / uss;
+    if (lane == s) {
+      code = (int)c;
+      ev = err;
+    }
+    if (lane > s) w = fma(-err, us, w);
+  }
+  if (lane < bsz) e_out[row * 64 + lane] = ev;
+  if (BITS == 8) {
+    if (lane < bsz) payload[row * k + k0 + lane] = (uint8_t)(int8_t)code;
+  } else {
+    const int nib = code + 8;
+    const int hi = __shfl_xor(nib, 1);
+    if (lane < bsz && (lane & 1) == 0)
+      payload[(row * k + k0 + lane) >> 1] = (uint8_t)(nib | (hi << 4));
+  }
+}
+
+int block_size(int bits, int64_t group) {
+  if (group <= 64) return (int)(group * (64 / group));
+  for (int b = 64; b >= 1; --b)
+    if (group % b == 0 && (bits == 8 || (b % 2) == 0)) return b;
+  return bits == 8 ? 1 : 2;
+}
+
+inline unsigned grid1(int64_t count) { return (unsigned)((count + 255) / 256); }
+
+}  // namespace
+
+// ------------------------------------------------------------------ API
+
+int64_t gptq_hessian_work_bytes(int64_t k, int64_t t) {
+  return hessian_splits(k, t) * k * k * (int64_t)sizeof(double);
+}
+
+hipError_t launch_gptq_hessian(int64_t k, int64_t t, const float* x, double* h, void* work,
+                               hipStream_t stream) {
+  const int64_t splits = hessian_splits(k, t);
+  const int64_t chunk = (t + splits - 1) / splits;
+  double* part = (double*)work;
+  // part[s] = X_s^T X_s with X_s the tokens [s*chunk, (s+1)*chunk)
+  G64 g = g64(x, 1, k, x, k, 1, part, k, 1, k, k, chunk, 1.0, 0.0);
+  g.lower = 1;
+  g.a_sz = chunk * k;
+  g.b_sz = chunk * k;
+  g.c_sz = k * k;
+  g.kred_total = t;
+  const int64_t used = (t + chunk - 1) / chunk;
+  hipError_t e = gemm64<float, float>(g, (int)used, stream);
+  if (e != hipSuccess) return e;
+  const int64_t tb = (k + 31) / 32;
+  hipLaunchKernelGGL(hess_reduce_kernel, dim3((unsigned)(tb * (tb + 1) / 2)), dim3(256), 0,
+                     stream, part, used, k, h);
+  return hipGetLastError();
+}
+
+int64_t gptq_factor_work_bytes(int64_t k) {
+  const int64_t kp = (k + kNb - 1) / kNb * kNb;
+  // a (kp x kp), the doubling temporary (kp x kp), the diagonal inverses,
+  // and lam
+  return (2 * kp * kp + kp * kNb + 1) * (int64_t)sizeof(double);
+}
+
+hipError_t launch_gptq_factor(int64_t k, const double* h, double damp, double* u, int32_t* info,
+                              void* work, hipStream_t stream) {
+  const int64_t kp = (k + kNb - 1) / kNb * kNb;
+  const int64_t nblk = kp / kNb;
+  double* a = (double*)work;
+  double* tmp = a + kp * kp;
+  double* dinv = tmp + kp * kp;
+  double* lam = dinv + kp * kNb;
+  hipError_t e;
+
+  hipLaunchKernelGGL(diag_mean_kernel, dim3(1), dim3(256), 0, stream, h, k, damp, lam, info);
+  hipLaunchKernelGGL(reverse_damp_kernel, dim3(grid1(kp * kp)), dim3(256), 0, stream, h, k,
+                     (const double*)lam, a, kp);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  // blocked Cholesky of the reversed matrix, a = L (lower)
+  for (int64_t p = 0; p < nblk; ++p) {
+    const int64_t p0 = p * kNb;
+    hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(256), 0, stream, a, kp, p0,
+                       dinv + p * kNb * kNb, info);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t rest = kp - p0 - kNb;
+    if (rest <= 0) continue;
+    // panel: L21 = A21 L11^-T, in place (one column tile, so each
+    // work-group reads its rows completely before writing them)
+    double* a21 = a + (p0 + kNb) * kp + p0;
+    const double* di = dinv + p * kNb * kNb;
+    e = gemm64<double, double>(g64(a21, kp, 1, di, 1, kNb, a21, kp, 1, rest, kNb, kNb, 1.0, 0.0),
+                               1, stream);
+    if (e != hipSuccess) return e;
+    // trailing: A22 -= L21 L21^T on the lower tiles
+    double* a22 = a + (p0 + kNb) * kp + (p0 + kNb);
+    G64 g = g64(a21, kp, 1, a21, 1, kp, a22, kp, 1, rest, rest, kNb, -1.0, 1.0);
+    g.lower = 1;
+    if ((e = gemm64<double, double>(g, 1, stream)) != hipSuccess) return e;
+  }
+
+  // triangular inverse in place: diagonal blocks first, then doubling
+  hipLaunchKernelGGL(put_diag_kernel, dim3((unsigned)nblk), dim3(256), 0, stream, a, kp,
+                     (const double*)dinv);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  for (int64_t b = kNb; b < kp; b *= 2) {
+    const int64_t nfull = kp / (2 * b);
+    const int64_t step = 2 * b * kp + 2 * b;  // next pair along the diagonal
+    if (nfull > 0) {
+      // T_j = L21_j X11_j
+      G64 g1 = g64(a + b * kp, kp, 1, a, kp, 1, tmp, b, 1, b, b, b, 1.0, 0.0);
+      g1.a_sz = step; g1.b_sz = step; g1.c_sz = b * b;
+      if ((e = gemm64<double, double>(g1, (int)nfull, stream)) != hipSuccess) return e;
+      // X21_j = -X22_j T_j
+      G64 g2 = g64(a + b * kp + b, kp, 1, tmp, b, 1, a + b * kp, kp, 1, b, b, b, -1.0, 0.0);
+      g2.a_sz = step; g2.b_sz = b * b; g2.c_sz = step;
+      if ((e = gemm64<double, double>(g2, (int)nfull, stream)) != hipSuccess) return e;
+    }
+    const int64_t top0 = nfull * 2 * b, bot0 = top0 + b;
+    if (bot0 < kp) {
+      const int64_t bb = kp - bot0;
+      double* tp = tmp + nfull * b * b;
+      e = gemm64<double, double>(
+          g64(a + bot0 * kp + top0, kp, 1, a + top0 * kp + top0, kp, 1, tp, b, 1, bb, b, b,
+              1.0, 0.0),
+          1, stream);
+      if (e != hipSuccess) return e;
+      e = gemm64<double, double>(
+          g64(a + bot0 * kp + bot0, kp, 1, tp, b, 1, a + bot0 * kp + top0, kp, 1, bb, b, bb,
+              -1.0, 0.0),
+          1, stream);
+      if (e != hipSuccess) return e;
+    }
+  }
+  hipLaunchKernelGGL(reverse_out_kernel, dim3(grid1(k * k)), dim3(256), 0, stream,
+                     (const double*)a, kp, k, u);
+  return hipGetLastError();
+}
+
+int64_t gptq_quantize_work_bytes(int64_t n, int64_t k) {
+  return (n * k + n * 64) * (int64_t)sizeof(double);
+}
+
+hipError_t launch_gptq_quantize_pack(const Mat& mt, const float* w, const double* u,
+                                     uint8_t* payload, float* scales, void* work,
+                                     hipStream_t stream) {
+  const int64_t n = mt.n, k = mt.k;
+  double* wd = (double*)work;
+  double* eb = wd + n * k;
+  hipLaunchKernelGGL(to_f64_kernel, dim3(grid1(n * k)), dim3(256), 0, stream, w, wd, n * k);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int bsz = block_size(mt.bits, mt.group);
+  const unsigned wgs = (unsigned)((n + 3) / 4);
+  for (int64_t k0 = 0; k0 < k; k0 += bsz) {
+    const int cur = (int)((k - k0) < bsz ? (k - k0) : bsz);
+    if (mt.bits == 8)
+      hipLaunchKernelGGL(gptq_block_kernel<8>, dim3(wgs), dim3(256), 0, stream,
+                         (const double*)wd, u, n, k, k0, cur, mt.group, eb, payload, scales);
+    else
+      hipLaunchKernelGGL(gptq_block_kernel<4>, dim3(wgs), dim3(256), 0, stream,
+                         (const double*)wd, u, n, k, k0, cur, mt.group, eb, payload, scales);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int64_t k1 = k0 + cur;
+    if (k1 < k) {
+      // W[:, k1:] -= E U[k0:k1, k1:]
+      e = gemm64<double, double>(g64(eb, 64, 1, u + k0 * k + k1, k, 1, wd + k1, k, 1, n, k - k1,
+                                     cur, -1.0, 1.0),
+                                 1, stream);
+      if (e != hipSuccess) return e;
+    }
+  }
+  return hipSuccess;
+}
+
+}  // namespace qw

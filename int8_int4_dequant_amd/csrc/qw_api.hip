@@ -60,6 +60,8 @@ const char* qw_status_string(int status) {
     case QW_ENULL: return "required pointer is NULL";
     case QW_EHIP: return "HIP launch failed (see qw_last_error)";
     case QW_ECOUNT: return "invalid batch count or descriptor";
+    case QW_EWORK: return "work buffer missing or too small";
+    case QW_EARG: return "argument out of range";
     default: return "unknown status";
   }
 }
@@ -190,6 +192,55 @@ int qw_gemm(int bits, int64_t group, int64_t n, int64_t k, const uint8_t* payloa
   if (k == 0) return record(qw::launch_fill_zero(y, m * n, (hipStream_t)stream));
   if (!payload || !scales || !x_bf16) return QW_ENULL;
   return record(qw::launch_gemm(mt, payload, scales, m, x_bf16, y, (hipStream_t)stream));
+}
+
+int64_t qw_gptq_hessian_work_bytes(int64_t k, int64_t t) {
+  if (k < 0 || t < 0 || mul_overflows(k, k)) return -1;
+  return qw::gptq_hessian_work_bytes(k, t);
+}
+
+int qw_gptq_hessian(int64_t k, int64_t t, const float* x, double* h, void* work,
+                    int64_t work_bytes, void* stream) {
+  if (k < 0 || t < 0 || mul_overflows(k, k) || mul_overflows(k, t)) return QW_ESHAPE;
+  if (k == 0 || t == 0) return QW_OK;
+  if (!x || !h) return QW_ENULL;
+  if (!work || work_bytes < qw::gptq_hessian_work_bytes(k, t)) return QW_EWORK;
+  return record(qw::launch_gptq_hessian(k, t, x, h, work, (hipStream_t)stream));
+}
+
+int64_t qw_gptq_factor_work_bytes(int64_t k) {
+  if (k < 0 || mul_overflows(k + 64, k + 64)) return -1;
+  return qw::gptq_factor_work_bytes(k);
+}
+
+int qw_gptq_factor(int64_t k, const double* h, double damp, double* u, int32_t* info,
+                   void* work, int64_t work_bytes, void* stream) {
+  if (k < 0 || mul_overflows(k + 64, k + 64)) return QW_ESHAPE;
+  if (!(damp >= 0.0) || !(damp < 1e300)) return QW_EARG;
+  if (k == 0) return QW_OK;
+  if (!h || !u) return QW_ENULL;
+  if (!work || work_bytes < qw::gptq_factor_work_bytes(k)) return QW_EWORK;
+  return record(qw::launch_gptq_factor(k, h, damp, u, info, work, (hipStream_t)stream));
+}
+
+int64_t qw_gptq_quantize_work_bytes(int64_t n, int64_t k) {
+  if (n < 0 || k < 0 || mul_overflows(n, k + 64)) return -1;
+  return qw::gptq_quantize_work_bytes(n, k);
+}
+
+int qw_gptq_quantize_pack(int bits, int64_t group, int64_t n, int64_t k, const float* w,
+                          const double* u, uint8_t* payload, float* scales, void* work,
+                          int64_t work_bytes, void* stream) {
+  qw::Mat mt;
+  int st = check_mat(bits, group, n, k, &mt);
+  if (st != QW_OK) return st;
+  if (mul_overflows(n, k + 64)) return QW_ESHAPE;
+  if (k > 0 && (k % group != 0 || (bits == 4 && group % 2 != 0))) return QW_EGROUP;
+  if (n * k == 0) return QW_OK;
+  if (!w || !u || !payload || !scales) return QW_ENULL;
+  if (!work || work_bytes < qw::gptq_quantize_work_bytes(n, k)) return QW_EWORK;
+  return record(qw::launch_gptq_quantize_pack(mt, w, u, payload, scales, work,
+                                              (hipStream_t)stream));
 }
 
 // Which kernel family a call with these arguments would take (1 = fast,

@@ -38,6 +38,19 @@ hipError_t launch_gemm(const Mat& mt, const uint8_t* payload, const float* scale
                        int64_t m, const uint16_t* x, float* y, hipStream_t stream);
 hipError_t launch_fill_zero(float* y, int64_t count, hipStream_t stream);
 
+// GPTQ (gptq.hip).  Work buffers are caller-provided device memory of at
+// least the returned sizes.
+int64_t gptq_hessian_work_bytes(int64_t k, int64_t t);
+hipError_t launch_gptq_hessian(int64_t k, int64_t t, const float* x, double* h, void* work,
+                               hipStream_t stream);
+int64_t gptq_factor_work_bytes(int64_t k);
+hipError_t launch_gptq_factor(int64_t k, const double* h, double damp, double* u, int32_t* info,
+                              void* work, hipStream_t stream);
+int64_t gptq_quantize_work_bytes(int64_t n, int64_t k);
+hipError_t launch_gptq_quantize_pack(const Mat& mt, const float* w, const double* u,
+                                     uint8_t* payload, float* scales, void* work,
+                                     hipStream_t stream);
+
 // Which kernel family a call takes (exposed for tests through qw_debug_path).
 enum Path { PATH_NONE = 0, PATH_FAST = 1, PATH_BLOCK = 2, PATH_GENERIC = 3 };
 int quantize_path(const Mat& mt, const float* w, const uint8_t* payload);

@@ -221,6 +221,13 @@ SMALLEM_INPUTS = {
 SMALLEM_OUTLIER_COMPONENTS = (112, 257, 285)
 
 
+def smallem_group(k):
+    """int4 group of a map with k inputs: 64, or for the 1368-input down map
+    (not a multiple of 64, and a group may not span two output channels)
+    72, the smallest divisor of 1368 above 64."""
+    return 64 if k % 64 == 0 else 72
+
+
 def calibration_activations(seed, t, k):
     """fp32 [t][k] correlated activations from ``default_rng(seed)``:
     x = (0.8 * z_c . F + 0.4 * z_i) * c, with z_c [t][r] and z_i [t][k]

@@ -25,12 +25,14 @@ BATCH_PER_LAUNCH = 256
 
 QW_OK = 0
 STATUS_NAMES = {0: "QW_OK", -1: "QW_EBITS", -2: "QW_EGROUP", -3: "QW_ESHAPE", -4: "QW_EM",
-                -5: "QW_ENULL", -6: "QW_EHIP", -7: "QW_ECOUNT"}
+                -5: "QW_ENULL", -6: "QW_EHIP", -7: "QW_ECOUNT", -8: "QW_EWORK", -9: "QW_EARG"}
 
 #: symbols declared in include/qw.h
 EXPORTS = ["qw_payload_bytes", "qw_num_scales", "qw_status_string", "qw_last_error",
            "qw_quantize_pack", "qw_quantize_pack_batched", "qw_unpack", "qw_gemv",
-           "qw_gemv_batched", "qw_gemm", "qw_debug_path"]
+           "qw_gemv_batched", "qw_gemm", "qw_debug_path",
+           "qw_gptq_hessian_work_bytes", "qw_gptq_hessian", "qw_gptq_factor_work_bytes",
+           "qw_gptq_factor", "qw_gptq_quantize_work_bytes", "qw_gptq_quantize_pack"]
 
 
 class QwQuantDesc(ctypes.Structure):
@@ -94,6 +96,18 @@ def lib():
     L.qw_gemm.restype = i32
     L.qw_debug_path.argtypes = [i32, i32, i64, i64, i64, vp, vp]
     L.qw_debug_path.restype = i32
+    L.qw_gptq_hessian_work_bytes.argtypes = [i64, i64]
+    L.qw_gptq_hessian_work_bytes.restype = i64
+    L.qw_gptq_hessian.argtypes = [i64, i64, vp, vp, vp, i64, vp]
+    L.qw_gptq_hessian.restype = i32
+    L.qw_gptq_factor_work_bytes.argtypes = [i64]
+    L.qw_gptq_factor_work_bytes.restype = i64
+    L.qw_gptq_factor.argtypes = [i64, vp, ctypes.c_double, vp, vp, vp, i64, vp]
+    L.qw_gptq_factor.restype = i32
+    L.qw_gptq_quantize_work_bytes.argtypes = [i64, i64]
+    L.qw_gptq_quantize_work_bytes.restype = i64
+    L.qw_gptq_quantize_pack.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp, vp, i64, vp]
+    L.qw_gptq_quantize_pack.restype = i32
     _lib = L
     return L
 
@@ -181,6 +195,34 @@ def qw_gemm(bits, group, n, k, payload, scales, m, x_bf16, y, stream=None):
 
 def qw_debug_path(op, bits, group, n, k, a=None, b=None):
     return lib().qw_debug_path(op, bits, group, n, k, _ptr(a), _ptr(b))
+
+
+def qw_gptq_hessian_work_bytes(k, t):
+    return lib().qw_gptq_hessian_work_bytes(k, t)
+
+
+def qw_gptq_hessian(k, t, x, h, work, work_bytes, stream=None):
+    return lib().qw_gptq_hessian(k, t, _ptr(x), _ptr(h), _ptr(work), work_bytes,
+                                 _stream(stream))
+
+
+def qw_gptq_factor_work_bytes(k):
+    return lib().qw_gptq_factor_work_bytes(k)
+
+
+def qw_gptq_factor(k, h, damp, u, info, work, work_bytes, stream=None):
+    return lib().qw_gptq_factor(k, _ptr(h), damp, _ptr(u), _ptr(info), _ptr(work), work_bytes,
+                                _stream(stream))
+
+
+def qw_gptq_quantize_work_bytes(n, k):
+    return lib().qw_gptq_quantize_work_bytes(n, k)
+
+
+def qw_gptq_quantize_pack(bits, group, n, k, w, u, payload, scales, work, work_bytes,
+                          stream=None):
+    return lib().qw_gptq_quantize_pack(bits, group, n, k, _ptr(w), _ptr(u), _ptr(payload),
+                                       _ptr(scales), _ptr(work), work_bytes, _stream(stream))
 
 
 # -------------------------------------------------------- convenience layer
@@ -279,3 +321,74 @@ def gemm(rec, x_bf16, out=None, stream=None):
     _check(qw_gemm(rec["bits"], rec["group"], n, k, rec["payload"], rec["scales"], m, x_bf16,
                    out, stream), "qw_gemm")
     return out
+
+
+# ------------------------------------------------------------------ GPTQ
+
+
+def _work(nbytes, device):
+    if nbytes < 0:
+        raise ValueError("invalid shape for a work-size query")
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def gptq_hessian(x, h=None, stream=None):
+    """h += x^T x for a contiguous fp32 device tensor x [t][k]; allocates a
+    zero fp64 [k][k] accumulator when ``h`` is None.  Returns h."""
+    if x.dtype != torch.float32 or not x.is_contiguous() or x.dim() != 2:
+        raise ValueError("x must be a contiguous float32 [t][k] tensor")
+    t, k = int(x.shape[0]), int(x.shape[1])
+    if h is None:
+        h = torch.zeros((k, k), dtype=torch.float64, device=x.device)
+    if h.dtype != torch.float64 or not h.is_contiguous() or tuple(h.shape) != (k, k):
+        raise ValueError("h must be a contiguous float64 [k][k] tensor")
+    nb = lib().qw_gptq_hessian_work_bytes(k, t)
+    work = _work(nb, x.device)
+    _check(qw_gptq_hessian(k, t, x, h, work, nb, stream), "qw_gptq_hessian")
+    return h
+
+
+def gptq_factor(h, damp=0.01, stream=None, check=True):
+    """U (fp64 [k][k], upper) with (h + damp*mean(diag h)*I)^-1 = U^T U.
+    With ``check`` the stream is synchronized and a non-positive-definite h
+    raises; otherwise (u, info) is returned with info a device int32."""
+    if h.dtype != torch.float64 or not h.is_contiguous() or h.dim() != 2 \
+            or h.shape[0] != h.shape[1]:
+        raise ValueError("h must be a contiguous float64 [k][k] tensor")
+    k = int(h.shape[0])
+    u = torch.empty((k, k), dtype=torch.float64, device=h.device)
+    info = torch.zeros(1, dtype=torch.int32, device=h.device)
+    nb = lib().qw_gptq_factor_work_bytes(k)
+    work = _work(nb, h.device)
+    _check(qw_gptq_factor(k, h, float(damp), u, info, work, nb, stream), "qw_gptq_factor")
+    if not check:
+        return u, info
+    if k and int(info.item()) != 0:
+        raise QwError(-9, "qw_gptq_factor: the damped H is not positive definite")
+    return u
+
+
+def gptq_quantize_pack(w, u, bits, group, stream=None):
+    """GPTQ codes of a contiguous fp32 device weight [n][k] with the factor
+    ``u`` from gptq_factor; returns a record like quantize_pack."""
+    if w.dtype != torch.float32 or not w.is_contiguous():
+        raise ValueError("w must be a contiguous float32 tensor")
+    n, k = _nk(w.shape)
+    if u.dtype != torch.float64 or not u.is_contiguous() or tuple(u.shape) != (k, k):
+        raise ValueError("u must be a contiguous float64 [k][k] tensor")
+    nb = lib().qw_payload_bytes(bits, n, k)
+    ns = lib().qw_num_scales(group, n, k)
+    if nb < 0 or ns < 0:
+        _check(QW_EBITS if bits not in (4, 8) else -2 if ns < 0 else -3, "gptq_quantize_pack")
+    payload = torch.empty(nb, dtype=torch.uint8, device=w.device)
+    scales = torch.empty(ns, dtype=torch.float32, device=w.device)
+    wb = lib().qw_gptq_quantize_work_bytes(n, k)
+    work = _work(wb, w.device)
+    _check(qw_gptq_quantize_pack(bits, group, n, k, w, u, payload, scales, work, wb, stream),
+           "qw_gptq_quantize_pack")
+    return dict(bits=bits, group=group, shape=[n, k], payload=payload, scales=scales)
+
+
+def gptq(w, h, bits, group, damp=0.01, stream=None):
+    """The whole chain from an accumulated h: damping, factor, codes."""
+    return gptq_quantize_pack(w, gptq_factor(h, damp, stream), bits, group, stream)
