@@ -59,7 +59,10 @@ def parse():
                          "(the known-size kernel that calibrates the HBM byte counters)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the traffic summary of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--no-gptq", action="store_true")
+    ap.add_argument("--gptq-reps", type=int, default=3)
     ap.add_argument("--cpu-sample-worker", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--gptq-cpu-sample-worker", action="store_true", help=argparse.SUPPRESS)
     return ap.parse_args()
 
 
@@ -203,6 +206,9 @@ def main():
     args = parse()
     if args.cpu_sample_worker:
         cpu_sample_worker()
+        return
+    if args.gptq_cpu_sample_worker:
+        gptq_cpu_sample_worker()
         return
     if args.pmc_summary:
         print("```json\n" + json.dumps(pmc_summary(*args.pmc_summary, copy_mib=1024), indent=1)
@@ -403,6 +409,8 @@ def main():
     if not args.no_gemm:
         gemm = bench_gemm(args, L, stream)
 
+    gptq = None if args.no_gptq else bench_gptq(args, L, stream)
+
     cpu = None if args.no_cpu_baseline else cpu_baseline()
 
     out = {
@@ -416,7 +424,7 @@ def main():
                    "layers": args.layers, "matrices": len(shapes), "weights": weights,
                    "bits": 4, "group": 32, "m": 1, "bytes_per_step": qbytes + gbytes},
         "roofline": roofline, "parts": parts, "decode_gemv_configs": gemv_cfgs,
-        "prefill_gemm": gemm, "cpu_baseline": cpu,
+        "prefill_gemm": gemm, "gptq": gptq, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
 
@@ -566,6 +574,205 @@ def bench_gemm(args, L, stream):
                          "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic("gemm"),
                          "algorithmic_bytes": n * k // 2 + n * k // 128 * 4 + m * k * 2 + m * n * 4}}
+
+
+# ------------------------------------------------------------------ GPTQ
+
+FP64_PEAK_TFLOPS = 78.6
+GPTQ_BATCHES = 8  # calibration batches per input (the page: 8 batches of 16 sequences)
+
+
+def gptq_cpu_sample_worker():
+    """Runs in a child process with one BLAS / OpenMP thread: the oracle on
+    the whole layer the GPU leg times (per input: H over the 65,536
+    calibration tokens in 8 batches, damping, factor, then the codes of
+    every map reading that input)."""
+    import numpy as np
+
+    from oracle import gptq as G
+    from int8_int4_dequant_amd import inputs
+
+    dt = 0.0
+    weights = 0
+    for src in inputs.SMALLEM_INPUTS:
+        x = inputs.smallem_calibration(src)
+        maps = [(s, m) for s, m in enumerate(inputs.SMALLEM_LAYER) if m[3] == src]
+        ws = [inputs.smallem_weight(s) for s, _ in maps]
+        t0 = time.perf_counter()
+        u = G.inverse_factor(G.damped(G.hessian(np.array_split(x, GPTQ_BATCHES))))
+        for w in ws:
+            G.quantize_pack(w, u, 4, inputs.smallem_group(w.shape[1]))
+        dt += time.perf_counter() - t0
+        weights += sum(w.size for w in ws)
+        del x
+    print(json.dumps(dict(seconds=dt, weights=weights, tokens=inputs.CALIB_TOKENS)))
+
+
+def gptq_cpu_baseline():
+    env = dict(os.environ)
+    for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "VECLIB_MAXIMUM_THREADS"):
+        env[v] = "1"
+    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--gptq-cpu-sample-worker"],
+                       capture_output=True, text=True, env=env, timeout=900)
+    if r.returncode != 0:
+        log(r.stderr[-2000:])
+        return None
+    d = json.loads(r.stdout.strip().splitlines()[-1])
+    return {"value": round(d["weights"] / d["seconds"], 1), "unit": "weights/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"the whole layer ({d['weights']} weights, 4 inputs of {d['tokens']} "
+                      f"tokens in {GPTQ_BATCHES} batches): oracle H, factor and codes, "
+                      f"{d['seconds']:.2f} s, one thread"}
+
+
+def bench_gptq(args, L, stream):
+    """GPTQ of one layer of the page's small model from its calibration
+    inputs: per input, H accumulated over 8 batches (qw_gptq_hessian), the
+    factor (qw_gptq_factor), then the codes of every map reading that input
+    (qw_gptq_quantize_pack).  Timed with events on the launch stream."""
+    import torch
+
+    from int8_int4_dequant_amd import inputs
+
+    dev = torch.device("cuda:0")
+    sp = stream.cuda_stream
+    groups = {}
+    for slot, (name, n, k, src) in enumerate(inputs.SMALLEM_LAYER):
+        groups.setdefault(src, []).append((slot, name, n, k))
+    T = inputs.CALIB_TOKENS
+    chunk = T // GPTQ_BATCHES
+    data = {}
+    for src, maps in groups.items():
+        k = maps[0][3]
+        x = torch.from_numpy(inputs.smallem_calibration(src)).to(dev)
+        h = torch.empty((k, k), dtype=torch.float64, device=dev)
+        u = torch.empty((k, k), dtype=torch.float64, device=dev)
+        info = torch.zeros(1, dtype=torch.int32, device=dev)
+        hw = L.qw_gptq_hessian_work_bytes(k, chunk)
+        fw = L.qw_gptq_factor_work_bytes(k)
+        recs = []
+        for slot, name, n, kk in maps:
+            g = inputs.smallem_group(kk)
+            w = torch.from_numpy(inputs.smallem_weight(slot)).to(dev)
+            recs.append(dict(name=name, n=n, k=kk, group=g, w=w,
+                             p=torch.empty(n * kk // 2, dtype=torch.uint8, device=dev),
+                             s=torch.empty(n * kk // g, dtype=torch.float32, device=dev),
+                             wb=L.qw_gptq_quantize_work_bytes(n, kk)))
+        qwb = max(r["wb"] for r in recs)
+        data[src] = dict(k=k, x=x, h=h, u=u, info=info, hw=hw, fw=fw, recs=recs,
+                         hwork=torch.empty(hw, dtype=torch.uint8, device=dev),
+                         fwork=torch.empty(fw, dtype=torch.uint8, device=dev),
+                         qwork=torch.empty(qwb, dtype=torch.uint8, device=dev))
+
+    def ck(r, what):
+        if r:
+            raise RuntimeError(f"{what} failed: {r}")
+
+    streams = {src: torch.cuda.Stream() for src in data}  # default priority
+
+    def run(ev=None, concurrent=False):
+        # one chain per input; with `concurrent` each runs on its own stream
+        # (they are independent), else all run on `stream` one after another
+        if concurrent:
+            start = torch.cuda.Event()
+            start.record(stream)
+        for src, d in data.items():
+            k = d["k"]
+            st = streams[src] if concurrent else stream
+            sp_ = st.cuda_stream
+            if concurrent:
+                st.wait_event(start)
+            if ev is not None:
+                ev[src][0].record(st)
+            with torch.cuda.stream(st):
+                d["h"].zero_()
+            for b in range(GPTQ_BATCHES):
+                ck(L.qw_gptq_hessian(k, chunk, d["x"][b * chunk:].data_ptr(), d["h"].data_ptr(),
+                                     d["hwork"].data_ptr(), d["hw"], sp_), "qw_gptq_hessian")
+            if ev is not None:
+                ev[src][1].record(st)
+            ck(L.qw_gptq_factor(k, d["h"].data_ptr(), 0.01, d["u"].data_ptr(),
+                                d["info"].data_ptr(), d["fwork"].data_ptr(), d["fw"], sp_),
+               "qw_gptq_factor")
+            if ev is not None:
+                ev[src][2].record(st)
+            for r in d["recs"]:
+                ck(L.qw_gptq_quantize_pack(4, r["group"], r["n"], r["k"], r["w"].data_ptr(),
+                                           d["u"].data_ptr(), r["p"].data_ptr(),
+                                           r["s"].data_ptr(), d["qwork"].data_ptr(),
+                                           d["qwork"].numel(), sp_), "qw_gptq_quantize_pack")
+            if ev is not None:
+                ev[src][3].record(st)
+        if concurrent:
+            for src in data:
+                stream.wait_stream(streams[src])
+
+    run()
+    run(concurrent=True)
+    torch.cuda.synchronize()
+    for src, d in data.items():
+        if int(d["info"].item()) != 0:
+            raise RuntimeError(f"GPTQ factor of {src} reported a non-positive-definite H")
+    # the layer with the four inputs' chains on four streams
+    conc = []
+    for _ in range(args.gptq_reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run(concurrent=True)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        conc.append(e0.elapsed_time(e1))
+    conc.sort()
+    conc_ms = conc[len(conc) // 2]
+    # per-stage times with the chains one after another on one stream
+    reps = []
+    for _ in range(args.gptq_reps):
+        ev = {src: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for src in data}
+        run(ev)
+        torch.cuda.synchronize()
+        reps.append({src: [e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]),
+                           e[2].elapsed_time(e[3])] for src, e in ev.items()})
+    # the rep with the median layer time
+    layer = sorted(reps, key=lambda r: sum(sum(v) for v in r.values()))[len(reps) // 2]
+    seq_ms = sum(sum(v) for v in layer.values())
+    layer_ms = min(conc_ms, seq_ms)
+    weights = sum(r["n"] * r["k"] for d in data.values() for r in d["recs"])
+    per_input = {}
+    for src, (th, tf, tq) in layer.items():
+        d = data[src]
+        k = d["k"]
+        flops = T * k * (k + 1)
+        per_input[src] = {"k": k, "maps": [r["name"] for r in d["recs"]],
+                          "hessian_us": round(th * 1e3, 1), "factor_us": round(tf * 1e3, 1),
+                          "quantize_us": round(tq * 1e3, 1),
+                          "hessian_TFLOP/s": round(flops / (th * 1e-3) / 1e12, 2)}
+    dom = max(per_input, key=lambda s: per_input[s]["hessian_us"])
+    dk = per_input[dom]["k"]
+    h_us_per_launch = per_input[dom]["hessian_us"] / GPTQ_BATCHES
+    tf = chunk * dk * (dk + 1) / (h_us_per_launch * 1e-6) / 1e12
+    log(f"gptq layer {layer_ms:.2f} ms ({weights / (layer_ms * 1e-3) / 1e6:.1f} M weights/s; "
+        f"4 streams {conc_ms:.2f} ms, one stream {seq_ms:.2f} ms); "
+        + "; ".join(f"{s}: H {v['hessian_us']:.0f} us ({v['hessian_TFLOP/s']:.1f} TF), factor "
+                    f"{v['factor_us']:.0f} us, codes {v['quantize_us']:.0f} us"
+                    for s, v in per_input.items()))
+    cpu = None if args.no_cpu_baseline else gptq_cpu_baseline()
+    return {
+        "workload": "GPTQ of one layer of the small model (width 512, feed-forward 1368): "
+                    "q, k, v, o 512x512, gate and up 1368x512, down 512x1368, int4 group 64 "
+                    "(72 for the 1368-input map); 65,536 calibration tokens per input in 8 "
+                    "batches; H, damping 1%, factor, codes",
+        "value": round(weights / (layer_ms * 1e-3), 1), "unit": "weights/s",
+        "layer_ms": round(layer_ms, 3), "layer_ms_four_streams": round(conc_ms, 3),
+        "layer_ms_one_stream": round(seq_ms, 3), "weights": weights, "reps": args.gptq_reps,
+        "per_input": per_input,
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP64_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / FP64_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": f"qw_gptq_hessian (fp64 MFMA X^T X + fixed-order reduce), "
+                               f"k={dk}, {chunk} tokens per launch",
+                     "algorithmic_flops_per_launch": chunk * dk * (dk + 1),
+                     "avg_launch_us": round(h_us_per_launch, 2)},
+        "cpu_baseline": cpu,
+    }
 
 
 if __name__ == "__main__":

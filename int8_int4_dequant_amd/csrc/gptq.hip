@@ -16,17 +16,20 @@
 //   U       With J the index reversal, JHJ = L L^T (lower Cholesky) gives
 //           H = R R^T with R = J L J upper, hence H^-1 = (R^-1)^T R^-1 and
 //           U = R^-1 = J L^-1 J.  One blocked Cholesky (64-wide diagonal
-//           blocks factored and inverted in LDS, panels as GEMMs with the
-//           block inverse, trailing updates as GEMMs on the lower tiles) and
-//           one blocked triangular inverse (diagonal block inverses, then
-//           doubling: X21 = -X22 (L21 X11) for pairs of ever larger blocks).
+//           blocks factored by one wave in registers, panels solved one row
+//           per thread, trailing updates as GEMMs on the lower tiles) and
+//           one blocked triangular inverse (all diagonal block inverses in
+//           one launch, then doubling: X21 = -X22 (L21 X11) for pairs of
+//           ever larger blocks).
 //   codes   The page's column loop, blocked: a block of up to 64 components
 //           is rounded by one wave per output channel (lane j holds
 //           component j of the block; the rounding error is broadcast with
-//           readlane and carried to the later lanes at once); the carried
-//           errors of the block are then applied to every later component
-//           with one GEMM, W[:, after] -= E . U[block, after].  This is the
-//           same arithmetic in another summation order.
+//           readlane and carried to the later lanes at once); the errors of
+//           the block are then applied to every later component with one
+//           GEMM, W[:, after] -= D . V[block, after].  The error carried by
+//           the page's loop, (w - w_hat) / U[c][c] times U[c][j], is used
+//           as (w - w_hat) times V[c][j] with V[c][j] = U[c][j] / U[c][c]
+//           computed once: the same arithmetic in another rounding order.
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -61,17 +64,31 @@ struct G64 {
   int32_t lower, tiles_n;
 };
 
-constexpr int kT = 64;     // tile edge
-constexpr int kS = 16;     // reduction step per LDS stage
-constexpr int kLd = kT + 4;
+// Two shapes: WB = 2 (64 x 64 tiles, waves of 2 x 2 MFMA blocks, reduction
+// stages of 32) and WB = 4 (128 x 128 tiles, waves of 4 x 4 blocks, stages
+// of 16, registers capped so two waves share each SIMD: one wave issues at
+// most one fp64 MFMA per 64 cycles and stalls at every stage boundary).
+// The larger tile reads half as many LDS bytes per MFMA.  The global loads
+// of the next stage are issued before the current stage's MFMAs.
+template <int WB>
+struct GShape {
+  static constexpr int kTile = 32 * WB;       // 2 x 2 waves of 16*WB
+  static constexpr int kStage = WB == 2 ? 32 : 16;
+  static constexpr int kLd = kTile + 4;
+  static constexpr int kPer = kTile * kStage / 256;  // staged elements per thread
+};
 
-template <typename T>
-__device__ inline double ld_as_double(const T* p, int64_t off) {
-  return (double)p[off];
-}
-
-template <typename TA, typename TB>
-__global__ __launch_bounds__(256) void gemm64_kernel(G64 g) {
+// AI: A is contiguous along i (a_sm == 1), else along the reduction
+// (a_sk == 1); BJ: B is contiguous along j (b_sn == 1), else along the
+// reduction (b_sk == 1).  Each thread stages kPer elements of each operand
+// per stage: one fixed index along the contiguous dimension and kPer
+// indices a fixed step apart along the other, so a stage's addresses are
+// one per-thread base plus uniform multiples of a stride.
+template <typename TA, typename TB, int WB, bool AI, bool BJ>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WB == 4 ? 2 : 1)))
+void gemm64_kernel(G64 g) {
+  using S = GShape<WB>;
+  constexpr int kT = S::kTile, kS = S::kStage, kLd = S::kLd, kPer = S::kPer;
   __shared__ double as[2][kS][kLd];
   __shared__ double bs[2][kS][kLd];
 
@@ -103,45 +120,62 @@ __global__ __launch_bounds__(256) void gemm64_kernel(G64 g) {
   const int wave = t >> 6;
   const int wi = wave >> 1, wj = wave & 1;
 
-  // global -> register mapping of the staged tiles (4 elements per thread)
-  const bool a_icontig = (g.a_sm == 1);
-  const bool b_jcontig = (g.b_sn == 1);
-  double ra[4], rb[4];
+  // A: element r of this thread is (ii, kk) of the tile
+  constexpr int kAStep = AI ? 256 / kT : 256 / kS;
+  const int a_fix = AI ? t % kT : t % kS;   // ii (AI) or kk
+  const int a_var = AI ? t / kT : t / kS;   // kk (AI) or ii, plus kAStep * r
+  const int64_t a_rstride = (int64_t)kAStep * (AI ? g.a_sk : g.a_sm);
+  constexpr int kBStep = BJ ? 256 / kT : 256 / kS;
+  const int b_fix = BJ ? t % kT : t % kS;
+  const int b_var = BJ ? t / kT : t / kS;
+  const int64_t b_rstride = (int64_t)kBStep * (BJ ? g.b_sk : g.b_sn);
+  // raw operand values of the next stage and which of them lie inside the
+  // operands; converted (or zeroed) only when stored to LDS, after the
+  // current stage's MFMAs, so the loads' latency overlaps them
+  TA ra[kPer];
+  TB rb[kPer];
+  uint32_t aok_mask = 0, bok_mask = 0;
 
   auto load_stage = [&](int64_t k0) {
+    const TA* abase = AI ? pa + (i0 + a_fix) + (k0 + a_var) * g.a_sk
+                         : pa + (i0 + a_var) * g.a_sm + (k0 + a_fix);
+    const TB* bbase = BJ ? pb + (k0 + b_var) * g.b_sk + (j0 + b_fix)
+                         : pb + (k0 + b_fix) + (j0 + b_var) * g.b_sn;
+    aok_mask = 0;
+    bok_mask = 0;
+    // every load is issued unconditionally (an element outside the operand
+    // reads element 0 instead and is replaced by zero when stored)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      int ii, kk;
-      if (a_icontig) { ii = t & 63; kk = (t >> 6) + 4 * r; }
-      else { kk = t & 15; ii = (t >> 4) + 16 * r; }
-      const int64_t gi = i0 + ii, gk = k0 + kk;
-      ra[r] = (gi < g.m && gk < kred) ? ld_as_double(pa, gi * g.a_sm + gk * g.a_sk) : 0.0;
-      int jj, kb;
-      if (b_jcontig) { jj = t & 63; kb = (t >> 6) + 4 * r; }
-      else { kb = t & 15; jj = (t >> 4) + 16 * r; }
-      const int64_t gj = j0 + jj, gkb = k0 + kb;
-      rb[r] = (gj < g.n && gkb < kred) ? ld_as_double(pb, gkb * g.b_sk + gj * g.b_sn) : 0.0;
+    for (int r = 0; r < kPer; ++r) {
+      const int v = a_var + kAStep * r;
+      const bool aok = AI ? (i0 + a_fix < g.m && k0 + v < kred) : (i0 + v < g.m && k0 + a_fix < kred);
+      ra[r] = *(aok ? abase + r * a_rstride : pa);
+      aok_mask |= (uint32_t)aok << r;
+      const int w = b_var + kBStep * r;
+      const bool bok = BJ ? (j0 + b_fix < g.n && k0 + w < kred) : (j0 + w < g.n && k0 + b_fix < kred);
+      rb[r] = *(bok ? bbase + r * b_rstride : pb);
+      bok_mask |= (uint32_t)bok << r;
     }
   };
   auto store_stage = [&](int buf) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      int ii, kk;
-      if (a_icontig) { ii = t & 63; kk = (t >> 6) + 4 * r; }
-      else { kk = t & 15; ii = (t >> 4) + 16 * r; }
-      as[buf][kk][ii] = ra[r];
-      int jj, kb;
-      if (b_jcontig) { jj = t & 63; kb = (t >> 6) + 4 * r; }
-      else { kb = t & 15; jj = (t >> 4) + 16 * r; }
-      bs[buf][kb][jj] = rb[r];
+    for (int r = 0; r < kPer; ++r) {
+      const double av = ((aok_mask >> r) & 1) ? (double)ra[r] : 0.0;
+      const int v = a_var + kAStep * r;
+      if (AI) as[buf][v][a_fix] = av;
+      else as[buf][a_fix][v] = av;
+      const double bv = ((bok_mask >> r) & 1) ? (double)rb[r] : 0.0;
+      const int w = b_var + kBStep * r;
+      if (BJ) bs[buf][w][b_fix] = bv;
+      else bs[buf][b_fix][w] = bv;
     }
   };
 
-  d4 acc[2][2];
+  d4 acc[WB][WB];
 #pragma unroll
-  for (int bi = 0; bi < 2; ++bi)
+  for (int bi = 0; bi < WB; ++bi)
 #pragma unroll
-    for (int bj = 0; bj < 2; ++bj) acc[bi][bj] = (d4){0.0, 0.0, 0.0, 0.0};
+    for (int bj = 0; bj < WB; ++bj) acc[bi][bj] = (d4){0.0, 0.0, 0.0, 0.0};
 
   const int64_t nstage = (kred + kS - 1) / kS;
   if (nstage > 0) {
@@ -155,15 +189,15 @@ __global__ __launch_bounds__(256) void gemm64_kernel(G64 g) {
 #pragma unroll
     for (int ks = 0; ks < kS / 4; ++ks) {
       const int kk = ks * 4 + (lane >> 4);
-      double fa[2], fb[2];
+      double fa[WB], fb[WB];
 #pragma unroll
-      for (int bi = 0; bi < 2; ++bi) fa[bi] = as[buf][kk][wi * 32 + bi * 16 + (lane & 15)];
+      for (int bi = 0; bi < WB; ++bi) fa[bi] = as[buf][kk][wi * 16 * WB + bi * 16 + (lane & 15)];
 #pragma unroll
-      for (int bj = 0; bj < 2; ++bj) fb[bj] = bs[buf][kk][wj * 32 + bj * 16 + (lane & 15)];
+      for (int bj = 0; bj < WB; ++bj) fb[bj] = bs[buf][kk][wj * 16 * WB + bj * 16 + (lane & 15)];
 #pragma unroll
-      for (int bi = 0; bi < 2; ++bi)
+      for (int bi = 0; bi < WB; ++bi)
 #pragma unroll
-        for (int bj = 0; bj < 2; ++bj)
+        for (int bj = 0; bj < WB; ++bj)
           acc[bi][bj] = __builtin_amdgcn_mfma_f64_16x16x4f64(fa[bi], fb[bj], acc[bi][bj], 0, 0, 0);
     }
     if (s + 1 < nstage) store_stage(buf ^ 1);
@@ -171,39 +205,71 @@ __global__ __launch_bounds__(256) void gemm64_kernel(G64 g) {
   }
 
   // D of v_mfma_f64_16x16x4f64: register r of lane l is row 4r + l/16,
-  // column l%16 of the 16x16 block.
+  // column l%16 of the 16x16 block.  With beta != 0 the old values of C are
+  // read first, one row of blocks at a time (clamped addresses as for the
+  // operands, so the reads are in flight together).
+  const bool use_beta = g.beta != 0.0;
 #pragma unroll
-  for (int bi = 0; bi < 2; ++bi)
+  for (int bi = 0; bi < WB; ++bi) {
+    double old[WB][4];
 #pragma unroll
-    for (int bj = 0; bj < 2; ++bj)
+    for (int bj = 0; bj < WB; ++bj)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int64_t gi = i0 + wi * 32 + bi * 16 + 4 * r + (lane >> 4);
-        const int64_t gj = j0 + wj * 32 + bj * 16 + (lane & 15);
-        if (gi < g.m && gj < g.n) {
-          double* p = pc + gi * g.c_sm + gj * g.c_sn;
-          double v = g.alpha * acc[bi][bj][r];
-          if (g.beta != 0.0) v += g.beta * *p;
-          *p = v;
-        }
+        const int64_t gi = i0 + wi * 16 * WB + bi * 16 + 4 * r + (lane >> 4);
+        const int64_t gj = j0 + wj * 16 * WB + bj * 16 + (lane & 15);
+        const bool ok = use_beta && gi < g.m && gj < g.n;
+        const double v = *(ok ? pc + gi * g.c_sm + gj * g.c_sn : pc);
+        old[bj][r] = ok ? v : 0.0;
       }
+#pragma unroll
+    for (int bj = 0; bj < WB; ++bj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t gi = i0 + wi * 16 * WB + bi * 16 + 4 * r + (lane >> 4);
+        const int64_t gj = j0 + wj * 16 * WB + bj * 16 + (lane & 15);
+        if (gi < g.m && gj < g.n)
+          pc[gi * g.c_sm + gj * g.c_sn] = g.alpha * acc[bi][bj][r] + g.beta * old[bj][r];
+      }
+  }
 }
 
+template <typename TA, typename TB, int WB>
+void gemm64_launch(const G64& g, unsigned grid, int batch, hipStream_t stream) {
+  const bool ai = g.a_sm == 1, bj = g.b_sn == 1;
+  if (ai && bj)
+    hipLaunchKernelGGL((gemm64_kernel<TA, TB, WB, true, true>), dim3(grid, 1, (unsigned)batch),
+                       dim3(256), 0, stream, g);
+  else if (ai)
+    hipLaunchKernelGGL((gemm64_kernel<TA, TB, WB, true, false>), dim3(grid, 1, (unsigned)batch),
+                       dim3(256), 0, stream, g);
+  else if (bj)
+    hipLaunchKernelGGL((gemm64_kernel<TA, TB, WB, false, true>), dim3(grid, 1, (unsigned)batch),
+                       dim3(256), 0, stream, g);
+  else
+    hipLaunchKernelGGL((gemm64_kernel<TA, TB, WB, false, false>), dim3(grid, 1, (unsigned)batch),
+                       dim3(256), 0, stream, g);
+}
+
+// Launch with 128-wide tiles when the output has enough of them to fill the
+// chip (or force_wb asks for a shape), else with 64-wide tiles.  Every
+// operand must be contiguous along one of its dimensions (a_sm or a_sk is
+// 1, b_sn or b_sk is 1).
 template <typename TA, typename TB>
-hipError_t gemm64(G64 g, int batch, hipStream_t stream) {
+hipError_t gemm64(G64 g, int batch, hipStream_t stream, int force_wb = 0) {
   if (g.m <= 0 || g.n <= 0 || batch <= 0) return hipSuccess;
-  const int64_t tm = (g.m + kT - 1) / kT, tn = (g.n + kT - 1) / kT;
-  int64_t tiles;
-  if (g.lower) {
-    // the lower mode needs a square tile grid
-    tiles = tm * (tm + 1) / 2;
-    g.tiles_n = (int32_t)tn;
-  } else {
-    tiles = tm * tn;
-    g.tiles_n = (int32_t)tn;
-  }
-  hipLaunchKernelGGL((gemm64_kernel<TA, TB>), dim3((unsigned)tiles, 1, (unsigned)batch),
-                     dim3(256), 0, stream, g);
+  if ((g.a_sm != 1 && g.a_sk != 1) || (g.b_sn != 1 && g.b_sk != 1)) return hipErrorInvalidValue;
+  auto tiles_for = [&](int64_t tile) {
+    const int64_t tm = (g.m + tile - 1) / tile, tn = (g.n + tile - 1) / tile;
+    return g.lower ? tm * (tm + 1) / 2 : tm * tn;
+  };
+  int wb = force_wb;
+  if (wb == 0) wb = (tiles_for(128) * batch >= 256 && g.kred >= 64) ? 4 : 2;
+  const int64_t tile = wb == 4 ? 128 : 64;
+  g.tiles_n = (int32_t)((g.n + tile - 1) / tile);
+  const unsigned grid = (unsigned)tiles_for(tile);
+  if (wb == 4) gemm64_launch<TA, TB, 4>(g, grid, batch, stream);
+  else gemm64_launch<TA, TB, 2>(g, grid, batch, stream);
   return hipGetLastError();
 }
 
@@ -221,18 +287,33 @@ G64 g64(const void* a, int64_t a_sm, int64_t a_sk, const void* b, int64_t b_sk, 
 
 // ------------------------------------------------------------------ H
 
-constexpr int64_t kHessTargetBlocks = 512;   // enough work-groups to fill the chip
-constexpr int64_t kHessMinChunk = 256;       // tokens per partial sum, at least
+// One round of the chip: 512 work-groups of either tile shape (two per
+// compute unit, set by LDS for 64-wide tiles and by registers for 128-wide
+// ones).  The tokens are split into as many chunks as fit in one round
+// without starting a second, partly filled one; the 128-wide tiles are used
+// when they still fill most of the round.
+constexpr int64_t kHessRound = 512;
+constexpr int64_t kHessMinChunk = 256;  // tokens per partial sum, at least
 
-int64_t hessian_splits(int64_t k, int64_t t) {
-  const int64_t tm = (k + kT - 1) / kT;
+int64_t hessian_splits_for(int64_t k, int64_t t, int64_t tile) {
+  const int64_t tm = (k + tile - 1) / tile;
   const int64_t tiles = tm * (tm + 1) / 2;
-  int64_t s = (kHessTargetBlocks + tiles - 1) / tiles;
+  int64_t s = kHessRound / tiles;
   int64_t smax = t / kHessMinChunk;
   if (smax < 1) smax = 1;
   if (s > smax) s = smax;
   if (s > 65535) s = 65535;
   return s < 1 ? 1 : s;
+}
+
+int64_t hessian_tile(int64_t k, int64_t t) {
+  const int64_t tm = (k + 127) / 128;
+  const int64_t tiles = tm * (tm + 1) / 2;
+  return tiles * hessian_splits_for(k, t, 128) * 5 >= kHessRound * 4 ? 128 : 64;
+}
+
+int64_t hessian_splits(int64_t k, int64_t t) {
+  return hessian_splits_for(k, t, hessian_tile(k, t));
 }
 
 // h[i][j] += sum_s part[s][max][min]: 32x32 tiles of the lower triangle,
@@ -308,65 +389,119 @@ __global__ __launch_bounds__(256) void reverse_damp_kernel(const double* __restr
   a[idx] = v;
 }
 
-// Factor the diagonal block at (p0, p0) in place (lower L, zeros above the
-// diagonal) and write its inverse to dinv (64 x 64, lower).  One work-group;
-// column by column: the pivot, the column below it, then the rank-1 update
-// of the rest of the block and the matching elimination step of the inverse
-// (which starts as the identity and is turned into L^-1 row by row).
-__global__ __launch_bounds__(256) void potrf_diag_kernel(double* __restrict__ a, int64_t kp,
-                                                         int64_t p0, double* __restrict__ dinv,
-                                                         int32_t* __restrict__ info) {
-  __shared__ double l[kNb][kNb + 1];
-  __shared__ double y[kNb][kNb + 1];
+__device__ inline double readlane_f64(double v, int lane) {
+  const uint64_t b = __double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)b, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(b >> 32), lane);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// The small kernels below run 64 dependent steps.  An fp64 operation takes
+// about 36 cycles to produce its result and a division or square root is a
+// chain of about ten of them, so the steps use reciprocals computed off the
+// dependent chain (rsqrt for the pivot, 1/L[c][c] staged in LDS), and the
+// triangular loops are unrolled so each step issues only the updates it
+// needs.  The panel kernel factors the diagonal block and solves the rows
+// below it in the same pass, so a block column costs one launch and one
+// dependent chain of 64 pivots.
+
+// The whole panel of block column p in one launch: the diagonal block and
+// every row below it, column by column.  A work-group holds the 64 rows of
+// the diagonal block (wave 0, recomputed by every work-group) and up to
+// kPanelOther rows below it, one row per thread in registers.  For each
+// column c: wave 0 takes the pivot from lane c (readlane), scales its
+// column by rsqrt(pivot) and publishes the column in LDS (double-buffered);
+// after one barrier every thread scales its own entry of column c and
+// updates its later columns with the published values.  Work-group 0
+// writes the diagonal block; every work-group writes its own rows.
+// info = 1 when a pivot is not positive.
+constexpr int kPanelThreads = 256;
+constexpr int kPanelOther = kPanelThreads - kNb;
+
+__global__ __launch_bounds__(kPanelThreads) void panel_factor_kernel(double* a, int64_t kp,
+                                                                     int64_t p0,
+                                                                     int32_t* __restrict__ info) {
+  __shared__ __align__(16) double col[2][kNb];
+  __shared__ double rps[2];
   const int t = threadIdx.x;
-  for (int e = t; e < kNb * kNb; e += 256) {
-    const int r = e / kNb, c = e % kNb;
-    l[r][c] = (r >= c) ? a[(p0 + r) * kp + (p0 + c)] : 0.0;
-    y[r][c] = (r == c) ? 1.0 : 0.0;
-  }
-  __syncthreads();
-  bool bad = false;
+  const bool diag = t < kNb;
+  const int64_t rest = kp - p0 - kNb;
+  const int64_t row = diag ? p0 + t : p0 + kNb + (int64_t)blockIdx.x * kPanelOther + (t - kNb);
+  const bool active = diag || (row < kp);
+  double x[kNb];
+  const double* ar = a + (active ? row : p0) * kp + p0;
+#pragma unroll
   for (int c = 0; c < kNb; ++c) {
-    const double d = l[c][c];
-    const double piv = sqrt(d);
-    if (!(d > 0.0)) bad = true;
-    __syncthreads();
-    // column c of L, row c of L^-1
-    if (t < kNb) {
-      if (t > c) l[t][c] = l[t][c] / piv;
-      else if (t == c) l[c][c] = piv;
-    } else if (t < 2 * kNb) {
-      const int j = t - kNb;
-      y[c][j] = y[c][j] / piv;
-    }
-    __syncthreads();
-    // trailing update: l[r][s] -= l[r][c] l[s][c] (c < s <= r);
-    // elimination:     y[r][j] -= l[r][c] y[c][j] (r > c, j <= c)
-    for (int e = t; e < kNb * kNb; e += 256) {
-      const int r = e / kNb, s = e % kNb;
-      if (r > c) {
-        if (s > c && s <= r) l[r][s] -= l[r][c] * l[s][c];
-        if (s <= c) y[r][s] -= l[r][c] * y[c][s];
-      }
-    }
-    __syncthreads();
+    const double v = ar[c];
+    x[c] = (active && (!diag || c <= t)) ? v : 0.0;
   }
-  if (bad && t == 0 && info) *info = 1;
-  for (int e = t; e < kNb * kNb; e += 256) {
-    const int r = e / kNb, c = e % kNb;
-    a[(p0 + r) * kp + (p0 + c)] = (r >= c) ? l[r][c] : 0.0;
-    dinv[r * kNb + c] = (r >= c) ? y[r][c] : 0.0;
+  bool bad = false;
+#pragma unroll
+  for (int c = 0; c < kNb; ++c) {
+    const int b = c & 1;
+    if (diag) {
+      // wave 0: the pivot and column c of the diagonal block
+      const double d = readlane_f64(x[c], c);
+      bad = bad || !(d > 0.0);
+      const double rp = rsqrt(d);
+      x[c] = (t == c) ? d * rp : x[c] * rp;
+      col[b][t] = x[c];
+      if (t == 0) rps[b] = rp;
+    }
+    __syncthreads();
+    if (!diag) x[c] *= rps[b];
+#pragma unroll
+    for (int s2 = c + 1; s2 < kNb; ++s2) x[s2] = fma(-x[c], col[b][s2], x[s2]);
+  }
+  if (active && (!diag || blockIdx.x == 0)) {
+    double* aw = a + row * kp + p0;
+#pragma unroll
+    for (int c = 0; c < kNb; ++c) aw[c] = (!diag || c <= t) ? x[c] : 0.0;
+  }
+  if (diag && bad && t == 0 && blockIdx.x == 0 && info) *info = 1;
+  (void)rest;
+}
+
+// A lower triangular 64 x 64 block L at (p0, p0) staged for the row solves:
+// lt[c][s] = L[s][c] (zero for s < c), rd[c] = 1 / L[c][c].
+__device__ inline void load_lt(double (*lt)[kNb], double* rd, const double* a, int64_t kp,
+                               int64_t p0) {
+  for (int e = threadIdx.x; e < kNb * kNb; e += blockDim.x) {
+    const int s = e / kNb, c = e % kNb;  // L[s][c], read along the row
+    lt[c][s] = (s >= c) ? a[(p0 + s) * kp + p0 + c] : 0.0;
+  }
+  for (int c = threadIdx.x; c < kNb; c += blockDim.x) rd[c] = 1.0 / a[(p0 + c) * kp + p0 + c];
+}
+
+// x L^T = x0 for one row x: x_c *= 1/L[c][c], then x_s -= x_c L[s][c] for
+// s > c.
+__device__ inline void solve_lt(double (&x)[kNb], const double (*lt)[kNb], const double* rd) {
+#pragma unroll
+  for (int c = 0; c < kNb; ++c) {
+    x[c] = x[c] * rd[c];
+#pragma unroll
+    for (int s = c + 1; s < kNb; ++s) x[s] = fma(-x[c], lt[c][s], x[s]);
   }
 }
 
-// Copy the 64 x 64 inverses back onto the diagonal blocks of a.
-__global__ __launch_bounds__(256) void put_diag_kernel(double* __restrict__ a, int64_t kp,
-                                                       const double* __restrict__ dinv) {
-  const int64_t p = blockIdx.x;
-  for (int e = threadIdx.x; e < kNb * kNb; e += 256) {
-    const int r = e / kNb, c = e % kNb;
-    a[(p * kNb + r) * kp + (p * kNb + c)] = dinv[p * kNb * kNb + e];
-  }
+// Every diagonal block replaced by its inverse (one work-group per block;
+// thread j solves x L^T = e_j, i.e. column j of L^-1).
+__global__ __launch_bounds__(64) void trtri_diag_kernel(double* a, int64_t kp) {
+  __shared__ __align__(16) double lt[kNb][kNb];
+  __shared__ double rd[kNb];
+  __shared__ double outb[kNb][kNb + 1];
+  const int64_t p0 = (int64_t)blockIdx.x * kNb;
+  load_lt(lt, rd, a, kp, p0);
+  __syncthreads();
+  const int j = threadIdx.x;
+  double x[kNb];
+#pragma unroll
+  for (int c = 0; c < kNb; ++c) x[c] = (c == j) ? 1.0 : 0.0;
+  solve_lt(x, lt, rd);
+#pragma unroll
+  for (int i = 0; i < kNb; ++i) outb[i][j] = (i >= j) ? x[i] : 0.0;
+  __syncthreads();
+  for (int i = 0; i < kNb; ++i) a[(p0 + i) * kp + p0 + j] = outb[i][j];
 }
 
 // u[i][j] = a[k-1-i][k-1-j] for i <= j, 0 below the diagonal.
@@ -386,36 +521,41 @@ __global__ __launch_bounds__(256) void to_f64_kernel(const float* __restrict__ w
   if (idx < count) wd[idx] = (double)w[idx];
 }
 
-__device__ inline double readlane_f64(double v, int lane) {
-  const uint64_t b = __double_as_longlong(v);
-  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)b, lane);
-  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(b >> 32), lane);
-  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-}
-
 __device__ inline float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;
 }
 
+// v[i][j] = u[i][j] / u[i][i] above and on the diagonal, 0 below: the
+// carrying factors per unit of rounding error, e * U[i][j] with
+// e = d / U[i][i] being d * v[i][j].  Computing them once, in parallel,
+// keeps an fp64 division off every step of the sequential loop.
+__global__ __launch_bounds__(256) void normalize_rows_kernel(const double* __restrict__ u,
+                                                             int64_t k, double* __restrict__ v) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= k * k) return;
+  const int64_t i = idx / k, j = idx % k;
+  v[idx] = (j >= i) ? u[idx] / u[i * k + i] : 0.0;
+}
+
 // One block of components [k0, k0 + bsz) (bsz <= 64) for 4 output channels
 // per work-group, one per wave.  Lane j holds component k0 + j of its
 // channel.  For each component s in order: the group scale when s starts a
 // group, the code of the component (same fp32 quantizer as the plain path),
-// the carried error e = (w_s - w_hat_s) / U[s][s], and w_j -= e * U[s][j]
-// on the lanes j > s.  The codes go to the payload, the errors to e_out
-// [n][64] for the update of the later components.
+// its rounding error d = w_s - w_hat_s, and w_j -= d * v[s][j] on the lanes
+// j > s (v = the normalized rows of U).  The codes go to the payload, the
+// errors to e_out [n][64] for the update of the later components.
 template <int BITS>
 __global__ __launch_bounds__(256) void gptq_block_kernel(
-    const double* __restrict__ wd, const double* __restrict__ u, int64_t n, int64_t k,
+    const double* __restrict__ wd, const double* __restrict__ v, int64_t n, int64_t k,
     int64_t k0, int bsz, int64_t group, double* __restrict__ e_out,
     uint8_t* __restrict__ payload, float* __restrict__ scales) {
   __shared__ double ub[64][64];
   const int t = threadIdx.x;
   for (int e = t; e < 64 * 64; e += 256) {
     const int s = e >> 6, j = e & 63;
-    ub[s][j] = (s < bsz && j < bsz) ? u[(k0 + s) * k + (k0 + j)] : 0.0;
+    ub[s][j] = (s < bsz && j < bsz) ? v[(k0 + s) * k + (k0 + j)] : 0.0;
   }
   __syncthreads();
   const int lane = t & 63;
@@ -446,18 +586,17 @@ __global__ __launch_bounds__(256) void gptq_block_kernel(
   for (int s = 0; s < bsz; ++s) {
     const double us = ub[s][lane];
     if (group <= bsz && ((k0 + s) % group) == 0) {
-      const float v = (lane >= s && lane < s + group) ? fabsf((float)w) : 0.0f;
-      const float m = wave_max(v);
+      const float aw = (lane >= s && lane < s + group) ? fabsf((float)w) : 0.0f;
+      const float m = wave_max(aw);
       sc = m / qmax;
       if (sc == 0.0f) sc = 1.0f;
       if (lane == 0) scales[row * ngroups + (k0 + s) / group] = sc;
     }
     const double ws = readlane_f64(w, s);
-    const double uss = readlane_f64(us, s);
     const float r = (float)ws / sc;
     const float c = fminf(fmaxf(rintf(r), -qmax), qmax);
     const float what = c * sc;
-    const double err = (ws - (double)what) / uss;
+    const double err = ws - (double)what;
     if (lane == s) {
       code = (int)c;
       ev = err;
@@ -505,7 +644,7 @@ hipError_t launch_gptq_hessian(int64_t k, int64_t t, const float* x, double* h, 
   g.c_sz = k * k;
   g.kred_total = t;
   const int64_t used = (t + chunk - 1) / chunk;
-  hipError_t e = gemm64<float, float>(g, (int)used, stream);
+  hipError_t e = gemm64<float, float>(g, (int)used, stream, hessian_tile(k, t) == 128 ? 4 : 2);
   if (e != hipSuccess) return e;
   const int64_t tb = (k + 31) / 32;
   hipLaunchKernelGGL(hess_reduce_kernel, dim3((unsigned)(tb * (tb + 1) / 2)), dim3(256), 0,
@@ -515,9 +654,8 @@ hipError_t launch_gptq_hessian(int64_t k, int64_t t, const float* x, double* h, 
 
 int64_t gptq_factor_work_bytes(int64_t k) {
   const int64_t kp = (k + kNb - 1) / kNb * kNb;
-  // a (kp x kp), the doubling temporary (kp x kp), the diagonal inverses,
-  // and lam
-  return (2 * kp * kp + kp * kNb + 1) * (int64_t)sizeof(double);
+  // a (kp x kp), the doubling temporary (kp x kp) and lam
+  return (2 * kp * kp + 2) * (int64_t)sizeof(double);
 }
 
 hipError_t launch_gptq_factor(int64_t k, const double* h, double damp, double* u, int32_t* info,
@@ -526,8 +664,7 @@ hipError_t launch_gptq_factor(int64_t k, const double* h, double damp, double* u
   const int64_t nblk = kp / kNb;
   double* a = (double*)work;
   double* tmp = a + kp * kp;
-  double* dinv = tmp + kp * kp;
-  double* lam = dinv + kp * kNb;
+  double* lam = tmp + kp * kp;
   hipError_t e;
 
   hipLaunchKernelGGL(diag_mean_kernel, dim3(1), dim3(256), 0, stream, h, k, damp, lam, info);
@@ -538,19 +675,15 @@ hipError_t launch_gptq_factor(int64_t k, const double* h, double damp, double* u
   // blocked Cholesky of the reversed matrix, a = L (lower)
   for (int64_t p = 0; p < nblk; ++p) {
     const int64_t p0 = p * kNb;
-    hipLaunchKernelGGL(potrf_diag_kernel, dim3(1), dim3(256), 0, stream, a, kp, p0,
-                       dinv + p * kNb * kNb, info);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t rest = kp - p0 - kNb;
+    // the diagonal block and the panel below it
+    const int64_t pwg = rest > 0 ? (rest + kPanelOther - 1) / kPanelOther : 1;
+    hipLaunchKernelGGL(panel_factor_kernel, dim3((unsigned)pwg), dim3(kPanelThreads), 0, stream,
+                       a, kp, p0, info);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     if (rest <= 0) continue;
-    // panel: L21 = A21 L11^-T, in place (one column tile, so each
-    // work-group reads its rows completely before writing them)
-    double* a21 = a + (p0 + kNb) * kp + p0;
-    const double* di = dinv + p * kNb * kNb;
-    e = gemm64<double, double>(g64(a21, kp, 1, di, 1, kNb, a21, kp, 1, rest, kNb, kNb, 1.0, 0.0),
-                               1, stream);
-    if (e != hipSuccess) return e;
     // trailing: A22 -= L21 L21^T on the lower tiles
+    double* a21 = a + (p0 + kNb) * kp + p0;
     double* a22 = a + (p0 + kNb) * kp + (p0 + kNb);
     G64 g = g64(a21, kp, 1, a21, 1, kp, a22, kp, 1, rest, rest, kNb, -1.0, 1.0);
     g.lower = 1;
@@ -558,8 +691,7 @@ hipError_t launch_gptq_factor(int64_t k, const double* h, double damp, double* u
   }
 
   // triangular inverse in place: diagonal blocks first, then doubling
-  hipLaunchKernelGGL(put_diag_kernel, dim3((unsigned)nblk), dim3(256), 0, stream, a, kp,
-                     (const double*)dinv);
+  hipLaunchKernelGGL(trtri_diag_kernel, dim3((unsigned)nblk), dim3(64), 0, stream, a, kp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   for (int64_t b = kNb; b < kp; b *= 2) {
     const int64_t nfull = kp / (2 * b);
@@ -596,7 +728,9 @@ hipError_t launch_gptq_factor(int64_t k, const double* h, double damp, double* u
 }
 
 int64_t gptq_quantize_work_bytes(int64_t n, int64_t k) {
-  return (n * k + n * 64) * (int64_t)sizeof(double);
+  // the fp64 weights being corrected, one block of errors, the normalized
+  // rows of U
+  return (n * k + n * 64 + k * k) * (int64_t)sizeof(double);
 }
 
 hipError_t launch_gptq_quantize_pack(const Mat& mt, const float* w, const double* u,
@@ -605,7 +739,9 @@ hipError_t launch_gptq_quantize_pack(const Mat& mt, const float* w, const double
   const int64_t n = mt.n, k = mt.k;
   double* wd = (double*)work;
   double* eb = wd + n * k;
+  double* v = eb + n * 64;
   hipLaunchKernelGGL(to_f64_kernel, dim3(grid1(n * k)), dim3(256), 0, stream, w, wd, n * k);
+  hipLaunchKernelGGL(normalize_rows_kernel, dim3(grid1(k * k)), dim3(256), 0, stream, u, k, v);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int bsz = block_size(mt.bits, mt.group);
@@ -614,15 +750,17 @@ hipError_t launch_gptq_quantize_pack(const Mat& mt, const float* w, const double
     const int cur = (int)((k - k0) < bsz ? (k - k0) : bsz);
     if (mt.bits == 8)
       hipLaunchKernelGGL(gptq_block_kernel<8>, dim3(wgs), dim3(256), 0, stream,
-                         (const double*)wd, u, n, k, k0, cur, mt.group, eb, payload, scales);
+                         (const double*)wd, (const double*)v, n, k, k0, cur, mt.group, eb,
+                         payload, scales);
     else
       hipLaunchKernelGGL(gptq_block_kernel<4>, dim3(wgs), dim3(256), 0, stream,
-                         (const double*)wd, u, n, k, k0, cur, mt.group, eb, payload, scales);
+                         (const double*)wd, (const double*)v, n, k, k0, cur, mt.group, eb,
+                         payload, scales);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const int64_t k1 = k0 + cur;
     if (k1 < k) {
-      // W[:, k1:] -= E U[k0:k1, k1:]
-      e = gemm64<double, double>(g64(eb, 64, 1, u + k0 * k + k1, k, 1, wd + k1, k, 1, n, k - k1,
+      // W[:, k1:] -= D V[k0:k1, k1:]
+      e = gemm64<double, double>(g64(eb, 64, 1, v + k0 * k + k1, k, 1, wd + k1, k, 1, n, k - k1,
                                      cur, -1.0, 1.0),
                                  1, stream);
       if (e != hipSuccess) return e;

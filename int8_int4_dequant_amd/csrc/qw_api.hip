@@ -224,7 +224,7 @@ int qw_gptq_factor(int64_t k, const double* h, double damp, double* u, int32_t* 
 }
 
 int64_t qw_gptq_quantize_work_bytes(int64_t n, int64_t k) {
-  if (n < 0 || k < 0 || mul_overflows(n, k + 64)) return -1;
+  if (n < 0 || k < 0 || mul_overflows(n, k + 64) || mul_overflows(k, k)) return -1;
   return qw::gptq_quantize_work_bytes(n, k);
 }
 
@@ -234,7 +234,7 @@ int qw_gptq_quantize_pack(int bits, int64_t group, int64_t n, int64_t k, const f
   qw::Mat mt;
   int st = check_mat(bits, group, n, k, &mt);
   if (st != QW_OK) return st;
-  if (mul_overflows(n, k + 64)) return QW_ESHAPE;
+  if (mul_overflows(n, k + 64) || mul_overflows(k, k)) return QW_ESHAPE;
   if (k > 0 && (k % group != 0 || (bits == 4 && group % 2 != 0))) return QW_EGROUP;
   if (n * k == 0) return QW_OK;
   if (!w || !u || !payload || !scales) return QW_ENULL;
