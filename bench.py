@@ -15,15 +15,26 @@ MLP weight of 28672 x 8192, int4 group 128, bf16 matrix cores) is timed on
 its own and reported under "prefill_gemm", and the CPU oracle is timed on a
 bounded sample of the stack under "cpu_baseline".
 
+The GPTQ leg ("gptq") quantizes one layer of the small model of the GPTQ
+section of "Huit bits, puis quatre" (width 512, feed-forward 1368) from
+synthetic calibration inputs of 65,536 tokens in 8 batches: per input the
+accumulation of H (qw_gptq_hessian), the factor (qw_gptq_factor) and the
+codes of every map reading that input (qw_gptq_quantize_pack).  Its value
+is weights per second over the layer with the four inputs' chains on four
+streams; its roofline is the fp64 MFMA accumulation of H for the
+1368-input map; the oracle runs the same layer on one core.  `--only-gptq`
+runs that leg alone (for profiling).
+
 Prints ONE JSON line.  `--gpus N` with N > 1 exits: this build runs on one
 GPU.
 
 HBM traffic ("roofline.traffic"): two rocprofv3 counter runs of this script
 with `--calib-copy-mib 1024` (FETCH_SIZE, then WRITE_SIZE) are reduced by
-`--pmc-summary FETCH_DIR WRITE_DIR` into profiles/pmc_traffic_c4_c5.md; each
+`--pmc-summary FETCH_DIR WRITE_DIR` into profiles/pmc_traffic_c4_c5_gptq_layer.md; each
 counter is scaled by what it reads for a plain device copy of known size.
-The benchmark reports that traffic only while the kernel sources still hash
-to the values recorded there (null otherwise).
+The benchmark reports a kernel's traffic only while its source file (and the
+shared internal header) still hash to the values recorded there (null
+otherwise).
 """
 
 import argparse
@@ -60,6 +71,8 @@ def parse():
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the traffic summary of two rocprofv3 --pmc runs and exit")
     ap.add_argument("--no-gptq", action="store_true")
+    ap.add_argument("--only-gptq", action="store_true",
+                    help="run only the GPTQ leg and print its JSON object (for profiling)")
     ap.add_argument("--gptq-reps", type=int, default=3)
     ap.add_argument("--cpu-sample-worker", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--gptq-cpu-sample-worker", action="store_true", help=argparse.SUPPRESS)
@@ -69,7 +82,7 @@ def parse():
 # ------------------------------------------------------- HBM traffic (PMC)
 
 CSRC = os.path.join(ROOT, "int8_int4_dequant_amd", "csrc")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_c4_c5.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_c4_c5_gptq_layer.md")
 # kernel-name fragment -> (label, source file whose hash pins the measurement,
 # grid size in threads or None): the benchmark's own launches -- the c5 GEMM is
 # the 262144-thread grid of gemm_kernel<4> (the M sweep launches it too)
@@ -77,6 +90,9 @@ PMC_KERNELS = {
     "quant_subgroup_batched_kernel": ("quantize_pack_batched", "quantize.hip", None),
     "gemv8_kernel<4, 1, 8, 256>": ("gemv_batched_m1", "gemv.hip", None),
     "gemm_kernel<4>": ("gemm", "gemm.hip", 262144),
+    # the GPTQ leg's H accumulation over the 1368-input map (the only launch
+    # of the 128-wide fp32-operand shape)
+    "gemm64_kernel<float, float, 4": ("gptq_hessian_k1368", "gptq.hip", None),
 }
 COPY_KERNEL = "neg_kernel"  # the calibration copy (torch.neg over a known-size buffer)
 
@@ -136,7 +152,10 @@ def measured_traffic(label):
         blob = json.loads(txt.split("```json")[1].split("```")[0])
     except (OSError, IndexError, ValueError):
         return None
-    if blob.get("source_sha256") != source_hashes():
+    # only the measured kernel's own source and the shared header matter
+    src = {v[0]: v[1] for v in PMC_KERNELS.values()}.get(label)
+    now, then = source_hashes(), blob.get("source_sha256", {})
+    if src is None or any(then.get(f) != now[f] for f in (src, "qw_internal.h")):
         return None
     k = blob.get("kernels", {}).get(label)
     return None if k is None else k["traffic_bytes"]
@@ -230,6 +249,10 @@ def main():
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
     L = qw.lib()
+
+    if args.only_gptq:
+        print(json.dumps(bench_gptq(args, L, stream)), flush=True)
+        return
 
     # ---- setup: the stack's fp32 weights resident in HBM, outputs allocated
     mats = [m for m in inputs.c4_matrices() if m[0] < args.layers]
@@ -766,7 +789,8 @@ def bench_gptq(args, L, stream):
         "layer_ms_one_stream": round(seq_ms, 3), "weights": weights, "reps": args.gptq_reps,
         "per_input": per_input,
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP64_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tf / FP64_PEAK_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(tf / FP64_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic("gptq_hessian_k1368"),
                      "kernel": f"qw_gptq_hessian (fp64 MFMA X^T X + fixed-order reduce), "
                                f"k={dk}, {chunk} tokens per launch",
                      "algorithmic_flops_per_launch": chunk * dk * (dk + 1),

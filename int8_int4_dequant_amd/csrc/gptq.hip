@@ -331,11 +331,22 @@ __global__ __launch_bounds__(256) void hess_reduce_kernel(const double* __restri
   const int64_t kk2 = k * k;
   for (int yy = ty; yy < 32; yy += 8) {
     const int64_t i = bi * 32 + yy, j = bj * 32 + tx;
+    const bool ok = i < k && j < k && i >= j;
+    const double* pp = part + (ok ? i * k + j : 0);
+    // partial sums added in chunk order; the loads of eight chunks are
+    // issued before their additions
     double s = 0.0;
-    if (i < k && j < k && i >= j)
-      for (int64_t p = 0; p < splits; ++p) s += part[p * kk2 + i * k + j];
+    int64_t p = 0;
+    for (; p + 8 <= splits; p += 8) {
+      double v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = pp[(p + q) * kk2];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) s += v[q];
+    }
+    for (; p < splits; ++p) s += pp[p * kk2];
     tile[yy][tx] = s;
-    if (i < k && j < k && i >= j) h[i * k + j] += s;
+    if (ok) h[i * k + j] += s;
   }
   __syncthreads();
   // mirrored half: h[j][i] += s(i, j) for i > j, read transposed from LDS

@@ -60,7 +60,7 @@ def test_sizes():
 
 def test_status_strings():
     L = qw.lib()
-    for st in range(-7, 1):
+    for st in range(-9, 1):
         assert L.qw_status_string(st)
     assert L.qw_status_string(0) == b"ok"
 
@@ -87,6 +87,46 @@ def test_validation_before_any_launch():
     assert L.qw_gemm(8, 32, 4, 32, None, None, -1, None, None, None) == -4
     assert L.qw_gemm(4, 32, 4, 32, None, None, 0, None, None, None) == 0
     assert L.qw_gemm(4, 32, 4, 32, None, None, 5, None, None, None) == -5
+
+
+def test_gptq_work_sizes():
+    L = qw.lib()
+    assert L.qw_gptq_hessian_work_bytes(-1, 5) == -1
+    assert L.qw_gptq_hessian_work_bytes(512, 8192) > 0
+    # the partial sums cover whole k x k matrices, one per token chunk
+    assert L.qw_gptq_hessian_work_bytes(512, 8192) % (512 * 512 * 8) == 0
+    kp = 1408  # 1368 rounded up to the 64-wide blocks of the factorization
+    assert L.qw_gptq_factor_work_bytes(1368) >= 2 * kp * kp * 8
+    assert L.qw_gptq_factor_work_bytes(-3) == -1
+    assert L.qw_gptq_quantize_work_bytes(512, 1368) >= (512 * 1368 + 1368 * 1368) * 8
+    assert L.qw_gptq_quantize_work_bytes(-1, 4) == -1
+
+
+def test_gptq_validation_before_any_launch():
+    L = qw.lib()
+    fake = 1 << 20  # never dereferenced: every call below fails validation
+    # H: shapes, pointers, work buffer
+    assert L.qw_gptq_hessian(-1, 4, fake, fake, fake, 1 << 30, None) == -3
+    assert L.qw_gptq_hessian(8, 0, None, None, None, 0, None) == 0
+    assert L.qw_gptq_hessian(8, 16, None, fake, fake, 1 << 30, None) == -5
+    need = L.qw_gptq_hessian_work_bytes(8, 16)
+    assert L.qw_gptq_hessian(8, 16, fake, fake, fake, need - 1, None) == -8
+    assert L.qw_gptq_hessian(8, 16, fake, fake, None, need, None) == -8
+    # factor: damping must be finite and >= 0
+    assert L.qw_gptq_factor(8, fake, -0.01, fake, None, fake, 1 << 30, None) == -9
+    assert L.qw_gptq_factor(8, fake, float("nan"), fake, None, fake, 1 << 30, None) == -9
+    assert L.qw_gptq_factor(8, fake, float("inf"), fake, None, fake, 1 << 30, None) == -9
+    assert L.qw_gptq_factor(0, None, 0.01, None, None, None, 0, None) == 0
+    assert L.qw_gptq_factor(8, None, 0.01, fake, None, fake, 1 << 30, None) == -5
+    assert L.qw_gptq_factor(8, fake, 0.01, fake, None, fake, 16, None) == -8
+    # codes: a group lies inside one output channel, even for int4
+    big = 1 << 30
+    assert L.qw_gptq_quantize_pack(4, 64, 4, 96, fake, fake, fake, fake, fake, big, None) == -2
+    assert L.qw_gptq_quantize_pack(4, 3, 4, 96, fake, fake, fake, fake, fake, big, None) == -2
+    assert L.qw_gptq_quantize_pack(5, 32, 4, 96, fake, fake, fake, fake, fake, big, None) == -1
+    assert L.qw_gptq_quantize_pack(8, 32, 0, 96, None, None, None, None, None, 0, None) == 0
+    assert L.qw_gptq_quantize_pack(8, 32, 4, 96, None, fake, fake, fake, fake, big, None) == -5
+    assert L.qw_gptq_quantize_pack(8, 32, 4, 96, fake, fake, fake, fake, fake, 8, None) == -8
 
 
 @pytest.mark.parametrize("bits,group,n,k,al,expect", [
