@@ -375,6 +375,8 @@ def main():
         f"one launch per matrix: {single_us:.1f} us; unpack pass {unpack_us:.1f} us "
         f"({ubytes / (unpack_us * 1e-6) / 1e9:.0f} GB/s)")
 
+    chain = bench_chain(args, L, stream, mats, shapes, P, S, xs, gbytes)
+
     dominant = "quantize_pack" if q_ms >= g_ms else "gemv"
     if dominant == "quantize_pack":
         ach, per_launch = q_gbs, qbytes / quant_launches
@@ -405,6 +407,7 @@ def main():
                    "frac_hbm": round(ubytes / (unpack_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                    "entry": "qw_unpack", "launches_per_pass": len(shapes),
                    "pass_us": round(unpack_us, 1), "bytes_per_pass": ubytes},
+        "decode_chain_m1": chain,
         "decode_gemv_m1_one_launch_per_matrix": {
             "pass_us": round(single_us, 1),
             "GB/s": round(gbytes / (single_us * 1e-6) / 1e9, 1)},
@@ -450,6 +453,95 @@ def main():
         "prefill_gemm": gemm, "gptq": gptq, "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_chain(args, L, stream, mats, shapes, P, S, xs, gbytes):
+    """The decode pass as a chain: in every layer q, k, v read the layer's
+    input, o reads v's output, gate and up read o's, down reads up's, and the
+    next layer reads down's (no attention or nonlinearity in between).  Four
+    dependent stages per layer, 128 for the stack, timed as one cooperative
+    launch (qw_gemv_chain), as one launch per stage, and as those launches
+    replayed from a HIP graph."""
+    import torch
+
+    from int8_int4_dequant_amd import qw
+
+    dev = torch.device("cuda:0")
+    ys = [torch.empty((1, n), dtype=torch.float32, device=dev) for n, _ in shapes]
+    slot_of = {"q": 0, "k": 1, "v": 2, "o": 3, "gate": 4, "up": 5, "down": 6}
+    wiring, stages = [], []
+    index = {}
+    for i, (layer, tag, n, k, _seed) in enumerate(mats):
+        index[(layer, tag)] = i
+    for i, (layer, tag, n, k, _seed) in enumerate(mats):
+        slot = slot_of[tag]
+        if slot <= 2:
+            x = xs[4096] if layer == 0 else ys[index[(layer - 1, "down")]]
+            st = 0
+        elif slot == 3:
+            x, st = ys[index[(layer, "v")]], 1
+        elif slot in (4, 5):
+            x, st = ys[index[(layer, "o")]], 2
+        else:
+            x, st = ys[index[(layer, "up")]], 3
+        wiring.append(x)
+        stages.append(4 * layer + st)
+    descs, nd = qw.make_gemv_descs((4, 32, n, k, P[i], S[i], wiring[i], ys[i])
+                                   for i, (n, k) in enumerate(shapes))
+    import ctypes
+    stg = (ctypes.c_int32 * nd)(*stages)
+
+    def run(sp):
+        r = L.qw_gemv_chain(nd, descs, stg, 1, sp)
+        if r:
+            raise RuntimeError(f"qw_gemv_chain failed: {r}")
+
+    def timed(fn, reps=max(3, args.steps)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return 1e3 * e0.elapsed_time(e1) / reps
+
+    sp = stream.cuda_stream
+    chain_us = timed(lambda: run(sp))
+    ref = [y.clone() for y in ys]
+    same = True
+    graph_us = None
+    try:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            run(side.cuda_stream)   # warm-up outside capture
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            run(torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        for _ in range(3):   # every replay must reproduce the eager result
+            for y in ys:
+                y.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            same = same and all(torch.equal(a, b) for a, b in zip(ref, ys))
+        graph_us = timed(g.replay)
+    except RuntimeError as exc:  # capture unsupported: report without it
+        log(f"chain graph capture skipped: {exc}")
+    gbs = lambda us: round(gbytes / (us * 1e-6) / 1e9, 1)
+    log(f"chained decode pass ({len(set(stages))} stages): {chain_us:.1f} us ({gbs(chain_us)} GB/s)"
+        + (f", graph replay {graph_us:.1f} us ({gbs(graph_us)} GB/s)" if graph_us else "")
+        + f"; replays identical: {same}")
+    return {"entry": "qw_gemv_chain", "stages": len(set(stages)), "matrices": nd,
+            "bytes_per_pass": gbytes, "pass_us": round(chain_us, 1), "GB/s": gbs(chain_us),
+            "frac_hbm": round(gbs(chain_us) / HBM_PEAK_GBS, 4),
+            "graph_replay_us": None if graph_us is None else round(graph_us, 1),
+            "graph_replay_GB/s": None if graph_us is None else gbs(graph_us),
+            "graph_replays_identical": bool(same)}
 
 
 def bench_gemv_configs(args, L, stream):

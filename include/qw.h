@@ -183,6 +183,24 @@ typedef struct qw_gemv_desc {
 int qw_gemv_batched(int count, const qw_gemv_desc* descs, int64_t m, void* stream);
 
 /*
+ * Chained decode pass: `count` GEMVs like qw_gemv_batched (common m,
+ * 0 <= m <= 8), grouped into stages by `stage` (a HOST array of `count`
+ * nondecreasing integers; equal values form one stage).  The products of a
+ * stage are independent; a product's x may be the y of a product in an
+ * earlier stage (a layer's output feeding the next layer), and sees that y
+ * complete.  Within a stage no y may overlap another y or any x of the stage.
+ * Each stage is one batched launch, enqueued back to back in one call (a HIP
+ * graph can capture it); a stage's products come out exactly as
+ * qw_gemv_batched computes the same group (a stage of one matrix also keeps
+ * the streaming kernel).  A decode step of many short kernels is dominated
+ * by their fixed cost (page "Huit bits, puis quatre", section "La vitesse"),
+ * which the stage grouping keeps to one launch per dependency level.  Validation as in
+ * qw_gemv_batched, plus QW_ECOUNT when `stage` is NULL or decreases.
+ */
+int qw_gemv_chain(int count, const qw_gemv_desc* descs, const int32_t* stage, int64_t m,
+                  void* stream);
+
+/*
  * Dequantizing GEMM (prefill), bf16 matrix cores, fp32 accumulate:
  *   x_bf16  bf16 bit patterns [m][k]  (read),   y  fp32 [m][n]  (written).
  * Any group dividing n*k is accepted; k % 64 == 0 with k % group == 0 and

@@ -33,6 +33,8 @@
 //     (chain length) * 2^-24 * sum|x * w_hat| -- far inside 1e-5 of it.
 //   * The R*M partial sums per lane are reduced across the wave with a
 //     butterfly reduce-scatter (each step halves the values a lane holds).
+#include <vector>
+
 #include "qw_internal.h"
 
 namespace qw {
@@ -204,20 +206,14 @@ __device__ __forceinline__ GemvDesc load_desc(int di) {
                   d.n, d.k, d.row_stride_b, d.per_row, d.gpr};
 }
 
-// Streaming kernel: 8-code chunks (4-byte int4 / 8-byte int8 payload loads
-// per lane and row, two 16-byte x loads per lane), any group that is a
-// multiple of 8 codes (or spans whole rows).
-template <int BITS, int M, int R, int NB>
-__global__ __launch_bounds__(256) void gemv8_kernel(const GemvBatch<NB> b) {
+// R rows of one matrix (rows row0 .. row0 + R - 1, clamped) for one wave:
+// 8-code chunks (4-byte int4 / 8-byte int8 payload loads per lane and row,
+// two 16-byte x loads per lane), any group that is a multiple of 8 codes (or
+// spans whole rows).
+template <int BITS, int M, int R>
+__device__ __forceinline__ void gemv8_rows(const GemvDesc& a, int row0, int lane) {
   constexpr int V = pow2_at_least(R * M);
   constexpr int PW = BITS == 4 ? 1 : 2;     // payload dwords per 8-code chunk
-  const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (item >= b.items) return;
-  const int di = find_desc(b, item);
-  const GemvDesc a = load_desc<NB>(di);
-  typedef const __attribute__((address_space(4))) GemvBatch<NB>* KArg;
-  const int row0 = (item - ((KArg)__builtin_amdgcn_kernarg_segment_ptr())->item0[di]) * R;
   const int nch = a.k / 8;
 
   const uint32_t* prow[R];
@@ -293,6 +289,19 @@ __global__ __launch_bounds__(256) void gemv8_kernel(const GemvBatch<NB> b) {
     const int r = idx / M, m = idx % M;
     if (row0 + r < a.n) a.y[(int64_t)m * a.n + row0 + r] = acc[0];
   }
+}
+
+// Streaming kernel: one work item (R rows of one matrix) per wave.
+template <int BITS, int M, int R, int NB>
+__global__ __launch_bounds__(256) void gemv8_kernel(const GemvBatch<NB> b) {
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (item >= b.items) return;
+  const int di = find_desc(b, item);
+  const GemvDesc a = load_desc<NB>(di);
+  typedef const __attribute__((address_space(4))) GemvBatch<NB>* KArg;
+  const int row0 = (item - ((KArg)__builtin_amdgcn_kernarg_segment_ptr())->item0[di]) * R;
+  gemv8_rows<BITS, M, R>(a, row0, lane);
 }
 
 // Split-K kernel for one matrix with few rows per wave of the GPU: a block's
@@ -554,6 +563,61 @@ hipError_t launch_gemv_batched(const Mat* mts, const uint8_t* const* payloads,
         if (e != hipSuccess) return e;
       }
     }
+  }
+  return hipSuccess;
+}
+
+// One stage of a chain on the streaming kernel, with the rows per work item
+// qw_gemv_batched would take for the same matrices (also for a lone one).
+template <int BITS, int M>
+hipError_t chain_stage_m(const GemvDesc* ds, int count, hipStream_t st) {
+  int64_t rows = 0;
+  for (int i = 0; i < count; ++i) rows += ds[i].n;
+  constexpr int RB = rows_big<M>();
+  return rows / RB >= 2048 ? launch_group<BITS, M, RB, GEMV_NB>(ds, count, st)
+                           : launch_group<BITS, M, kRowsSmall, GEMV_NB>(ds, count, st);
+}
+
+template <int BITS>
+hipError_t chain_stage(const GemvDesc* ds, int count, int m, hipStream_t st) {
+  switch (m) {
+    case 1: return chain_stage_m<BITS, 1>(ds, count, st);
+    case 2: return chain_stage_m<BITS, 2>(ds, count, st);
+    case 3: return chain_stage_m<BITS, 3>(ds, count, st);
+    case 4: return chain_stage_m<BITS, 4>(ds, count, st);
+    case 5: return chain_stage_m<BITS, 5>(ds, count, st);
+    case 6: return chain_stage_m<BITS, 6>(ds, count, st);
+    case 7: return chain_stage_m<BITS, 7>(ds, count, st);
+    default: return chain_stage_m<BITS, 8>(ds, count, st);
+  }
+}
+
+hipError_t launch_gemv_chain(const Mat* mts, const uint8_t* const* payloads,
+                             const float* const* scales, int m, const float* const* xs,
+                             float* const* ys, const int* stage, int count, hipStream_t st) {
+  std::vector<GemvDesc> ds;
+  for (int i0 = 0; i0 < count;) {
+    int i1 = i0 + 1;
+    while (i1 < count && stage[i1] == stage[i0]) ++i1;
+    // a stage of one bit width on the streaming kernel: one launch of it;
+    // otherwise the batched dispatch
+    bool uniform = true;
+    for (int i = i0; i < i1 && uniform; ++i)
+      if (mts[i].bits != mts[i0].bits || gemv_path(mts[i], payloads[i], xs[i]) != PATH_FAST)
+        uniform = false;
+    hipError_t e;
+    if (uniform) {
+      ds.clear();
+      for (int i = i0; i < i1; ++i)
+        ds.push_back(make_desc(mts[i], payloads[i], scales[i], xs[i], ys[i]));
+      e = mts[i0].bits == 4 ? chain_stage<4>(ds.data(), i1 - i0, m, st)
+                            : chain_stage<8>(ds.data(), i1 - i0, m, st);
+    } else {
+      e = launch_gemv_batched(mts + i0, payloads + i0, scales + i0, m, xs + i0, ys + i0, i1 - i0,
+                              st);
+    }
+    if (e != hipSuccess) return e;
+    i0 = i1;
   }
   return hipSuccess;
 }

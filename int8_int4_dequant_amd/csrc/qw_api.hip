@@ -2,6 +2,8 @@
 // dispatch to the HIP kernels.  No allocation, no synchronization.
 #include <string.h>
 
+#include <vector>
+
 #include "../../include/qw.h"
 #include "qw_internal.h"
 
@@ -179,6 +181,57 @@ int qw_gemv_batched(int count, const qw_gemv_desc* descs, int64_t m, void* strea
     if (st != QW_OK) return st;
   }
   return QW_OK;
+}
+
+int qw_gemv_chain(int count, const qw_gemv_desc* descs, const int32_t* stage, int64_t m,
+                  void* stream) {
+  if (count < 0) return QW_ECOUNT;
+  if (count == 0) return QW_OK;
+  if (!descs) return QW_ENULL;
+  if (!stage) return QW_ECOUNT;
+  if (m < 0 || m > 8) return QW_EM;
+  for (int i = 1; i < count; ++i)
+    if (stage[i] < stage[i - 1]) return QW_ECOUNT;
+  for (int i = 0; i < count; ++i) {
+    const qw_gemv_desc& d = descs[i];
+    if (d.reserved != 0) return QW_ECOUNT;
+    qw::Mat mt;
+    int st = check_mat(d.bits, d.group, d.n, d.k, &mt);
+    if (st != QW_OK) return st;
+    if (d.n == 0) continue;
+    if (!d.y) return QW_ENULL;
+    if (d.k > 0 && (!d.payload || !d.scales || !d.x)) return QW_ENULL;
+  }
+  if (m == 0) return QW_OK;
+  // every product keeps its place in its stage; products with n == 0 have
+  // nothing to do, products with k == 0 write zeros (launched first: their
+  // y may still be read by a later stage only after the fill)
+  std::vector<qw::Mat> mts;
+  std::vector<const uint8_t*> ps;
+  std::vector<const float*> ss, xs;
+  std::vector<float*> ys;
+  std::vector<int> stg;
+  for (int i = 0; i < count; ++i) {
+    const qw_gemv_desc& d = descs[i];
+    if (d.n == 0) continue;
+    if (d.k == 0) {
+      int st = record(qw::launch_fill_zero(d.y, m * d.n, (hipStream_t)stream));
+      if (st != QW_OK) return st;
+      continue;
+    }
+    qw::Mat mt;
+    check_mat(d.bits, d.group, d.n, d.k, &mt);
+    mts.push_back(mt);
+    ps.push_back(d.payload);
+    ss.push_back(d.scales);
+    xs.push_back(d.x);
+    ys.push_back(d.y);
+    stg.push_back(stage[i]);
+  }
+  if (mts.empty()) return QW_OK;
+  return record(qw::launch_gemv_chain(mts.data(), ps.data(), ss.data(), (int)m, xs.data(),
+                                      ys.data(), stg.data(), (int)mts.size(),
+                                      (hipStream_t)stream));
 }
 
 int qw_gemm(int bits, int64_t group, int64_t n, int64_t k, const uint8_t* payload,

@@ -30,7 +30,7 @@ STATUS_NAMES = {0: "QW_OK", -1: "QW_EBITS", -2: "QW_EGROUP", -3: "QW_ESHAPE", -4
 #: symbols declared in include/qw.h
 EXPORTS = ["qw_payload_bytes", "qw_num_scales", "qw_status_string", "qw_last_error",
            "qw_quantize_pack", "qw_quantize_pack_batched", "qw_unpack", "qw_gemv",
-           "qw_gemv_batched", "qw_gemm", "qw_debug_path",
+           "qw_gemv_batched", "qw_gemv_chain", "qw_gemm", "qw_debug_path",
            "qw_gptq_hessian_work_bytes", "qw_gptq_hessian", "qw_gptq_factor_work_bytes",
            "qw_gptq_factor", "qw_gptq_quantize_work_bytes", "qw_gptq_quantize_pack"]
 
@@ -92,6 +92,9 @@ def lib():
     L.qw_gemv.restype = i32
     L.qw_gemv_batched.argtypes = [i32, ctypes.POINTER(QwGemvDesc), i64, vp]
     L.qw_gemv_batched.restype = i32
+    L.qw_gemv_chain.argtypes = [i32, ctypes.POINTER(QwGemvDesc), ctypes.POINTER(ctypes.c_int32),
+                                i64, vp]
+    L.qw_gemv_chain.restype = i32
     L.qw_gemm.argtypes = [i32, i64, i64, i64, vp, vp, i64, vp, vp, vp]
     L.qw_gemm.restype = i32
     L.qw_debug_path.argtypes = [i32, i32, i64, i64, i64, vp, vp]
@@ -186,6 +189,13 @@ def make_gemv_descs(items):
 
 def qw_gemv_batched(count, descs, m, stream=None):
     return lib().qw_gemv_batched(count, descs, m, _stream(stream))
+
+
+def qw_gemv_chain(count, descs, stages, m, stream=None):
+    """``stages``: a ctypes int32 array (or a list) of ``count`` stage numbers."""
+    if not isinstance(stages, ctypes.Array):
+        stages = (ctypes.c_int32 * max(1, len(stages)))(*stages)
+    return lib().qw_gemv_chain(count, descs, stages, m, _stream(stream))
 
 
 def qw_gemm(bits, group, n, k, payload, scales, m, x_bf16, y, stream=None):
@@ -305,6 +315,23 @@ def gemv_batched(recs, xs, outs=None, stream=None):
                                 r["scales"], x, y) for r, x, y in zip(recs, xs, outs))
     _check(qw_gemv_batched(cnt, arr, m, stream), "qw_gemv_batched")
     return outs
+
+
+def gemv_chain(recs, xs, ys, stages, stream=None):
+    """A chained decode pass: product i computes ys[i] = xs[i] . W_i^T in
+    stage stages[i]; an x may be the y of an earlier stage.  All tensors are
+    preallocated, contiguous fp32 [m][k] / [m][n] with a common m."""
+    m = xs[0].shape[0]
+    for r, x, y in zip(recs, xs, ys):
+        n, k = _nk(r["shape"])
+        if x.dtype != torch.float32 or not x.is_contiguous() or tuple(x.shape) != (m, k):
+            raise ValueError("each x must be a contiguous float32 [m][k] tensor")
+        if y.dtype != torch.float32 or not y.is_contiguous() or tuple(y.shape) != (m, n):
+            raise ValueError("each y must be a contiguous float32 [m][n] tensor")
+    arr, cnt = make_gemv_descs((r["bits"], r["group"], r["shape"][0], r["shape"][1], r["payload"],
+                                r["scales"], x, y) for r, x, y in zip(recs, xs, ys))
+    _check(qw_gemv_chain(cnt, arr, list(stages), m, stream), "qw_gemv_chain")
+    return ys
 
 
 def gemm(rec, x_bf16, out=None, stream=None):

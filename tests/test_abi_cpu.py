@@ -89,6 +89,20 @@ def test_validation_before_any_launch():
     assert L.qw_gemm(4, 32, 4, 32, None, None, 5, None, None, None) == -5
 
 
+def test_chain_validation_before_any_launch():
+    L = qw.lib()
+    arr = (qw.QwGemvDesc * 2)()
+    for i in range(2):
+        arr[i] = qw.QwGemvDesc(None, None, None, None, 64, 64, 32, 4, 0)
+    st = (ctypes.c_int32 * 2)(0, 1)
+    assert L.qw_gemv_chain(2, arr, None, 1, None) == -7       # no stage list
+    assert L.qw_gemv_chain(2, arr, (ctypes.c_int32 * 2)(1, 0), 1, None) == -7
+    assert L.qw_gemv_chain(2, arr, st, 9, None) == -4
+    assert L.qw_gemv_chain(2, arr, st, 1, None) == -5         # null pointers
+    assert L.qw_gemv_chain(-1, arr, st, 1, None) == -7
+    assert L.qw_gemv_chain(0, None, None, 1, None) == 0
+
+
 def test_gptq_work_sizes():
     L = qw.lib()
     assert L.qw_gptq_hessian_work_bytes(-1, 5) == -1
