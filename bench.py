@@ -314,10 +314,10 @@ def main():
             if st:
                 raise RuntimeError(f"qw_quantize_pack failed: {st}")
 
-    def single_gemv_pass():
+    def single_gemv_pass(sp=None):
         for i, (n, k) in enumerate(shapes):
             st = L.qw_gemv(4, 32, n, k, P[i].data_ptr(), S[i].data_ptr(), 1,
-                           xs[k].data_ptr(), Y[i].data_ptr(), sptr)
+                           xs[k].data_ptr(), Y[i].data_ptr(), sptr if sp is None else sp)
             if st:
                 raise RuntimeError(f"qw_gemv failed: {st}")
 
@@ -352,6 +352,32 @@ def main():
 
     single_us = timed(single_gemv_pass)
     single_q_us = timed(single_quant_pass)
+    # the same one-launch-per-matrix pass replayed from a HIP graph (every
+    # replay checked against the eager outputs)
+    single_graph_us = None
+    try:
+        ref = [y.clone() for y in Y]
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            single_gemv_pass(side.cuda_stream)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            single_gemv_pass(torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            for y in Y:
+                y.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            if not all(torch.equal(a, b) for a, b in zip(ref, Y)):
+                raise RuntimeError("graph replay differs from the eager pass")
+        single_graph_us = timed(g.replay)
+        del g
+    except RuntimeError as exc:
+        log(f"graph replay of the per-matrix pass skipped: {exc}")
 
     # unpack (a5 on its own): every matrix back to fp32, one call per matrix
     wout = torch.empty(max(n * k for n, k in shapes), dtype=torch.float32, device=dev)
@@ -372,7 +398,9 @@ def main():
     log(f"step {ms_per_step:.3f} ms; quantize {q_gbs:.0f} GB/s ({quant_launches} launches, avg "
         f"{q_avg_us:.1f} us); one quantize launch per matrix: {single_q_us:.1f} us; "
         f"gemv pass {g_gbs:.0f} GB/s ({1e3 * g_ms / args.steps:.1f} us, {gemv_launches} launches); "
-        f"one launch per matrix: {single_us:.1f} us; unpack pass {unpack_us:.1f} us "
+        f"one launch per matrix: {single_us:.1f} us (graph replay "
+        f"{single_graph_us if single_graph_us is None else round(single_graph_us, 1)} us); "
+        f"unpack pass {unpack_us:.1f} us "
         f"({ubytes / (unpack_us * 1e-6) / 1e9:.0f} GB/s)")
 
     chain = bench_chain(args, L, stream, mats, shapes, P, S, xs, gbytes)
@@ -410,7 +438,10 @@ def main():
         "decode_chain_m1": chain,
         "decode_gemv_m1_one_launch_per_matrix": {
             "pass_us": round(single_us, 1),
-            "GB/s": round(gbytes / (single_us * 1e-6) / 1e9, 1)},
+            "GB/s": round(gbytes / (single_us * 1e-6) / 1e9, 1),
+            "graph_replay_pass_us": None if single_graph_us is None else round(single_graph_us, 1),
+            "graph_replay_GB/s": None if single_graph_us is None
+            else round(gbytes / (single_graph_us * 1e-6) / 1e9, 1)},
     }
 
     if args.calib_copy_mib:
