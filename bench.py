@@ -187,6 +187,59 @@ def cpu_sample_worker():
     print(json.dumps(dict(seconds=elapsed, bytes=total_bytes, weights=weights)))
 
 
+def _oracle_matrix(slot):
+    """One matrix of layer 0: oracle quantize + pack, then the M = 1 GEMV
+    (worker of the all-cores baseline; returns seconds and bytes)."""
+    import oracle
+    from int8_int4_dequant_amd import inputs
+
+    tag, n, k = inputs.C4_SLOTS[slot]
+    w = inputs.c4_weight(0, slot)
+    x = inputs.c4_x(k)
+    t0 = time.perf_counter()
+    rec = oracle.quantize_pack(w, 4, 32)
+    oracle.gemv_ref(rec, x)
+    return time.perf_counter() - t0, step_bytes_matrix(n, k)
+
+
+def cpu_baseline_all_cores():
+    """The same layer-0 sample with the 7 matrices spread over a process
+    pool (one matrix per process, default BLAS threads), timed wall-clock."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+
+    cores = len(os.sched_getaffinity(0))
+    procs = min(7, cores)
+    ctx = mp.get_context("spawn")
+    # BLAS threads per process so the pool does not oversubscribe the cores
+    saved = {v: os.environ.get(v) for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                            "MKL_NUM_THREADS")}
+    for v in saved:
+        os.environ[v] = str(max(1, cores // procs))
+    try:
+        res, wall = _pool_run(cf, ctx, procs)
+    finally:
+        for v, old in saved.items():
+            if old is None:
+                os.environ.pop(v, None)
+            else:
+                os.environ[v] = old
+    total = sum(b for _, b in res)
+    return {"value": round(total / wall / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "processes": procs, "kind": "oracle",
+            "sample": f"layer 0 of the stack (7 matrices), one process per matrix on {cores} "
+                      f"host cores, {wall:.2f} s wall"}
+
+
+def _pool_run(cf, ctx, procs):
+    with cf.ProcessPoolExecutor(max_workers=procs, mp_context=ctx) as ex:
+        list(ex.map(_oracle_matrix, [0]))  # start-up outside the timing
+        t0 = time.perf_counter()
+        res = list(ex.map(_oracle_matrix, range(7)))
+        wall = time.perf_counter() - t0
+    return res, wall
+
+
 def cpu_baseline():
     env = dict(os.environ)
     for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "VECLIB_MAXIMUM_THREADS"):
@@ -469,6 +522,12 @@ def main():
     gptq = None if args.no_gptq else bench_gptq(args, L, stream)
 
     cpu = None if args.no_cpu_baseline else cpu_baseline()
+    cpu_all = None
+    if not args.no_cpu_baseline:
+        try:
+            cpu_all = cpu_baseline_all_cores()
+        except Exception as exc:  # a pool that cannot start is reported, not fatal
+            log(f"all-cores oracle baseline skipped: {exc}")
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
@@ -482,6 +541,7 @@ def main():
                    "bits": 4, "group": 32, "m": 1, "bytes_per_step": qbytes + gbytes},
         "roofline": roofline, "parts": parts, "decode_gemv_configs": gemv_cfgs,
         "prefill_gemm": gemm, "gptq": gptq, "cpu_baseline": cpu,
+        "cpu_baseline_all_cores": cpu_all,
     }
     print(json.dumps(out), flush=True)
 

@@ -41,13 +41,6 @@ namespace qw {
 namespace {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Streaming (non-temporal) 16-byte load of packed codes: read once.
-__device__ __forceinline__ uint4 ldnt(const uint4* p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
 
 // Unsigned division by a runtime constant d >= 1 for numerators < 2^31:
 // q = (umulhi(n, mul) + n * add) >> shift  -- computed on the host
