@@ -856,15 +856,18 @@ def bench_gptq(args, L, stream):
         info = torch.zeros(1, dtype=torch.int32, device=dev)
         hw = L.qw_gptq_hessian_work_bytes(k, chunk)
         fw = L.qw_gptq_factor_work_bytes(k)
-        recs = []
-        for slot, name, n, kk in maps:
-            g = inputs.smallem_group(kk)
-            w = torch.from_numpy(inputs.smallem_weight(slot)).to(dev)
-            recs.append(dict(name=name, n=n, k=kk, group=g, w=w,
-                             p=torch.empty(n * kk // 2, dtype=torch.uint8, device=dev),
-                             s=torch.empty(n * kk // g, dtype=torch.float32, device=dev),
-                             wb=L.qw_gptq_quantize_work_bytes(n, kk)))
-        qwb = max(r["wb"] for r in recs)
+        # the maps reading one input share its H and U, and GPTQ treats every
+        # output channel on its own: they are stacked along n into one call
+        # (q, k, v: 1536 rows; gate, up: 2736), whose payload and scales are
+        # the maps' own, one after the other
+        g = inputs.smallem_group(k)
+        n = sum(mp_[2] for mp_ in maps)
+        w = torch.cat([torch.from_numpy(inputs.smallem_weight(slot)) for slot, *_ in maps]).to(dev)
+        recs = [dict(name="+".join(mp_[1] for mp_ in maps), n=n, k=k, group=g, w=w,
+                     p=torch.empty(n * k // 2, dtype=torch.uint8, device=dev),
+                     s=torch.empty(n * k // g, dtype=torch.float32, device=dev),
+                     wb=L.qw_gptq_quantize_work_bytes(n, k))]
+        qwb = recs[0]["wb"]
         data[src] = dict(k=k, x=x, h=h, u=u, info=info, hw=hw, fw=fw, recs=recs,
                          hwork=torch.empty(hw, dtype=torch.uint8, device=dev),
                          fwork=torch.empty(fw, dtype=torch.uint8, device=dev),
@@ -966,7 +969,7 @@ def bench_gptq(args, L, stream):
         "workload": "GPTQ of one layer of the small model (width 512, feed-forward 1368): "
                     "q, k, v, o 512x512, gate and up 1368x512, down 512x1368, int4 group 64 "
                     "(72 for the 1368-input map); 65,536 calibration tokens per input in 8 "
-                    "batches; H, damping 1%, factor, codes",
+                    "batches; H, damping 1%, factor, codes (maps sharing an input in one call)",
         "value": round(weights / (layer_ms * 1e-3), 1), "unit": "weights/s",
         "layer_ms": round(layer_ms, 3), "layer_ms_four_streams": round(conc_ms, 3),
         "layer_ms_one_stream": round(seq_ms, 3), "weights": weights, "reps": args.gptq_reps,
