@@ -85,10 +85,12 @@ CSRC = os.path.join(ROOT, "int8_int4_dequant_amd", "csrc")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_c4_c5_gptq_layer.md")
 # kernel-name fragment -> (label, source file whose hash pins the measurement,
 # grid size in threads or None): the benchmark's own launches -- the c5 GEMM is
-# the 262144-thread grid of gemm_kernel<4> (the M sweep launches it too)
+# the 262144-thread grid of gemm_kernel<4> (the M sweep launches it too), the
+# decode pass the 10878976-thread grid of gemv8_kernel<4, 1, 8, 256>
 PMC_KERNELS = {
     "quant_subgroup_batched_kernel": ("quantize_pack_batched", "quantize.hip", None),
-    "gemv8_kernel<4, 1, 8, 256>": ("gemv_batched_m1", "gemv.hip", None),
+    # the whole-stack pass (the chained pass launches the same kernel per stage)
+    "gemv8_kernel<4, 1, 8, 256>": ("gemv_batched_m1", "gemv.hip", 10878976),
     "gemm_kernel<4>": ("gemm", "gemm.hip", 262144),
     # the GPTQ leg's H accumulation over the 1368-input map (the only launch
     # of the 128-wide fp32-operand shape)
