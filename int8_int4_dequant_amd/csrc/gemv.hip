@@ -455,10 +455,13 @@ template <int BITS, int M>
 hipError_t launch_m(const GemvDesc* ds, int count, hipStream_t st) {
   int64_t rows = 0;
   for (int i = 0; i < count; ++i) rows += ds[i].n;
-  // big items when they still give about two waves per SIMD (2048 items)
+  // big items when they still give about two waves per SIMD (2048 items);
+  // a lone matrix keeps the split-K kernel up to four per SIMD (4096 items),
+  // since its waves each run a short loop whose load latency few waves hide
+  // (an 11008-row matrix at m = 8: 34 -> 25 us)
   constexpr int RB = rows_big<M>();
   if (count == 1) {
-    if (rows / RB >= 2048) return launch_group<BITS, M, RB, 1>(ds, count, st);
+    if (rows / RB >= 4096) return launch_group<BITS, M, RB, 1>(ds, count, st);
     // a lone matrix with fewer rows: split K over the 4 waves of a block
     constexpr int RS = M >= 4 ? 2 * kRowsSplit : kRowsSplit;  // x reused over more rows
     gemv8_split_kernel<BITS, M, RS><<<(unsigned)((ds[0].n + RS - 1) / RS), 256, 0, st>>>(ds[0]);

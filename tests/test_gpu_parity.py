@@ -175,14 +175,14 @@ def test_gemv_shapes_all_m(bits, group, n, k):
         check_gemv(ref, rec, inputs.activations(m * 13 + n, m, k))
 
 
-# A lone matrix with fewer than 16384 rows (M <= 4; 8192 for M > 4) runs the
+# A lone matrix with fewer than 32768 rows (M <= 4; 16384 for M > 4) runs the
 # split-K kernel (four waves per block share rows, each a quarter of K); a
 # taller one the row-streaming kernel.  Short rows (k = 8, 16, 24: some waves
 # get no chunk), a row count that is not a multiple of the block's 4 rows,
 # and both kernels at every m.
 @pytest.mark.parametrize("bits,group,n,k", [
     (4, 8, 9, 8), (8, 16, 6, 16), (4, 24, 7, 24), (4, 32, 4099, 512),
-    (4, 32, 16384 + 5, 256), (8, 256, 8192 + 3, 256),
+    (4, 32, 32768 + 5, 256), (8, 256, 16384 + 3, 256),
 ])
 def test_gemv_split_and_stream_kernels(bits, group, n, k):
     w = inputs.weight(n + 3 * k, n, k, 0.02)
