@@ -887,7 +887,9 @@ def bench_gptq(args, L, stream):
         if concurrent:
             start = torch.cuda.Event()
             start.record(stream)
-        for src, d in data.items():
+        # the longest chain (largest k) first, so its factor and codes overlap
+        # the other inputs' accumulation of H
+        for src, d in sorted(data.items(), key=lambda kv: -kv[1]["k"]):
             k = d["k"]
             st = streams[src] if concurrent else stream
             sp_ = st.cuda_stream
