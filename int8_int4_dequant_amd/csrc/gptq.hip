@@ -423,14 +423,18 @@ __device__ inline double readlane_f64(double v, int lane) {
 // column c: wave 0 takes the pivot from lane c (readlane), scales its
 // column by rsqrt(pivot) and publishes the column in LDS (double-buffered);
 // after one barrier every thread scales its own entry of column c and
-// updates its later columns with the published values.  Work-group 0
-// writes the diagonal block; every work-group writes its own rows.
+// updates its later columns with the published values.  Every work-group
+// writes its own rows of the panel; work-group 0 writes the factored
+// diagonal block to l11 (64 x 64, row-major, zero above the diagonal), not
+// back into a: the other work-groups read the unfactored block from a when
+// they start, and nothing orders that read after work-group 0 finishes.
 // info = 1 when a pivot is not positive.
 constexpr int kPanelThreads = 256;
 constexpr int kPanelOther = kPanelThreads - kNb;
 
 __global__ __launch_bounds__(kPanelThreads) void panel_factor_kernel(double* a, int64_t kp,
                                                                      int64_t p0,
+                                                                     double* __restrict__ l11,
                                                                      int32_t* __restrict__ info) {
   __shared__ __align__(16) double col[2][kNb];
   __shared__ double rps[2];
@@ -465,7 +469,7 @@ __global__ __launch_bounds__(kPanelThreads) void panel_factor_kernel(double* a, 
     for (int s2 = c + 1; s2 < kNb; ++s2) x[s2] = fma(-x[c], col[b][s2], x[s2]);
   }
   if (active && (!diag || blockIdx.x == 0)) {
-    double* aw = a + row * kp + p0;
+    double* aw = diag ? l11 + t * kNb : a + row * kp + p0;
 #pragma unroll
     for (int c = 0; c < kNb; ++c) aw[c] = (!diag || c <= t) ? x[c] : 0.0;
   }
@@ -473,15 +477,15 @@ __global__ __launch_bounds__(kPanelThreads) void panel_factor_kernel(double* a, 
   (void)rest;
 }
 
-// A lower triangular 64 x 64 block L at (p0, p0) staged for the row solves:
-// lt[c][s] = L[s][c] (zero for s < c), rd[c] = 1 / L[c][c].
-__device__ inline void load_lt(double (*lt)[kNb], double* rd, const double* a, int64_t kp,
-                               int64_t p0) {
+// A lower triangular 64 x 64 block L (row-major, leading dimension 64)
+// staged for the row solves: lt[c][s] = L[s][c] (zero for s < c),
+// rd[c] = 1 / L[c][c].
+__device__ inline void load_lt(double (*lt)[kNb], double* rd, const double* l) {
   for (int e = threadIdx.x; e < kNb * kNb; e += blockDim.x) {
     const int s = e / kNb, c = e % kNb;  // L[s][c], read along the row
-    lt[c][s] = (s >= c) ? a[(p0 + s) * kp + p0 + c] : 0.0;
+    lt[c][s] = (s >= c) ? l[s * kNb + c] : 0.0;
   }
-  for (int c = threadIdx.x; c < kNb; c += blockDim.x) rd[c] = 1.0 / a[(p0 + c) * kp + p0 + c];
+  for (int c = threadIdx.x; c < kNb; c += blockDim.x) rd[c] = 1.0 / l[c * kNb + c];
 }
 
 // x L^T = x0 for one row x: x_c *= 1/L[c][c], then x_s -= x_c L[s][c] for
@@ -495,14 +499,17 @@ __device__ inline void solve_lt(double (&x)[kNb], const double (*lt)[kNb], const
   }
 }
 
-// Every diagonal block replaced by its inverse (one work-group per block;
-// thread j solves x L^T = e_j, i.e. column j of L^-1).
-__global__ __launch_bounds__(64) void trtri_diag_kernel(double* a, int64_t kp) {
+// The inverse of every diagonal block of L (read from lblk, block p at
+// lblk + p * 64 * 64) written into the diagonal blocks of a (one
+// work-group per block; thread j solves x L^T = e_j, i.e. column j of
+// L^-1).
+__global__ __launch_bounds__(64) void trtri_diag_kernel(const double* __restrict__ lblk, double* a,
+                                                        int64_t kp) {
   __shared__ __align__(16) double lt[kNb][kNb];
   __shared__ double rd[kNb];
   __shared__ double outb[kNb][kNb + 1];
   const int64_t p0 = (int64_t)blockIdx.x * kNb;
-  load_lt(lt, rd, a, kp, p0);
+  load_lt(lt, rd, lblk + (int64_t)blockIdx.x * kNb * kNb);
   __syncthreads();
   const int j = threadIdx.x;
   double x[kNb];
@@ -683,14 +690,16 @@ hipError_t launch_gptq_factor(int64_t k, const double* h, double damp, double* u
                      (const double*)lam, a, kp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
-  // blocked Cholesky of the reversed matrix, a = L (lower)
+  // blocked Cholesky of the reversed matrix: a = L below the diagonal
+  // blocks, the diagonal blocks of L in tmp (block p at tmp + p * 64 * 64;
+  // tmp is free until the doubling, which starts after they are inverted)
   for (int64_t p = 0; p < nblk; ++p) {
     const int64_t p0 = p * kNb;
     const int64_t rest = kp - p0 - kNb;
     // the diagonal block and the panel below it
     const int64_t pwg = rest > 0 ? (rest + kPanelOther - 1) / kPanelOther : 1;
     hipLaunchKernelGGL(panel_factor_kernel, dim3((unsigned)pwg), dim3(kPanelThreads), 0, stream,
-                       a, kp, p0, info);
+                       a, kp, p0, tmp + p * kNb * kNb, info);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (rest <= 0) continue;
     // trailing: A22 -= L21 L21^T on the lower tiles
@@ -702,7 +711,8 @@ hipError_t launch_gptq_factor(int64_t k, const double* h, double damp, double* u
   }
 
   // triangular inverse in place: diagonal blocks first, then doubling
-  hipLaunchKernelGGL(trtri_diag_kernel, dim3((unsigned)nblk), dim3(64), 0, stream, a, kp);
+  hipLaunchKernelGGL(trtri_diag_kernel, dim3((unsigned)nblk), dim3(64), 0, stream,
+                     (const double*)tmp, a, kp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   for (int64_t b = kNb; b < kp; b *= 2) {
     const int64_t nfull = kp / (2 * b);

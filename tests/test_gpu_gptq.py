@@ -95,6 +95,40 @@ def test_factor_reports_not_positive_definite(h, damp):
         qw.gptq_factor(dev(h), damp)
 
 
+def test_concurrent_factors_match_the_factor_alone():
+    """Factors running at once on four streams, beside Hessian accumulations
+    that keep the compute units busy on two more, equal bit for bit the
+    factor computed alone.  The panel of a block column is spread over
+    several work-groups whose start times are not ordered, so a work-group
+    that starts late must still find the unfactored diagonal block."""
+    ks = [1368, 512, 1000, 700]
+    hs = [dev(G.hessian([inputs.calibration_activations([8, 13, k], 2 * k, k)])) for k in ks]
+    alone = [qw.gptq_factor(h) for h in hs]
+    gen = torch.Generator(device="cuda").manual_seed(14)
+    busy_x = torch.randn((32768, 1368), dtype=torch.float32, device="cuda", generator=gen)
+    cur = torch.cuda.current_stream()
+    fs = [torch.cuda.Stream() for _ in ks]       # default priority
+    bs = [torch.cuda.Stream() for _ in range(2)]
+    for rep in range(3):
+        _say("gptq_factor concurrent", rep)
+        for s in fs + bs:
+            s.wait_stream(cur)
+        for s in bs:
+            with torch.cuda.stream(s):
+                for _ in range(8):
+                    qw.gptq_hessian(busy_x)
+        res = []
+        for h, s in zip(hs, fs):
+            with torch.cuda.stream(s):
+                res.append(qw.gptq_factor(h, check=False))
+        for s in fs + bs:
+            cur.wait_stream(s)
+        torch.cuda.synchronize()
+        for k, (u, info), ua in zip(ks, res, alone):
+            assert int(info.item()) == 0, f"k={k}: not positive definite"
+            assert torch.equal(u, ua), f"k={k}: factor differs from the one computed alone"
+
+
 # ----------------------------------------------------------------- codes
 
 # (bits, group, n, k): groups below, equal to and above the 64-component
