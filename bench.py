@@ -740,20 +740,27 @@ def bench_gemm(args, L, stream):
     flops = 2.0 * m * n * k
 
     # the same weight against the number of rows: qw_gemm (bf16, matrix cores)
-    # and, up to 8 rows, qw_gemv (fp32) -- where one product overtakes the other
+    # and, up to 8 rows, qw_gemv (fp32) -- where one product overtakes the
+    # other.  Three copies of the packed weight (372 MB) are taken in turn, so
+    # the 256 MB Infinity Cache cannot serve a repeat.
     sweep = {}
     xf = torch.from_numpy(inputs.activations(7, 8, k)).to(dev)
     yv = torch.empty((8, n), dtype=torch.float32, device=dev)
+    copies = [(p, s), (p.clone(), s.clone()), (p.clone(), s.clone())]
     for mm in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024):
         def g(mm=mm):
-            r = L.qw_gemm(4, 128, n, k, p.data_ptr(), s.data_ptr(), mm, x.data_ptr(), y.data_ptr(), sp)
-            if r:
-                raise RuntimeError(f"qw_gemm failed: {r}")
+            for pc, sc in copies:
+                r = L.qw_gemm(4, 128, n, k, pc.data_ptr(), sc.data_ptr(), mm, x.data_ptr(),
+                              y.data_ptr(), sp)
+                if r:
+                    raise RuntimeError(f"qw_gemm failed: {r}")
 
         def v(mm=mm):
-            r = L.qw_gemv(4, 128, n, k, p.data_ptr(), s.data_ptr(), mm, xf.data_ptr(), yv.data_ptr(), sp)
-            if r:
-                raise RuntimeError(f"qw_gemv failed: {r}")
+            for pc, sc in copies:
+                r = L.qw_gemv(4, 128, n, k, pc.data_ptr(), sc.data_ptr(), mm, xf.data_ptr(),
+                              yv.data_ptr(), sp)
+                if r:
+                    raise RuntimeError(f"qw_gemv failed: {r}")
 
         row = {}
         for name, fn in (("gemm_us", g), ("gemv_us", v)):
@@ -762,13 +769,14 @@ def bench_gemm(args, L, stream):
             fn()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            for _ in range(5):
+            for _ in range(3):
                 fn()
             e1.record(stream)
             torch.cuda.synchronize()
-            row[name] = round(1e3 * e0.elapsed_time(e1) / 5, 2)
+            row[name] = round(1e3 * e0.elapsed_time(e1) / (3 * len(copies)), 2)
         row["gemm_TFLOP/s"] = round(2.0 * mm * n * k / (row["gemm_us"] * 1e-6) / 1e12, 1)
         sweep[str(mm)] = row
+    del copies
     log("gemm/gemv against m: " + ", ".join(
         f"m={k_}: {r_['gemm_us']:.0f}" + (f"/{r_['gemv_us']:.0f}" if "gemv_us" in r_ else "") + " us"
         for k_, r_ in sweep.items()))
@@ -920,12 +928,19 @@ def bench_gptq(args, L, stream):
             for src in data:
                 stream.wait_stream(streams[src])
 
+    def outputs():
+        torch.cuda.synchronize()
+        for src, d in data.items():
+            if int(d["info"].item()) != 0:
+                raise RuntimeError(f"GPTQ factor of {src} reported a non-positive-definite H")
+        return [t.clone() for d in data.values() for r in d["recs"] for t in (r["p"], r["s"])]
+
     run()
+    one_stream = outputs()
     run(concurrent=True)
-    torch.cuda.synchronize()
-    for src, d in data.items():
-        if int(d["info"].item()) != 0:
-            raise RuntimeError(f"GPTQ factor of {src} reported a non-positive-definite H")
+    # the chains are deterministic: four streams must give the same codes
+    if not all(torch.equal(a, b) for a, b in zip(one_stream, outputs())):
+        raise RuntimeError("GPTQ codes on four streams differ from those on one stream")
     # the layer with the four inputs' chains on four streams
     conc = []
     for _ in range(args.gptq_reps):
@@ -935,6 +950,8 @@ def bench_gptq(args, L, stream):
         e1.record(stream)
         torch.cuda.synchronize()
         conc.append(e0.elapsed_time(e1))
+    if not all(torch.equal(a, b) for a, b in zip(one_stream, outputs())):
+        raise RuntimeError("GPTQ codes of a timed four-stream pass differ from one stream")
     conc.sort()
     conc_ms = conc[len(conc) // 2]
     # per-stage times with the chains one after another on one stream

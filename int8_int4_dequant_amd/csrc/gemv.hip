@@ -199,14 +199,25 @@ __device__ __forceinline__ GemvDesc load_desc(int di) {
                   d.n, d.k, d.row_stride_b, d.per_row, d.gpr};
 }
 
-// R rows of one matrix (rows row0 .. row0 + R - 1, clamped) for one wave:
-// 8-code chunks (4-byte int4 / 8-byte int8 payload loads per lane and row,
-// two 16-byte x loads per lane), any group that is a multiple of 8 codes (or
-// spans whole rows).
-template <int BITS, int M, int R>
-__device__ __forceinline__ void gemv8_rows(const GemvDesc& a, int row0, int lane) {
+// Streaming kernel: one work item (R rows of one matrix, rows row0 ..
+// row0 + R - 1, clamped) per wave; 8-code chunks (4-byte int4 / 8-byte int8
+// payload loads per lane and row, two 16-byte x loads per lane), any group
+// that is a multiple of 8 codes (or spans whole rows).  The body stays in
+// the kernel itself: moved into an inlined helper, the compiler stopped
+// issuing the next chunk's loads ahead of the current chunk's arithmetic for
+// M >= 4 (one wait per load; 106 -> 158 us for a 28672 x 8192 int4 matrix
+// at m = 8).
+template <int BITS, int M, int R, int NB>
+__global__ __launch_bounds__(256) void gemv8_kernel(const GemvBatch<NB> b) {
   constexpr int V = pow2_at_least(R * M);
   constexpr int PW = BITS == 4 ? 1 : 2;     // payload dwords per 8-code chunk
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (item >= b.items) return;
+  const int di = find_desc(b, item);
+  const GemvDesc a = load_desc<NB>(di);
+  typedef const __attribute__((address_space(4))) GemvBatch<NB>* KArg;
+  const int row0 = (item - ((KArg)__builtin_amdgcn_kernarg_segment_ptr())->item0[di]) * R;
   const int nch = a.k / 8;
 
   const uint32_t* prow[R];
@@ -282,19 +293,6 @@ __device__ __forceinline__ void gemv8_rows(const GemvDesc& a, int row0, int lane
     const int r = idx / M, m = idx % M;
     if (row0 + r < a.n) a.y[(int64_t)m * a.n + row0 + r] = acc[0];
   }
-}
-
-// Streaming kernel: one work item (R rows of one matrix) per wave.
-template <int BITS, int M, int R, int NB>
-__global__ __launch_bounds__(256) void gemv8_kernel(const GemvBatch<NB> b) {
-  const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  if (item >= b.items) return;
-  const int di = find_desc(b, item);
-  const GemvDesc a = load_desc<NB>(di);
-  typedef const __attribute__((address_space(4))) GemvBatch<NB>* KArg;
-  const int row0 = (item - ((KArg)__builtin_amdgcn_kernarg_segment_ptr())->item0[di]) * R;
-  gemv8_rows<BITS, M, R>(a, row0, lane);
 }
 
 // Split-K kernel for one matrix with few rows per wave of the GPU: a block's
@@ -458,7 +456,8 @@ hipError_t launch_m(const GemvDesc* ds, int count, hipStream_t st) {
   // big items when they still give about two waves per SIMD (2048 items);
   // a lone matrix keeps the split-K kernel up to four per SIMD (4096 items),
   // since its waves each run a short loop whose load latency few waves hide
-  // (an 11008-row matrix at m = 8: 34 -> 25 us)
+  // (int4 group 128 at m = 8: 14336 x 4096 34 -> 27 us, 8192 x 28672
+  // 107 -> 86 us)
   constexpr int RB = rows_big<M>();
   if (count == 1) {
     if (rows / RB >= 4096) return launch_group<BITS, M, RB, 1>(ds, count, st);
