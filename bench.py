@@ -746,6 +746,10 @@ def bench_gemm(args, L, stream):
     sweep = {}
     xf = torch.from_numpy(inputs.activations(7, 8, k)).to(dev)
     yv = torch.empty((8, n), dtype=torch.float32, device=dev)
+    # fp32 activations for qw_matmul (QuantizedMatmul: GEMV up to
+    # MATMUL_GEMV_MAX_M rows, else bf16 rounding into `mw` and the GEMM)
+    xm = torch.from_numpy(inputs.activations(8, 1024, k)).to(dev)
+    mw = torch.empty(max(1, L.qw_matmul_work_bytes(1024, k)), dtype=torch.uint8, device=dev)
     copies = [(p, s), (p.clone(), s.clone()), (p.clone(), s.clone())]
     for mm in (1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024):
         def g(mm=mm):
@@ -762,8 +766,15 @@ def bench_gemm(args, L, stream):
                 if r:
                     raise RuntimeError(f"qw_gemv failed: {r}")
 
+        def mmul(mm=mm):
+            for pc, sc in copies:
+                r = L.qw_matmul(4, 128, n, k, pc.data_ptr(), sc.data_ptr(), mm, xm.data_ptr(),
+                                y.data_ptr(), mw.data_ptr(), mw.numel(), sp)
+                if r:
+                    raise RuntimeError(f"qw_matmul failed: {r}")
+
         row = {}
-        for name, fn in (("gemm_us", g), ("gemv_us", v)):
+        for name, fn in (("gemm_us", g), ("gemv_us", v), ("matmul_us", mmul)):
             if name == "gemv_us" and mm > 8:
                 continue
             fn()
@@ -776,10 +787,12 @@ def bench_gemm(args, L, stream):
             row[name] = round(1e3 * e0.elapsed_time(e1) / (3 * len(copies)), 2)
         row["gemm_TFLOP/s"] = round(2.0 * mm * n * k / (row["gemm_us"] * 1e-6) / 1e12, 1)
         sweep[str(mm)] = row
-    del copies
+    del copies, xm, mw
     log("gemm/gemv against m: " + ", ".join(
         f"m={k_}: {r_['gemm_us']:.0f}" + (f"/{r_['gemv_us']:.0f}" if "gemv_us" in r_ else "") + " us"
         for k_, r_ in sweep.items()))
+    log("qw_matmul against m: " + ", ".join(f"m={k_}: {r_['matmul_us']:.0f} us"
+                                           for k_, r_ in sweep.items()))
     tf = flops / (med * 1e-3) / 1e12
     log(f"gemm: median {med * 1e3:.1f} us, {tf:.1f} TFLOP/s ({tf / BF16_PEAK_TFLOPS:.1%} of bf16 peak)")
     return {"workload": "c5: M=2048 bf16 x (28672 x 8192) int4 group 128, fp32 accumulate",

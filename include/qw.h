@@ -211,6 +211,32 @@ int qw_gemm(int bits, int64_t group, int64_t n, int64_t k,
             int64_t m, const uint16_t* x_bf16, float* y, void* stream);
 
 /*
+ * QuantizedMatmul for any number of rows (page "Huit bits, puis quatre",
+ * section "Ranger des entiers dans des f32": the generation products read
+ * the codes, where the time goes to memory; the large products of an
+ * evaluation use the dequantized weights, where it goes to arithmetic):
+ *   x  fp32 [m][k]  (read),   y  fp32 [m][n]  (written),   m >= 0.
+ * m <= QW_MATMUL_GEMV_MAX_M is qw_gemv itself: fp32 arithmetic on the codes,
+ *   error <= 1e-5 * sum_j |x[m][j] * w_hat[i][j]|; no work buffer is needed.
+ * Larger m rounds x to bf16 (round to nearest even) into `work` and runs
+ *   qw_gemm on it: the weights are dequantized in registers, not kept as a
+ *   second copy.  Error <= 8e-3 * sum_j |x[m][j] * w_hat[i][j]| (rounding
+ *   x adds at most 2^-9 of it to the GEMM's own bound).
+ * The bound is the fastest side of the measured crossover on MI355X
+ * (4096- to 28672-row int4 matrices: the GEMV wins up to 4 rows, the GEMM
+ * from 8).  `work`: a device buffer of at least qw_matmul_work_bytes(m, k)
+ * bytes (may be NULL when that is 0); after the call it holds the bf16 bit
+ * patterns of x, row-major.  QW_EWORK when it is missing or too small;
+ * other validation as in qw_gemv / qw_gemm.
+ */
+#define QW_MATMUL_GEMV_MAX_M 4
+int64_t qw_matmul_work_bytes(int64_t m, int64_t k);
+int qw_matmul(int bits, int64_t group, int64_t n, int64_t k,
+              const uint8_t* payload, const float* scales,
+              int64_t m, const float* x, float* y,
+              void* work, int64_t work_bytes, void* stream);
+
+/*
  * GPTQ codes (page "Huit bits, puis quatre", section "Arrondir mieux :
  * GPTQ").  Rounding every weight to its nearest code minimises each weight's
  * error, not the error of the layer's output X W^T on typical inputs X.

@@ -589,6 +589,28 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(
   y[mm * n + nn] = sum;
 }
 
+// ------------------------------------------------------ activation rounding
+
+// fp32 activations rounded to bf16 (round to nearest even: the conversion
+// the tiled kernels apply to the weights) for the dequantizing GEMM; 8 values
+// per thread, two 16-byte loads and one 16-byte store when both buffers are
+// 16-byte aligned.
+__global__ __launch_bounds__(256) void round_bf16_kernel(const float* __restrict__ x,
+                                                         uint16_t* __restrict__ xb, int64_t count,
+                                                         int vec) {
+  const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i0 >= count) return;
+  if (vec && i0 + 8 <= count) {
+    const float4 a = *reinterpret_cast<const float4*>(x + i0);
+    const float4 b = *reinterpret_cast<const float4*>(x + i0 + 4);
+    *reinterpret_cast<u32x4*>(xb + i0) = u32x4{pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w),
+                                               pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w)};
+  } else {
+    for (int64_t i = i0; i < count && i < i0 + 8; ++i)
+      xb[i] = (uint16_t)(pack_bf16x2(x[i], 0.0f) & 0xffffu);
+  }
+}
+
 }  // namespace
 
 int gemm_path(const Mat& mt, const uint8_t* payload, const uint16_t* x) {
@@ -698,6 +720,14 @@ hipError_t launch_gemm(const Mat& mt, const uint8_t* payload, const float* scale
     gemm_generic_kernel<4><<<grid, 256, 0, st>>>(x, payload, scales, y, m, mt.n, mt.k, mt.group);
   else
     gemm_generic_kernel<8><<<grid, 256, 0, st>>>(x, payload, scales, y, m, mt.n, mt.k, mt.group);
+  return hipGetLastError();
+}
+
+hipError_t launch_round_bf16(const float* x, uint16_t* xb, int64_t count, hipStream_t st) {
+  const int64_t threads = (count + 7) / 8;
+  if ((threads + 255) / 256 >= (1ll << 31)) return hipErrorInvalidValue;
+  const int vec = aligned(x, 16) && aligned(xb, 16) ? 1 : 0;
+  round_bf16_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(x, xb, count, vec);
   return hipGetLastError();
 }
 

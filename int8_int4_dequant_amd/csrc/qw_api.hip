@@ -247,6 +247,32 @@ int qw_gemm(int bits, int64_t group, int64_t n, int64_t k, const uint8_t* payloa
   return record(qw::launch_gemm(mt, payload, scales, m, x_bf16, y, (hipStream_t)stream));
 }
 
+int64_t qw_matmul_work_bytes(int64_t m, int64_t k) {
+  if (m < 0 || k < 0 || mul_overflows(m, k)) return -1;
+  if (m <= QW_MATMUL_GEMV_MAX_M) return 0;
+  return (m * k * 2 + 255) / 256 * 256;  // bf16 copy of x
+}
+
+int qw_matmul(int bits, int64_t group, int64_t n, int64_t k, const uint8_t* payload,
+              const float* scales, int64_t m, const float* x, float* y, void* work,
+              int64_t work_bytes, void* stream) {
+  qw::Mat mt;
+  int st = check_mat(bits, group, n, k, &mt);
+  if (st != QW_OK) return st;
+  if (m < 0 || mul_overflows(m, n) || mul_overflows(m, k)) return QW_EM;
+  if (m <= QW_MATMUL_GEMV_MAX_M)
+    return qw_gemv(bits, group, n, k, payload, scales, m, x, y, stream);
+  if (n == 0) return QW_OK;
+  if (!y) return QW_ENULL;
+  if (k == 0) return record(qw::launch_fill_zero(y, m * n, (hipStream_t)stream));
+  if (!payload || !scales || !x) return QW_ENULL;
+  if (!work || work_bytes < qw_matmul_work_bytes(m, k)) return QW_EWORK;
+  uint16_t* xb = (uint16_t*)work;
+  hipError_t e = qw::launch_round_bf16(x, xb, m * k, (hipStream_t)stream);
+  if (e != hipSuccess) return record(e);
+  return record(qw::launch_gemm(mt, payload, scales, m, xb, y, (hipStream_t)stream));
+}
+
 int64_t qw_gptq_hessian_work_bytes(int64_t k, int64_t t) {
   if (k < 0 || t < 0 || mul_overflows(k, k)) return -1;
   return qw::gptq_hessian_work_bytes(k, t);

@@ -42,6 +42,8 @@ hipError_t launch_gemv_chain(const Mat* mts, const uint8_t* const* payloads,
 hipError_t launch_gemm(const Mat& mt, const uint8_t* payload, const float* scales,
                        int64_t m, const uint16_t* x, float* y, hipStream_t stream);
 hipError_t launch_fill_zero(float* y, int64_t count, hipStream_t stream);
+// x fp32 [count] -> bf16 bit patterns, round to nearest even (gemm.hip).
+hipError_t launch_round_bf16(const float* x, uint16_t* xb, int64_t count, hipStream_t stream);
 
 // GPTQ (gptq.hip).  Work buffers are caller-provided device memory of at
 // least the returned sizes.

@@ -30,9 +30,14 @@ STATUS_NAMES = {0: "QW_OK", -1: "QW_EBITS", -2: "QW_EGROUP", -3: "QW_ESHAPE", -4
 #: symbols declared in include/qw.h
 EXPORTS = ["qw_payload_bytes", "qw_num_scales", "qw_status_string", "qw_last_error",
            "qw_quantize_pack", "qw_quantize_pack_batched", "qw_unpack", "qw_gemv",
-           "qw_gemv_batched", "qw_gemv_chain", "qw_gemm", "qw_debug_path",
+           "qw_gemv_batched", "qw_gemv_chain", "qw_gemm", "qw_matmul_work_bytes", "qw_matmul",
+           "qw_debug_path",
            "qw_gptq_hessian_work_bytes", "qw_gptq_hessian", "qw_gptq_factor_work_bytes",
            "qw_gptq_factor", "qw_gptq_quantize_work_bytes", "qw_gptq_quantize_pack"]
+
+
+# Rows up to which qw_matmul runs the codes GEMV (QW_MATMUL_GEMV_MAX_M in qw.h).
+MATMUL_GEMV_MAX_M = 4
 
 
 class QwQuantDesc(ctypes.Structure):
@@ -97,6 +102,10 @@ def lib():
     L.qw_gemv_chain.restype = i32
     L.qw_gemm.argtypes = [i32, i64, i64, i64, vp, vp, i64, vp, vp, vp]
     L.qw_gemm.restype = i32
+    L.qw_matmul_work_bytes.argtypes = [i64, i64]
+    L.qw_matmul_work_bytes.restype = i64
+    L.qw_matmul.argtypes = [i32, i64, i64, i64, vp, vp, i64, vp, vp, vp, i64, vp]
+    L.qw_matmul.restype = i32
     L.qw_debug_path.argtypes = [i32, i32, i64, i64, i64, vp, vp]
     L.qw_debug_path.restype = i32
     L.qw_gptq_hessian_work_bytes.argtypes = [i64, i64]
@@ -201,6 +210,15 @@ def qw_gemv_chain(count, descs, stages, m, stream=None):
 def qw_gemm(bits, group, n, k, payload, scales, m, x_bf16, y, stream=None):
     return lib().qw_gemm(bits, group, n, k, _ptr(payload), _ptr(scales), m, _ptr(x_bf16),
                          _ptr(y), _stream(stream))
+
+
+def qw_matmul_work_bytes(m, k):
+    return lib().qw_matmul_work_bytes(m, k)
+
+
+def qw_matmul(bits, group, n, k, payload, scales, m, x, y, work, work_bytes, stream=None):
+    return lib().qw_matmul(bits, group, n, k, _ptr(payload), _ptr(scales), m, _ptr(x), _ptr(y),
+                           _ptr(work), work_bytes, _stream(stream))
 
 
 def qw_debug_path(op, bits, group, n, k, a=None, b=None):
@@ -347,6 +365,26 @@ def gemm(rec, x_bf16, out=None, stream=None):
         out = torch.empty((m, n), dtype=torch.float32, device=x_bf16.device)
     _check(qw_gemm(rec["bits"], rec["group"], n, k, rec["payload"], rec["scales"], m, x_bf16,
                    out, stream), "qw_gemm")
+    return out
+
+
+def matmul(rec, x, out=None, work=None, stream=None):
+    """QuantizedMatmul: fp32 x [m][k] (any m) times the quantized weight;
+    returns fp32 y [m][n].  Up to QW_MATMUL_GEMV_MAX_M rows this is the codes
+    GEMV; beyond, x is rounded to bf16 into ``work`` (allocated here when not
+    given) and the matrix-core GEMM runs."""
+    n, k = _nk(rec["shape"])
+    if x.dtype != torch.float32 or not x.is_contiguous() or x.dim() != 2 or x.shape[1] != k:
+        raise ValueError("x must be a contiguous float32 [m][k] tensor")
+    m = x.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    nb = lib().qw_matmul_work_bytes(m, k)
+    if work is None:
+        work = _work(nb, x.device) if nb > 0 else None
+    wb = work.numel() * work.element_size() if work is not None else 0
+    _check(qw_matmul(rec["bits"], rec["group"], n, k, rec["payload"], rec["scales"], m, x, out,
+                     work, wb, stream), "qw_matmul")
     return out
 
 

@@ -40,6 +40,7 @@ from .rtn import (  # noqa: F401
 )
 from .matmul import (  # noqa: F401
     bf16_bits_to_f32,
+    bf16_round,
     gemv_ref,
     gemm_ref,
     error_base,

@@ -45,6 +45,36 @@ def bf16_bits_to_f32(bits):
     return b.view(np.float32)
 
 
+def bf16_round(x):
+    """fp32 values rounded to the nearest bf16 number, ties to the even bit
+    pattern (the rounding the GEMM path applies to fp32 activations), as
+    uint16 bit patterns.  Inputs must be finite.
+
+    Written from the definition: below |x| lies the bf16 number whose
+    pattern is the top half of |x|'s pattern (truncation), above it the
+    next pattern; the one at the smaller exact distance wins (the pattern
+    0x7F80 above the largest finite bf16 counts as 2^128, so values past the
+    last midpoint go to infinity, as round to nearest does)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    mag = x.view(np.uint32) & np.uint32(0x7FFFFFFF)
+    sign = (x.view(np.uint32) >> np.uint32(16)) & np.uint32(0x8000)
+    lo = mag >> np.uint32(16)
+    hi = lo + np.uint32(1)
+
+    def value(p):                      # exact magnitude of a bf16 pattern
+        e = (p >> np.uint32(7)).astype(np.int64)
+        f = (p & np.uint32(0x7F)).astype(np.float64)
+        normal = np.ldexp(1.0 + f / 128.0, e - 127)
+        sub = np.ldexp(f / 128.0, -126)
+        return np.where(e == 0, sub, normal)
+
+    a = mag.view(np.float32).astype(np.float64)
+    d_lo = a - value(lo)
+    d_hi = value(hi) - a
+    up = (d_hi < d_lo) | ((d_hi == d_lo) & ((lo & np.uint32(1)) == 1))
+    return (np.where(up, hi, lo) | sign).astype(np.uint16)
+
+
 def _as_matrix(rec):
     shape = rec["shape"]
     if len(shape) != 2:

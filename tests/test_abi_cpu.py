@@ -103,6 +103,28 @@ def test_chain_validation_before_any_launch():
     assert L.qw_gemv_chain(0, None, None, 1, None) == 0
 
 
+def test_matmul_work_size_and_validation():
+    L = qw.lib()
+    t = qw.MATMUL_GEMV_MAX_M
+    assert L.qw_matmul_work_bytes(t, 4096) == 0          # the GEMV side needs none
+    assert L.qw_matmul_work_bytes(t + 1, 4096) >= (t + 1) * 4096 * 2
+    assert L.qw_matmul_work_bytes(300, 1000) % 256 == 0
+    assert L.qw_matmul_work_bytes(-1, 8) == -1
+    fake = 1 << 20  # never dereferenced: every call below fails validation or is empty
+    need = L.qw_matmul_work_bytes(9, 256)
+    assert L.qw_matmul(4, 32, 64, 256, fake, fake, 9, fake, fake, None, need, None) == -8
+    assert L.qw_matmul(4, 32, 64, 256, fake, fake, 9, fake, fake, fake, need - 1, None) == -8
+    assert L.qw_matmul(3, 32, 64, 256, fake, fake, 9, fake, fake, fake, need, None) == -1
+    assert L.qw_matmul(4, 48, 64, 100, fake, fake, 9, fake, fake, fake, need, None) == -2
+    assert L.qw_matmul(4, 32, 64, 256, fake, fake, -1, fake, fake, fake, need, None) == -4
+    assert L.qw_matmul(4, 32, 64, 256, None, fake, 9, fake, fake, fake, need, None) == -5
+    assert L.qw_matmul(4, 32, 64, 256, fake, fake, 9, fake, None, fake, need, None) == -5
+    assert L.qw_matmul(4, 32, 0, 256, None, None, 9, None, None, None, 0, None) == 0
+    assert L.qw_matmul(4, 32, 64, 256, fake, fake, 0, fake, fake, None, 0, None) == 0
+    # the GEMV side keeps qw_gemv's own limits and needs no work buffer
+    assert L.qw_matmul(4, 32, 64, 256, None, fake, 3, fake, fake, None, 0, None) == -5
+
+
 def test_gptq_work_sizes():
     L = qw.lib()
     assert L.qw_gptq_hessian_work_bytes(-1, 5) == -1

@@ -249,6 +249,62 @@ def test_codes_path_agrees_with_dequantized_path():
             assert np.all(np.abs(yv - xf @ w_hat.T) <= GEMV_TOL * B)
 
 
+@pytest.mark.parametrize("bits,group,n,k", [(4, 32, 256, 1024), (8, 128, 300, 512),
+                                           (4, 128, 520, 256)])
+def test_matmul_dispatch_across_m(bits, group, n, k):
+    """qw_matmul (QuantizedMatmul) at the Smallem test rows 1, 9, 40, 300 and
+    around the crossover: up to MATMUL_GEMV_MAX_M rows it is the codes GEMV
+    (bit for bit, and within the GEMV bar); above, the work buffer holds
+    exactly the oracle's bf16 rounding of x, the result equals qw_gemm on
+    those bits, and it is within the GEMM bar of the fp32-x product."""
+    w = inputs.weight(n + k + bits, n, k, 0.02)
+    ref, rec = quant_both(w, bits, group)
+    for m in (1, 4, 5, 9, 40, 300):
+        x = inputs.activations(900 + m, m, k)
+        xd = dev(x)
+        nb = qw.qw_matmul_work_bytes(m, k)
+        assert (nb == 0) == (m <= qw.MATMUL_GEMV_MAX_M)
+        work = torch.zeros(max(nb, 1), dtype=torch.uint8, device="cuda")
+        y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        assert qw.qw_matmul(bits, group, n, k, rec["payload"], rec["scales"], m, xd, y,
+                            work if nb else None, nb) == 0
+        yh = host(y)
+        yr = oracle.gemv_ref(ref, x)
+        B = oracle.error_base(ref, x)
+        err = np.abs(yh.astype(np.float64) - yr)
+        if m <= qw.MATMUL_GEMV_MAX_M:
+            assert same_bits(yh, host(qw.gemv(rec, xd)))
+            assert np.all(err <= GEMV_TOL * B)
+        else:
+            xb = oracle.bf16_round(x)
+            got = host(work)[: m * k * 2].view(np.uint16).reshape(m, k)
+            assert np.array_equal(got, xb), "bf16 rounding of x differs"
+            assert same_bits(yh, host(qw.gemm(rec, dev(xb.view(np.int16)))))
+            assert np.all(err <= GEMM_TOL * B)
+
+
+@pytest.mark.parametrize("offset", [0, 1])
+def test_matmul_rounding_tail_and_unaligned_x(offset):
+    """The bf16 rounding of x on its element-wise path: a count that is not a
+    multiple of 8 (5 x 100 = 500 values) and, with offset 1, an x that is
+    only 4-byte aligned."""
+    n, k, m = 40, 100, 5
+    w = inputs.weight(61, n, k, 0.05)
+    ref, rec = quant_both(w, 4, 4)
+    x = inputs.activations(62, m, k)
+    buf = torch.zeros(m * k + offset, dtype=torch.float32, device="cuda")
+    buf[offset:] = dev(x.reshape(-1))
+    xv = buf[offset:].view(m, k)
+    nb = qw.qw_matmul_work_bytes(m, k)
+    work = torch.zeros(nb, dtype=torch.uint8, device="cuda")
+    y = qw.matmul(rec, xv, work=work)
+    got = host(work)[: m * k * 2].view(np.uint16).reshape(m, k)
+    assert np.array_equal(got, oracle.bf16_round(x))
+    yr = oracle.gemv_ref(ref, x)
+    B = oracle.error_base(ref, x)
+    assert np.all(np.abs(host(y).astype(np.float64) - yr) <= GEMM_TOL * B)
+
+
 # The tiled kernel runs one 256 x 256 output tile per block.  When the last
 # round of tiles would leave at least half the compute units idle, those
 # tiles are split in two along K and both halves add into Y (zeroed first).

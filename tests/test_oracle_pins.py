@@ -445,6 +445,31 @@ def test_gemm_bf16_decode_and_rounding(golden_dir):
         assert float(oracle.bf16_bits_to_f32(bits)[0]) == d["bf16_value"]
 
 
+def test_bf16_round_pins(golden_dir):
+    """oracle.bf16_round: the float-format page's rounded values, hand-worked
+    ties (1 + 2^-8 lies halfway between 1 and 1 + 2^-7 and goes to the even
+    pattern 0x3F80; 1 + 3 * 2^-8 goes up to 0x3F82), identity on values bf16
+    already holds, and torch's CPU bf16 conversion (a library routine) on
+    normal, subnormal and near-overflow values."""
+    import torch
+
+    g = _golden(golden_dir, "float_formats_bf16.json")
+    for d in g["rounded"]:
+        bits = oracle.bf16_round(np.array([d["fp32"]], np.float32))
+        assert float(oracle.bf16_bits_to_f32(bits)[0]) == d["bf16_value"]
+    # the last: 1.5 units of the smallest bf16 subnormal (2^-133), a tie -> 2 units
+    ties = np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 1 + 2 ** -8 + 2 ** -20,
+                     2 ** -133 * 1.5], np.float32)
+    assert [int(v) for v in oracle.bf16_round(ties)] == [0x3F80, 0x3F82, 0xBF80, 0x3F81, 0x0002]
+    rng = np.random.default_rng(41)
+    pats = rng.integers(0, 0x7F80, 20000, dtype=np.uint16) | (rng.integers(0, 2, 20000).astype(np.uint16) << 15)
+    assert np.array_equal(oracle.bf16_round(oracle.bf16_bits_to_f32(pats)), pats)
+    x = np.concatenate([rng.standard_normal(50000), rng.standard_normal(2000) * 1e-39,
+                        rng.uniform(-3.4e38, 3.4e38, 2000)]).astype(np.float32)
+    t = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.bf16_round(x), t)
+
+
 def test_gemm_ref_is_gemv_ref_on_bf16_values():
     w = inputs.weight(9, 6, 32, 0.2)
     xb = inputs.bf16_activations(10, 3, 32)
