@@ -552,9 +552,9 @@ def bench_chain(args, L, stream, mats, shapes, P, S, xs, gbytes):
     """The decode pass as a chain: in every layer q, k, v read the layer's
     input, o reads v's output, gate and up read o's, down reads up's, and the
     next layer reads down's (no attention or nonlinearity in between).  Four
-    dependent stages per layer, 128 for the stack, timed as one cooperative
-    launch (qw_gemv_chain), as one launch per stage, and as those launches
-    replayed from a HIP graph."""
+    dependent stages per layer, 128 for the stack, timed as one
+    qw_gemv_chain call (one launch per stage) and as those launches replayed
+    from a HIP graph."""
     import torch
 
     from int8_int4_dequant_amd import qw

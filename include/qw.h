@@ -169,7 +169,9 @@ typedef struct qw_gemv_desc {
 
 /*
  * Batched dequantizing GEMV: `count` independent products y_i = x_i * W_i^T
- * with a common m (0 <= m <= 8), each exactly as qw_gemv would compute it,
+ * with a common m (0 <= m <= 8), each within qw_gemv's error bound (the
+ * kernel, and so the summation order, follows the rows of the whole launch:
+ * a product may differ from a lone qw_gemv call in its last bits), and
  * enqueued as a few launches (up to QW_BATCH_PER_LAUNCH matrices of one bit
  * width each) that stream the weights back to back instead of one launch
  * per matrix (the fixed cost of many short kernels is what
@@ -189,12 +191,12 @@ int qw_gemv_batched(int count, const qw_gemv_desc* descs, int64_t m, void* strea
  * stage are independent; a product's x may be the y of a product in an
  * earlier stage (a layer's output feeding the next layer), and sees that y
  * complete.  Within a stage no y may overlap another y or any x of the stage.
- * Each stage is one batched launch, enqueued back to back in one call (a HIP
- * graph can capture it); a stage's products come out exactly as
- * qw_gemv_batched computes the same group (a stage of one matrix also keeps
- * the streaming kernel).  A decode step of many short kernels is dominated
- * by their fixed cost (page "Huit bits, puis quatre", section "La vitesse"),
- * which the stage grouping keeps to one launch per dependency level.  Validation as in
+ * Each stage is the batched call over its matrices (one launch per bit
+ * width), enqueued back to back in one call (a HIP graph can capture it), so
+ * a stage's products come out exactly as qw_gemv_batched computes the same
+ * group.  A decode step of many short kernels is dominated by their fixed
+ * cost (page "Huit bits, puis quatre", section "La vitesse"), which the
+ * stage grouping keeps to one launch per dependency level.  Validation as in
  * qw_gemv_batched, plus QW_ECOUNT when `stage` is NULL or decreases.
  */
 int qw_gemv_chain(int count, const qw_gemv_desc* descs, const int32_t* stage, int64_t m,

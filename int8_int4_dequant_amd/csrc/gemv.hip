@@ -33,7 +33,6 @@
 //     (chain length) * 2^-24 * sum|x * w_hat| -- far inside 1e-5 of it.
 //   * The R*M partial sums per lane are reduced across the wave with a
 //     butterfly reduce-scatter (each step halves the values a lane holds).
-#include <vector>
 
 #include "qw_internal.h"
 
@@ -295,20 +294,26 @@ __global__ __launch_bounds__(256) void gemv8_kernel(const GemvBatch<NB> b) {
   }
 }
 
-// Split-K kernel for one matrix with few rows per wave of the GPU: a block's
-// 4 waves share R rows and each takes a quarter of the row's 8-code chunks
-// (lane l of wave w: chunks q*w + l, q*w + l + 64, ... below q*(w+1)); the
-// four partial sums meet in LDS and are added in wave order (deterministic).
-// Four times the waves of gemv8_kernel for the same rows, so a single decode
-// matrix still fills the GPU.
-template <int BITS, int M, int R>
-__global__ __launch_bounds__(256) void gemv8_split_kernel(const GemvDesc a) {
+// Split-K kernel for matrices with few rows for the GPU (one matrix, or a
+// batch such as one stage of a chained decode pass): a block takes one work
+// item of R rows of one matrix; its 4 waves each take a quarter of the row's
+// 8-code chunks (lane l of wave w: chunks q*w + l, q*w + l + 64, ... below
+// q*(w+1)); the four partial sums meet in LDS and are added in wave order
+// (deterministic).  Four times the waves of gemv8_kernel for the same rows,
+// so a single decode matrix still fills the GPU.
+template <int BITS, int M, int R, int NB>
+__global__ __launch_bounds__(256) void gemv8_split_kernel(const GemvBatch<NB> b) {
   constexpr int V = pow2_at_least(R * M);
   constexpr int PW = BITS == 4 ? 1 : 2;     // payload dwords per 8-code chunk
   __shared__ float part_lds[4][R * M];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int row0 = blockIdx.x * R;
+  const int item = blockIdx.x;               // one work item (R rows) per block
+  if (item >= b.items) return;
+  const int di = find_desc(b, item);
+  const GemvDesc a = load_desc<NB>(di);
+  typedef const __attribute__((address_space(4))) GemvBatch<NB>* KArg;
+  const int row0 = (item - ((KArg)__builtin_amdgcn_kernarg_segment_ptr())->item0[di]) * R;
   const int nch = a.k / 8;
   const int q = (nch + 3) >> 2;              // chunks per wave
   const int cbeg = wave * q;
@@ -420,13 +425,14 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(
   if (lane == 0) y[mm * n + row] = sum;
 }
 
-// Rows per wave: as many as the registers allow (x reused across more rows,
-// fewer reductions); fewer when the matrices have too few rows to give every
-// SIMD waves (a lone such matrix takes the split-K kernel instead).
+// Rows per wave of the streaming kernel: as many as the registers allow (x
+// reused across more rows, fewer reductions).  Matrices with too few rows to
+// give every SIMD waves that way take the split-K kernel instead.
 template <int M>
 constexpr int rows_big() { return M <= 4 ? 8 : 4; }
-constexpr int kRowsSmall = 2;
 constexpr int kRowsSplit = 4;  // rows per block of the split-K kernel (8 for m >= 4)
+// Work items of R rows from which several matrices take the streaming kernel.
+constexpr int kBigItemsMany = 2048;
 
 // Launches `count` descriptors (same bits, m), GEMV_NB per launch, R rows per
 // work item.
@@ -449,6 +455,26 @@ hipError_t launch_group(const GemvDesc* ds, int count, hipStream_t st) {
   return hipSuccess;
 }
 
+// The same for the split-K kernel: one block per work item of R rows.
+template <int BITS, int M, int R, int NB>
+hipError_t launch_split_group(const GemvDesc* ds, int count, hipStream_t st) {
+  for (int base = 0; base < count; base += NB) {
+    GemvBatch<NB> b{};
+    b.count = count - base < NB ? count - base : NB;
+    int items = 0;
+    for (int i = 0; i < b.count; ++i) {
+      b.d[i] = ds[base + i];
+      b.item0[i] = items;
+      items += (b.d[i].n + R - 1) / R;
+    }
+    b.items = items;
+    gemv8_split_kernel<BITS, M, R, NB><<<(unsigned)items, 256, 0, st>>>(b);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 template <int BITS, int M>
 hipError_t launch_m(const GemvDesc* ds, int count, hipStream_t st) {
   int64_t rows = 0;
@@ -457,17 +483,16 @@ hipError_t launch_m(const GemvDesc* ds, int count, hipStream_t st) {
   // a lone matrix keeps the split-K kernel up to four per SIMD (4096 items),
   // since its waves each run a short loop whose load latency few waves hide
   // (int4 group 128 at m = 8: 14336 x 4096 34 -> 27 us, 8192 x 28672
-  // 107 -> 86 us)
+  // 107 -> 86 us).  Below that, the split-K kernel: the 4 waves of a block
+  // share R rows and split K, four times the waves for the same rows.
   constexpr int RB = rows_big<M>();
-  if (count == 1) {
-    if (rows / RB >= 4096) return launch_group<BITS, M, RB, 1>(ds, count, st);
-    // a lone matrix with fewer rows: split K over the 4 waves of a block
-    constexpr int RS = M >= 4 ? 2 * kRowsSplit : kRowsSplit;  // x reused over more rows
-    gemv8_split_kernel<BITS, M, RS><<<(unsigned)((ds[0].n + RS - 1) / RS), 256, 0, st>>>(ds[0]);
-    return hipGetLastError();
-  }
-  return rows / RB >= 2048 ? launch_group<BITS, M, RB, GEMV_NB>(ds, count, st)
-                           : launch_group<BITS, M, kRowsSmall, GEMV_NB>(ds, count, st);
+  constexpr int RS = M >= 4 ? 2 * kRowsSplit : kRowsSplit;  // x reused over more rows
+  const bool big = rows / RB >= (count == 1 ? 4096 : kBigItemsMany);
+  if (count == 1)
+    return big ? launch_group<BITS, M, RB, 1>(ds, count, st)
+               : launch_split_group<BITS, M, RS, 1>(ds, count, st);
+  return big ? launch_group<BITS, M, RB, GEMV_NB>(ds, count, st)
+             : launch_split_group<BITS, M, RS, GEMV_NB>(ds, count, st);
 }
 
 template <int BITS>
@@ -562,55 +587,16 @@ hipError_t launch_gemv_batched(const Mat* mts, const uint8_t* const* payloads,
   return hipSuccess;
 }
 
-// One stage of a chain on the streaming kernel, with the rows per work item
-// qw_gemv_batched would take for the same matrices (also for a lone one).
-template <int BITS, int M>
-hipError_t chain_stage_m(const GemvDesc* ds, int count, hipStream_t st) {
-  int64_t rows = 0;
-  for (int i = 0; i < count; ++i) rows += ds[i].n;
-  constexpr int RB = rows_big<M>();
-  return rows / RB >= 2048 ? launch_group<BITS, M, RB, GEMV_NB>(ds, count, st)
-                           : launch_group<BITS, M, kRowsSmall, GEMV_NB>(ds, count, st);
-}
-
-template <int BITS>
-hipError_t chain_stage(const GemvDesc* ds, int count, int m, hipStream_t st) {
-  switch (m) {
-    case 1: return chain_stage_m<BITS, 1>(ds, count, st);
-    case 2: return chain_stage_m<BITS, 2>(ds, count, st);
-    case 3: return chain_stage_m<BITS, 3>(ds, count, st);
-    case 4: return chain_stage_m<BITS, 4>(ds, count, st);
-    case 5: return chain_stage_m<BITS, 5>(ds, count, st);
-    case 6: return chain_stage_m<BITS, 6>(ds, count, st);
-    case 7: return chain_stage_m<BITS, 7>(ds, count, st);
-    default: return chain_stage_m<BITS, 8>(ds, count, st);
-  }
-}
-
 hipError_t launch_gemv_chain(const Mat* mts, const uint8_t* const* payloads,
                              const float* const* scales, int m, const float* const* xs,
                              float* const* ys, const int* stage, int count, hipStream_t st) {
-  std::vector<GemvDesc> ds;
+  // each stage is exactly the batched call over its matrices, enqueued in
+  // stage order on one stream
   for (int i0 = 0; i0 < count;) {
     int i1 = i0 + 1;
     while (i1 < count && stage[i1] == stage[i0]) ++i1;
-    // a stage of one bit width on the streaming kernel: one launch of it;
-    // otherwise the batched dispatch
-    bool uniform = true;
-    for (int i = i0; i < i1 && uniform; ++i)
-      if (mts[i].bits != mts[i0].bits || gemv_path(mts[i], payloads[i], xs[i]) != PATH_FAST)
-        uniform = false;
-    hipError_t e;
-    if (uniform) {
-      ds.clear();
-      for (int i = i0; i < i1; ++i)
-        ds.push_back(make_desc(mts[i], payloads[i], scales[i], xs[i], ys[i]));
-      e = mts[i0].bits == 4 ? chain_stage<4>(ds.data(), i1 - i0, m, st)
-                            : chain_stage<8>(ds.data(), i1 - i0, m, st);
-    } else {
-      e = launch_gemv_batched(mts + i0, payloads + i0, scales + i0, m, xs + i0, ys + i0, i1 - i0,
-                              st);
-    }
+    hipError_t e = launch_gemv_batched(mts + i0, payloads + i0, scales + i0, m, xs + i0, ys + i0,
+                                       i1 - i0, st);
     if (e != hipSuccess) return e;
     i0 = i1;
   }
