@@ -208,6 +208,8 @@ __device__ __forceinline__ GemvDesc load_desc(int di) {
 // at m = 8).
 template <int BITS, int M, int R, int NB>
 __global__ __launch_bounds__(256) void gemv8_kernel(const GemvBatch<NB> b) {
+  static_assert(R * M <= 64, "a lane holds at most 64 partial sums (one per lane after the"
+                            " reduce-scatter)");
   constexpr int V = pow2_at_least(R * M);
   constexpr int PW = BITS == 4 ? 1 : 2;     // payload dwords per 8-code chunk
   const int lane = threadIdx.x & 63;
@@ -303,6 +305,8 @@ __global__ __launch_bounds__(256) void gemv8_kernel(const GemvBatch<NB> b) {
 // so a single decode matrix still fills the GPU.
 template <int BITS, int M, int R, int NB>
 __global__ __launch_bounds__(256) void gemv8_split_kernel(const GemvBatch<NB> b) {
+  static_assert(R * M <= 64, "a lane holds at most 64 partial sums (one per lane after the"
+                            " reduce-scatter)");
   constexpr int V = pow2_at_least(R * M);
   constexpr int PW = BITS == 4 ? 1 : 2;     // payload dwords per 8-code chunk
   __shared__ float part_lds[4][R * M];
@@ -425,12 +429,24 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(
   if (lane == 0) y[mm * n + row] = sum;
 }
 
-// Rows per wave of the streaming kernel: as many as the registers allow (x
-// reused across more rows, fewer reductions).  Matrices with too few rows to
-// give every SIMD waves that way take the split-K kernel instead.
+// Rows per wave of the streaming kernel: 8 (x reused across more rows, fewer
+// reductions; 8 * m <= 64 partial sums per lane).  Matrices with too few rows
+// to give every SIMD waves that way take the split-K kernel instead (with
+// 4 rows per wave at m > 4, a 28672-row matrix still streamed and took 108 us
+// at m = 8; the split-K kernel takes 88 us).
 template <int M>
-constexpr int rows_big() { return M <= 4 ? 8 : 4; }
-constexpr int kRowsSplit = 4;  // rows per block of the split-K kernel (8 for m >= 4)
+constexpr int rows_big() { return 8; }
+// Rows per block of the split-K kernel.  Every row of a block reuses the
+// block's x chunks, so more rows cut x traffic (M rows of x against one
+// payload row); fewer rows give a small matrix more blocks.  Measured on int4
+// matrices of 4096 to 28672 rows: 8 rows are faster from m = 2 on every
+// shape, and at m = 1 from 12288 rows (4096-row matrices prefer 4, 11008-row
+// ones are even to slightly slower with 8).
+template <int M>
+constexpr int rows_split_many() { return 8; }
+template <int M>
+constexpr int rows_split_few() { return M == 1 ? 4 : 8; }
+constexpr int64_t kSplitManyRows = 12288;
 // Work items of R rows from which several matrices take the streaming kernel.
 constexpr int kBigItemsMany = 2048;
 
@@ -486,13 +502,17 @@ hipError_t launch_m(const GemvDesc* ds, int count, hipStream_t st) {
   // 107 -> 86 us).  Below that, the split-K kernel: the 4 waves of a block
   // share R rows and split K, four times the waves for the same rows.
   constexpr int RB = rows_big<M>();
-  constexpr int RS = M >= 4 ? 2 * kRowsSplit : kRowsSplit;  // x reused over more rows
+  constexpr int RSM = rows_split_many<M>(), RSF = rows_split_few<M>();
   const bool big = rows / RB >= (count == 1 ? 4096 : kBigItemsMany);
-  if (count == 1)
-    return big ? launch_group<BITS, M, RB, 1>(ds, count, st)
-               : launch_split_group<BITS, M, RS, 1>(ds, count, st);
-  return big ? launch_group<BITS, M, RB, GEMV_NB>(ds, count, st)
-             : launch_split_group<BITS, M, RS, GEMV_NB>(ds, count, st);
+  const bool many = rows >= kSplitManyRows;
+  if (count == 1) {
+    if (big) return launch_group<BITS, M, RB, 1>(ds, count, st);
+    return many ? launch_split_group<BITS, M, RSM, 1>(ds, count, st)
+                : launch_split_group<BITS, M, RSF, 1>(ds, count, st);
+  }
+  if (big) return launch_group<BITS, M, RB, GEMV_NB>(ds, count, st);
+  return many ? launch_split_group<BITS, M, RSM, GEMV_NB>(ds, count, st)
+              : launch_split_group<BITS, M, RSF, GEMV_NB>(ds, count, st);
 }
 
 template <int BITS>
