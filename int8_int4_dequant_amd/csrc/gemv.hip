@@ -313,11 +313,16 @@ __global__ __launch_bounds__(256) void gemv8_split_kernel(const GemvBatch<NB> b)
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int item = blockIdx.x;               // one work item (R rows) per block
-  if (item >= b.items) return;
-  const int di = find_desc(b, item);
+  // a lone matrix (grid = its items) needs no lookup: two dependent
+  // kernel-argument loads fewer before the first payload load
+  int di = 0, row0 = item * R;
+  if constexpr (NB > 1) {
+    if (item >= b.items) return;
+    di = find_desc(b, item);
+    typedef const __attribute__((address_space(4))) GemvBatch<NB>* KArg;
+    row0 = (item - ((KArg)__builtin_amdgcn_kernarg_segment_ptr())->item0[di]) * R;
+  }
   const GemvDesc a = load_desc<NB>(di);
-  typedef const __attribute__((address_space(4))) GemvBatch<NB>* KArg;
-  const int row0 = (item - ((KArg)__builtin_amdgcn_kernarg_segment_ptr())->item0[di]) * R;
   const int nch = a.k / 8;
   const int q = (nch + 3) >> 2;              // chunks per wave
   const int cbeg = wave * q;
