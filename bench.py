@@ -434,18 +434,28 @@ def main():
     except RuntimeError as exc:
         log(f"graph replay of the per-matrix pass skipped: {exc}")
 
-    # unpack (a5 on its own): every matrix back to fp32, one call per matrix
-    wout = torch.empty(max(n * k for n, k in shapes), dtype=torch.float32, device=dev)
+    # unpack (a5 on its own): every matrix back to fp32, as one batched call
+    # (qw_unpack_batched, distinct outputs) and as one call per matrix
+    wouts = [torch.empty(n * k, dtype=torch.float32, device=dev) for n, k in shapes]
+    udescs, und = qw.make_unpack_descs((4, 32, n, k, P[i], S[i], wouts[i])
+                                       for i, (n, k) in enumerate(shapes))
 
     def unpack_pass():
+        st = L.qw_unpack_batched(und, udescs, sptr)
+        if st:
+            raise RuntimeError(f"qw_unpack_batched failed: {st}")
+
+    def unpack_single_pass():
         for i, (n, k) in enumerate(shapes):
-            st = L.qw_unpack(4, 32, n, k, P[i].data_ptr(), S[i].data_ptr(), wout.data_ptr(), sptr)
+            st = L.qw_unpack(4, 32, n, k, P[i].data_ptr(), S[i].data_ptr(), wouts[i].data_ptr(),
+                             sptr)
             if st:
                 raise RuntimeError(f"qw_unpack failed: {st}")
 
     unpack_us = timed(unpack_pass)
+    unpack_single_us = timed(unpack_single_pass)
     ubytes = sum(n * k * 4 + n * k // 2 + 4 * (n * k // 32) for n, k in shapes)
-    del wout
+    del wouts, udescs
     q_gbs = qbytes * args.steps / (q_ms * 1e-3) / 1e9
     g_gbs = gbytes * args.steps / (g_ms * 1e-3) / 1e9
     ms_per_step = 1e3 * t_total / args.steps
@@ -456,7 +466,8 @@ def main():
         f"one launch per matrix: {single_us:.1f} us (graph replay "
         f"{single_graph_us if single_graph_us is None else round(single_graph_us, 1)} us); "
         f"unpack pass {unpack_us:.1f} us "
-        f"({ubytes / (unpack_us * 1e-6) / 1e9:.0f} GB/s)")
+        f"({ubytes / (unpack_us * 1e-6) / 1e9:.0f} GB/s, 1 batched call; one launch per matrix: "
+        f"{unpack_single_us:.1f} us)")
 
     chain = bench_chain(args, L, stream, mats, shapes, P, S, xs, gbytes)
 
@@ -488,8 +499,11 @@ def main():
                            "pass_us": round(1e3 * g_ms / args.steps, 1)},
         "unpack": {"GB/s": round(ubytes / (unpack_us * 1e-6) / 1e9, 1),
                    "frac_hbm": round(ubytes / (unpack_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                   "entry": "qw_unpack", "launches_per_pass": len(shapes),
+                   "entry": "qw_unpack_batched", "launches_per_pass": 1,
                    "pass_us": round(unpack_us, 1), "bytes_per_pass": ubytes},
+        "unpack_one_launch_per_matrix": {
+            "pass_us": round(unpack_single_us, 1),
+            "GB/s": round(ubytes / (unpack_single_us * 1e-6) / 1e9, 1)},
         "decode_chain_m1": chain,
         "decode_gemv_m1_one_launch_per_matrix": {
             "pass_us": round(single_us, 1),

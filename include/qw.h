@@ -141,6 +141,36 @@ int qw_unpack(int bits, int64_t group, int64_t n, int64_t k,
               void* stream);
 
 /*
+ * One matrix of a batched unpack (see qw_unpack_batched); the fields mean
+ * what the qw_unpack arguments of the same names mean.
+ */
+typedef struct qw_unpack_desc {
+    const uint8_t* payload;  /* qw_payload_bytes(bits, n, k) bytes */
+    const float* scales;     /* qw_num_scales(group, n, k) floats */
+    float* w_out;            /* fp32 [n][k] */
+    int64_t n;
+    int64_t k;
+    int64_t group;
+    int32_t bits;
+    int32_t reserved;        /* must be 0 */
+} qw_unpack_desc;
+
+/*
+ * Batched unpack: `count` independent matrices (for instance a whole
+ * model's layers turned back into fp32, the dequantized copy page "Huit bits,
+ * puis quatre", section "Ranger des entiers dans des f32", keeps beside the
+ * codes), each bit-identical to what qw_unpack writes, enqueued as a few
+ * large launches instead of one per matrix (matrices of the same bit width
+ * share a launch, up to QW_BATCH_PER_LAUNCH of them; matrices the vector
+ * kernel does not take are launched on their own).  `descs` is a HOST array
+ * read before the call returns; outputs must not overlap each other or any
+ * input.  Every entry is validated first; on any invalid entry nothing is
+ * enqueued and its status (or QW_ECOUNT for count < 0 / reserved != 0) is
+ * returned.
+ */
+int qw_unpack_batched(int count, const qw_unpack_desc* descs, void* stream);
+
+/*
  * Dequantizing GEMV (decode), fp32:
  *   x  fp32 [m][k]  (read),   y  fp32 [m][n]  (written),   0 <= m <= 8.
  * Any group dividing n*k is accepted; with k % 8 == 0 and either

@@ -368,14 +368,15 @@ __device__ __forceinline__ int nibble_or_byte(uint32_t v, int i) {
 // scales[v >> vshift] (groups of a power-of-two number of vectors), else
 // scales[v / vpg].
 template <int BITS>
-__global__ __launch_bounds__(256) void unpack_vec_kernel(
+__device__ __forceinline__ void unpack_vec_body(
     const uint8_t* __restrict__ payload, const float* __restrict__ scales,
-    float* __restrict__ out, uint64_t nvec, uint64_t vpg /* vectors per group */, int vshift) {
+    float* __restrict__ out, uint64_t nvec, uint64_t vpg /* vectors per group */, int vshift,
+    uint64_t block) {
   constexpr int PB = BITS / 2;  // payload bytes per vector
   __shared__ __attribute__((aligned(16))) uint8_t stage[4][64 * QV * PB];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
-  const uint64_t base = ((uint64_t)blockIdx.x * 4 + wv) * (64 * QV);
+  const uint64_t base = (block * 4 + wv) * (64 * QV);
   const uint64_t v0 = base + (uint64_t)QV * lane;  // first vector of this lane's load
   if (v0 + QV <= nvec) {
     if constexpr (QV * PB == 8) {
@@ -411,6 +412,47 @@ __global__ __launch_bounds__(256) void unpack_vec_kernel(
     }
     stnt(reinterpret_cast<float4*>(out) + idx, make_float4(v[0], v[1], v[2], v[3]));
   }
+}
+
+template <int BITS>
+__global__ __launch_bounds__(256) void unpack_vec_kernel(
+    const uint8_t* __restrict__ payload, const float* __restrict__ scales,
+    float* __restrict__ out, uint64_t nvec, uint64_t vpg, int vshift) {
+  unpack_vec_body<BITS>(payload, scales, out, nvec, vpg, vshift, blockIdx.x);
+}
+
+// Several matrices of one bit width in one launch (any groups the vector
+// kernel takes), found like the batched quantize: descriptors in the kernel
+// arguments, a wave-uniform binary search over the first-block table.
+struct UnpackDesc {
+  const uint8_t* payload;
+  const float* scales;
+  float* out;
+  uint64_t nvec;    // float4 vectors of the matrix
+  uint64_t vpg;     // vectors per group
+  int vshift;       // log2(vpg) when vpg is a power of two, else -1
+  int pad;
+};
+constexpr int UNPACK_NB = QW_BATCH_PER_LAUNCH;
+struct UnpackBatch {
+  uint32_t block0[UNPACK_NB];  // first block of each matrix, ascending, block0[0] = 0
+  UnpackDesc d[UNPACK_NB];
+  int count;
+  int blocks;
+};
+
+template <int BITS>
+__global__ __launch_bounds__(256) void unpack_vec_batched_kernel(const UnpackBatch b) {
+  typedef const __attribute__((address_space(4))) UnpackBatch* KArg;
+  const KArg kb = (KArg)__builtin_amdgcn_kernarg_segment_ptr();
+  const uint32_t blk = blockIdx.x;
+  int lo = 0, hi = b.count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (kb->block0[mid] <= blk) lo = mid; else hi = mid - 1;
+  }
+  const auto& d = kb->d[lo];
+  unpack_vec_body<BITS>(d.payload, d.scales, d.out, d.nvec, d.vpg, d.vshift, blk - kb->block0[lo]);
 }
 
 // One thread per weight; any group and alignment.
@@ -466,6 +508,14 @@ hipError_t quantize_bits(const Mat& mt, const float* w, uint8_t* payload, float*
   return hipGetLastError();
 }
 
+// log2(vpg) for a power of two, else -1 (the kernel then divides).
+inline int vec_shift(uint64_t vpg) {
+  if ((vpg & (vpg - 1)) != 0) return -1;
+  int v = 0;
+  while ((1ull << v) < vpg) ++v;
+  return v;
+}
+
 template <int BITS>
 hipError_t unpack_bits(const Mat& mt, const uint8_t* payload, const float* scales, float* out,
                        hipStream_t st) {
@@ -475,11 +525,7 @@ hipError_t unpack_bits(const Mat& mt, const uint8_t* payload, const float* scale
     const uint64_t nvec = count / 4;
     const unsigned grid = (unsigned)((nvec + 4 * 64 * QV - 1) / (4 * 64 * QV));
     const uint64_t vpg = group / 4;
-    int vshift = -1;
-    if ((vpg & (vpg - 1)) == 0) {
-      vshift = 0;
-      while ((1ull << vshift) < vpg) ++vshift;
-    }
+    const int vshift = vec_shift(vpg);
     unpack_vec_kernel<BITS><<<grid, 256, 0, st>>>(payload, scales, out, nvec, vpg, vshift);
   } else {
     unpack_generic_kernel<BITS><<<blocks_for(count), 256, 0, st>>>(payload, scales, out, count, group);
@@ -592,6 +638,57 @@ hipError_t launch_quantize_pack_batched(const Mat* mts, const float* const* ws,
                                   : launch_quant_batch_g<8>(b, bk.group, st);
       if (e != hipSuccess) return e;
     }
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_unpack_batched(const Mat* mts, const uint8_t* const* payloads,
+                                 const float* const* scales, float* const* outs, int count,
+                                 hipStream_t st) {
+  // vector-path matrices of one bit width go out UNPACK_NB per launch (and
+  // fewer than 2^31 blocks); any other matrix takes the single call
+  const uint64_t kMaxBlocks = (1ull << 31) - 1;
+  for (int bits = 4; bits <= 8; bits += 4) {
+    UnpackBatch b{};
+    uint64_t blocks = 0;
+    auto flush = [&]() -> hipError_t {
+      if (b.count == 0) return hipSuccess;
+      b.blocks = (int)blocks;
+      if (bits == 4)
+        unpack_vec_batched_kernel<4><<<(unsigned)blocks, 256, 0, st>>>(b);
+      else
+        unpack_vec_batched_kernel<8><<<(unsigned)blocks, 256, 0, st>>>(b);
+      b.count = 0;
+      blocks = 0;
+      return hipGetLastError();
+    };
+    for (int i = 0; i < count; ++i) {
+      if (mts[i].bits != bits || mts[i].n * mts[i].k == 0) continue;
+      if (unpack_path(mts[i], payloads[i], outs[i]) != PATH_FAST) {
+        hipError_t e = launch_unpack(mts[i], payloads[i], scales[i], outs[i], st);
+        if (e != hipSuccess) return e;
+        continue;
+      }
+      const uint64_t nvec = (uint64_t)(mts[i].n * mts[i].k) / 4;
+      const uint64_t nblk = (nvec + 4 * 64 * QV - 1) / (4 * 64 * QV);
+      if (nblk > kMaxBlocks) return hipErrorInvalidValue;
+      if (b.count == UNPACK_NB || blocks + nblk > kMaxBlocks) {
+        hipError_t e = flush();
+        if (e != hipSuccess) return e;
+      }
+      b.block0[b.count] = (uint32_t)blocks;
+      UnpackDesc& d = b.d[b.count++];
+      d.payload = payloads[i];
+      d.scales = scales[i];
+      d.out = outs[i];
+      d.nvec = nvec;
+      d.vpg = (uint64_t)mts[i].group / 4;
+      d.vshift = vec_shift(d.vpg);
+      d.pad = 0;
+      blocks += nblk;
+    }
+    hipError_t e = flush();
+    if (e != hipSuccess) return e;
   }
   return hipSuccess;
 }

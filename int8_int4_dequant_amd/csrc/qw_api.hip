@@ -124,6 +124,40 @@ int qw_unpack(int bits, int64_t group, int64_t n, int64_t k, const uint8_t* payl
   return record(qw::launch_unpack(mt, payload, scales, w_out, (hipStream_t)stream));
 }
 
+int qw_unpack_batched(int count, const qw_unpack_desc* descs, void* stream) {
+  if (count < 0) return QW_ECOUNT;
+  if (count == 0) return QW_OK;
+  if (!descs) return QW_ENULL;
+  for (int i = 0; i < count; ++i) {
+    const qw_unpack_desc& d = descs[i];
+    if (d.reserved != 0) return QW_ECOUNT;
+    qw::Mat mt;
+    int st = check_mat(d.bits, d.group, d.n, d.k, &mt);
+    if (st != QW_OK) return st;
+    if (d.n * d.k > 0 && (!d.payload || !d.scales || !d.w_out)) return QW_ENULL;
+  }
+  const int kChunk = 256;
+  qw::Mat mts[kChunk];
+  const uint8_t* ps[kChunk];
+  const float* ss[kChunk];
+  float* os[kChunk];
+  for (int base = 0; base < count; base += kChunk) {
+    int nb = 0;
+    for (int i = base; i < count && i < base + kChunk; ++i) {
+      const qw_unpack_desc& d = descs[i];
+      if (d.n * d.k == 0) continue;
+      check_mat(d.bits, d.group, d.n, d.k, &mts[nb]);
+      ps[nb] = d.payload;
+      ss[nb] = d.scales;
+      os[nb] = d.w_out;
+      ++nb;
+    }
+    int st = record(qw::launch_unpack_batched(mts, ps, ss, os, nb, (hipStream_t)stream));
+    if (st != QW_OK) return st;
+  }
+  return QW_OK;
+}
+
 int qw_gemv(int bits, int64_t group, int64_t n, int64_t k, const uint8_t* payload,
             const float* scales, int64_t m, const float* x, float* y, void* stream) {
   qw::Mat mt;

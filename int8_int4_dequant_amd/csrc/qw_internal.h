@@ -29,6 +29,11 @@ hipError_t launch_quantize_pack_batched(const Mat* mts, const float* const* ws,
                                         int count, hipStream_t stream);
 hipError_t launch_unpack(const Mat& mt, const uint8_t* payload,
                          const float* scales, float* w_out, hipStream_t stream);
+// Several matrices, each exactly as launch_unpack writes it; vector-path
+// matrices of one bit width share launches (QW_BATCH_PER_LAUNCH at a time).
+hipError_t launch_unpack_batched(const Mat* mts, const uint8_t* const* payloads,
+                                 const float* const* scales, float* const* outs, int count,
+                                 hipStream_t stream);
 hipError_t launch_gemv(const Mat& mt, const uint8_t* payload, const float* scales,
                        int m, const float* x, float* y, hipStream_t stream);
 hipError_t launch_gemv_batched(const Mat* mts, const uint8_t* const* payloads,

@@ -29,7 +29,8 @@ STATUS_NAMES = {0: "QW_OK", -1: "QW_EBITS", -2: "QW_EGROUP", -3: "QW_ESHAPE", -4
 
 #: symbols declared in include/qw.h
 EXPORTS = ["qw_payload_bytes", "qw_num_scales", "qw_status_string", "qw_last_error",
-           "qw_quantize_pack", "qw_quantize_pack_batched", "qw_unpack", "qw_gemv",
+           "qw_quantize_pack", "qw_quantize_pack_batched", "qw_unpack", "qw_unpack_batched",
+           "qw_gemv",
            "qw_gemv_batched", "qw_gemv_chain", "qw_gemm", "qw_matmul_work_bytes", "qw_matmul",
            "qw_debug_path",
            "qw_gptq_hessian_work_bytes", "qw_gptq_hessian", "qw_gptq_factor_work_bytes",
@@ -43,6 +44,14 @@ MATMUL_GEMV_MAX_M = 4
 class QwQuantDesc(ctypes.Structure):
     """Mirror of `qw_quant_desc` in include/qw.h."""
     _fields_ = [("w", ctypes.c_void_p), ("payload", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("n", ctypes.c_int64), ("k", ctypes.c_int64), ("group", ctypes.c_int64),
+                ("bits", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class QwUnpackDesc(ctypes.Structure):
+    """Mirror of `qw_unpack_desc` in include/qw.h."""
+    _fields_ = [("payload", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("w_out", ctypes.c_void_p),
                 ("n", ctypes.c_int64), ("k", ctypes.c_int64), ("group", ctypes.c_int64),
                 ("bits", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
@@ -93,6 +102,8 @@ def lib():
     L.qw_quantize_pack_batched.restype = i32
     L.qw_unpack.argtypes = [i32, i64, i64, i64, vp, vp, vp, vp]
     L.qw_unpack.restype = i32
+    L.qw_unpack_batched.argtypes = [i32, ctypes.POINTER(QwUnpackDesc), vp]
+    L.qw_unpack_batched.restype = i32
     L.qw_gemv.argtypes = [i32, i64, i64, i64, vp, vp, i64, vp, vp, vp]
     L.qw_gemv.restype = i32
     L.qw_gemv_batched.argtypes = [i32, ctypes.POINTER(QwGemvDesc), i64, vp]
@@ -178,6 +189,20 @@ def qw_quantize_pack_batched(count, descs, stream=None):
 def qw_unpack(bits, group, n, k, payload, scales, w_out, stream=None):
     return lib().qw_unpack(bits, group, n, k, _ptr(payload), _ptr(scales), _ptr(w_out),
                            _stream(stream))
+
+
+def make_unpack_descs(items):
+    """items: iterable of (bits, group, n, k, payload, scales, w_out); returns
+    a ctypes array for qw_unpack_batched and its length."""
+    items = list(items)
+    arr = (QwUnpackDesc * max(1, len(items)))()
+    for i, (bits, group, n, k, payload, scales, w_out) in enumerate(items):
+        arr[i] = QwUnpackDesc(_ptr(payload), _ptr(scales), _ptr(w_out), n, k, group, bits, 0)
+    return arr, len(items)
+
+
+def qw_unpack_batched(count, descs, stream=None):
+    return lib().qw_unpack_batched(count, descs, _stream(stream))
 
 
 def qw_gemv(bits, group, n, k, payload, scales, m, x, y, stream=None):
@@ -296,6 +321,23 @@ def quantize_pack_batched(ws, bits, group, stream=None):
                                  r["scales"]) for w, r in zip(ws, recs))
     _check(qw_quantize_pack_batched(cnt, arr, stream), "qw_quantize_pack_batched")
     return recs
+
+
+def unpack_batched(recs, outs=None, stream=None):
+    """Unpack a list of records in a few launches; returns fp32 tensors of
+    their shapes (or fills ``outs``)."""
+    if outs is None:
+        outs = [torch.empty(tuple(int(d) for d in r["shape"]), dtype=torch.float32,
+                            device=r["payload"].device) for r in recs]
+    items = []
+    for r, o in zip(recs, outs):
+        n, k = _nk(r["shape"])
+        if o.dtype != torch.float32 or not o.is_contiguous() or o.numel() != n * k:
+            raise ValueError("each output must be a contiguous float32 tensor of n*k elements")
+        items.append((r["bits"], r["group"], n, k, r["payload"], r["scales"], o))
+    arr, cnt = make_unpack_descs(items)
+    _check(qw_unpack_batched(cnt, arr, stream), "qw_unpack_batched")
+    return outs
 
 
 def unpack(rec, out=None, stream=None):

@@ -103,6 +103,24 @@ def test_chain_validation_before_any_launch():
     assert L.qw_gemv_chain(0, None, None, 1, None) == 0
 
 
+def test_unpack_batched_validation():
+    L = qw.lib()
+    fake = 1 << 20  # never dereferenced: every call below fails validation or is empty
+    arr, cnt = qw.make_unpack_descs([(4, 32, 64, 256, None, fake, fake)])
+    assert L.qw_unpack_batched(cnt, arr, None) == -5
+    arr, cnt = qw.make_unpack_descs([(4, 32, 64, 256, fake, fake, fake),
+                                     (4, 33, 64, 256, fake, fake, fake)])
+    assert L.qw_unpack_batched(cnt, arr, None) == -2        # nothing enqueued for the first
+    arr, cnt = qw.make_unpack_descs([(3, 32, 64, 256, fake, fake, fake)])
+    assert L.qw_unpack_batched(cnt, arr, None) == -1
+    arr[0].bits, arr[0].reserved = 4, 1
+    assert L.qw_unpack_batched(cnt, arr, None) == -7
+    assert L.qw_unpack_batched(-1, arr, None) == -7
+    assert L.qw_unpack_batched(0, None, None) == 0
+    arr, cnt = qw.make_unpack_descs([(4, 32, 0, 256, None, None, None)])
+    assert L.qw_unpack_batched(cnt, arr, None) == 0          # empty: nothing to do
+
+
 def test_matmul_work_size_and_validation():
     L = qw.lib()
     t = qw.MATMUL_GEMV_MAX_M

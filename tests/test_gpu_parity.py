@@ -471,6 +471,32 @@ def test_quantize_pack_batched_mixed():
         assert same_bits(host(rec["payload"]), ref["payload"])
 
 
+def test_unpack_batched_mixed():
+    # both bit widths; groups of a power-of-two and of another number of
+    # float4 vectors; a group the vector kernel does not take (6); an empty
+    # matrix; an output that is only 4-byte aligned (single-call path); and
+    # more matrices than one launch holds.  Every output bit-identical to the
+    # oracle's unpack.
+    nmany = qw.BATCH_PER_LAUNCH + 9
+    specs = [(4, 32, 16, 256)] * nmany + [(8, 128, 33, 512), (4, 4096, 4, 4096), (8, 6, 5, 12),
+                                          (4, 32, 0, 64), (4, 1024, 2, 2048), (8, 8, 3, 8),
+                                          (4, 12, 4, 24), (8, 20, 5, 40), (4, 64, 7, 64)]
+    refs, recs = [], []
+    for j, (bits, group, n, k) in enumerate(specs):
+        ref = oracle.quantize_pack(inputs.weight(800 + j, n, k, 0.05), bits, group)
+        refs.append(ref)
+        recs.append(dict(bits=bits, group=group, shape=[n, k], payload=dev(ref["payload"]),
+                         scales=dev(ref["scales"])))
+    outs = [torch.full((n, k), float("nan"), dtype=torch.float32, device="cuda")
+            for (_b, _g, n, k) in specs]
+    n_last, k_last = specs[-1][2], specs[-1][3]
+    buf = torch.full((n_last * k_last + 1,), float("nan"), dtype=torch.float32, device="cuda")
+    outs[-1] = buf[1:].view(n_last, k_last)          # 4-byte aligned only
+    qw.unpack_batched(recs, outs)
+    for ref, out in zip(refs, outs):
+        assert same_bits(host(out), oracle.unpack(ref).reshape(out.shape))
+
+
 def test_quantize_pack_batched_validation():
     arr, cnt = qw.make_quant_descs([(4, 32, 64, 256, None, None, None)])
     assert qw.qw_quantize_pack_batched(cnt, arr) == -5
