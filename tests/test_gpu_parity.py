@@ -390,9 +390,10 @@ def _rows_check(rec, w, bits, group, rows, x=None, y=None):
 
 
 def test_config4_layers_sampled():
-    # layers 0 and 31 of the 7B stack: per-matrix quantize, then the decode
+    # layers 0 and 31 of the 7B stack: batched quantize, then the decode
     # GEMVs as one batched call (the launch configuration of the benchmark)
-    # and as single calls; sampled rows against the oracle.
+    # and as single calls, and the batched unpack; sampled rows against the
+    # oracle.
     rng = np.random.default_rng(4)
     ws, xs = [], []
     for layer in (0, 31):
@@ -401,13 +402,17 @@ def test_config4_layers_sampled():
             xs.append(dev(inputs.c4_x(k)))
     recs = qw.quantize_pack_batched([dev(w) for w in ws], 4, 32)
     ys = [host(y) for y in qw.gemv_batched(recs, xs)]
-    for w, rec, x, y in zip(ws, recs, xs, ys):
+    # the batched unpack of the same matrices (also the benchmark's launch)
+    w_hats = [host(o) for o in qw.unpack_batched(recs)]
+    for w, rec, x, y, w_hat in zip(ws, recs, xs, ys, w_hats):
         n, k = w.shape
         rows = np.sort(rng.choice(n, size=96, replace=False))
         rows[0], rows[-1] = 0, n - 1
         _rows_check(rec, w, 4, 32, rows, host(x), y)
         y1 = host(qw.gemv(rec, x))
         _rows_check(rec, w, 4, 32, rows, host(x), y1)
+        ref_rows = oracle.unpack(oracle.quantize_pack(w[rows], 4, 32)).reshape(len(rows), k)
+        assert same_bits(w_hat.reshape(n, k)[rows], ref_rows)
 
 
 @pytest.mark.parametrize("m", [1, 3, 8])
