@@ -25,8 +25,8 @@ streams; its roofline is the fp64 MFMA accumulation of H for the
 1368-input map; the oracle runs the same layer on one core.  `--only-gptq`
 runs that leg alone (for profiling).
 
-Prints ONE JSON line.  `--gpus N` with N > 1 exits: this build runs on one
-GPU.
+Prints ONE JSON line.  `--gpus N` with N > 1 exits: the library and this
+benchmark run on one GPU.
 
 HBM traffic ("roofline.traffic"): two rocprofv3 counter runs of this script
 with `--calib-copy-mib 1024` (FETCH_SIZE, then WRITE_SIZE) are reduced by
@@ -290,7 +290,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
-              "the quantization path has no multi-GPU mode in this build", file=sys.stderr)
+              "the library has no multi-GPU mode", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

@@ -185,7 +185,7 @@ def test_bits_per_weight(golden_dir):
     # fp16 scale per 64 weights: the page's 4.25 bits
     assert f"{oracle.bits_per_weight(4, 64, scale_bytes=2):.2f}" == \
         g["printed"]["int4_bits_with_fp16_scale_per_64"]
-    # this build stores fp32 scales: 4 + 32/group
+    # the library stores fp32 scales: 4 + 32/group
     assert oracle.bits_per_weight(4, 128) == 4.25
     assert oracle.bits_per_weight(4, 32) == 5.0
     assert oracle.bits_per_weight(8, 4096) == 8 + 32 / 4096
