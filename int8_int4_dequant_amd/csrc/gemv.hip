@@ -143,6 +143,31 @@ __device__ __forceinline__ void decode4_int8(uint32_t w, float (&q)[4]) {
 
 // ------------------------------------------------------------------ kernels
 
+// A buffer resource over one payload row (raw addressing, `bytes` long:
+// reads past it return zero instead of leaving the row).  Loads through it
+// take a 32-bit byte offset and the resource in scalar registers, so they
+// need no per-lane 64-bit address arithmetic.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const uint8_t* row, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(row), (short)0, bytes,
+                                           0x00020000 /* 32-bit data format */);
+}
+
+// The PW payload dwords of one 8-code chunk at byte offset `off`
+// (non-temporal: each weight is read once).
+template <int PW>
+__device__ __forceinline__ void load_chunk(__amdgpu_buffer_rsrc_t rs, uint32_t off,
+                                           uint32_t (&p)[PW]) {
+  constexpr int kNT = 2;  // cache policy: non-temporal
+  if constexpr (PW == 1) {
+    p[0] = __builtin_amdgcn_raw_buffer_load_b32(rs, (int)off, 0, kNT);
+  } else {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, (int)off, 0, kNT);
+    p[0] = v.x;
+    p[1] = v.y;
+  }
+}
+
 // One matrix of a (possibly batched) call, validated on the host.
 struct GemvDesc {
   const uint8_t* payload;
@@ -221,12 +246,12 @@ __global__ __launch_bounds__(256) void gemv8_kernel(const GemvBatch<NB> b) {
   const int row0 = (item - ((KArg)__builtin_amdgcn_kernarg_segment_ptr())->item0[di]) * R;
   const int nch = a.k / 8;
 
-  const uint32_t* prow[R];
+  __amdgpu_buffer_rsrc_t prsrc[R];
   const float* srow[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int row = min(row0 + r, a.n - 1);
-    prow[r] = reinterpret_cast<const uint32_t*>(a.payload + (int64_t)row * a.row_stride_b);
+    prsrc[r] = row_rsrc(a.payload + (int64_t)row * a.row_stride_b, a.row_stride_b);
     srow[r] = a.scales + (a.per_row ? (int64_t)row * a.gpr : ((int64_t)row * a.k) / a.group);
   }
   float acc[V];
@@ -245,18 +270,21 @@ __global__ __launch_bounds__(256) void gemv8_kernel(const GemvBatch<NB> b) {
     step_r = 64u - step_g * cpg;
   }
   for (int c = lane; c < nch; c += 64) {
+    // 32-bit byte offsets from the wave-uniform row bases: the loads then
+    // take a scalar base and a 32-bit offset, with no 64-bit address add
+    const uint32_t poff = (uint32_t)c * (4u * PW), soff = gc * 4u, xoff = (uint32_t)c * 32u;
     uint32_t p[R][PW];
     float s[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-#pragma unroll
-      for (int i = 0; i < PW; ++i) p[r][i] = __builtin_nontemporal_load(prow[r] + PW * c + i);
-      s[r] = srow[r][gc];
+      load_chunk<PW>(prsrc[r], poff, p[r]);
+      s[r] = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(srow[r]) + soff);
     }
     float xv[M][8];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      const float4* xp = reinterpret_cast<const float4*>(a.x + (int64_t)m * a.k) + 2 * c;
+      const float4* xp = reinterpret_cast<const float4*>(
+          reinterpret_cast<const uint8_t*>(a.x + (int64_t)m * a.k) + xoff);
       const float4 x0 = xp[0], x1 = xp[1];
       xv[m][0] = x0.x; xv[m][1] = x0.y; xv[m][2] = x0.z; xv[m][3] = x0.w;
       xv[m][4] = x1.x; xv[m][5] = x1.y; xv[m][6] = x1.z; xv[m][7] = x1.w;
@@ -328,12 +356,12 @@ __global__ __launch_bounds__(256) void gemv8_split_kernel(const GemvBatch<NB> b)
   const int cbeg = wave * q;
   const int cend = min(nch, cbeg + q);
 
-  const uint32_t* prow[R];
+  __amdgpu_buffer_rsrc_t prsrc[R];
   const float* srow[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     const int row = min(row0 + r, a.n - 1);
-    prow[r] = reinterpret_cast<const uint32_t*>(a.payload + (int64_t)row * a.row_stride_b);
+    prsrc[r] = row_rsrc(a.payload + (int64_t)row * a.row_stride_b, a.row_stride_b);
     srow[r] = a.scales + (a.per_row ? (int64_t)row * a.gpr : ((int64_t)row * a.k) / a.group);
   }
   float acc[V];
@@ -350,18 +378,19 @@ __global__ __launch_bounds__(256) void gemv8_split_kernel(const GemvBatch<NB> b)
     step_r = 64u - step_g * cpg;
   }
   for (int c = cbeg + lane; c < cend; c += 64) {
+    const uint32_t poff = (uint32_t)c * (4u * PW), soff = gc * 4u, xoff = (uint32_t)c * 32u;
     uint32_t p[R][PW];
     float s[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-#pragma unroll
-      for (int i = 0; i < PW; ++i) p[r][i] = __builtin_nontemporal_load(prow[r] + PW * c + i);
-      s[r] = srow[r][gc];
+      load_chunk<PW>(prsrc[r], poff, p[r]);
+      s[r] = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(srow[r]) + soff);
     }
     float xv[M][8];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      const float4* xp = reinterpret_cast<const float4*>(a.x + (int64_t)m * a.k) + 2 * c;
+      const float4* xp = reinterpret_cast<const float4*>(
+          reinterpret_cast<const uint8_t*>(a.x + (int64_t)m * a.k) + xoff);
       const float4 x0 = xp[0], x1 = xp[1];
       xv[m][0] = x0.x; xv[m][1] = x0.y; xv[m][2] = x0.z; xv[m][3] = x0.w;
       xv[m][4] = x1.x; xv[m][5] = x1.y; xv[m][6] = x1.z; xv[m][7] = x1.w;
