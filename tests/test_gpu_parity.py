@@ -415,6 +415,43 @@ def test_config4_layers_sampled():
         assert same_bits(w_hat.reshape(n, k)[rows], ref_rows)
 
 
+@pytest.mark.parametrize("bits", [4, 8])
+def test_matrix_beyond_32bit_indexing(bits):
+    """One matrix of 65,537 x 32,768 = 2^31 + 32,768 weights (at int8 also
+    more than 2^31 payload bytes), drawn on the GPU from a seeded generator:
+    quantize, unpack, GEMV (m = 1) and GEMM (m = 16) through the C ABI,
+    checked against the oracle on rows at both ends and in the middle, so
+    every element index and byte offset past 2^31 is exercised."""
+    n, k, group = 65537, 32768, 128
+    print("beyond-2^31 matrix", bits, flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(77 + bits)
+    w = torch.randn((n, k), dtype=torch.float32, device="cuda", generator=gen) * 0.02
+    rec = qw.quantize_pack(w, bits, group)
+    rows = np.array([0, 1, n // 2, n - 4, n - 3, n - 2, n - 1])
+    w_rows = host(w[torch.from_numpy(rows).cuda()])
+    ref = oracle.quantize_pack(w_rows, bits, group)
+    pb = k * bits // 8
+    assert same_bits(host(rec["payload"].view(n, pb)[torch.from_numpy(rows).cuda()]).reshape(-1),
+                     ref["payload"])
+    assert same_bits(host(rec["scales"].view(n, k // group)[torch.from_numpy(rows).cuda()])
+                     .reshape(-1), ref["scales"])
+    # unpack of the whole matrix, sampled rows
+    w_hat = qw.unpack(rec)
+    assert same_bits(host(w_hat[torch.from_numpy(rows).cuda()]),
+                     oracle.unpack(ref).reshape(len(rows), k))
+    del w_hat, w
+    torch.cuda.empty_cache()
+    # GEMV and GEMM outputs of the sampled rows
+    x = inputs.activations([77, bits], 1, k)
+    y = host(qw.gemv(rec, dev(x)))[:, rows]
+    B = oracle.error_base(ref, x)
+    assert np.all(np.abs(y - oracle.gemv_ref(ref, x)) <= GEMV_TOL * B)
+    xb = inputs.bf16_activations([78, bits], 16, k)
+    yg = host(qw.gemm(rec, dev(xb.view(np.int16))))[:, rows]
+    Bg = oracle.error_base(ref, oracle.bf16_bits_to_f32(xb))
+    assert np.all(np.abs(yg - oracle.gemm_ref(ref, xb)) <= GEMM_TOL * Bg)
+
+
 @pytest.mark.parametrize("m", [1, 3, 8])
 def test_gemv_batched_mixed(m):
     # mixed bit widths, groups, shapes, a generic-path matrix, an empty one
