@@ -3,9 +3,10 @@
 A step is one pass of the whole path over the 7B-shaped linear stack (32
 layers x q, k, v, o, gate, up, down = 224 matrices, 6,476,005,376 fp32
 weights resident in HBM): quantize and pack every matrix to int4 with group
-32 (qw_quantize_pack), then one M = 1 dequantizing GEMV through every matrix
-(qw_gemv, which unpacks the codes in registers).  `value` is the step's
-algorithmic HBM bytes divided by the step time.
+32 (qw_quantize_pack_batched, all 224 matrices in one launch), then one M = 1
+dequantizing GEMV through every matrix (qw_gemv_batched, one launch, the
+codes unpacked in registers).  `value` is the step's algorithmic HBM bytes
+divided by the step time.
 
 In the same run the single-matrix decode GEMVs (4096 x 4096 int8 with one
 scale per output channel at M = 1; the 7B MLP up and down matrices at int4
@@ -40,6 +41,7 @@ otherwise).
 import argparse
 import json
 import os
+import statistics
 import subprocess
 import sys
 import time
@@ -393,6 +395,15 @@ def main():
     g_ms = sum(evs[s][2][0].elapsed_time(evs[s][3][0]) for s in range(args.steps))
     q_avg_us = 1e3 * q_ms / (args.steps * quant_launches)
     g_avg_us = 1e3 * g_ms / (args.steps * gemv_launches)
+    # per-step spread (GPU time between the events of each step)
+    def med_p90_us(pairs):
+        t = sorted(1e3 * e0.elapsed_time(e1) for e0, e1 in pairs)
+        return {"median_us": round(statistics.median(t), 1),
+                "p90_us": round(t[int(0.9 * (len(t) - 1))], 1)}
+
+    q_spread = med_p90_us([(evs[s][0][0], evs[s][1][0]) for s in range(args.steps)])
+    g_spread = med_p90_us([(evs[s][2][0], evs[s][3][0]) for s in range(args.steps)])
+    step_spread = med_p90_us([(evs[s][0][0], evs[s][3][0]) for s in range(args.steps)])
 
     # for comparison (not part of the step): the same passes as one launch per matrix
     def timed(fn):
@@ -488,7 +499,7 @@ def main():
         "quantize_pack": {"GB/s": round(q_gbs, 1), "frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4),
                           "entry": "qw_quantize_pack_batched", "launches_per_pass": quant_launches,
                           "avg_launch_us": round(q_avg_us, 3), "bytes_per_step": qbytes,
-                          "pass_us": round(1e3 * q_ms / args.steps, 1)},
+                          "pass_us": round(1e3 * q_ms / args.steps, 1), **q_spread},
         "quantize_pack_one_launch_per_matrix": {
             "pass_us": round(single_q_us, 1),
             "GB/s": round(qbytes / (single_q_us * 1e-6) / 1e9, 1)},
@@ -496,7 +507,8 @@ def main():
                            "entry": "qw_gemv_batched", "launches_per_pass": gemv_launches,
                            "avg_launch_us": round(g_avg_us, 3), "bytes_per_step": gbytes,
                            "traffic_per_launch": measured_traffic("gemv_batched_m1"),
-                           "pass_us": round(1e3 * g_ms / args.steps, 1)},
+                           "pass_us": round(1e3 * g_ms / args.steps, 1), **g_spread},
+        "step": {"entries": "qw_quantize_pack_batched then qw_gemv_batched", **step_spread},
         "unpack": {"GB/s": round(ubytes / (unpack_us * 1e-6) / 1e9, 1),
                    "frac_hbm": round(ubytes / (unpack_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                    "entry": "qw_unpack_batched", "launches_per_pass": 1,
