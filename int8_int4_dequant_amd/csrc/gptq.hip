@@ -312,8 +312,33 @@ int64_t hessian_tile(int64_t k, int64_t t) {
   return tiles * hessian_splits_for(k, t, 128) * 5 >= kHessRound * 4 ? 128 : 64;
 }
 
+// Tokens per partial sum.  s equal chunks fill s * tiles slots of the round.
+// When the slots left over can take at least half the tiles once more, the
+// tokens are cut into s full chunks and a short last one instead: the short
+// chunks' work-groups that find a free slot at the start finish early, the
+// others take the slots they free, and all are done when the full chunks
+// are, so the round lasts as long as a chunk of 2t / (2s + 1) tokens rather
+// than t / s (the 1368-input map over 8192 tokens: 66 tiles, 8 chunks of at
+// most 1093 tokens instead of 7 of 1171).
+int64_t hessian_chunk(int64_t k, int64_t t) {
+  const int64_t tile = hessian_tile(k, t);
+  const int64_t tm = (k + tile - 1) / tile;
+  const int64_t tiles = tm * (tm + 1) / 2;
+  const int64_t s = hessian_splits_for(k, t, tile);
+  int64_t chunk = (t + s - 1) / s;
+  const int64_t spare = kHessRound - s * tiles;
+  // only when the round, not the chunk floor, set s
+  if (s == kHessRound / tiles && spare > 0 && tiles <= 2 * spare) {
+    const int64_t c = (2 * t + 2 * s) / (2 * s + 1);  // ceil(2t / (2s + 1))
+    if (c >= kHessMinChunk && (t + c - 1) / c == s + 1) chunk = c;
+  }
+  return chunk < 1 ? 1 : chunk;
+}
+
+// Partial sums (chunks) of one call.
 int64_t hessian_splits(int64_t k, int64_t t) {
-  return hessian_splits_for(k, t, hessian_tile(k, t));
+  const int64_t chunk = hessian_chunk(k, t);
+  return t > 0 ? (t + chunk - 1) / chunk : 1;
 }
 
 // h[i][j] += sum_s part[s][max][min]: 32x32 tiles of the lower triangle,
@@ -651,8 +676,7 @@ int64_t gptq_hessian_work_bytes(int64_t k, int64_t t) {
 
 hipError_t launch_gptq_hessian(int64_t k, int64_t t, const float* x, double* h, void* work,
                                hipStream_t stream) {
-  const int64_t splits = hessian_splits(k, t);
-  const int64_t chunk = (t + splits - 1) / splits;
+  const int64_t chunk = hessian_chunk(k, t);
   double* part = (double*)work;
   // part[s] = X_s^T X_s with X_s the tokens [s*chunk, (s+1)*chunk)
   G64 g = g64(x, 1, k, x, k, 1, part, k, 1, k, k, chunk, 1.0, 0.0);

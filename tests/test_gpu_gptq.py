@@ -44,8 +44,9 @@ def _say(*a):
 # ----------------------------------------------------------------- H
 
 
+# (1368, 2048): the tokens cut into 7 full chunks and a short eighth
 @pytest.mark.parametrize("k,t", [(1, 7), (64, 64), (65, 3000), (130, 255), (200, 1000),
-                                 (512, 4096)])
+                                 (512, 4096), (1368, 2048)])
 def test_hessian_parity(k, t):
     _say("gptq_hessian", k, t)
     x0 = inputs.calibration_activations([8, 1, k], 33, k)
