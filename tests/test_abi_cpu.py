@@ -149,6 +149,13 @@ def test_gptq_work_sizes():
     assert L.qw_gptq_hessian_work_bytes(512, 8192) > 0
     # the partial sums cover whole k x k matrices, one per token chunk
     assert L.qw_gptq_hessian_work_bytes(512, 8192) % (512 * 512 * 8) == 0
+    # one partial sum per token chunk: 14 chunks for 36 64-wide tiles at k = 512
+    # (504 of the 512 work-group slots); at k = 1368, 66 128-wide tiles take
+    # 7 full chunks and a short eighth (528 work-groups)
+    assert L.qw_gptq_hessian_work_bytes(512, 8192) == 14 * 512 * 512 * 8
+    assert L.qw_gptq_hessian_work_bytes(1368, 8192) == 8 * 1368 * 1368 * 8
+    # few tokens: chunks of at least 256 tokens
+    assert L.qw_gptq_hessian_work_bytes(200, 1000) == 3 * 200 * 200 * 8
     kp = 1408  # 1368 rounded up to the 64-wide blocks of the factorization
     assert L.qw_gptq_factor_work_bytes(1368) >= 2 * kp * kp * 8
     assert L.qw_gptq_factor_work_bytes(-3) == -1
