@@ -58,6 +58,91 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+class ClockSampler:
+    """Samples the GPU's graphics clock (each XCD's current value, averaged)
+    and its socket power through amdsmi in a background thread, and reports
+    their medians over the samples taken after the first `skip_s` seconds.
+    The device refreshes these figures every few tens of milliseconds, so
+    they describe a sustained load, not a single short kernel.  Reports None
+    where amdsmi is missing or returns nothing."""
+
+    def __init__(self, enabled=True, interval_s=0.005, skip_s=0.4):
+        self.enabled, self.interval, self.skip = enabled, interval_s, skip_s
+        self.samples = []   # (seconds since start, MHz or None, W or None)
+        self._stop = None
+
+    def __enter__(self):
+        if not self.enabled:
+            return self
+        try:
+            import threading
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self._smi = amdsmi
+            self._h = amdsmi.amdsmi_get_processor_handles()[0]
+        except Exception as exc:  # no amdsmi, no device: no clock figure
+            log(f"clock sampling off: {exc}")
+            self.enabled = False
+            return self
+        self._stop = threading.Event()
+        t0 = time.perf_counter()
+
+        def run():
+            while not self._stop.is_set():
+                try:
+                    m = self._smi.amdsmi_get_gpu_metrics_info(self._h)
+                    clks = [c for c in m.get("current_gfxclks", [])
+                            if isinstance(c, int) and 0 < c < 65535]
+                    pw = m.get("current_socket_power")
+                    self.samples.append((time.perf_counter() - t0,
+                                         sum(clks) / len(clks) if clks else None,
+                                         pw if isinstance(pw, (int, float)) else None))
+                except Exception:
+                    pass
+                self._stop.wait(self.interval)
+
+        self._t = threading.Thread(target=run, daemon=True)
+        self._t.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._stop is not None:
+            self._stop.set()
+            self._t.join()
+            try:
+                self._smi.amdsmi_shut_down()
+            except Exception:
+                pass
+        return False
+
+    def summary(self):
+        kept = [(c, w) for t, c, w in self.samples if t >= self.skip]
+        c = [v for v, _ in kept if v is not None]
+        w = [v for _, v in kept if v is not None]
+        if not c:
+            return None
+        return {"gfx_mhz_median": round(statistics.median(c)), "gfx_mhz_min": round(min(c)),
+                "gfx_mhz_max": round(max(c)),
+                "socket_w_median": round(statistics.median(w)) if w else None,
+                "samples": len(c),
+                "source": "amdsmi current_gfxclks (mean over XCDs) and current_socket_power"}
+
+
+def sustained_clock(args, fn, seconds=3.0):
+    """Clock and power while `fn` (one enqueue of the timed work) runs back to
+    back for `seconds`, after the timed region and outside it."""
+    import torch
+    if args.no_clock:
+        return None
+    with ClockSampler(skip_s=1.5) as c:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            for _ in range(4):
+                fn()
+            torch.cuda.synchronize()
+    return c.summary()
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -76,6 +161,8 @@ def parse():
     ap.add_argument("--only-gptq", action="store_true",
                     help="run only the GPTQ leg and print its JSON object (for profiling)")
     ap.add_argument("--gptq-reps", type=int, default=3)
+    ap.add_argument("--no-clock", action="store_true",
+                    help="do not sample the GPU clock and power during the timed regions")
     ap.add_argument("--cpu-sample-worker", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--gptq-cpu-sample-worker", action="store_true", help=argparse.SUPPRESS)
     return ap.parse_args()
@@ -390,6 +477,8 @@ def main():
         run_step(evs[s])
     torch.cuda.synchronize()
     t_total = time.perf_counter() - t_start
+    # the clock the step runs at (a sustained run after the timed one)
+    step_clock = sustained_clock(args, run_step)
 
     q_ms = sum(evs[s][0][0].elapsed_time(evs[s][1][0]) for s in range(args.steps))
     g_ms = sum(evs[s][2][0].elapsed_time(evs[s][3][0]) for s in range(args.steps))
@@ -508,7 +597,8 @@ def main():
                            "avg_launch_us": round(g_avg_us, 3), "bytes_per_step": gbytes,
                            "traffic_per_launch": measured_traffic("gemv_batched_m1"),
                            "pass_us": round(1e3 * g_ms / args.steps, 1), **g_spread},
-        "step": {"entries": "qw_quantize_pack_batched then qw_gemv_batched", **step_spread},
+        "step": {"entries": "qw_quantize_pack_batched then qw_gemv_batched", **step_spread,
+                 "gpu_clock_sustained": step_clock},
         "unpack": {"GB/s": round(ubytes / (unpack_us * 1e-6) / 1e9, 1),
                    "frac_hbm": round(ubytes / (unpack_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                    "entry": "qw_unpack_batched", "launches_per_pass": 1,
@@ -762,6 +852,7 @@ def bench_gemm(args, L, stream):
         b.record(stream)
     torch.cuda.synchronize()
     times = sorted(a.elapsed_time(b) for a, b in ev)
+    clock = sustained_clock(args, run)
     med = times[len(times) // 2]
     flops = 2.0 * m * n * k
 
@@ -820,11 +911,17 @@ def bench_gemm(args, L, stream):
     log("qw_matmul against m: " + ", ".join(f"m={k_}: {r_['matmul_us']:.0f} us"
                                            for k_, r_ in sweep.items()))
     tf = flops / (med * 1e-3) / 1e12
-    log(f"gemm: median {med * 1e3:.1f} us, {tf:.1f} TFLOP/s ({tf / BF16_PEAK_TFLOPS:.1%} of bf16 peak)")
+    if clock is not None:
+        # the dense bf16 peak scales with the clock (2.5 PFLOP/s at 2.4 GHz)
+        clock["bf16_peak_tflops_at_median_clock"] = round(
+            BF16_PEAK_TFLOPS * clock["gfx_mhz_median"] / 2400.0, 1)
+    log(f"gemm: median {med * 1e3:.1f} us, {tf:.1f} TFLOP/s ({tf / BF16_PEAK_TFLOPS:.1%} of bf16 peak)"
+        + ("" if clock is None else f"; clock {clock['gfx_mhz_median']} MHz, "
+           f"{clock['socket_w_median']} W ({clock['samples']} samples)"))
     return {"workload": "c5: M=2048 bf16 x (28672 x 8192) int4 group 128, fp32 accumulate",
             "m_sweep_same_weight": sweep,
             "median_us": round(med * 1e3, 2), "p90_us": round(times[int(0.9 * (len(times) - 1))] * 1e3, 2),
-            "TFLOP/s": round(tf, 2),
+            "TFLOP/s": round(tf, 2), "gpu_clock_sustained": clock,
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic("gemm"),

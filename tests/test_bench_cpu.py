@@ -88,3 +88,28 @@ def test_traffic_is_withdrawn_when_the_source_changes(tmp_path, monkeypatch):
     # a missing or unreadable summary gives null, not an error
     monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "absent.md"))
     assert bench.measured_traffic("quantize_pack_batched") is None
+
+
+def test_clock_sampler_reports_nothing_without_a_gpu():
+    # switched off, or with no device to read, the sampler yields no figure
+    # and does not raise; the timed region runs the same either way
+    with bench.ClockSampler(enabled=False) as off:
+        pass
+    assert off.summary() is None
+    with bench.ClockSampler() as c:
+        pass
+    if not c.enabled:
+        assert c.summary() is None
+
+
+def test_clock_summary_medians():
+    # samples of the first skip_s seconds (the ramp, and figures the device
+    # has not refreshed yet) are left out
+    c = bench.ClockSampler(enabled=False, skip_s=0.4)
+    c.samples = [(0.1, 700.0, 300), (0.39, 2400.0, 300),
+                 (0.5, 1800.0, 1300), (0.6, 2000.0, 1400), (0.7, None, None), (0.8, 1900.0, None)]
+    s = c.summary()
+    assert s["gfx_mhz_median"] == 1900 and s["gfx_mhz_min"] == 1800 and s["gfx_mhz_max"] == 2000
+    assert s["socket_w_median"] == 1350 and s["samples"] == 3
+    c.samples = c.samples[:2]
+    assert c.summary() is None
