@@ -69,6 +69,10 @@ struct GemmArgs {
   // rest), which add their partial sums into Y (zeroed beforehand).
   int full_tiles;
   int nk_lo;
+  // Small-M kernel: codes per scale along a row when that is a multiple of
+  // the k-step (a k-step then inside one group, so a step that does not start
+  // a group reuses the previous step's scales); 0 = load them every step.
+  int64_t scale_period;
 };
 
 // Tile index -> (tile row, tile column).  With the XCD-aware order, tiles
@@ -455,17 +459,36 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
   // last k-step a load may touch (idle waves, ks0 == nk, still issue the prologue loads)
   const int klast = min(nk - 1, max(ks0, ks1 - 1)) * BK;
 
+  // Scales: a k-step that starts no group (inside one scale period) keeps the
+  // scales of the step before, so only steps that start a group load them.
+  // kin_load / kin_use: position inside the period of the next step loaded /
+  // dequantized (wave-uniform; both advance one k-step per call, in order).
+  const int64_t kin0 = a.scale_period > 0 ? ((int64_t)ks0 * BK) % a.scale_period : 0;
+  int64_t kin_load = kin0, kin_use = kin0;
+  bool first_load = true, first_use = true;
+  float s_cur[NBW];
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb) s_cur[nb] = 0.0f;
+  auto advance = [&](int64_t& kin) __attribute__((always_inline)) {
+    if (a.scale_period > 0) {
+      kin += BK;
+      if (kin >= a.scale_period) kin -= a.scale_period;
+    }
+  };
   auto load_w = [&](BRegs<BITS> (&br)[NBW], int k0) __attribute__((always_inline)) {
     k0 = k0 < klast ? k0 : klast;
     const uint32_t kk = (uint32_t)(k0 + 32 * g);
     const uint32_t t = __umulhi(kk, a.gdiv_mul);
     const uint32_t gi = ((t + ((kk - t) >> 1)) >> (a.gdiv_shift - 1)) & a.gmask;
+    const bool need_s = a.scale_period == 0 || kin_load == 0 || first_load;
+    first_load = false;
+    advance(kin_load);
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
       const uint8_t* src = prow[nb] + (int64_t)k0 * BITS / 8;
       br[nb].p[0] = *reinterpret_cast<const u32x4*>(src);
       if constexpr (BITS == 8) br[nb].p[1] = *reinterpret_cast<const u32x4*>(src + 16);
-      br[nb].s = srow[nb][gi];
+      if (need_s) br[nb].s = srow[nb][gi];
     }
   };
   auto load_a = [&](u32x4 (&af)[MB][4], int k0) __attribute__((always_inline)) {
@@ -475,8 +498,8 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) af[mb][s] = *reinterpret_cast<const u32x4*>(xrow[mb] + k0 + 8 * s);
   };
-  auto dequant = [&](const BRegs<BITS>& br, u32x4 (&bq)[4]) __attribute__((always_inline)) {
-    const float sc = br.s;
+  auto dequant = [&](const BRegs<BITS>& br, float sc, u32x4 (&bq)[4])
+      __attribute__((always_inline)) {
     if constexpr (BITS == 4) {
       const u32x4 p = br.p[0];
       bq[0] = dequant8_int4(p.x, sc);
@@ -508,9 +531,16 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
   load_a(afE, ks0 * BK);
   auto kstep = [&](int ks, BRegs<BITS> (&br)[NBW], const u32x4 (&af)[MB][4],
                    u32x4 (&af_nxt)[MB][4]) __attribute__((always_inline)) {
+    // this step's scales: loaded with its codes when it starts a group
+    const bool new_s = a.scale_period == 0 || kin_use == 0 || first_use;
+    first_use = false;
+    advance(kin_use);
     u32x4 bq[NBW][4];
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) dequant(br[nb], bq[nb]);
+    for (int nb = 0; nb < NBW; ++nb) {
+      if (new_s) s_cur[nb] = br[nb].s;
+      dequant(br[nb], s_cur[nb], bq[nb]);
+    }
     load_w(br, (ks + 2) * BK);
     load_a(af_nxt, (ks + 1) * BK);
 #pragma unroll
@@ -664,6 +694,8 @@ hipError_t launch_gemm(const Mat& mt, const uint8_t* payload, const float* scale
       a.gdiv_shift = 1;
       a.gmask = 0;
     }
+    // one scale per `group` codes along a row (per-row groups), or per row
+    a.scale_period = a.per_row_groups ? (mt.group % BK == 0 ? mt.group : 0) : mt.k;
     if (m <= kSmallMaxM) {
       // few rows: the small-M kernel, tile 32 x 32*NBW, K split over the block's waves
       const int cus = compute_units();
