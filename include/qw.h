@@ -49,9 +49,14 @@
  *   - Empty work (n*k == 0, or m == 0) is valid and enqueues nothing, except
  *     that a product with k == 0 writes zeros to y.  Pointers may then be
  *     NULL.
- *   - Errors are returned as negative status codes and never abort; on error
- *     nothing is enqueued (QW_EHIP: a launch failed; its HIP error text is
- *     available from qw_last_error()).
+ *   - Errors are returned as negative status codes and never abort.  Every
+ *     argument is validated before anything is enqueued, so a call that
+ *     returns a validation error (any status but QW_EHIP) has enqueued
+ *     nothing.  QW_EHIP means a kernel launch failed (its HIP error text is
+ *     available from qw_last_error()); a call that makes several launches
+ *     (the batched and chained calls, qw_gemm with a split tail, qw_matmul,
+ *     the GPTQ calls) may already have enqueued the launches before the
+ *     failing one, and its outputs are then undefined.
  */
 #ifndef QW_H
 #define QW_H

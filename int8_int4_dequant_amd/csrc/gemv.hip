@@ -641,22 +641,6 @@ hipError_t launch_gemv_batched(const Mat* mts, const uint8_t* const* payloads,
   return hipSuccess;
 }
 
-hipError_t launch_gemv_chain(const Mat* mts, const uint8_t* const* payloads,
-                             const float* const* scales, int m, const float* const* xs,
-                             float* const* ys, const int* stage, int count, hipStream_t st) {
-  // each stage is exactly the batched call over its matrices, enqueued in
-  // stage order on one stream
-  for (int i0 = 0; i0 < count;) {
-    int i1 = i0 + 1;
-    while (i1 < count && stage[i1] == stage[i0]) ++i1;
-    hipError_t e = launch_gemv_batched(mts + i0, payloads + i0, scales + i0, m, xs + i0, ys + i0,
-                                       i1 - i0, st);
-    if (e != hipSuccess) return e;
-    i0 = i1;
-  }
-  return hipSuccess;
-}
-
 __global__ void fill_zero_kernel(float* y, int64_t count) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < count) y[i] = 0.0f;

@@ -237,35 +237,46 @@ int qw_gemv_chain(int count, const qw_gemv_desc* descs, const int32_t* stage, in
     if (d.k > 0 && (!d.payload || !d.scales || !d.x)) return QW_ENULL;
   }
   if (m == 0) return QW_OK;
-  // every product keeps its place in its stage; products with n == 0 have
-  // nothing to do, products with k == 0 write zeros (launched first: their
-  // y may still be read by a later stage only after the fill)
+  // Stage by stage, in order: the zero fills of the stage's products with
+  // k == 0, then one batched launch over its other products.  A y filled
+  // here is read only by later stages, which are enqueued after it.
   std::vector<qw::Mat> mts;
   std::vector<const uint8_t*> ps;
   std::vector<const float*> ss, xs;
   std::vector<float*> ys;
-  std::vector<int> stg;
-  for (int i = 0; i < count; ++i) {
-    const qw_gemv_desc& d = descs[i];
-    if (d.n == 0) continue;
-    if (d.k == 0) {
-      int st = record(qw::launch_fill_zero(d.y, m * d.n, (hipStream_t)stream));
-      if (st != QW_OK) return st;
-      continue;
+  for (int i0 = 0; i0 < count;) {
+    int i1 = i0 + 1;
+    while (i1 < count && stage[i1] == stage[i0]) ++i1;
+    mts.clear();
+    ps.clear();
+    ss.clear();
+    xs.clear();
+    ys.clear();
+    for (int i = i0; i < i1; ++i) {
+      const qw_gemv_desc& d = descs[i];
+      if (d.n == 0) continue;
+      if (d.k == 0) {
+        int st = record(qw::launch_fill_zero(d.y, m * d.n, (hipStream_t)stream));
+        if (st != QW_OK) return st;
+        continue;
+      }
+      qw::Mat mt;
+      check_mat(d.bits, d.group, d.n, d.k, &mt);
+      mts.push_back(mt);
+      ps.push_back(d.payload);
+      ss.push_back(d.scales);
+      xs.push_back(d.x);
+      ys.push_back(d.y);
     }
-    qw::Mat mt;
-    check_mat(d.bits, d.group, d.n, d.k, &mt);
-    mts.push_back(mt);
-    ps.push_back(d.payload);
-    ss.push_back(d.scales);
-    xs.push_back(d.x);
-    ys.push_back(d.y);
-    stg.push_back(stage[i]);
+    if (!mts.empty()) {
+      int st = record(qw::launch_gemv_batched(mts.data(), ps.data(), ss.data(), (int)m,
+                                              xs.data(), ys.data(), (int)mts.size(),
+                                              (hipStream_t)stream));
+      if (st != QW_OK) return st;
+    }
+    i0 = i1;
   }
-  if (mts.empty()) return QW_OK;
-  return record(qw::launch_gemv_chain(mts.data(), ps.data(), ss.data(), (int)m, xs.data(),
-                                      ys.data(), stg.data(), (int)mts.size(),
-                                      (hipStream_t)stream));
+  return QW_OK;
 }
 
 int qw_gemm(int bits, int64_t group, int64_t n, int64_t k, const uint8_t* payload,

@@ -39,11 +39,6 @@ hipError_t launch_gemv(const Mat& mt, const uint8_t* payload, const float* scale
 hipError_t launch_gemv_batched(const Mat* mts, const uint8_t* const* payloads,
                                const float* const* scales, int m, const float* const* xs,
                                float* const* ys, int count, hipStream_t stream);
-// `stage[i]` nondecreasing; matrices of one stage are independent, later
-// stages may read earlier stages' outputs; one launch per stage.
-hipError_t launch_gemv_chain(const Mat* mts, const uint8_t* const* payloads,
-                             const float* const* scales, int m, const float* const* xs,
-                             float* const* ys, const int* stage, int count, hipStream_t stream);
 hipError_t launch_gemm(const Mat& mt, const uint8_t* payload, const float* scales,
                        int64_t m, const uint16_t* x, float* y, hipStream_t stream);
 hipError_t launch_fill_zero(float* y, int64_t count, hipStream_t stream);

@@ -287,6 +287,48 @@ def _nk(shape):
     return int(shape[0]), int(shape[1])
 
 
+def _check_tensor(t, dtype, numel, what, shape=None):
+    """A tensor the kernels read or write: of `dtype`, contiguous, holding
+    exactly `numel` elements (of `shape` when given).  The C ABI takes bare
+    pointers and cannot see sizes, so a buffer that is too small would be read
+    or written past its end on the device.  (``_on_device`` checks where the
+    tensors live once all sizes have been checked.)"""
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{what} must be a torch tensor")
+    if t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise ValueError(f"{what} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{what} holds {t.numel()} elements, expected {numel}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _on_device(*ts):
+    """Every non-empty tensor the call passes must be a device tensor."""
+    for t in ts:
+        if isinstance(t, dict):
+            _on_device(t["payload"], t["scales"])
+        elif isinstance(t, torch.Tensor) and t.numel() and not t.is_cuda:
+            raise ValueError("libqw takes device tensors; a host tensor was passed")
+
+
+def _check_rec(rec, what="record"):
+    """(n, k) of a record whose payload and scales match its bits, group and
+    shape (qw_payload_bytes / qw_num_scales)."""
+    n, k = _nk(rec["shape"])
+    bits, group = int(rec["bits"]), int(rec["group"])
+    nb = lib().qw_payload_bytes(bits, n, k)
+    ns = lib().qw_num_scales(group, n, k)
+    if nb < 0 or ns < 0:
+        raise ValueError(f"{what}: invalid bits {bits}, group {group} or shape {[n, k]}")
+    _check_tensor(rec["payload"], torch.uint8, nb, f"{what} payload")
+    _check_tensor(rec["scales"], torch.float32, ns, f"{what} scales")
+    return n, k
+
+
 def quantize_pack(w, bits, group, stream=None):
     """Quantize a contiguous fp32 device tensor [n][k]; returns a record
     ``{bits, group, shape, payload (uint8), scales (float32)}``."""
@@ -329,21 +371,25 @@ def unpack_batched(recs, outs=None, stream=None):
     if outs is None:
         outs = [torch.empty(tuple(int(d) for d in r["shape"]), dtype=torch.float32,
                             device=r["payload"].device) for r in recs]
+    if len(outs) != len(recs):
+        raise ValueError("one output per record")
     items = []
     for r, o in zip(recs, outs):
-        n, k = _nk(r["shape"])
-        if o.dtype != torch.float32 or not o.is_contiguous() or o.numel() != n * k:
-            raise ValueError("each output must be a contiguous float32 tensor of n*k elements")
+        n, k = _check_rec(r)
+        _check_tensor(o, torch.float32, n * k, "output")
         items.append((r["bits"], r["group"], n, k, r["payload"], r["scales"], o))
+    _on_device(*recs, *outs)
     arr, cnt = make_unpack_descs(items)
     _check(qw_unpack_batched(cnt, arr, stream), "qw_unpack_batched")
     return outs
 
 
 def unpack(rec, out=None, stream=None):
-    n, k = _nk(rec["shape"])
+    n, k = _check_rec(rec)
     if out is None:
         out = torch.empty((n, k), dtype=torch.float32, device=rec["payload"].device)
+    _check_tensor(out, torch.float32, n * k, "out")
+    _on_device(rec, out)
     _check(qw_unpack(rec["bits"], rec["group"], n, k, rec["payload"], rec["scales"], out,
                      stream), "qw_unpack")
     return out
@@ -351,12 +397,15 @@ def unpack(rec, out=None, stream=None):
 
 def gemv(rec, x, out=None, stream=None):
     """fp32 x [m][k] (m <= 8) times the quantized weight; returns y [m][n]."""
-    n, k = _nk(rec["shape"])
-    if x.dtype != torch.float32 or not x.is_contiguous() or x.dim() != 2 or x.shape[1] != k:
+    n, k = _check_rec(rec)
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.shape[1] != k:
         raise ValueError("x must be a contiguous float32 [m][k] tensor")
     m = x.shape[0]
+    _check_tensor(x, torch.float32, m * k, "x")
     if out is None:
         out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _check_tensor(out, torch.float32, m * n, "out", (m, n))
+    _on_device(rec, x, out)
     _check(qw_gemv(rec["bits"], rec["group"], n, k, rec["payload"], rec["scales"], m, x, out,
                    stream), "qw_gemv")
     return out
@@ -364,13 +413,17 @@ def gemv(rec, x, out=None, stream=None):
 
 def gemv_batched(recs, xs, outs=None, stream=None):
     """Independent GEMVs (common m) in a few launches; returns the list of y."""
+    if len(xs) != len(recs) or (outs is not None and len(outs) != len(recs)):
+        raise ValueError("one x (and one output) per record")
     m = xs[0].shape[0]
     if outs is None:
         outs = [torch.empty((m, r["shape"][0]), dtype=torch.float32, device=x.device)
                 for r, x in zip(recs, xs)]
-    for r, x in zip(recs, xs):
-        if x.dtype != torch.float32 or not x.is_contiguous() or x.shape != (m, r["shape"][1]):
-            raise ValueError("each x must be a contiguous float32 [m][k] tensor")
+    for r, x, y in zip(recs, xs, outs):
+        n, k = _check_rec(r)
+        _check_tensor(x, torch.float32, m * k, "x", (m, k))
+        _check_tensor(y, torch.float32, m * n, "output", (m, n))
+    _on_device(*recs, *xs, *outs)
     arr, cnt = make_gemv_descs((r["bits"], r["group"], r["shape"][0], r["shape"][1], r["payload"],
                                 r["scales"], x, y) for r, x, y in zip(recs, xs, outs))
     _check(qw_gemv_batched(cnt, arr, m, stream), "qw_gemv_batched")
@@ -381,13 +434,14 @@ def gemv_chain(recs, xs, ys, stages, stream=None):
     """A chained decode pass: product i computes ys[i] = xs[i] . W_i^T in
     stage stages[i]; an x may be the y of an earlier stage.  All tensors are
     preallocated, contiguous fp32 [m][k] / [m][n] with a common m."""
+    if not len(recs) == len(xs) == len(ys) == len(stages):
+        raise ValueError("one x, y and stage per record")
     m = xs[0].shape[0]
     for r, x, y in zip(recs, xs, ys):
-        n, k = _nk(r["shape"])
-        if x.dtype != torch.float32 or not x.is_contiguous() or tuple(x.shape) != (m, k):
-            raise ValueError("each x must be a contiguous float32 [m][k] tensor")
-        if y.dtype != torch.float32 or not y.is_contiguous() or tuple(y.shape) != (m, n):
-            raise ValueError("each y must be a contiguous float32 [m][n] tensor")
+        n, k = _check_rec(r)
+        _check_tensor(x, torch.float32, m * k, "x", (m, k))
+        _check_tensor(y, torch.float32, m * n, "y", (m, n))
+    _on_device(*recs, *xs, *ys)
     arr, cnt = make_gemv_descs((r["bits"], r["group"], r["shape"][0], r["shape"][1], r["payload"],
                                 r["scales"], x, y) for r, x, y in zip(recs, xs, ys))
     _check(qw_gemv_chain(cnt, arr, list(stages), m, stream), "qw_gemv_chain")
@@ -397,14 +451,15 @@ def gemv_chain(recs, xs, ys, stages, stream=None):
 def gemm(rec, x_bf16, out=None, stream=None):
     """bf16 x [m][k] (torch.bfloat16, or int16/uint16 bit patterns) times the
     quantized weight on the matrix cores; returns fp32 y [m][n]."""
-    n, k = _nk(rec["shape"])
-    if x_bf16.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
-        raise ValueError("x must hold bf16 values or bit patterns")
-    if not x_bf16.is_contiguous() or x_bf16.dim() != 2 or x_bf16.shape[1] != k:
+    n, k = _check_rec(rec)
+    if not isinstance(x_bf16, torch.Tensor) or x_bf16.dim() != 2 or x_bf16.shape[1] != k:
         raise ValueError("x must be a contiguous [m][k] tensor")
     m = x_bf16.shape[0]
+    _check_tensor(x_bf16, (torch.bfloat16, torch.int16, torch.uint16), m * k, "x (bf16)")
     if out is None:
         out = torch.empty((m, n), dtype=torch.float32, device=x_bf16.device)
+    _check_tensor(out, torch.float32, m * n, "out", (m, n))
+    _on_device(rec, x_bf16, out)
     _check(qw_gemm(rec["bits"], rec["group"], n, k, rec["payload"], rec["scales"], m, x_bf16,
                    out, stream), "qw_gemm")
     return out
@@ -415,15 +470,20 @@ def matmul(rec, x, out=None, work=None, stream=None):
     returns fp32 y [m][n].  Up to QW_MATMUL_GEMV_MAX_M rows this is the codes
     GEMV; beyond, x is rounded to bf16 into ``work`` (allocated here when not
     given) and the matrix-core GEMM runs."""
-    n, k = _nk(rec["shape"])
-    if x.dtype != torch.float32 or not x.is_contiguous() or x.dim() != 2 or x.shape[1] != k:
+    n, k = _check_rec(rec)
+    if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.shape[1] != k:
         raise ValueError("x must be a contiguous float32 [m][k] tensor")
     m = x.shape[0]
+    _check_tensor(x, torch.float32, m * k, "x")
     if out is None:
         out = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _check_tensor(out, torch.float32, m * n, "out", (m, n))
     nb = lib().qw_matmul_work_bytes(m, k)
     if work is None:
         work = _work(nb, x.device) if nb > 0 else None
+    if work is not None and (not isinstance(work, torch.Tensor) or not work.is_contiguous()):
+        raise ValueError("work must be a contiguous tensor")
+    _on_device(rec, x, out, work)
     wb = work.numel() * work.element_size() if work is not None else 0
     _check(qw_matmul(rec["bits"], rec["group"], n, k, rec["payload"], rec["scales"], m, x, out,
                      work, wb, stream), "qw_matmul")

@@ -212,3 +212,40 @@ def test_quantize_dispatch(bits, group, n, k, al, expect):
 def test_product_dispatch(op, bits, group, n, k, expect):
     base = 1 << 20
     assert qw.lib().qw_debug_path(op, bits, group, n, k, base, base) == expect
+
+
+def test_binding_checks_buffers_before_any_call():
+    """The C ABI takes bare pointers, so the Python binding checks every
+    buffer a kernel would touch (dtype, contiguity, element count, device)
+    and every record's payload and scales against its bits, group and shape
+    before calling it; a mismatch raises ValueError and reaches no kernel."""
+    import torch
+
+    n, k, m = 8, 64, 2
+    good = dict(bits=4, group=32, shape=[n, k],
+                payload=torch.zeros(n * k // 2, dtype=torch.uint8),
+                scales=torch.ones(n * k // 32, dtype=torch.float32))
+    x = torch.zeros((m, k), dtype=torch.float32)
+    cases = [
+        (lambda: qw.gemv(dict(good, payload=good["payload"][:-1]), x), "payload"),
+        (lambda: qw.gemv(dict(good, scales=good["scales"][:-1]), x), "scales"),
+        (lambda: qw.gemv(dict(good, scales=good["scales"].double()), x), "scales"),
+        (lambda: qw.gemv(dict(good, group=48), x), "group"),
+        (lambda: qw.gemv(good, x, out=torch.empty((m, n - 1))), "out"),
+        (lambda: qw.gemv(good, x, out=torch.empty((m, n), dtype=torch.float64)), "out"),
+        (lambda: qw.gemv(good, x, out=torch.empty((n, m)).t()), "out"),
+        (lambda: qw.gemv(good, x[:, :k - 1]), "x"),
+        (lambda: qw.unpack(good, out=torch.empty(n * k - 1)), "out"),
+        (lambda: qw.unpack_batched([good], [torch.empty(n * k + 1)]), "output"),
+        (lambda: qw.gemv_batched([good], [x], [torch.empty((m, n + 1))]), "output"),
+        (lambda: qw.gemv_chain([good], [x], [torch.empty((m, n - 1))], [0]), "y"),
+        (lambda: qw.gemm(good, torch.zeros((m, k), dtype=torch.int16),
+                         out=torch.empty((m + 1, n))), "out"),
+        (lambda: qw.gemm(good, torch.zeros((m, k), dtype=torch.float32)), "x"),
+        (lambda: qw.matmul(good, torch.zeros((9, k)), out=torch.empty((9, n - 1))), "out"),
+        # right sizes everywhere, but host tensors: refused as well
+        (lambda: qw.gemv(good, x), "device"),
+    ]
+    for fn, word in cases:
+        with pytest.raises(ValueError, match=word):
+            fn()

@@ -100,3 +100,24 @@ def test_rejects_bad_stage_lists():
                                   for r, y in zip(recs, ys))
     assert qw.qw_gemv_chain(cnt, arr, [1, 0], 1) == -7
     assert qw.qw_gemv_chain(cnt, arr, [0, 1], 9) == -4
+
+
+def test_zero_fill_waits_for_its_stage():
+    """A product with k == 0 writes zeros to its y in its own stage: when an
+    earlier stage reads that buffer as x, it still sees the values it held
+    before the call (the fill is not hoisted in front of stage 0)."""
+    m, n, k = 2, 64, 64
+    recs, hosts = _recs(4, 32, [(n, k)], 13)
+    x_host = inputs.activations([11, 13, 5], m, k)
+    z = torch.from_numpy(x_host).cuda()          # read in stage 0, zeroed in stage 1
+    y0 = torch.full((m, n), float("nan"), device="cuda")
+    empty = dict(bits=4, group=32, shape=[k, 0],
+                 payload=torch.empty(0, dtype=torch.uint8, device="cuda"),
+                 scales=torch.empty(0, dtype=torch.float32, device="cuda"))
+    x_empty = torch.empty((m, 0), dtype=torch.float32, device="cuda")
+    qw.gemv_chain([recs[0], empty], [z, x_empty], [y0, z], [0, 1])
+    torch.cuda.synchronize()
+    got = y0.cpu().numpy()
+    ref = oracle.gemv_ref(hosts[0], x_host)
+    assert np.all(np.abs(got - ref) <= 1e-5 * oracle.error_base(hosts[0], x_host))
+    assert torch.count_nonzero(z).item() == 0

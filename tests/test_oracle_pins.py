@@ -91,13 +91,16 @@ def decode_by_hand(payload, bits, count):
 # ------------------------------------------- Chapter 23 worked example (P2)
 
 
-def chapter23_quantise_fp64(ws, bits):
-    """The per-tensor special case in binary64, as the Chapter 23 script's
-    ``quantise`` states it (scale from max|w|, Python round, clip)."""
+def binary64_tensor_codes(ws, bits):
+    """Codes of the per-tensor rule evaluated in binary64 instead of fp32:
+    one step for the whole tensor, the largest magnitude divided by qmax; each
+    weight's quotient by that step goes to the nearest integer (halves to the
+    even neighbour) and is kept inside [-qmax-1, qmax] (the Chapter 23 page's
+    bounds).  Returns the list of codes."""
     qmax = 2 ** (bits - 1) - 1
-    scale = max(abs(w) for w in ws) / qmax
-    codes = [max(-qmax - 1, min(qmax, round(w / scale))) for w in ws]
-    return scale, codes, [c * scale for c in codes]
+    v = np.asarray(ws, dtype=np.float64).reshape(-1)
+    step = np.max(np.abs(v)) / qmax
+    return np.clip(np.rint(v / step), -qmax - 1, qmax).astype(np.int64).tolist()
 
 
 def _errors(ws, deq):
@@ -133,7 +136,7 @@ def test_chapter23_codes_and_bytes_exact(golden_dir):
         assert rec["q"].tolist() == codes
         assert rec["payload"].tobytes() == pack_bytes_by_hand(codes, bits)
         # the fp64 script of the page picks the same codes
-        assert chapter23_quantise_fp64(ws, bits)[1] == codes
+        assert binary64_tensor_codes(ws, bits) == codes
     # the bytes written out once by hand from the format description
     assert _oracle_tensor(ws, 8)[0]["payload"].tobytes().hex() == "1e9052ec7fc911a4"
     assert _oracle_tensor(ws, 4)[0]["payload"].tobytes().hex() == "2a7d5f39"
@@ -221,6 +224,33 @@ def test_smallem_sizes(golden_dir):
     # with nibble packing the same change costs more (1/8 more bits)
     grow_nib = oracle.bits_per_weight(4, 32) / oracle.bits_per_weight(4, 64) - 1
     assert abs(grow_nib - (5.0 / 4.5 - 1)) < 1e-12
+
+
+def test_num_scales_and_payload_bytes():
+    """oracle.num_scales / payload_bytes against the records the oracle
+    writes (one fp32 scale per group, bits / 8 bytes per weight) and against
+    the closed forms the pages fix: four bytes per scale (page "Huit bits,
+    puis quatre", section "Ce que perd le modèle"), so int4 with group 32
+    costs 4 + 32/32 = 5 bits per weight and group 128 costs 4.25; and the
+    7B stack of 224 matrices (32 layers of q, k, v, o 4096 x 4096, gate and
+    up 11008 x 4096, down 4096 x 11008) holds 6,476,005,376 weights, so its
+    int4 payload is half that many bytes and its group-32 scales a 32nd of
+    that many floats."""
+    for (n, k, group) in ((3, 64, 32), (5, 96, 96 * 5), (7, 48, 6), (4, 4096, 4096)):
+        for bits in (4, 8):
+            rec = oracle.quantize_pack(np.ones((n, k), np.float32), bits, group)
+            assert oracle.num_scales(group, n, k) == rec["scales"].size == n * k // group
+            assert oracle.payload_bytes(bits, n, k) == rec["payload"].size
+            bpw = 8 * (oracle.payload_bytes(bits, n, k) + 4 * oracle.num_scales(group, n, k))
+            assert bpw == pytest.approx(n * k * oracle.bits_per_weight(bits, group), rel=1e-12)
+    assert 8 * (oracle.payload_bytes(4, 1, 128) + 4 * oracle.num_scales(128, 1, 128)) / 128 == 4.25
+    assert 8 * (oracle.payload_bytes(4, 1, 32) + 4 * oracle.num_scales(32, 1, 32)) / 32 == 5.0
+    shapes = [(4096, 4096)] * 4 + [(11008, 4096)] * 2 + [(4096, 11008)]
+    weights = 32 * sum(n * k for n, k in shapes)
+    assert weights == 6_476_005_376
+    assert 32 * sum(oracle.payload_bytes(4, n, k) for n, k in shapes) == weights // 2
+    assert 32 * sum(oracle.num_scales(32, n, k) for n, k in shapes) == weights // 32
+    assert 32 * sum(4 * oracle.num_scales(32, n, k) for n, k in shapes) == 809_500_672
 
 
 # ------------------------------------------------ the P1 script's own checks
@@ -358,8 +388,7 @@ def test_per_tensor_is_chapter23_quantise(bits):
     w = inputs.weight(21, 16, 24, 0.3)
     rec = oracle.quantize_pack(w, bits, w.size)
     assert rec["scales"].shape == (1,)
-    _, codes, _ = chapter23_quantise_fp64([float(v) for v in w.reshape(-1)], bits)
-    assert rec["q"].tolist() == codes
+    assert rec["q"].tolist() == binary64_tensor_codes(w, bits)
 
 
 # ------------------------------------------------------- invariants
