@@ -1,0 +1,52 @@
+"""Oracle side of the full-size parity checks, run in worker processes.
+
+The GPU results of a whole workload (payload, scales, GEMV outputs and
+per-row checksums of the unpacked weights) are written by the test into
+memory-mapped files; each worker regenerates one seeded weight (the same
+draw the GPU was given), runs the oracle on it and compares.  Workers use
+only numpy, the oracle and the input generators: they never touch the GPU.
+"""
+
+import numpy as np
+
+import oracle
+from int8_int4_dequant_amd import inputs
+
+GEMV_TOL = 1e-5
+
+
+def row_checksums(bits32, k):
+    """Per-row sum over j of (bit pattern as int64) * (j + 1): any change of
+    one element changes its row's value.  ``bits32`` is int32 [n * k]."""
+    a = np.asarray(bits32, np.int32).reshape(-1, k).astype(np.int64)
+    return a @ np.arange(1, k + 1, dtype=np.int64)
+
+
+def c4_check(job):
+    """job = (index, layer, slot, files, offsets): compares matrix `index` of
+    the 7B stack with the oracle.  Returns a dict of findings."""
+    index, layer, slot, files, off = job
+    tag, n, k = inputs.C4_SLOTS[slot]
+    w = inputs.c4_weight(layer, slot)
+    ref = oracle.quantize_pack(w, 4, 32)
+    pay = np.memmap(files["payload"], np.uint8, "r", off["payload"], n * k // 2)
+    sca = np.memmap(files["scales"], np.uint32, "r", 4 * off["scales"], n * k // 32)
+    out = {"index": index, "tag": tag}
+    out["payload_diff"] = int(np.count_nonzero(np.asarray(pay) != ref["payload"]))
+    out["scales_diff"] = int(np.count_nonzero(np.asarray(sca) != ref["scales"].view(np.uint32)))
+    w_hat = oracle.unpack(ref)
+    ck = np.memmap(files["unpack_ck"], np.int64, "r", 8 * off["rows"], n)
+    out["unpack_rows_diff"] = int(np.count_nonzero(
+        np.asarray(ck) != row_checksums(w_hat.view(np.int32), k)))
+    x = inputs.c4_x(k)
+    yr = oracle.gemv_ref(ref, x)
+    base = oracle.error_base(ref, x)
+    worst = 0.0
+    for name in ("y_batched", "y_single"):
+        y = np.memmap(files[name], np.float32, "r", 4 * off["rows"], n).reshape(1, n)
+        err = np.abs(y.astype(np.float64) - yr)
+        bad = err > GEMV_TOL * base
+        out[name + "_bad"] = int(np.count_nonzero(bad))
+        worst = max(worst, float(np.max(err / np.maximum(base, 1e-300))))
+    out["gemv_worst_err_over_base"] = worst
+    return out

@@ -8,10 +8,13 @@ section "Arrondir mieux : GPTQ") against the CPU oracle ``oracle.gptq``.
   well conditioned: its condition number is at most 100 k + 1, so both
   factors are within ~1e-11 of the exact one), exact zeros below the
   diagonal.
-* Codes and scales: bit-identical to the oracle.  The code of a component
-  is decided in fp32 from an fp64 weight on both sides; the two fp64 weights
-  differ only by summation order (~1e-16 relative), which changes a code
-  only if the fp32 quotient lands within that of a rounding boundary.
+* Codes and scales: identical to the oracle's row by row, except rows whose
+  first difference is a rounding-boundary case (tests/gptq_check.py): the
+  code of a component is decided in fp32 from an fp64 weight on both sides,
+  and the two fp64 weights differ by summation order (and, when the GPU
+  uses its own factor, by the factors' last bits), so a code may flip when
+  the oracle's weight lies within that derived bound of a boundary.  Such
+  rows are counted and must be rare (none occur in the cases below today).
 * The page's two checks on the GPU results: a diagonal H gives exactly the
   plain codes of qw_quantize_pack; correlated inputs cut the output error by
   more than 30 %.
@@ -21,6 +24,7 @@ import numpy as np
 import pytest
 import torch
 
+import gptq_check
 import oracle
 from oracle import gptq as G
 from int8_int4_dequant_amd import inputs, qw
@@ -149,8 +153,17 @@ def test_quantize_parity_given_u(bits, group, n, k):
     w = inputs.weight([8, 6, n, k], n, k, 0.02)
     want = G.quantize_pack(w, u, bits, group)
     rec = qw.gptq_quantize_pack(dev(w), dev(u), bits, group)
-    assert np.array_equal(host(rec["scales"]).view(np.uint32), want["scales"].view(np.uint32))
-    assert np.array_equal(host(rec["payload"]), want["payload"])
+    _assert_codes(w, u, want, rec, bits, group)
+
+
+def _assert_codes(w, u_ref, want, rec, bits, group, u_gpu=None):
+    """Row-by-row comparison with the oracle under the boundary rule."""
+    n = w.shape[0]
+    exact, excused, bad = gptq_check.compare(w, u_ref, want, host(rec["payload"]),
+                                             host(rec["scales"]), bits, group, u_gpu)
+    _say(f"  rows exact {exact}, boundary cases {excused}")
+    assert bad == [], bad[:5]
+    assert excused <= max(2, n // 100)
 
 
 def test_end_to_end_chain():
@@ -158,10 +171,15 @@ def test_end_to_end_chain():
     _say("gptq_chain", n, k, t)
     x = inputs.calibration_activations([8, 7], t, k)
     w = inputs.weight([8, 8], n, k, 0.02)
-    want = G.gptq(w, G.hessian([x]), 4, 32)
-    rec = qw.gptq(dev(w), qw.gptq_hessian(dev(x)), 4, 32)
-    assert np.array_equal(host(rec["payload"]), want["payload"])
-    assert np.array_equal(host(rec["scales"]).view(np.uint32), want["scales"].view(np.uint32))
+    u_ref = G.inverse_factor(G.damped(G.hessian([x])))
+    want = G.quantize_pack(w, u_ref, 4, 32)
+    u_gpu = qw.gptq_factor(qw.gptq_hessian(dev(x)))
+    rec = qw.gptq_quantize_pack(dev(w), u_gpu, 4, 32)
+    _assert_codes(w, u_ref, want, rec, 4, 32, host(u_gpu))
+    # qw.gptq is the same chain
+    rec2 = qw.gptq(dev(w), qw.gptq_hessian(dev(x)), 4, 32)
+    assert torch.equal(rec2["payload"], rec["payload"])
+    assert torch.equal(rec2["scales"], rec["scales"])
 
 
 @pytest.mark.parametrize("bits,group", [(4, 32), (8, 128)])
@@ -204,8 +222,8 @@ def test_largest_matrix_of_the_small_model():
     """The page's largest matrix (the feed-forward down map, 1368 inputs,
     512 outputs) with its calibration budget of 65,536 tokens: the whole GPU
     chain against the oracle's, int4 (group 72, which divides 1368) and int8
-    per output channel, codes bit for bit, and the output error more than
-    30 % below plain rounding."""
+    per output channel, codes row by row under the boundary rule, and the
+    output error more than 30 % below plain rounding."""
     slot = 6
     name, n, k, src = inputs.SMALLEM_LAYER[slot]
     _say("gptq_full", name, n, k, inputs.CALIB_TOKENS)
@@ -219,11 +237,7 @@ def test_largest_matrix_of_the_small_model():
         _say("gptq_full codes", bits, group)
         rec = qw.gptq_quantize_pack(wd, u_gpu, bits, group)
         want = G.quantize_pack(w, u_ref, bits, group)
-        got_payload = host(rec["payload"])
-        mism = int(np.count_nonzero(got_payload != want["payload"]))
-        assert mism == 0, f"{mism} payload bytes differ"
-        assert np.array_equal(host(rec["scales"]).view(np.uint32),
-                              want["scales"].view(np.uint32))
+        _assert_codes(w, u_ref, want, rec, bits, group, host(u_gpu))
         # output error on the calibration inputs, against plain rounding
         plain = qw.quantize_pack(wd, bits, group)
         err_g = torch.linalg.norm(xd.double() @ (qw.unpack(rec).double() - wt).T).item()

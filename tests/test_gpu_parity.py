@@ -2,11 +2,14 @@
 
 Bars: payload, scales and unpacked weights bit-identical; GEMV outputs within
 1e-5 * sum|x * w_hat| and GEMM outputs within 8e-3 * sum|x * w_hat| per
-element.  Small cases compare every element; the full-size workloads compare
-every byte of the quantization where the oracle is quick enough, otherwise
-sampled rows (groups never cross rows there, so a row's payload depends on
-that row only), in the same launch configuration the benchmark times.
+element.  Every case compares every element: the small ones directly, the
+full-size workloads (the 7B stack, the 70B MLP weight) in the launch
+configuration the benchmark times, with the oracle run over the whole
+workload (for the stack in worker processes, one matrix each).  Only the
+matrix past 2^31 weights is checked on sampled rows.
 """
+
+import os
 
 import numpy as np
 import pytest
@@ -164,11 +167,14 @@ def test_unaligned_pointers_take_generic_kernels(bits):
 # ------------------------------------------------------------------- GEMV
 
 
-@pytest.mark.parametrize("bits,group", [(4, 32), (4, 128), (8, 16), (8, 4096 // 4)])
-@pytest.mark.parametrize("n,k", [(13, 4096), (77, 11008), (200, 1024), (8, 32 * 3)])
+GEMV_SHAPE_CASES = [(bits, group, n, k)
+                    for bits, group in [(4, 32), (4, 128), (8, 16), (8, 4096 // 4)]
+                    for n, k in [(13, 4096), (77, 11008), (200, 1024), (8, 32 * 3)]
+                    if k % group == 0]
+
+
+@pytest.mark.parametrize("bits,group,n,k", GEMV_SHAPE_CASES)
 def test_gemv_shapes_all_m(bits, group, n, k):
-    if k % group:
-        pytest.skip("group does not divide k")
     w = inputs.weight(n * 7 + k, n, k, 0.02)
     ref, rec = quant_both(w, bits, group)
     for m in range(1, 9):
@@ -337,6 +343,21 @@ def test_gemm_small_m(bits, group, m, n, k):
     check_gemm(ref, rec, inputs.bf16_activations(m * 5 + 3, m, k))
 
 
+# The small-M kernel loads a scale only at the k-steps that start a group.
+# With k = 640, group 128 (10 k-steps, 3 per wave) waves 1 and 3 start in the
+# middle of a group and cross into the next one a step later; with k = 960,
+# group 192 (15 k-steps, 4 per wave) waves 1 and 2 start 64 and 128 codes
+# into a group.
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("m", [1, 17])
+@pytest.mark.parametrize("group,k", [(128, 640), (192, 960)])
+def test_gemm_small_m_waves_start_inside_a_group(bits, m, group, k):
+    n = 96
+    w = inputs.weight(m + group + k + bits, n, k, 0.02)
+    ref, rec = quant_both(w, bits, group)
+    check_gemm(ref, rec, inputs.bf16_activations(m * 7 + group, m, k))
+
+
 def test_gemm_ignores_stale_output():
     # the split tiles accumulate into Y: stale contents (NaN) must not leak
     w = inputs.weight(21, 300, 512, 0.02)
@@ -374,45 +395,102 @@ def test_config3_int4_g128(j):
         check_gemv(ref, rec, inputs.c3_x(j, m))
 
 
-def _rows_check(rec, w, bits, group, rows, x=None, y=None):
-    """Oracle on selected rows only (groups lie inside rows)."""
-    n, k = w.shape
-    ref = oracle.quantize_pack(w[rows], bits, group)
-    pb = k * bits // 8
-    payload = host(rec["payload"]).reshape(n, pb)[rows]
-    scales = host(rec["scales"]).reshape(n, k // group)[rows]
-    assert same_bits(payload.reshape(-1), ref["payload"])
-    assert same_bits(scales.reshape(-1), ref["scales"])
-    if x is not None:
-        yr = oracle.gemv_ref(ref, x)
-        B = oracle.error_base(ref, x)
-        assert np.all(np.abs(y[:, rows] - yr) <= GEMV_TOL * B)
+def _pool_workers():
+    # the host cores this process may use, at most 16 (a GPU machine's share)
+    return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
-def test_config4_layers_sampled():
-    # layers 0 and 31 of the 7B stack: batched quantize, then the decode
-    # GEMVs as one batched call (the launch configuration of the benchmark)
-    # and as single calls, and the batched unpack; sampled rows against the
-    # oracle.
-    rng = np.random.default_rng(4)
-    ws, xs = [], []
-    for layer in (0, 31):
-        for slot, (tag, n, k) in enumerate(inputs.C4_SLOTS):
-            ws.append(inputs.c4_weight(layer, slot))
-            xs.append(dev(inputs.c4_x(k)))
-    recs = qw.quantize_pack_batched([dev(w) for w in ws], 4, 32)
-    ys = [host(y) for y in qw.gemv_batched(recs, xs)]
-    # the batched unpack of the same matrices (also the benchmark's launch)
-    w_hats = [host(o) for o in qw.unpack_batched(recs)]
-    for w, rec, x, y, w_hat in zip(ws, recs, xs, ys, w_hats):
-        n, k = w.shape
-        rows = np.sort(rng.choice(n, size=96, replace=False))
-        rows[0], rows[-1] = 0, n - 1
-        _rows_check(rec, w, 4, 32, rows, host(x), y)
-        y1 = host(qw.gemv(rec, x))
-        _rows_check(rec, w, 4, 32, rows, host(x), y1)
-        ref_rows = oracle.unpack(oracle.quantize_pack(w[rows], 4, 32)).reshape(len(rows), k)
-        assert same_bits(w_hat.reshape(n, k)[rows], ref_rows)
+@pytest.mark.timeout(900)
+def test_config4_full_stack():
+    """The whole 7B stack (224 matrices, 6.48e9 weights) in the launch
+    configuration the benchmark times: one batched quantize launch, one
+    batched M = 1 GEMV launch, one batched unpack launch, and every matrix
+    also as a lone qw_gemv call.  Every payload byte, every scale and every
+    GEMV output of every matrix is compared with the oracle (worker
+    processes regenerate each seeded weight and run the oracle on it); the
+    unpacked weights are compared through exact per-row checksums of their
+    bit patterns, computed on both sides."""
+    import concurrent.futures as cf
+    import multiprocessing as mp
+    import tempfile
+
+    import full_parity
+
+    mats = inputs.c4_matrices()
+    W = [None] * len(mats)
+
+    def upload(i, layer, tag, w):
+        W[i] = dev(w)
+        if (i + 1) % 56 == 0:
+            print(f"c4 full: {i + 1} weights on the GPU", flush=True)
+
+    inputs.c4_weights_parallel(upload, threads=_pool_workers())
+    recs = qw.quantize_pack_batched(W, 4, 32)
+    del W
+    xs = {k: dev(inputs.c4_x(k)) for k in (4096, 11008)}
+    xin = [xs[m[3]] for m in mats]
+    ys = qw.gemv_batched(recs, xin)
+    y1 = [qw.gemv(r, x) for r, x in zip(recs, xin)]
+    w_hats = qw.unpack_batched(recs)
+    torch.cuda.synchronize()
+    print("c4 full: GPU passes done", flush=True)
+    with tempfile.TemporaryDirectory(dir="/dev/shm" if os.path.isdir("/dev/shm") else None) as d:
+        files = {name: os.path.join(d, name) for name in
+                 ("payload", "scales", "y_batched", "y_single", "unpack_ck")}
+        tot_p = sum(n * k // 2 for _, _, n, k, _ in mats)
+        tot_s = sum(n * k // 32 for _, _, n, k, _ in mats)
+        tot_r = sum(n for _, _, n, k, _ in mats)
+        mm = {"payload": np.memmap(files["payload"], np.uint8, "w+", shape=(tot_p,)),
+              "scales": np.memmap(files["scales"], np.float32, "w+", shape=(tot_s,)),
+              "y_batched": np.memmap(files["y_batched"], np.float32, "w+", shape=(tot_r,)),
+              "y_single": np.memmap(files["y_single"], np.float32, "w+", shape=(tot_r,)),
+              "unpack_ck": np.memmap(files["unpack_ck"], np.int64, "w+", shape=(tot_r,))}
+        jobs, op, os_, orow = [], 0, 0, 0
+        for i, ((layer, tag, n, k, _seed), rec) in enumerate(zip(mats, recs)):
+            mm["payload"][op:op + n * k // 2] = host(rec["payload"])
+            mm["scales"][os_:os_ + n * k // 32] = host(rec["scales"])
+            mm["y_batched"][orow:orow + n] = host(ys[i]).reshape(-1)
+            mm["y_single"][orow:orow + n] = host(y1[i]).reshape(-1)
+            bitsv = w_hats[i].view(torch.int32).view(n, k).to(torch.int64)
+            wk = torch.arange(1, k + 1, dtype=torch.int64, device="cuda")
+            mm["unpack_ck"][orow:orow + n] = host((bitsv * wk).sum(dim=1))
+            del bitsv
+            jobs.append((i, layer, [t for t, *_ in inputs.C4_SLOTS].index(tag), files,
+                         {"payload": op, "scales": os_, "rows": orow}))
+            op += n * k // 2
+            os_ += n * k // 32
+            orow += n
+        for a in mm.values():
+            a.flush()
+        del mm, w_hats
+        torch.cuda.empty_cache()
+        jobs.sort(key=lambda j: -inputs.C4_SLOTS[j[2]][1] * inputs.C4_SLOTS[j[2]][2])
+        workers = _pool_workers()
+        saved = {v: os.environ.get(v) for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                                "MKL_NUM_THREADS")}
+        for v in saved:
+            os.environ[v] = "1"
+        results = []
+        try:
+            with cf.ProcessPoolExecutor(max_workers=workers,
+                                        mp_context=mp.get_context("spawn")) as ex:
+                for r in ex.map(full_parity.c4_check, jobs):
+                    results.append(r)
+                    if len(results) % 32 == 0:
+                        print(f"c4 full: {len(results)} matrices checked", flush=True)
+        finally:
+            for v, old in saved.items():
+                if old is None:
+                    os.environ.pop(v, None)
+                else:
+                    os.environ[v] = old
+    assert len(results) == len(mats)
+    worst = max(r["gemv_worst_err_over_base"] for r in results)
+    print(f"c4 full: {len(results)} matrices, worst GEMV |err|/B = {worst:.3g}", flush=True)
+    for r in results:
+        assert r["payload_diff"] == 0 and r["scales_diff"] == 0, r
+        assert r["unpack_rows_diff"] == 0, r
+        assert r["y_batched_bad"] == 0 and r["y_single_bad"] == 0, r
 
 
 @pytest.mark.parametrize("bits", [4, 8])
@@ -556,20 +634,30 @@ def test_gemv_batched_validation():
     assert qw.qw_gemv_batched(1, arr, 9) == -4
 
 
-def test_config5_gemm_sampled():
+@pytest.mark.timeout(600)
+def test_config5_full():
+    """The 70B MLP weight (28672 x 8192, int4 group 128) and 2048 bf16 rows,
+    in the benchmark's launch (the split-tail GEMM): every payload byte and
+    scale, and every one of the 2048 x 28672 outputs against the oracle's
+    fp64 product, in blocks of 4096 weight rows."""
     w = inputs.c5_weight()
     n, k = w.shape
     rec = qw.quantize_pack(dev(w), 4, 128)
-    rng = np.random.default_rng(5)
-    rows = np.sort(rng.choice(n, size=64, replace=False))
-    rows[0], rows[-1] = 0, n - 1
-    _rows_check(rec, w, 4, 128, rows)
     xb = inputs.c5_x_bf16()
     y = host(qw.gemm(rec, dev(xb.view(np.int16))))
-    ms = np.sort(rng.choice(xb.shape[0], size=48, replace=False))
-    ms[0], ms[-1] = 0, xb.shape[0] - 1
-    ref = oracle.quantize_pack(w[rows], 4, 128)
-    yr = oracle.gemm_ref(ref, xb[ms])
-    B = oracle.error_base(ref, oracle.bf16_bits_to_f32(xb[ms]))
-    got = y[np.ix_(ms, rows)]
-    assert np.all(np.abs(got - yr) <= GEMM_TOL * B)
+    payload = host(rec["payload"]).reshape(n, k // 2)
+    scales = host(rec["scales"]).reshape(n, k // 128)
+    xf = oracle.bf16_bits_to_f32(xb)
+    worst = 0.0
+    for r0 in range(0, n, 4096):
+        r1 = min(n, r0 + 4096)
+        ref = oracle.quantize_pack(w[r0:r1], 4, 128)
+        assert same_bits(payload[r0:r1].reshape(-1), ref["payload"]), r0
+        assert same_bits(scales[r0:r1].reshape(-1), ref["scales"]), r0
+        yr = oracle.gemm_ref(ref, xb)
+        B = oracle.error_base(ref, xf)
+        err = np.abs(y[:, r0:r1].astype(np.float64) - yr)
+        worst = max(worst, float(np.max(err / np.maximum(B, 1e-300))))
+        assert np.all(err <= GEMM_TOL * B), r0
+        print(f"c5 full: rows {r0}..{r1} ok", flush=True)
+    print(f"c5 full: worst |err|/B = {worst:.3g}", flush=True)

@@ -220,3 +220,74 @@ def test_zero_weights_give_zero_codes():
     assert np.all(rec["q"] == 0)
     assert np.all(rec["payload"] == 0x88)
     assert np.all(rec["scales"] == 1.0)
+
+
+# ------------------------------------------------ the GPU comparison rule
+
+
+def _pack4(q):
+    u = (np.asarray(q, np.int16).reshape(-1) + 8).astype(np.uint8)
+    return (u[0::2] | (u[1::2] << 4)).astype(np.uint8)
+
+
+def test_comparison_rule_accepts_identical_codes_and_rejects_planted_ones():
+    """tests/gptq_check.compare: the oracle's own codes are all exact; a code
+    moved by one step, or a scale moved by a factor, where the oracle's
+    weight is nowhere near a rounding boundary, is reported."""
+    import gptq_check
+
+    n, k, group = 6, 64, 16
+    w = inputs.weight([8, 30], n, k, 0.02)
+    h = G.hessian([inputs.calibration_activations([8, 31], 4 * k, k)])
+    u = G.inverse_factor(G.damped(h))
+    want = G.quantize_pack(w, u, 4, group)
+    exact, excused, bad = gptq_check.compare(w, u, want, want["payload"], want["scales"], 4, group)
+    assert (exact, excused, bad) == (n, 0, [])
+    # a code one step off, at the component whose quotient is farthest from a
+    # rounding boundary
+    r = want["w_at_quant"][2] / np.repeat(want["scales"].reshape(n, -1)[2], group)
+    c = int(np.argmin(np.abs(r - np.rint(r))))
+    q = want["q"].reshape(n, k).copy()
+    q[2, c] += 1 if q[2, c] < 7 else -1
+    _, _, bad = gptq_check.compare(w, u, want, _pack4(q), want["scales"], 4, group)
+    assert [b[:2] for b in bad] == [(2, c)]
+    s = want["scales"].copy()
+    s[5 * (k // group) + 1] *= np.float32(1.01)
+    _, _, bad = gptq_check.compare(w, u, want, want["payload"], s, 4, group)
+    assert [b[:2] for b in bad] == [(5, group)]
+
+
+def test_comparison_rule_excuses_a_boundary_case():
+    """A weight planted in the oracle's record exactly halfway between two
+    fp32 numbers whose quotients round to neighbouring codes: either code is
+    a correct decision within any nonzero summation difference, so the row
+    is excused (not failed), and only that row."""
+    import gptq_check
+
+    n, k, group = 4, 32, 16
+    w = inputs.weight([8, 32], n, k, 0.02)
+    u = np.eye(k)
+    want = G.quantize_pack(w, u, 4, group)
+    want = dict(want, w_at_quant=want["w_at_quant"].copy())
+    i, c = 1, 5
+    S = want["scales"].reshape(n, -1)[i, c // group]
+    qv = int(want["q"].reshape(n, k)[i, c])
+    up = 1 if qv < 7 else -1
+    # f2: the first fp32 number (moving away from the oracle's value) whose
+    # code is qv + up; f1 the one before it
+    f = np.float32(want["w_at_quant"][i, c])
+    step = np.float32(np.inf) if up > 0 else np.float32(-np.inf)
+    while np.rint(np.float32(f / S)) == qv:
+        f1, f = f, np.nextafter(f, step)
+    mid = (np.float64(f1) + np.float64(f)) / 2.0
+    want["w_at_quant"][i, c] = mid
+    # the GPU's plausible decision: the neighbouring code (the record keeps qv)
+    q = want["q"].reshape(n, k).copy()
+    q[i, c] = qv + up
+    assert int(np.rint(np.float32(f / S))) == qv + up
+    exact, excused, bad = gptq_check.compare(w, u, want, _pack4(q), want["scales"], 4, group)
+    assert (exact, excused, bad) == (n - 1, 1, [])
+    # the same code one step further is no boundary case
+    q[i, c] = qv + 2 * up if abs(qv + 2 * up) <= 7 else qv - up
+    _, _, bad = gptq_check.compare(w, u, want, _pack4(q), want["scales"], 4, group)
+    assert [b[:2] for b in bad] == [(i, c)]
