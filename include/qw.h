@@ -77,7 +77,8 @@ enum qw_status {
     QW_EHIP = -6,    /* a HIP launch failed                                  */
     QW_ECOUNT = -7,  /* batched call: count < 0 or a descriptor is invalid   */
     QW_EWORK = -8,   /* work buffer NULL or smaller than the size query says */
-    QW_EARG = -9     /* another argument out of range (see the entry point)  */
+    QW_EARG = -9,    /* another argument out of range (see the entry point)  */
+    QW_ESCRATCH = -10 /* qw_matmul_noalloc: input larger than its scratch     */
 };
 
 /* Largest number of matrices the batched calls put into one kernel launch
@@ -272,6 +273,29 @@ int qw_matmul(int bits, int64_t group, int64_t n, int64_t k,
               const uint8_t* payload, const float* scales,
               int64_t m, const float* x, float* y,
               void* work, int64_t work_bytes, void* stream);
+
+/*
+ * qw_matmul for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments and results as qw_matmul (bit-identical outputs: the same
+ * kernels run), without the work buffer: the bf16 copy of x goes to a
+ * static device array of QW_MATMUL_NOALLOC_MAX_BYTES that the library holds
+ * on every GPU it runs on until the process ends.  The call allocates and
+ * frees nothing.
+ *   - m * k * 2 (the bytes of x in bf16) above QW_MATMUL_NOALLOC_MAX_BYTES,
+ *     for m > QW_MATMUL_GEMV_MAX_M, returns QW_ESCRATCH and enqueues
+ *     nothing; up to QW_MATMUL_GEMV_MAX_M rows no scratch is used.
+ *   - The scratch of the CURRENT device is used; `stream` (if not NULL)
+ *     must belong to that device (QW_EARG otherwise).  Its address is looked
+ *     up on the first call on each device.
+ *   - Every call on one GPU shares that GPU's array: two calls whose work
+ *     overlaps in time on one GPU (different streams, or host threads) race
+ *     and give undefined results.  Calls ordered on one stream are safe.
+ */
+#define QW_MATMUL_NOALLOC_MAX_BYTES (32ll << 20)
+int qw_matmul_noalloc(int bits, int64_t group, int64_t n, int64_t k,
+                      const uint8_t* payload, const float* scales,
+                      int64_t m, const float* x, float* y, void* stream);
 
 /*
  * GPTQ codes (page "Huit bits, puis quatre", section "Arrondir mieux :

@@ -2,6 +2,7 @@
 // dispatch to the HIP kernels.  No allocation, no synchronization.
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "../../include/qw.h"
@@ -64,6 +65,9 @@ const char* qw_status_string(int status) {
     case QW_ECOUNT: return "invalid batch count or descriptor";
     case QW_EWORK: return "work buffer missing or too small";
     case QW_EARG: return "argument out of range";
+    case QW_ESCRATCH:
+      return "input too large for the static scratch of qw_matmul_noalloc "
+             "(m * k * 2 bytes of bf16 x above QW_MATMUL_NOALLOC_MAX_BYTES)";
     default: return "unknown status";
   }
 }
@@ -298,6 +302,60 @@ int64_t qw_matmul_work_bytes(int64_t m, int64_t k) {
   return (m * k * 2 + 255) / 256 * 256;  // bf16 copy of x
 }
 
+}  // extern "C"
+
+// The static scratch of qw_matmul_noalloc: each device holds its own copy
+// from the library's first use on it until the process ends.  Host code
+// never passes the array's name to a kernel (in host code it is only a
+// stand-in for the symbol); it passes the device address looked up once per
+// device with hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[QW_MATMUL_NOALLOC_MAX_BYTES];
+
+namespace {
+
+// qw_matmul with a resolved work pointer (the caller's buffer, or this
+// device's static scratch).  Arguments are validated by the callers.
+int matmul_with_work(const qw::Mat& mt, const uint8_t* payload, const float* scales, int64_t m,
+                     const float* x, float* y, void* work, hipStream_t stream) {
+  uint16_t* xb = (uint16_t*)work;
+  hipError_t e = qw::launch_round_bf16(x, xb, m * mt.k, stream);
+  if (e != hipSuccess) return record(e);
+  return record(qw::launch_gemm(mt, payload, scales, m, xb, y, stream));
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's address of `scratch`, looked up on the first call on the
+// device (the current device, on which `stream` must run).
+int scratch_address(hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return record(e);
+  if (dev < 0 || dev >= kMaxDevices) return QW_EARG;
+  if (stream) {
+    hipDevice_t sdev = 0;
+    e = hipStreamGetDevice(stream, &sdev);
+    if (e != hipSuccess) return record(e);
+    if ((int)sdev != dev) return QW_EARG;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return record(e);
+    if (!p) return QW_EHIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return QW_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int qw_matmul(int bits, int64_t group, int64_t n, int64_t k, const uint8_t* payload,
               const float* scales, int64_t m, const float* x, float* y, void* work,
               int64_t work_bytes, void* stream) {
@@ -312,10 +370,26 @@ int qw_matmul(int bits, int64_t group, int64_t n, int64_t k, const uint8_t* payl
   if (k == 0) return record(qw::launch_fill_zero(y, m * n, (hipStream_t)stream));
   if (!payload || !scales || !x) return QW_ENULL;
   if (!work || work_bytes < qw_matmul_work_bytes(m, k)) return QW_EWORK;
-  uint16_t* xb = (uint16_t*)work;
-  hipError_t e = qw::launch_round_bf16(x, xb, m * k, (hipStream_t)stream);
-  if (e != hipSuccess) return record(e);
-  return record(qw::launch_gemm(mt, payload, scales, m, xb, y, (hipStream_t)stream));
+  return matmul_with_work(mt, payload, scales, m, x, y, work, (hipStream_t)stream);
+}
+
+int qw_matmul_noalloc(int bits, int64_t group, int64_t n, int64_t k, const uint8_t* payload,
+                      const float* scales, int64_t m, const float* x, float* y, void* stream) {
+  qw::Mat mt;
+  int st = check_mat(bits, group, n, k, &mt);
+  if (st != QW_OK) return st;
+  if (m < 0 || mul_overflows(m, n) || mul_overflows(m, k)) return QW_EM;
+  if (m <= QW_MATMUL_GEMV_MAX_M)
+    return qw_gemv(bits, group, n, k, payload, scales, m, x, y, stream);
+  if (n == 0) return QW_OK;
+  if (qw_matmul_work_bytes(m, k) > QW_MATMUL_NOALLOC_MAX_BYTES) return QW_ESCRATCH;
+  if (!y) return QW_ENULL;
+  if (k == 0) return record(qw::launch_fill_zero(y, m * n, (hipStream_t)stream));
+  if (!payload || !scales || !x) return QW_ENULL;
+  void* work = nullptr;
+  st = scratch_address((hipStream_t)stream, &work);
+  if (st != QW_OK) return st;
+  return matmul_with_work(mt, payload, scales, m, x, y, work, (hipStream_t)stream);
 }
 
 int64_t qw_gptq_hessian_work_bytes(int64_t k, int64_t t) {

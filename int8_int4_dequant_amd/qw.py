@@ -25,13 +25,15 @@ BATCH_PER_LAUNCH = 256
 
 QW_OK = 0
 STATUS_NAMES = {0: "QW_OK", -1: "QW_EBITS", -2: "QW_EGROUP", -3: "QW_ESHAPE", -4: "QW_EM",
-                -5: "QW_ENULL", -6: "QW_EHIP", -7: "QW_ECOUNT", -8: "QW_EWORK", -9: "QW_EARG"}
+                -5: "QW_ENULL", -6: "QW_EHIP", -7: "QW_ECOUNT", -8: "QW_EWORK", -9: "QW_EARG",
+                -10: "QW_ESCRATCH"}
 
 #: symbols declared in include/qw.h
 EXPORTS = ["qw_payload_bytes", "qw_num_scales", "qw_status_string", "qw_last_error",
            "qw_quantize_pack", "qw_quantize_pack_batched", "qw_unpack", "qw_unpack_batched",
            "qw_gemv",
            "qw_gemv_batched", "qw_gemv_chain", "qw_gemm", "qw_matmul_work_bytes", "qw_matmul",
+           "qw_matmul_noalloc",
            "qw_debug_path",
            "qw_gptq_hessian_work_bytes", "qw_gptq_hessian", "qw_gptq_factor_work_bytes",
            "qw_gptq_factor", "qw_gptq_quantize_work_bytes", "qw_gptq_quantize_pack"]
@@ -39,6 +41,8 @@ EXPORTS = ["qw_payload_bytes", "qw_num_scales", "qw_status_string", "qw_last_err
 
 # Rows up to which qw_matmul runs the codes GEMV (QW_MATMUL_GEMV_MAX_M in qw.h).
 MATMUL_GEMV_MAX_M = 4
+# Bytes of the static scratch of qw_matmul_noalloc (QW_MATMUL_NOALLOC_MAX_BYTES).
+MATMUL_NOALLOC_MAX_BYTES = 32 << 20
 
 
 class QwQuantDesc(ctypes.Structure):
@@ -117,6 +121,8 @@ def lib():
     L.qw_matmul_work_bytes.restype = i64
     L.qw_matmul.argtypes = [i32, i64, i64, i64, vp, vp, i64, vp, vp, vp, i64, vp]
     L.qw_matmul.restype = i32
+    L.qw_matmul_noalloc.argtypes = [i32, i64, i64, i64, vp, vp, i64, vp, vp, vp]
+    L.qw_matmul_noalloc.restype = i32
     L.qw_debug_path.argtypes = [i32, i32, i64, i64, i64, vp, vp]
     L.qw_debug_path.restype = i32
     L.qw_gptq_hessian_work_bytes.argtypes = [i64, i64]
@@ -244,6 +250,11 @@ def qw_matmul_work_bytes(m, k):
 def qw_matmul(bits, group, n, k, payload, scales, m, x, y, work, work_bytes, stream=None):
     return lib().qw_matmul(bits, group, n, k, _ptr(payload), _ptr(scales), m, _ptr(x), _ptr(y),
                            _ptr(work), work_bytes, _stream(stream))
+
+
+def qw_matmul_noalloc(bits, group, n, k, payload, scales, m, x, y, stream=None):
+    return lib().qw_matmul_noalloc(bits, group, n, k, _ptr(payload), _ptr(scales), m, _ptr(x),
+                                   _ptr(y), _stream(stream))
 
 
 def qw_debug_path(op, bits, group, n, k, a=None, b=None):

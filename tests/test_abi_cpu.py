@@ -249,3 +249,22 @@ def test_binding_checks_buffers_before_any_call():
     for fn, word in cases:
         with pytest.raises(ValueError, match=word):
             fn()
+
+
+def test_noalloc_matmul_size_limit_before_any_launch():
+    """qw_matmul_noalloc refuses an x whose bf16 copy exceeds its static
+    scratch (QW_ESCRATCH) during validation, before it looks up the scratch
+    or launches anything (so this runs without a GPU)."""
+    L = qw.lib()
+    cap = qw.MATMUL_NOALLOC_MAX_BYTES
+    k = 4096
+    m_ok, m_big = cap // (2 * k), cap // (2 * k) + 1
+    assert L.qw_matmul_work_bytes(m_ok, k) <= cap < L.qw_matmul_work_bytes(m_big, k)
+    assert L.qw_matmul_noalloc(4, 128, 16, k, None, None, m_big, None, None, None) == -10
+    assert L.qw_matmul_noalloc(4, 128, 16, k, None, None, m_ok, None, None, None) == -5
+    assert L.qw_matmul_noalloc(4, 100, 16, k, None, None, m_ok, None, None, None) == -2
+    assert L.qw_matmul_noalloc(4, 128, 16, k, None, None, -1, None, None, None) == -4
+    assert b"scratch" in L.qw_status_string(-10)
+    txt = open(os.path.join(ROOT, "include", "qw.h")).read()
+    assert re.search(r"#define QW_MATMUL_NOALLOC_MAX_BYTES \(32ll << 20\)", txt)
+    assert cap == 32 << 20
