@@ -155,15 +155,23 @@ def parse():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="after the timed steps, copy a buffer of this many MiB on the device "
                          "(the known-size kernel that calibrates the HBM byte counters)")
+    ap.add_argument("--pmc-table", nargs="+", metavar="DIR",
+                    help="print the activity-counter table of rocprofv3 --pmc CSV runs and exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the traffic summary of two rocprofv3 --pmc runs and exit")
     ap.add_argument("--no-gptq", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the context legs (device copy and read, torch.matmul bf16)")
     ap.add_argument("--only-gptq", action="store_true",
                     help="run only the GPTQ leg and print its JSON object (for profiling)")
     ap.add_argument("--gptq-reps", type=int, default=3)
     ap.add_argument("--no-clock", action="store_true",
                     help="do not sample the GPU clock and power during the timed regions")
-    ap.add_argument("--cpu-sample-worker", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--cpu-protocol", metavar="OUT_MD",
+                    help="run only the oracle timing protocol in full (the page's 20 warm-ups + "
+                         "101 reps on c1-c3, the whole stack and the whole GEMM, both modes); "
+                         "write its table to OUT_MD and print the JSON")
+    ap.add_argument("--cpu-worker", help=argparse.SUPPRESS)
     ap.add_argument("--gptq-cpu-sample-worker", action="store_true", help=argparse.SUPPRESS)
     return ap.parse_args()
 
@@ -175,11 +183,11 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "pmc_traffic_c4_c5_gptq_layer.md")
 # kernel-name fragment -> (label, source file whose hash pins the measurement,
 # grid size in threads or None): the benchmark's own launches -- the c5 GEMM is
 # the 262144-thread grid of gemm_kernel<4> (the M sweep launches it too), the
-# decode pass the 10878976-thread grid of gemv8_kernel<4, 1, 8, 256>
+# decode pass the 5439488-thread grid of gemv8_kernel<4, 1, 16, 256>
 PMC_KERNELS = {
     "quant_subgroup_batched_kernel": ("quantize_pack_batched", "quantize.hip", None),
     # the whole-stack pass (the chained pass launches the same kernel per stage)
-    "gemv8_kernel<4, 1, 8, 256>": ("gemv_batched_m1", "gemv.hip", 10878976),
+    "gemv8_kernel<4, 1, 16, 256>": ("gemv_batched_m1", "gemv.hip", 5439488),
     "gemm_kernel<4>": ("gemm", "gemm.hip", 262144),
     # the GPTQ leg's H accumulation over the 1368-input map (the only launch
     # of the 128-wide fp32-operand shape)
@@ -235,6 +243,82 @@ def pmc_summary(fetch_dir, write_dir, copy_mib):
             "kernels": kernels, "source_sha256": source_hashes()}
 
 
+# Launches whose activity counters `--pmc-table` reports: (label, kernel-name
+# fragment, grid size in threads or None).
+PMC_TABLE_KERNELS = [
+    ("c4 decode pass (qw_gemv_batched, M=1, 224 matrices)", "gemv8_kernel<4, 1, 16, 256>",
+     21248 * 256),
+    ("c3 up 11008x4096 M=1 (qw_gemv)", "gemv8_split_kernel<4, 1, 4, 1>", 2752 * 256),
+    ("c3 up 11008x4096 M=4", "gemv8_split_kernel<4, 4, 8, 1>", 1376 * 256),
+    ("c3 down 4096x11008 M=4", "gemv8_split_kernel<4, 4, 8, 1>", 512 * 256),
+    ("c3 up 11008x4096 M=8", "gemv8_split_kernel<4, 8, 8, 1>", 1376 * 256),
+    ("c3 down 4096x11008 M=8", "gemv8_split_kernel<4, 8, 8, 1>", 512 * 256),
+    ("c5 prefill GEMM 2048x28672x8192", "gemm_kernel<4>", 262144),
+    ("c4 quantize pass (qw_quantize_pack_batched)", "quant_subgroup_batched_kernel<4, 8>", None),
+]
+SIMDS = 1024   # 256 compute units x 4
+XCDS = 8
+
+
+def pmc_table(dirs):
+    """Markdown table of the activity counters of PMC_TABLE_KERNELS from
+    rocprofv3 --pmc CSV runs (one counter set per directory): the mean per
+    dispatch of each counter, and derived ratios."""
+    import csv
+    import glob
+    vals = {}   # label -> counter -> [values]
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                for label, frag, grid in PMC_TABLE_KERNELS:
+                    if frag in r["Kernel_Name"] and (grid is None or int(r["Grid_Size"]) == grid):
+                        vals.setdefault(label, {}).setdefault(r["Counter_Name"], []).append(
+                            float(r["Counter_Value"]))
+    mean = {lb: {c: sum(v) / len(v) for c, v in cs.items()} for lb, cs in vals.items()}
+    counters = sorted({c for cs in mean.values() for c in cs})
+    labels = [lb for lb, _, _ in PMC_TABLE_KERNELS if lb in mean]
+    lines = ["| counter (mean per dispatch) | " + " | ".join(labels) + " |",
+             "|---|" + "---:|" * len(labels)]
+    for c in counters:
+        lines.append(f"| {c} | " + " | ".join(
+            f"{mean[lb][c]:,.0f}" if c in mean[lb] else "" for lb in labels) + " |")
+
+    def ratio(lb, a, b, scale=1.0):
+        m = mean[lb]
+        return f"{scale * m[a] / m[b]:.3f}" if a in m and b in m and m[b] else ""
+    derived = [
+        ("VALU instructions issued per SIMD per cycle (SQ_INSTS_VALU / (GRBM_GUI_ACTIVE / 8 "
+         "XCDs) / 1024 SIMDs)", "SQ_INSTS_VALU", "GRBM_GUI_ACTIVE", XCDS / SIMDS),
+        ("share of wave cycles issuing VALU (SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES)",
+         "SQ_ACTIVE_INST_VALU", "SQ_WAVE_CYCLES", 1.0),
+        ("share of wave cycles waiting (SQ_WAIT_ANY / SQ_WAVE_CYCLES)", "SQ_WAIT_ANY",
+         "SQ_WAVE_CYCLES", 1.0),
+        ("share of wave cycles waiting on an instruction (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES)",
+         "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES", 1.0),
+        ("resident waves per SIMD (SQ_WAVE_CYCLES / (GRBM_GUI_ACTIVE / 8) / 1024)",
+         "SQ_WAVE_CYCLES", "GRBM_GUI_ACTIVE", XCDS / SIMDS),
+        ("matrix-core busy share of SIMD cycles (SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / "
+         "8) / 1024)", "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE", XCDS / SIMDS),
+        ("vector memory instructions per wave (SQ_INSTS_VMEM_RD / SQ_WAVES)", "SQ_INSTS_VMEM_RD",
+         "SQ_WAVES", 1.0),
+        ("mean vector memory instructions in flight per wave (SQ_INST_LEVEL_VMEM / "
+         "SQ_WAVE_CYCLES)", "SQ_INST_LEVEL_VMEM", "SQ_WAVE_CYCLES", 1.0),
+        ("L2 hit share (TCC_HIT_sum / (TCC_HIT_sum + TCC_MISS_sum))", "TCC_HIT_sum",
+         "TCC_REQ_EST", 1.0),
+        ("mean L1->L2 read latency, cycles (TCP_TCC_READ_REQ_LATENCY_sum / TCP_TCC_READ_REQ_sum)",
+         "TCP_TCC_READ_REQ_LATENCY_sum", "TCP_TCC_READ_REQ_sum", 1.0),
+    ]
+    for m in mean.values():
+        if "TCC_HIT_sum" in m and "TCC_MISS_sum" in m:
+            m["TCC_REQ_EST"] = m["TCC_HIT_sum"] + m["TCC_MISS_sum"]
+    lines += ["", "| derived | " + " | ".join(labels) + " |", "|---|" + "---:|" * len(labels)]
+    for name, a, b, sc in derived:
+        lines.append(f"| {name} | " + " | ".join(ratio(lb, a, b, sc) for lb in labels) + " |")
+    n = {lb: max(len(v) for v in vals[lb].values()) for lb in labels}
+    lines += ["", "Dispatches averaged: " + ", ".join(f"{lb}: {n[lb]}" for lb in labels) + "."]
+    return "\n".join(lines)
+
+
 def measured_traffic(label):
     """HBM bytes per launch of `label` from the committed counter summary, or
     None when the summary is missing or the kernel sources changed since."""
@@ -253,98 +337,360 @@ def measured_traffic(label):
 
 
 # ---------------------------------------------------------------- CPU leg
+#
+# The oracle on this machine's host cores, timed the way the 量化推理 page's
+# script times its CPU paths (function `benchmark`: warm-up calls, then timed
+# calls, median and p90 of the per-call times), in two modes:
+#   one thread -- BLAS / OpenMP threads pinned to 1, as that script pins them;
+#   all cores  -- each call split into row blocks (a group never crosses a
+#                 row) over a pool of one process per host core, one BLAS
+#                 thread each; weights, payload and scales sit in shared
+#                 memory, so no timed call ships them between processes.
+# The default run stays bounded (~20 s of CPU work per mode): the page's 20
+# warm-ups + 101 reps on the tiny config, fewer on the 4096 and MLP matrices
+# (the counts are reported with each figure), layer 0 of the 7B stack, and a
+# 256-row block of the 70B GEMM.  `--cpu-protocol` runs 20 + 101 on c1-c3,
+# the whole stack streamed one matrix at a time (3 reps) and the whole GEMM
+# (3 reps), with the one-thread legs in separate processes on separate cores.
+
+CPU_DEFAULT = {"c1": (20, 101), "c2": (2, 5), "c3": (1, 2), "c4": (0, 3), "c5": (1, 3),
+               "c4_layers": 1, "c5_rows": 256}
+CPU_FULL = {"c1": (20, 101), "c2": (20, 101), "c3": (20, 101), "c4": (0, 3), "c5": (0, 3),
+            "c4_layers": 32, "c5_rows": 28672}
 
 
-def cpu_sample_worker():
-    """Runs in a child process with one BLAS / OpenMP thread: the oracle on
-    layer 0 of the stack (7 matrices), quantize + pack then the M = 1 GEMV."""
+def _stats(ts_ns):
+    t = sorted(ts_ns)
+    return {"median_us": round(statistics.median(t) / 1e3, 1),
+            "p90_us": round(t[int(0.9 * (len(t) - 1))] / 1e3, 1)}
+
+
+def _entry(cfg, op, ts_ns, warm, nbytes=None, flops=None, **extra):
+    e = {"config": cfg, "op": op, "warmups": warm, "reps": len(ts_ns), **_stats(ts_ns), **extra}
+    med_s = statistics.median(ts_ns) * 1e-9
+    if nbytes is not None:
+        e["bytes"] = nbytes
+        e["GB/s"] = round(nbytes / med_s / 1e9, 4)
+    if flops is not None:
+        e["flops"] = flops
+        e["TFLOP/s"] = round(flops / med_s / 1e12, 5)
+    return e
+
+
+def _timed(fn, warm, reps):
+    for _ in range(warm):
+        fn()
+    ts = []
+    for _ in range(reps):
+        t0 = time.perf_counter_ns()
+        fn()
+        ts.append(time.perf_counter_ns() - t0)
+    return ts
+
+
+class _Runner:
+    """Runs oracle calls on row blocks: in this process (one thread) or over
+    a process pool with the arrays in shared memory (all cores)."""
+
+    def __init__(self, pool=None, folder=None):
+        self.pool, self.folder, self.n = pool, folder, 0
+
+    def share(self, a):
+        """The array as the workers will see it (a memmap path or itself)."""
+        if self.pool is None:
+            return a
+        self.n += 1
+        path = os.path.join(self.folder, f"a{self.n}.npy")
+        np = __import__("numpy")
+        mm = np.lib.format.open_memmap(path, mode="w+", dtype=a.dtype, shape=a.shape)
+        mm[...] = a
+        mm.flush()
+        return path
+
+    def out(self, dtype, shape):
+        np = __import__("numpy")
+        if self.pool is None:
+            return np.empty(shape, dtype)
+        self.n += 1
+        path = os.path.join(self.folder, f"a{self.n}.npy")
+        np.lib.format.open_memmap(path, mode="w+", dtype=dtype, shape=shape).flush()
+        return path
+
+    def release(self):
+        """Delete the shared arrays made so far (all-cores mode)."""
+        if self.pool is None:
+            return
+        for f in os.listdir(self.folder):
+            os.remove(os.path.join(self.folder, f))
+
+    def call(self, op, n, **kw):
+        """op over rows [0, n): inline, or as row blocks over the pool."""
+        if self.pool is None:
+            _cpu_block((op, 0, n, kw))
+            return
+        parts = max(1, min(n, self.pool._max_workers))
+        step = -(-n // parts)
+        list(self.pool.map(_cpu_block, [(op, r, min(n, r + step), kw)
+                                        for r in range(0, n, step)]))
+
+
+def _arr(a, mode="r"):
+    np = __import__("numpy")
+    return np.load(a, mmap_mode=mode) if isinstance(a, str) else a
+
+
+def _cpu_block(task):
+    """One row block [r0, r1) of an oracle call (weights [n][k], groups
+    inside rows): quantize_pack, unpack, gemv (x fp32) or gemm (x bf16)."""
     import numpy as np
 
     import oracle
-    from int8_int4_dequant_amd import inputs
 
-    total_bytes = 0
-    elapsed = 0.0
-    weights = 0
-    for slot, (tag, n, k) in enumerate(inputs.C4_SLOTS):
-        w = inputs.c4_weight(0, slot)
-        x = inputs.c4_x(k)
-        t0 = time.perf_counter()
-        rec = oracle.quantize_pack(w, 4, 32)
-        oracle.gemv_ref(rec, x)
-        elapsed += time.perf_counter() - t0
-        total_bytes += step_bytes_matrix(n, k)
-        weights += n * k
-    print(json.dumps(dict(seconds=elapsed, bytes=total_bytes, weights=weights)))
-
-
-def _oracle_matrix(slot):
-    """One matrix of layer 0: oracle quantize + pack, then the M = 1 GEMV
-    (worker of the all-cores baseline; returns seconds and bytes)."""
-    import oracle
-    from int8_int4_dequant_amd import inputs
-
-    tag, n, k = inputs.C4_SLOTS[slot]
-    w = inputs.c4_weight(0, slot)
-    x = inputs.c4_x(k)
-    t0 = time.perf_counter()
-    rec = oracle.quantize_pack(w, 4, 32)
-    oracle.gemv_ref(rec, x)
-    return time.perf_counter() - t0, step_bytes_matrix(n, k)
+    op, r0, r1, kw = task
+    bits, group, k = kw["bits"], kw["group"], kw["k"]
+    pb, sg = k * bits // 8, k // group
+    if op == "quantize_pack":
+        w = _arr(kw["w"])
+        rec = oracle.quantize_pack(np.asarray(w[r0:r1]), bits, group)
+        _arr(kw["payload"], "r+")[r0 * pb:r1 * pb] = rec["payload"]
+        _arr(kw["scales"], "r+")[r0 * sg:r1 * sg] = rec["scales"]
+        return
+    rec = dict(bits=bits, group=group, shape=[r1 - r0, k],
+               payload=np.asarray(_arr(kw["payload"])[r0 * pb:r1 * pb]),
+               scales=np.asarray(_arr(kw["scales"])[r0 * sg:r1 * sg]))
+    if op == "unpack":
+        _arr(kw["out"], "r+")[r0:r1] = oracle.unpack(rec)
+    elif op == "gemv":
+        _arr(kw["out"], "r+")[:, r0:r1] = oracle.gemv_ref(rec, _arr(kw["x"]))
+    else:
+        _arr(kw["out"], "r+")[:, r0:r1] = oracle.gemm_ref(rec, _arr(kw["x"]))
 
 
-def cpu_baseline_all_cores():
-    """The same layer-0 sample with the 7 matrices spread over a process
-    pool (one matrix per process, default BLAS threads), timed wall-clock."""
+def _qbytes(n, k, bits, group):
+    return n * k * 4 + n * k * bits // 8 + 4 * (n * k // group)
+
+
+def _ubytes(n, k, bits, group):
+    return n * k * bits // 8 + 4 * (n * k // group) + 4 * n * k
+
+
+def _gbytes(n, k, bits, group, m):
+    return n * k * bits // 8 + 4 * (n * k // group) + 4 * m * k + 4 * m * n
+
+
+def _matrix_legs(run, cfg, w, bits, group, reps, ms, x_of, tag=""):
+    """quantize_pack, unpack and the GEMV at every m of one matrix."""
+    n, k = w.shape
+    warm, nrep = reps
+    kw = dict(bits=bits, group=group, k=k, w=run.share(w))
+    kw["payload"] = run.out("uint8", (n * k * bits // 8,))
+    kw["scales"] = run.out("float32", (n * k // group,))
+    out = [_entry(cfg, f"quantize_pack{tag}", _timed(lambda: run.call("quantize_pack", n, **kw),
+                                                     warm, nrep), warm, _qbytes(n, k, bits, group))]
+    kw["out"] = run.out("float32", (n, k))
+    out.append(_entry(cfg, f"unpack{tag}", _timed(lambda: run.call("unpack", n, **kw), warm, nrep),
+                      warm, _ubytes(n, k, bits, group)))
+    for m in ms:
+        kg = dict(kw, x=run.share(x_of(m)), out=run.out("float64", (m, n)))
+        out.append(_entry(cfg, f"gemv_m{m}{tag}", _timed(lambda: run.call("gemv", n, **kg), warm,
+                                                        nrep), warm, _gbytes(n, k, bits, group, m),
+                          2 * m * n * k))
+    return out
+
+
+def cpu_legs(mode, plan, legs):
+    """The oracle legs `legs` (c1 .. c5) in this process, one thread or all
+    cores; returns a list of entries."""
     import concurrent.futures as cf
     import multiprocessing as mp
+    import tempfile
 
-    cores = len(os.sched_getaffinity(0))
-    procs = min(7, cores)
-    ctx = mp.get_context("spawn")
-    # BLAS threads per process so the pool does not oversubscribe the cores
-    saved = {v: os.environ.get(v) for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
-                                            "MKL_NUM_THREADS")}
-    for v in saved:
-        os.environ[v] = str(max(1, cores // procs))
+    from int8_int4_dequant_amd import inputs
+
+    pool, tmp = None, None
+    if mode == "all_cores":
+        cores = len(os.sched_getaffinity(0))
+        for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+            os.environ[v] = "1"
+        pool = cf.ProcessPoolExecutor(max_workers=cores, mp_context=mp.get_context("spawn"))
+        tmp = tempfile.TemporaryDirectory(dir="/dev/shm" if os.path.isdir("/dev/shm") else None)
+    run = _Runner(pool, tmp.name if tmp else None)
+    out = []
     try:
-        res, wall = _pool_run(cf, ctx, procs)
+        if pool is not None:  # start every worker (imports) outside the timing
+            list(pool.map(time.sleep, [0.2] * (2 * pool._max_workers)))
+        if "c1" in legs:
+            w, x = inputs.c1_weight(), inputs.c1_x()
+            for bits in (8, 4):
+                out += _matrix_legs(run, "c1", w, bits, 32, plan["c1"], [1], lambda m: x,
+                                    f"_int{bits}")
+        if "c2" in legs:
+            out += _matrix_legs(run, "c2", inputs.c2_weight(), 8, 4096, plan["c2"], [1],
+                                lambda m: inputs.c2_x())
+        for j, mat in enumerate(inputs.C3["mats"]):
+            if f"c3_{mat['tag']}" in legs or "c3" in legs:
+                out += _matrix_legs(run, "c3", inputs.c3_weight(j), 4, 128, plan["c3"],
+                                    inputs.C3["ms"], lambda m, j=j: inputs.c3_x(j, m),
+                                    f"_{mat['tag']}")
+        for leg in legs:
+            if leg.startswith("c4"):
+                out.append(_c4_leg(run, plan, leg))
+        if "c5" in legs:
+            out.append(_c5_leg(run, plan))
     finally:
-        for v, old in saved.items():
-            if old is None:
-                os.environ.pop(v, None)
-            else:
-                os.environ[v] = old
-    total = sum(b for _, b in res)
-    return {"value": round(total / wall / 1e9, 4), "unit": "GB/s", "cores": cores,
-            "processes": procs, "kind": "oracle",
-            "sample": f"layer 0 of the stack (7 matrices), one process per matrix on {cores} "
-                      f"host cores, {wall:.2f} s wall"}
+        if pool is not None:
+            pool.shutdown()
+        if tmp is not None:
+            tmp.cleanup()
+    return out
 
 
-def _pool_run(cf, ctx, procs):
-    with cf.ProcessPoolExecutor(max_workers=procs, mp_context=ctx) as ex:
-        list(ex.map(_oracle_matrix, [0]))  # start-up outside the timing
-        t0 = time.perf_counter()
-        res = list(ex.map(_oracle_matrix, range(7)))
-        wall = time.perf_counter() - t0
-    return res, wall
+def _c4_leg(run, plan, leg):
+    """The step's work on the stack (quantize_pack then the M = 1 GEMV of
+    every matrix), one matrix at a time, weights generated outside the
+    timing; `leg` = "c4" or "c4:i/s" (shard i of s of the matrices)."""
+    from int8_int4_dequant_amd import inputs
+
+    mats = [m for m in inputs.c4_matrices() if m[0] < plan["c4_layers"]]
+    if ":" in leg:
+        i, s = map(int, leg.split(":")[1].split("/"))
+        mats = mats[i::s]
+    warm, nrep = plan["c4"]
+    reps, nbytes = [0] * nrep, 0
+    for layer, tag, n, k, seed in mats:
+        w = inputs.weight(seed, n, k, inputs.C4["sigma"])
+        kw = dict(bits=4, group=32, k=k, w=run.share(w), x=run.share(inputs.c4_x(k)))
+        kw["payload"] = run.out("uint8", (n * k // 2,))
+        kw["scales"] = run.out("float32", (n * k // 32,))
+        kw["out"] = run.out("float64", (1, n))
+
+        def step():
+            run.call("quantize_pack", n, **kw)
+            run.call("gemv", n, **kw)
+        for r, t in enumerate(_timed(step, warm, nrep)):
+            reps[r] += t
+        nbytes += _qbytes(n, k, 4, 32) + _gbytes(n, k, 4, 32, 1)
+        run.release()
+    return _entry("c4", f"quantize_pack+gemv_m1 ({len(mats)} matrices)", reps, warm, nbytes,
+                  matrices=len(mats), rep_us=[round(t / 1e3, 1) for t in reps])
 
 
-def cpu_baseline():
+def _c5_leg(run, plan):
+    """The prefill GEMM's oracle (fp64 product of the 2048 bf16 rows with the
+    dequantized weight) on the first `c5_rows` weight rows, plus their
+    quantize_pack outside the timing; TFLOP/s of that block."""
+    from int8_int4_dequant_amd import inputs
+
+    c = inputs.C5
+    rows = plan["c5_rows"]
+    w = inputs.c5_weight()[:rows]
+    xb = inputs.c5_x_bf16()
+    kw = dict(bits=4, group=128, k=c["k"], w=run.share(w), x=run.share(xb))
+    kw["payload"] = run.out("uint8", (rows * c["k"] // 2,))
+    kw["scales"] = run.out("float32", (rows * c["k"] // 128,))
+    kw["out"] = run.out("float64", (c["m"], rows))
+    run.call("quantize_pack", rows, **kw)
+    warm, nrep = plan["c5"]
+    ts = _timed(lambda: run.call("gemm", rows, **kw), warm, nrep)
+    return _entry("c5", f"gemm ({c['m']} x {rows} x {c['k']}, fp64)", ts, warm,
+                  flops=2 * c["m"] * rows * c["k"], rows=rows)
+
+
+def cpu_worker(spec):
+    """Child-process entry: spec = {mode, plan, legs}; prints the entries."""
+    d = json.loads(spec)
+    print(json.dumps(cpu_legs(d["mode"], d["plan"], d["legs"])))
+
+
+def _run_cpu_child(mode, plan, legs, core=None, timeout=3600):
     env = dict(os.environ)
-    for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "VECLIB_MAXIMUM_THREADS"):
-        env[v] = "1"
-    r = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-sample-worker"],
-                       capture_output=True, text=True, env=env, timeout=900)
-    if r.returncode != 0:
-        log(r.stderr[-2000:])
-        return None
-    d = json.loads(r.stdout.strip().splitlines()[-1])
-    return {"value": round(d["bytes"] / d["seconds"] / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
-            "sample": f"layer 0 of the stack (7 matrices, {d['weights']} weights): oracle "
-                      f"quantize_pack + fp64 GEMV, {d['seconds']:.2f} s, one thread"}
+    if mode == "one_thread":
+        for v in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS",
+                  "VECLIB_MAXIMUM_THREADS"):
+            env[v] = "1"
+    spec = json.dumps({"mode": mode, "plan": plan, "legs": legs})
+    pre = (lambda: os.sched_setaffinity(0, {core})) if core is not None else None
+    return subprocess.Popen([sys.executable, os.path.abspath(__file__), "--cpu-worker", spec],
+                            stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, env=env,
+                            preexec_fn=pre)
+
+
+def _collect(procs, timeout=3600):
+    out = []
+    for p in procs:
+        so, se = p.communicate(timeout=timeout)
+        if p.returncode != 0:
+            log(se[-2000:])
+            raise RuntimeError("oracle timing child failed")
+        out += json.loads(so.strip().splitlines()[-1])
+    return out
+
+
+def cpu_baselines(full=False):
+    """Both modes over every config; returns (cpu_baseline, all_cores,
+    configs).  The default plan runs each mode in one child process; the
+    full protocol runs the one-thread legs in parallel children, one core
+    each (reported), then the all-cores legs."""
+    plan = CPU_FULL if full else CPU_DEFAULT
+    cores = sorted(os.sched_getaffinity(0))
+    if full:
+        shards = max(1, min(8, len(cores) - 5))
+        legs = [["c1", "c2"], ["c3_up"], ["c3_down"], ["c5"]] + \
+            [[f"c4:{i}/{shards}"] for i in range(shards)]
+        procs = [_run_cpu_child("one_thread", plan, lg, cores[i % len(cores)])
+                 for i, lg in enumerate(legs)]
+        one = _collect(procs)
+        # the c4 shards of each rep add up to the stack's rep
+        c4 = [e for e in one if e["config"] == "c4"]
+        if c4:
+            one = [e for e in one if e["config"] != "c4"] + [_merge_c4(c4)]
+        concurrent = len(legs)
+    else:
+        one = _collect([_run_cpu_child("one_thread", plan, ["c1", "c2", "c3", "c4", "c5"])])
+        concurrent = 1
+    # (the 256 x 256 matrix is too small to split: its calls would time the
+    # pool's dispatch, so it runs in the one-thread mode only)
+    allc = _collect([_run_cpu_child("all_cores", plan, ["c2", "c3", "c4", "c5"])])
+    c4a = next(e for e in one if e["config"] == "c4")
+    c4b = next(e for e in allc if e["config"] == "c4")
+    sample = (f"{c4a['op']} of the 7B stack ({'all 32 layers' if plan['c4_layers'] == 32 else 'layer 0'}), "
+              f"weights generated outside the timing; median of {c4a['reps']} reps")
+    one_thread = {"value": c4a["GB/s"], "unit": "GB/s", "cores": 1, "kind": "oracle",
+                  "sample": sample, "median_us": c4a["median_us"], "p90_us": c4a["p90_us"]}
+    all_cores = {"value": c4b["GB/s"], "unit": "GB/s", "cores": len(cores), "kind": "oracle",
+                 "sample": sample + "; row blocks over one process per core",
+                 "median_us": c4b["median_us"], "p90_us": c4b["p90_us"]}
+    configs = {"protocol": "full (the page's 20 warm-ups + 101 reps on c1-c3)" if full
+               else "bounded (reps per entry)",
+               "host_cores": len(cores), "one_thread_processes_at_once": concurrent,
+               "one_thread": one, "all_cores": allc}
+    return one_thread, all_cores, configs
+
+
+def _merge_c4(parts):
+    """The stack's reps from its shards' reps (each shard timed one thread,
+    on its own core): rep r of the stack = the sum of the shards' rep r."""
+    reps = [sum(p["rep_us"][r] for p in parts) * 1e3 for r in range(len(parts[0]["rep_us"]))]
+    matrices = sum(p["matrices"] for p in parts)
+    return _entry("c4", f"quantize_pack+gemv_m1 ({matrices} matrices; {len(parts)} shards "
+                        f"timed on separate cores, reps summed)", reps, parts[0]["warmups"],
+                  sum(p["bytes"] for p in parts), matrices=matrices,
+                  rep_us=[round(t / 1e3, 1) for t in reps])
+
+
+def cpu_protocol_summary(res):
+    """Markdown table of a --cpu-protocol run."""
+    one, allc, cfgs = res
+    lines = [f"Host cores: {cfgs['host_cores']}; one-thread legs run "
+             f"{cfgs['one_thread_processes_at_once']} processes at once, one core each.", "",
+             "| mode | config | op | warm-ups | reps | median µs | p90 µs | GB/s | TFLOP/s |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for mode in ("one_thread", "all_cores"):
+        for e in cfgs[mode]:
+            lines.append(f"| {mode} | {e['config']} | {e['op']} | {e['warmups']} | {e['reps']} | "
+                         f"{e['median_us']} | {e['p90_us']} | {e.get('GB/s', '')} | "
+                         f"{e.get('TFLOP/s', '')} |")
+    return "\n".join(lines)
 
 
 # ------------------------------------------------------------ accounting
@@ -358,20 +704,26 @@ def gemv_bytes(n, k, m=1, bits=4, group=32):
     return n * k * bits // 8 + 4 * (n * k // group) + 4 * m * k + 4 * m * n
 
 
-def step_bytes_matrix(n, k):
-    return quant_bytes(n, k) + gemv_bytes(n, k)
-
-
 # ----------------------------------------------------------------- main
 
 
 def main():
     args = parse()
-    if args.cpu_sample_worker:
-        cpu_sample_worker()
+    if args.cpu_worker:
+        cpu_worker(args.cpu_worker)
+        return
+    if args.cpu_protocol:
+        res = cpu_baselines(full=True)
+        with open(args.cpu_protocol, "w") as f:
+            f.write(cpu_protocol_summary(res) + "\n")
+        print(json.dumps({"cpu_baseline": res[0], "cpu_baseline_all_cores": res[1],
+                          "cpu_baseline_configs": res[2]}), flush=True)
         return
     if args.gptq_cpu_sample_worker:
         gptq_cpu_sample_worker()
+        return
+    if args.pmc_table:
+        print(pmc_table(args.pmc_table))
         return
     if args.pmc_summary:
         print("```json\n" + json.dumps(pmc_summary(*args.pmc_summary, copy_mib=1024), indent=1)
@@ -584,6 +936,12 @@ def main():
                            else "qw_gemv_batched") + " (int4 g32, 224 matrices per step)",
                 "algorithmic_bytes_per_launch": round(per_launch),
                 "avg_launch_us": round(q_avg_us if dominant == "quantize_pack" else g_avg_us, 3)}
+    roofline_gemv = {"bound": "hbm", "achieved": round(g_gbs, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(g_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("gemv_batched_m1"),
+                     "kernel": "qw_gemv_batched M=1 (int4 g32, 224 matrices per launch)",
+                     "algorithmic_bytes_per_launch": round(gbytes / gemv_launches),
+                     "avg_launch_us": round(g_avg_us, 3)}
     parts = {
         "quantize_pack": {"GB/s": round(q_gbs, 1), "frac_hbm": round(q_gbs / HBM_PEAK_GBS, 4),
                           "entry": "qw_quantize_pack_batched", "launches_per_pass": quant_launches,
@@ -639,13 +997,14 @@ def main():
 
     gptq = None if args.no_gptq else bench_gptq(args, L, stream)
 
-    cpu = None if args.no_cpu_baseline else cpu_baseline()
-    cpu_all = None
+    context = None if args.no_context else bench_context(args, stream)
+
+    cpu = cpu_all = cpu_cfgs = None
     if not args.no_cpu_baseline:
         try:
-            cpu_all = cpu_baseline_all_cores()
-        except Exception as exc:  # a pool that cannot start is reported, not fatal
-            log(f"all-cores oracle baseline skipped: {exc}")
+            cpu, cpu_all, cpu_cfgs = cpu_baselines()
+        except Exception as exc:  # a child that cannot run is reported, not fatal
+            log(f"oracle baseline skipped: {exc}")
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
@@ -653,13 +1012,17 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
         "data": "synthetic (seeded N(0,0.02) fp32 weights in place of trained 7B layers)",
         "config": {"workload": "c4: 7B-shaped linear stack, 32 layers x (4 x 4096x4096 + 2 x "
-                               "11008x4096 + 4096x11008), int4 group 32; step = quantize+pack "
-                               "all + one M=1 GEMV pass",
+                               "11008x4096 + 4096x11008), int4 group 32. One step = quantize+pack "
+                               "of all 224 matrices (one launch) then one M=1 dequant-GEMV pass "
+                               "(one launch); value = (quantize bytes + GEMV bytes) / step time, "
+                               "a blend of the two kernels. The GEMV pass alone: roofline_gemv "
+                               "and parts.decode_gemv_m1",
                    "layers": args.layers, "matrices": len(shapes), "weights": weights,
                    "bits": 4, "group": 32, "m": 1, "bytes_per_step": qbytes + gbytes},
-        "roofline": roofline, "parts": parts, "decode_gemv_configs": gemv_cfgs,
+        "roofline": roofline, "roofline_gemv": roofline_gemv, "parts": parts,
+        "decode_gemv_configs": gemv_cfgs, "context": context,
         "prefill_gemm": gemm, "gptq": gptq, "cpu_baseline": cpu,
-        "cpu_baseline_all_cores": cpu_all,
+        "cpu_baseline_all_cores": cpu_all, "cpu_baseline_configs": cpu_cfgs,
     }
     print(json.dumps(out), flush=True)
 
@@ -751,6 +1114,74 @@ def bench_chain(args, L, stream, mats, shapes, P, S, xs, gbytes):
             "graph_replay_us": None if graph_us is None else round(graph_us, 1),
             "graph_replay_GB/s": None if graph_us is None else gbs(graph_us),
             "graph_replays_identical": bool(same)}
+
+
+def _event_us(stream, fn, reps):
+    """Per-call GPU times (µs) of `fn`, each bracketed by events on `stream`."""
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return sorted(1e3 * a.elapsed_time(b) for a, b in ev)
+
+
+def bench_context(args, stream):
+    """Practical ceilings of this part, timed in the same run as the
+    kernels: a device copy of 2 GiB (torch: 2 GiB read + 2 GiB written), a
+    read-only reduction over 4 GiB (torch.sum), and the vendor BLAS bf16
+    product (torch.matmul, bf16 in and out, no dequantization) at the
+    prefill shape 2048 x 28672 x 8192 on random operands, with the clock it
+    sustains."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    out = {}
+    gen = torch.Generator(device=dev).manual_seed(1234)
+    n = (2 << 30) // 4
+    src = torch.rand(n, dtype=torch.float32, device=dev, generator=gen)
+    dst = torch.empty_like(src)
+    t = _event_us(stream, lambda: dst.copy_(src), 10)
+    med = statistics.median(t)
+    out["device_copy_2GiB"] = {"bytes": 8 * n, "median_us": round(med, 1),
+                               "GB/s": round(8 * n / (med * 1e-6) / 1e9, 1),
+                               "frac_hbm": round(8 * n / (med * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    del dst
+    big = torch.cat([src, src])
+    del src
+    t = _event_us(stream, lambda: big.sum(), 10)
+    med = statistics.median(t)
+    out["device_read_4GiB"] = {"bytes": 4 * big.numel(), "median_us": round(med, 1),
+                               "GB/s": round(4 * big.numel() / (med * 1e-6) / 1e9, 1),
+                               "frac_hbm": round(4 * big.numel() / (med * 1e-6) / 1e9
+                                                 / HBM_PEAK_GBS, 4)}
+    del big
+    torch.cuda.empty_cache()
+    m, nn, k = 2048, 28672, 8192
+    x = torch.randn((m, k), dtype=torch.float32, device=dev, generator=gen).to(torch.bfloat16)
+    wt = (torch.randn((k, nn), dtype=torch.float32, device=dev, generator=gen) * 0.015
+          ).to(torch.bfloat16)              # the weight's transpose, contiguous
+    y = torch.empty((m, nn), dtype=torch.bfloat16, device=dev)
+    mm = lambda: torch.matmul(x, wt, out=y)  # noqa: E731
+    t = _event_us(stream, mm, 20)
+    med = statistics.median(t)
+    tf = 2.0 * m * nn * k / (med * 1e-6) / 1e12
+    out["torch_matmul_bf16_2048x28672x8192"] = {
+        "median_us": round(med, 1), "p90_us": round(t[int(0.9 * (len(t) - 1))], 1),
+        "TFLOP/s": round(tf, 1), "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
+        "gpu_clock_sustained": sustained_clock(args, mm)}
+    del x, wt, y
+    torch.cuda.empty_cache()
+    log("context: copy {GB/s} GB/s, ".format(**out["device_copy_2GiB"])
+        + "read {GB/s} GB/s, ".format(**out["device_read_4GiB"])
+        + "torch.matmul bf16 {median_us} us = {TFLOP/s} TFLOP/s".format(
+            **out["torch_matmul_bf16_2048x28672x8192"]))
+    return out
 
 
 def bench_gemv_configs(args, L, stream):
@@ -921,6 +1352,7 @@ def bench_gemm(args, L, stream):
     return {"workload": "c5: M=2048 bf16 x (28672 x 8192) int4 group 128, fp32 accumulate",
             "m_sweep_same_weight": sweep,
             "median_us": round(med * 1e3, 2), "p90_us": round(times[int(0.9 * (len(times) - 1))] * 1e3, 2),
+            "rep_us_sorted": [round(t_ * 1e3, 1) for t_ in times],
             "TFLOP/s": round(tf, 2), "gpu_clock_sustained": clock,
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / BF16_PEAK_TFLOPS, 4),

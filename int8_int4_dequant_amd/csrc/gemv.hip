@@ -22,10 +22,14 @@
 //     slices per lane, x staged in LDS, persistent prefetching waves -- were
 //     slower on gfx950: per-lane 128-byte x slices touch 64 cache lines per
 //     load instruction.)  Generic kernel for any other group or alignment.
-//   * int4 decode: two masks split a dword into low and high nibbles as
-//     bytes 0x0u; v_cvt_pk_f32_fp8 turns two such bytes into u * 2^-9
-//     exactly (an OCP e4m3 byte 0x0u has value u * 2^-9 for u < 16) and one
-//     fma gives q = u - 8 exactly.  int8 decode: one sign-extending byte
+//   * int4 decode: flipping a nibble's top bit turns the stored u = q + 8
+//     into q's 4-bit two's complement; moved into the top half of a byte it
+//     is the signed byte 16 * q, which one sign-extending byte conversion
+//     (v_cvt_f32_i32 with a byte select) turns into the exact float 16 * q.
+//     Two three-input bit operations and one shift prepare the 8 codes of a
+//     dword, so 8 codes cost 11 instructions.  The factor 16 is a power of
+//     two: it scales every product, sum and the result exactly and is
+//     removed once per output.  int8 decode: one sign-extending byte
 //     conversion per code.
 //   * fp32 FMAs accumulate x * q over a chunk (8 terms, one group); the chunk
 //     sum times the group's scale is added to the row accumulator.  Every
@@ -117,21 +121,24 @@ constexpr int pow2_at_least(int v) {
 
 // ------------------------------------------------------------ decode helpers
 
-// 8 int4 codes of one dword, in element order, as exact floats q.  An OCP
-// e4m3 byte 0x0u has the value u * 2^-9 for u < 16, so one conversion turns
-// two nibble bytes into u * 2^-9; u * 2^-9 * 512 - 8 = q is exact in an fma.
-__device__ __forceinline__ void decode8_int4(uint32_t w, float (&q)[8]) {
-  const uint32_t lo = w & 0x0F0F0F0Fu;         // elements 0, 2, 4, 6 as bytes 0x0u
-  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;  // elements 1, 3, 5, 7
-  const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
-  const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
-  const f32x2 c = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
-  const f32x2 d = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
-  q[0] = __builtin_fmaf(a.x, 512.0f, -8.0f); q[2] = __builtin_fmaf(a.y, 512.0f, -8.0f);
-  q[4] = __builtin_fmaf(b.x, 512.0f, -8.0f); q[6] = __builtin_fmaf(b.y, 512.0f, -8.0f);
-  q[1] = __builtin_fmaf(c.x, 512.0f, -8.0f); q[3] = __builtin_fmaf(c.y, 512.0f, -8.0f);
-  q[5] = __builtin_fmaf(d.x, 512.0f, -8.0f); q[7] = __builtin_fmaf(d.y, 512.0f, -8.0f);
+// 8 int4 codes of one dword, in element order, as the exact floats 16 * q.
+// Byte i of the dword holds u = q + 8 of elements 2i (low nibble) and 2i + 1
+// (high nibble); u XOR 8 is q's 4-bit two's complement, so with that nibble
+// in the top half of a byte (the low half zero) the byte, read as a signed
+// 8-bit integer, is exactly 16 * q.
+__device__ __forceinline__ void decode8_int4_x16(uint32_t w, float (&q)[8]) {
+  const uint32_t hi = (w & 0xF0F0F0F0u) ^ 0x80808080u;          // elements 1, 3, 5, 7
+  const uint32_t lo = ((w << 4) & 0xF0F0F0F0u) ^ 0x80808080u;   // elements 0, 2, 4, 6
+  q[0] = (float)(int8_t)(lo);       q[1] = (float)(int8_t)(hi);
+  q[2] = (float)(int8_t)(lo >> 8);  q[3] = (float)(int8_t)(hi >> 8);
+  q[4] = (float)(int8_t)(lo >> 16); q[5] = (float)(int8_t)(hi >> 16);
+  q[6] = (float)(int8_t)(lo >> 24); q[7] = (float)(int8_t)(hi >> 24);
 }
+
+// The factor the decoded codes carry (16 for int4, 1 for int8), removed from
+// each output once.
+template <int BITS>
+constexpr float code_unscale() { return BITS == 4 ? 0.0625f : 1.0f; }
 
 // 4 int8 codes of one dword, in element order, exact.
 __device__ __forceinline__ void decode4_int8(uint32_t w, float (&q)[4]) {
@@ -142,6 +149,29 @@ __device__ __forceinline__ void decode4_int8(uint32_t w, float (&q)[4]) {
 }
 
 // ------------------------------------------------------------------ kernels
+
+// acc += (sum over the chunk's 8 codes of x * code) * s.  With one x row the
+// chunk sum runs as two chains of four products (independent instructions
+// for the issue slots); with several rows the rows' chains interleave.
+template <int M>
+__device__ __forceinline__ void chunk_dot(const float (&xm)[8], const float (&q)[8], float s,
+                                          float& acc) {
+  float part;
+  if constexpr (M == 1) {
+    float p0 = xm[0] * q[0], p1 = xm[1] * q[1];
+#pragma unroll
+    for (int e = 2; e < 8; e += 2) {
+      p0 = __builtin_fmaf(xm[e], q[e], p0);
+      p1 = __builtin_fmaf(xm[e + 1], q[e + 1], p1);
+    }
+    part = p0 + p1;
+  } else {
+    part = xm[0] * q[0];
+#pragma unroll
+    for (int e = 1; e < 8; ++e) part = __builtin_fmaf(xm[e], q[e], part);
+  }
+  acc = __builtin_fmaf(part, s, acc);
+}
 
 // A buffer resource over one payload row (raw addressing, `bytes` long:
 // reads past it return zero instead of leaving the row).  Loads through it
@@ -293,7 +323,7 @@ __global__ __launch_bounds__(256) void gemv8_kernel(const GemvBatch<NB> b) {
     for (int r = 0; r < R; ++r) {
       float q[8];
       if constexpr (BITS == 4) {
-        decode8_int4(p[r][0], q);
+        decode8_int4_x16(p[r][0], q);
       } else {
         float q0[4], q1[4];
         decode4_int8(p[r][0], q0);
@@ -302,12 +332,7 @@ __global__ __launch_bounds__(256) void gemv8_kernel(const GemvBatch<NB> b) {
         for (int e = 0; e < 4; ++e) { q[e] = q0[e]; q[4 + e] = q1[e]; }
       }
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        float part = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) part = __builtin_fmaf(xv[m][e], q[e], part);
-        acc[r * M + m] = __builtin_fmaf(part, s[r], acc[r * M + m]);
-      }
+      for (int m = 0; m < M; ++m) chunk_dot<M>(xv[m], q, s[r], acc[r * M + m]);
     }
     if (cpg) {
       gc += step_g;
@@ -320,7 +345,7 @@ __global__ __launch_bounds__(256) void gemv8_kernel(const GemvBatch<NB> b) {
   const int idx = scatter_index<V>(lane);
   if ((lane & (64 / V - 1)) == 0 && idx < R * M) {
     const int r = idx / M, m = idx % M;
-    if (row0 + r < a.n) a.y[(int64_t)m * a.n + row0 + r] = acc[0];
+    if (row0 + r < a.n) a.y[(int64_t)m * a.n + row0 + r] = acc[0] * code_unscale<BITS>();
   }
 }
 
@@ -399,7 +424,7 @@ __global__ __launch_bounds__(256) void gemv8_split_kernel(const GemvBatch<NB> b)
     for (int r = 0; r < R; ++r) {
       float q8[8];
       if constexpr (BITS == 4) {
-        decode8_int4(p[r][0], q8);
+        decode8_int4_x16(p[r][0], q8);
       } else {
         float q0[4], q1[4];
         decode4_int8(p[r][0], q0);
@@ -408,12 +433,7 @@ __global__ __launch_bounds__(256) void gemv8_split_kernel(const GemvBatch<NB> b)
         for (int e = 0; e < 4; ++e) { q8[e] = q0[e]; q8[4 + e] = q1[e]; }
       }
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        float part = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) part = __builtin_fmaf(xv[m][e], q8[e], part);
-        acc[r * M + m] = __builtin_fmaf(part, s[r], acc[r * M + m]);
-      }
+      for (int m = 0; m < M; ++m) chunk_dot<M>(xv[m], q8, s[r], acc[r * M + m]);
     }
     if (cpg) {
       gc += step_g;
@@ -427,7 +447,8 @@ __global__ __launch_bounds__(256) void gemv8_split_kernel(const GemvBatch<NB> b)
   if ((lane & (64 / V - 1)) == 0 && idx < R * M) part_lds[wave][idx] = acc[0];
   __syncthreads();
   if (wave == 0 && lane < R * M) {
-    const float v = ((part_lds[0][lane] + part_lds[1][lane]) + part_lds[2][lane]) + part_lds[3][lane];
+    const float v = (((part_lds[0][lane] + part_lds[1][lane]) + part_lds[2][lane]) +
+                     part_lds[3][lane]) * code_unscale<BITS>();
     const int r = lane / M, m = lane % M;
     if (row0 + r < a.n) a.y[(int64_t)m * a.n + row0 + r] = v;
   }
@@ -463,13 +484,15 @@ __global__ __launch_bounds__(256) void gemv_generic_kernel(
   if (lane == 0) y[mm * n + row] = sum;
 }
 
-// Rows per wave of the streaming kernel: 8 (x reused across more rows, fewer
-// reductions; 8 * m <= 64 partial sums per lane).  Matrices with too few rows
-// to give every SIMD waves that way take the split-K kernel instead (with
-// 4 rows per wave at m > 4, a 28672-row matrix still streamed and took 108 us
-// at m = 8; the split-K kernel takes 88 us).
+// Rows per wave of the streaming kernel: 16 at m = 1, 8 above (x reused
+// across more rows, fewer reductions per row; R * m <= 64 partial sums per
+// lane).  On the 7B stack's decode pass (224 matrices, one launch) 16 rows
+// took 0.94x the time of 8 and 32 rows 1.14x (occupancy 4).  Matrices with
+// too few rows to give every SIMD waves that way take the split-K kernel
+// instead (with 4 rows per wave at m > 4, a 28672-row matrix still streamed
+// and took 108 us at m = 8; the split-K kernel takes 88 us).
 template <int M>
-constexpr int rows_big() { return 8; }
+constexpr int rows_big() { return M == 1 ? 16 : 8; }
 // Rows per block of the split-K kernel.  Every row of a block reuses the
 // block's x chunks, so more rows cut x traffic (M rows of x against one
 // payload row); fewer rows give a small matrix more blocks.  Measured on int4
@@ -481,8 +504,9 @@ constexpr int rows_split_many() { return 8; }
 template <int M>
 constexpr int rows_split_few() { return M == 1 ? 4 : 8; }
 constexpr int64_t kSplitManyRows = 12288;
-// Work items of R rows from which several matrices take the streaming kernel.
-constexpr int kBigItemsMany = 2048;
+// Rows from which several matrices (or a lone one) take the streaming kernel.
+constexpr int64_t kBigRowsMany = 16384;
+constexpr int64_t kBigRowsLone = 32768;
 
 // Launches `count` descriptors (same bits, m), GEMV_NB per launch, R rows per
 // work item.
@@ -529,15 +553,16 @@ template <int BITS, int M>
 hipError_t launch_m(const GemvDesc* ds, int count, hipStream_t st) {
   int64_t rows = 0;
   for (int i = 0; i < count; ++i) rows += ds[i].n;
-  // big items when they still give about two waves per SIMD (2048 items);
-  // a lone matrix keeps the split-K kernel up to four per SIMD (4096 items),
-  // since its waves each run a short loop whose load latency few waves hide
+  // streaming items when the rows still give about two waves per SIMD in
+  // 8-row items (16384 rows); a lone matrix keeps the split-K kernel up to
+  // four per SIMD (32768 rows), since its waves each run a short loop whose
+  // load latency few waves hide
   // (int4 group 128 at m = 8: 14336 x 4096 34 -> 27 us, 8192 x 28672
   // 107 -> 86 us).  Below that, the split-K kernel: the 4 waves of a block
   // share R rows and split K, four times the waves for the same rows.
   constexpr int RB = rows_big<M>();
   constexpr int RSM = rows_split_many<M>(), RSF = rows_split_few<M>();
-  const bool big = rows / RB >= (count == 1 ? 4096 : kBigItemsMany);
+  const bool big = rows >= (count == 1 ? kBigRowsLone : kBigRowsMany);
   const bool many = rows >= kSplitManyRows;
   if (count == 1) {
     if (big) return launch_group<BITS, M, RB, 1>(ds, count, st);

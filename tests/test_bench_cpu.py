@@ -15,7 +15,7 @@ import bench  # noqa: E402
 
 COPY = "void at::native::vectorized_elementwise_kernel<neg_kernel_cuda>"  # any name holding the copy fragment
 QUANT = "void qw::(anonymous namespace)::quant_subgroup_batched_kernel<4, 8>(qw::QuantBatch)"
-GEMV = "void qw::(anonymous namespace)::gemv8_kernel<4, 1, 8, 256>(qw::GemvBatch<256>)"
+GEMV = "void qw::(anonymous namespace)::gemv8_kernel<4, 1, 16, 256>(qw::GemvBatch<256>)"
 
 
 def _counters(d, counter, rows):
@@ -43,13 +43,13 @@ def _summary(tmp_path):
     _counters(tmp_path / "f", "FETCH_SIZE", [
         (COPY, 1 << 20, 524288.0),
         (QUANT, 4096, 900.0), (QUANT, 4096, 1100.0),   # mean 1000 KiB
-        (GEMV, 10878976, 100.0),
+        (GEMV, 5439488, 100.0),
         (GEMV, 64, 99999.0),                           # another grid: not the measured launch
     ])
     _counters(tmp_path / "w", "WRITE_SIZE", [
         (COPY, 1 << 20, 1048576.0),
         (QUANT, 4096, 300.0),
-        (GEMV, 10878976, 50.0),
+        (GEMV, 5439488, 50.0),
     ])
     return bench.pmc_summary(str(tmp_path / "f"), str(tmp_path / "w"), copy_mib=1024)
 
