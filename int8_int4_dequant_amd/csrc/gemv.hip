@@ -40,6 +40,9 @@
 
 #include "qw_internal.h"
 
+#include <algorithm>
+#include <vector>
+
 namespace qw {
 namespace {
 
@@ -646,18 +649,28 @@ hipError_t launch_gemv_batched(const Mat* mts, const uint8_t* const* payloads,
                                const float* const* scales, int m, const float* const* xs,
                                float* const* ys, int count, hipStream_t st) {
   // fast-path matrices, grouped by bit width, go out GEMV_NB per launch;
-  // the others take the generic kernel one by one.
+  // the others take the generic kernel one by one.  Within a launch the
+  // matrices are taken longest rows first: work items of one row length
+  // then stream back to back (the 7B decode pass in layer order, where
+  // 4096- and 11008-code rows alternate, took 1.04x the time of either
+  // sorted order).  Every product is computed by its own work items, so the
+  // order does not change any result.
+  std::vector<int> order(count);
+  for (int i = 0; i < count; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(),
+                   [&](int a, int b) { return mts[a].k > mts[b].k; });
   for (int bits = 4; bits <= 8; bits += 4) {
     GemvDesc ds[GEMV_NB];
     int nd = 0;
-    for (int i = 0; i <= count; ++i) {
-      const bool flush = (i == count) || nd == GEMV_NB;
+    for (int oi = 0; oi <= count; ++oi) {
+      const bool flush = (oi == count) || nd == GEMV_NB;
       if (flush && nd) {
         hipError_t e = bits == 4 ? launch_bits<4>(ds, nd, m, st) : launch_bits<8>(ds, nd, m, st);
         if (e != hipSuccess) return e;
         nd = 0;
       }
-      if (i == count) break;
+      if (oi == count) break;
+      const int i = order[oi];
       if (mts[i].bits != bits || mts[i].n * mts[i].k == 0) continue;
       if (gemv_path(mts[i], payloads[i], xs[i]) == PATH_FAST) {
         ds[nd++] = make_desc(mts[i], payloads[i], scales[i], xs[i], ys[i]);
