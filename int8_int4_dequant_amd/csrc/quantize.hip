@@ -121,28 +121,43 @@ __device__ __forceinline__ uint32_t pack4_int8(const float* r) {
   return v;
 }
 
-constexpr int QV = 4;  // float4 vectors per lane in the subgroup kernel
+constexpr int QV = 4;  // float4 vectors per lane in the unpack kernel
 
-// A wave owns 64*QV consecutive float4 vectors; its j-th load instruction
+// Subgroup quantize kernel: float4 vectors per lane (a wave takes 64 * QVq)
+// and waves per block.  Measured on the 7B stack (int4 group 32, one launch,
+// interleaved with the 4-vector, 4-wave form): 2 vectors per lane in 2-wave
+// blocks took 0.967 of the time, 2 in 4-wave blocks 0.97-0.98, 4 in 1-wave
+// blocks 0.975, 4 in 8- or 16-wave blocks 1.02-1.03.  Groups of more than 64
+// vectors span 2 or 4 load instructions, so they keep 4 vectors per lane.
+template <int G>
+constexpr int quant_qv() { return G <= 64 ? 2 : 4; }
+constexpr int QUANT_WAVES = 2;
+// float4 vectors one block quantizes, for a group of `group` weights
+inline uint64_t quant_block_vecs(int64_t group) {
+  return (uint64_t)64 * (group / 4 <= 64 ? 2 : 4) * QUANT_WAVES;
+}
+
+// A wave owns 64*QVq consecutive float4 vectors; its j-th load instruction
 // reads vectors [base + 64j, base + 64j + 64) -- one fully coalesced 1 KiB
 // run per instruction.  A group of G vectors (G = group / 4, a power of two
 // from 2 to 256) is G consecutive lanes of one instruction (G <= 64) or the
 // same lane across 2 or 4 instructions (G = 128, 256); max|w| is reduced
 // with cross-lane shuffles.  The wave's payload (2 or 4 bytes per vector)
 // and scales are assembled in LDS and written with one wide non-temporal
-// store per lane (8 or 16 payload bytes, 4 or 8 scale bytes): stores of 2
-// bytes per lane were the slowest part of the kernel.
+// store per lane (4, 8 or 16 payload bytes): stores of 2 bytes per lane were
+// the slowest part of the kernel.
 template <int BITS, int G>
 __device__ __forceinline__ void quant_subgroup_body(
     const float* __restrict__ w, uint8_t* __restrict__ payload,
     float* __restrict__ scales, uint64_t nvec, uint64_t block) {
+  constexpr int QV = quant_qv<G>();         // float4 vectors per lane
   constexpr int PB = BITS / 2;               // payload bytes per vector (2 or 4)
   constexpr int NS = 64 * QV / G;            // scales per wave (1 .. 128)
-  __shared__ __attribute__((aligned(16))) uint8_t stage_p[4][64 * QV * PB];
-  __shared__ __attribute__((aligned(16))) float stage_s[4][NS];
+  __shared__ __attribute__((aligned(16))) uint8_t stage_p[QUANT_WAVES][64 * QV * PB];
+  __shared__ __attribute__((aligned(16))) float stage_s[QUANT_WAVES][NS];
   const int lane = threadIdx.x & 63;
   const int wv = threadIdx.x >> 6;
-  const uint64_t base = (block * 4 + wv) * (64 * QV);
+  const uint64_t base = (block * QUANT_WAVES + wv) * (64 * QV);
   float v[QV][4];
   float m[QV];
 #pragma unroll
@@ -190,12 +205,15 @@ __device__ __forceinline__ void quant_subgroup_body(
   // lane L writes vectors [QV*L, QV*L + QV) of the wave: QV * PB contiguous bytes
   const uint64_t v0 = base + (uint64_t)QV * lane;
   if (v0 + QV <= nvec) {
-    if constexpr (QV * PB == 8) {
+    if constexpr (QV * PB == 4) {
+      __builtin_nontemporal_store(reinterpret_cast<const uint32_t*>(stage_p[wv])[lane],
+                                  reinterpret_cast<uint32_t*>(payload + v0 * PB));
+    } else if constexpr (QV * PB == 8) {
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
       __builtin_nontemporal_store(reinterpret_cast<const u32x2*>(stage_p[wv])[lane],
                                   reinterpret_cast<u32x2*>(payload + v0 * PB));
     } else {
-      static_assert(QV * PB == 16, "QV * PB must be 8 or 16");
+      static_assert(QV * PB == 16, "QV * PB must be 4, 8 or 16");
       typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
       __builtin_nontemporal_store(reinterpret_cast<const u32x4*>(stage_p[wv])[lane],
                                   reinterpret_cast<u32x4*>(payload + v0 * PB));
@@ -221,7 +239,7 @@ __device__ __forceinline__ void quant_subgroup_body(
 }
 
 template <int BITS, int G>
-__global__ __launch_bounds__(256) void quant_subgroup_kernel(
+__global__ __launch_bounds__(64 * QUANT_WAVES) void quant_subgroup_kernel(
     const float* __restrict__ w, uint8_t* __restrict__ payload,
     float* __restrict__ scales, uint64_t nvec) {
   quant_subgroup_body<BITS, G>(w, payload, scales, nvec, blockIdx.x);
@@ -247,7 +265,7 @@ struct QuantBatch {
 };
 
 template <int BITS, int G>
-__global__ __launch_bounds__(256) void quant_subgroup_batched_kernel(const QuantBatch b) {
+__global__ __launch_bounds__(64 * QUANT_WAVES) void quant_subgroup_batched_kernel(const QuantBatch b) {
   typedef const __attribute__((address_space(4))) QuantBatch* KArg;
   const KArg kb = (KArg)__builtin_amdgcn_kernarg_segment_ptr();
   const uint32_t blk = blockIdx.x;
@@ -482,16 +500,17 @@ hipError_t quantize_bits(const Mat& mt, const float* w, uint8_t* payload, float*
   const int path = quantize_path(mt, w, payload);
   if (path == PATH_FAST) {
     const uint64_t nvec = count / 4;
-    const unsigned grid = (unsigned)((nvec + 4 * 64 * QV - 1) / (4 * 64 * QV));
+    const uint64_t bv = quant_block_vecs(mt.group);
+    const unsigned grid = (unsigned)((nvec + bv - 1) / bv);
     switch (group / 4) {
-      case 2: quant_subgroup_kernel<BITS, 2><<<grid, 256, 0, st>>>(w, payload, scales, nvec); break;
-      case 4: quant_subgroup_kernel<BITS, 4><<<grid, 256, 0, st>>>(w, payload, scales, nvec); break;
-      case 8: quant_subgroup_kernel<BITS, 8><<<grid, 256, 0, st>>>(w, payload, scales, nvec); break;
-      case 16: quant_subgroup_kernel<BITS, 16><<<grid, 256, 0, st>>>(w, payload, scales, nvec); break;
-      case 32: quant_subgroup_kernel<BITS, 32><<<grid, 256, 0, st>>>(w, payload, scales, nvec); break;
-      case 64: quant_subgroup_kernel<BITS, 64><<<grid, 256, 0, st>>>(w, payload, scales, nvec); break;
-      case 128: quant_subgroup_kernel<BITS, 128><<<grid, 256, 0, st>>>(w, payload, scales, nvec); break;
-      default: quant_subgroup_kernel<BITS, 256><<<grid, 256, 0, st>>>(w, payload, scales, nvec); break;
+      case 2: quant_subgroup_kernel<BITS, 2><<<grid, 64 * QUANT_WAVES, 0, st>>>(w, payload, scales, nvec); break;
+      case 4: quant_subgroup_kernel<BITS, 4><<<grid, 64 * QUANT_WAVES, 0, st>>>(w, payload, scales, nvec); break;
+      case 8: quant_subgroup_kernel<BITS, 8><<<grid, 64 * QUANT_WAVES, 0, st>>>(w, payload, scales, nvec); break;
+      case 16: quant_subgroup_kernel<BITS, 16><<<grid, 64 * QUANT_WAVES, 0, st>>>(w, payload, scales, nvec); break;
+      case 32: quant_subgroup_kernel<BITS, 32><<<grid, 64 * QUANT_WAVES, 0, st>>>(w, payload, scales, nvec); break;
+      case 64: quant_subgroup_kernel<BITS, 64><<<grid, 64 * QUANT_WAVES, 0, st>>>(w, payload, scales, nvec); break;
+      case 128: quant_subgroup_kernel<BITS, 128><<<grid, 64 * QUANT_WAVES, 0, st>>>(w, payload, scales, nvec); break;
+      default: quant_subgroup_kernel<BITS, 256><<<grid, 64 * QUANT_WAVES, 0, st>>>(w, payload, scales, nvec); break;
     }
   } else if (path == PATH_BLOCK) {
     const uint64_t ngroups = count / group;
@@ -539,7 +558,8 @@ int quantize_path(const Mat& mt, const float* w, const uint8_t* payload) {
   const uint64_t count = (uint64_t)mt.n * (uint64_t)mt.k;
   const uint64_t group = (uint64_t)mt.group;
   const bool al = aligned(w, 16) && aligned(payload, mt.bits == 4 ? 4 : 8);
-  const uint64_t blocks_needed = (count / 4 + 1023) / 1024;
+  const uint64_t blocks_needed = (count / 4 + quant_block_vecs(mt.group) - 1) /
+                                 quant_block_vecs(mt.group);
   const bool pow2 = (group & (group - 1)) == 0;
   if (al && pow2 && group >= 8 && group <= 1024 && blocks_needed < (1ull << 31))
     return PATH_FAST;
@@ -565,7 +585,7 @@ namespace {
 
 template <int BITS, int G>
 hipError_t launch_quant_batch(const QuantBatch& b, hipStream_t st) {
-  quant_subgroup_batched_kernel<BITS, G><<<b.blocks, 256, 0, st>>>(b);
+  quant_subgroup_batched_kernel<BITS, G><<<b.blocks, 64 * QUANT_WAVES, 0, st>>>(b);
   return hipGetLastError();
 }
 
@@ -622,7 +642,8 @@ hipError_t launch_quantize_pack_batched(const Mat* mts, const float* const* ws,
       for (; j < bk.idx.size() && b.count < QUANT_NB; ++j) {
         const int i = bk.idx[j];
         const uint64_t nvec = (uint64_t)(mts[i].n * mts[i].k) / 4;
-        const uint64_t nblk = (nvec + 4 * 64 * QV - 1) / (4 * 64 * QV);
+        const uint64_t bv = quant_block_vecs(bk.group);
+        const uint64_t nblk = (nvec + bv - 1) / bv;
         if (nblk > kMaxBlocks) return hipErrorInvalidValue;
         if (blocks + nblk > kMaxBlocks) break;  // next launch
         b.block0[b.count] = (uint32_t)blocks;
