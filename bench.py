@@ -143,12 +143,29 @@ def sustained_clock(args, fn, seconds=3.0):
     return c.summary()
 
 
+def prewarm(args, fn):
+    """Runs `fn` (one enqueue of the timed work) back to back, untimed, for
+    --prewarm-s seconds.  From idle, the GPU's clock and power controller
+    overshoots for the first few milliseconds to a quarter second of load
+    (launch durations up to 30% above their sustained value); the timed
+    region that follows then sees the sustained state."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < args.prewarm_s:
+        for _ in range(4):
+            fn()
+        torch.cuda.synchronize()
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--gemm-reps", type=int, default=20)
+    ap.add_argument("--prewarm-s", type=float, default=0.5,
+                    help="seconds of untimed back-to-back runs before each leg's warm-up "
+                         "(0: time from a cold start)")
     ap.add_argument("--no-gemm", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layers", type=int, default=32, help="layers of the stack (default: all 32)")
@@ -157,6 +174,8 @@ def parse():
                          "(the known-size kernel that calibrates the HBM byte counters)")
     ap.add_argument("--pmc-table", nargs="+", metavar="DIR",
                     help="print the activity-counter table of rocprofv3 --pmc CSV runs and exit")
+    ap.add_argument("--trace-table", metavar="DIR",
+                    help="print the per-kernel table of a rocprofv3 --kernel-trace CSV run and exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the traffic summary of two rocprofv3 --pmc runs and exit")
     ap.add_argument("--no-gptq", action="store_true")
@@ -319,6 +338,60 @@ def pmc_table(dirs):
     return "\n".join(lines)
 
 
+def trace_table(d, top=40):
+    """Markdown table of a rocprofv3 --kernel-trace CSV run: one row per
+    (kernel, grid, block) with call count and duration statistics in
+    microseconds, and the register, LDS and scratch figures the trace records,
+    sorted by total time."""
+    import csv
+    import glob
+
+    def num(r, *names):
+        for n in names:
+            if r.get(n) not in (None, ""):
+                return int(float(r[n]))
+        return 0
+    def short(name):
+        # drop the trailing parameter list, the return type and the library's
+        # own namespace
+        name = name.strip()
+        if name.endswith(")"):
+            depth = 0
+            for i in range(len(name) - 1, -1, -1):
+                depth += {")": 1, "(": -1}.get(name[i], 0)
+                if depth == 0:
+                    name = name[:i]
+                    break
+        if name.startswith("void "):
+            name = name[5:]
+        return name.replace("qw::(anonymous namespace)::", "")[:120]
+
+    rows = {}
+    for f in glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            gx = num(r, "Grid_Size_X", "Grid_Size")
+            gz = num(r, "Grid_Size_Z")
+            name = short(r["Kernel_Name"])
+            if gz > 1:
+                name += f" (grid z {gz})"
+            key = (name, gx, num(r, "Workgroup_Size_X", "Workgroup_Size"))
+            e = rows.setdefault(key, {"us": [], "vgpr": num(r, "VGPR_Count", "Arch_VGPR_Count"),
+                                      "agpr": num(r, "Accum_VGPR_Count"),
+                                      "lds": num(r, "LDS_Block_Size", "Group_Segment_Size"),
+                                      "scratch": num(r, "Scratch_Size", "Private_Segment_Size")})
+            e["us"].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    order = sorted(rows.items(), key=lambda kv: -sum(kv[1]["us"]))
+    lines = ["| kernel | grid threads | block | calls | avg us | median us | min us | max us | "
+             "VGPR (alloc) | AGPR | LDS B | scratch B |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for (name, gx, bx), e in order[:top]:
+        us = e["us"]
+        lines.append(f"| `{name}` | {gx} | {bx} | {len(us)} | {sum(us) / len(us):.2f} | "
+                     f"{statistics.median(us):.2f} | {min(us):.2f} | {max(us):.2f} | "
+                     f"{e['vgpr']} | {e['agpr']} | {e['lds']} | {e['scratch']} |")
+    return "\n".join(lines)
+
+
 def measured_traffic(label):
     """HBM bytes per launch of `label` from the committed counter summary, or
     None when the summary is missing or the kernel sources changed since."""
@@ -377,14 +450,18 @@ def _entry(cfg, op, ts_ns, warm, nbytes=None, flops=None, **extra):
     return e
 
 
-def _timed(fn, warm, reps):
+def _timed(fn, warm, reps, what=None):
+    """Per-call times (ns) of `reps` calls after `warm` untimed ones; with
+    `what`, one progress line per call that takes over 10 s."""
     for _ in range(warm):
         fn()
     ts = []
-    for _ in range(reps):
+    for r in range(reps):
         t0 = time.perf_counter_ns()
         fn()
         ts.append(time.perf_counter_ns() - t0)
+        if what is not None and ts[-1] > 10e9:
+            log(f"[oracle timing] {what}: rep {r + 1}/{reps} {ts[-1] / 1e9:.1f} s")
     return ts
 
 
@@ -487,15 +564,23 @@ def _matrix_legs(run, cfg, w, bits, group, reps, ms, x_of, tag=""):
     kw["scales"] = run.out("float32", (n * k // group,))
     out = [_entry(cfg, f"quantize_pack{tag}", _timed(lambda: run.call("quantize_pack", n, **kw),
                                                      warm, nrep), warm, _qbytes(n, k, bits, group))]
+    _progress(out[-1])
     kw["out"] = run.out("float32", (n, k))
     out.append(_entry(cfg, f"unpack{tag}", _timed(lambda: run.call("unpack", n, **kw), warm, nrep),
                       warm, _ubytes(n, k, bits, group)))
+    _progress(out[-1])
     for m in ms:
         kg = dict(kw, x=run.share(x_of(m)), out=run.out("float64", (m, n)))
         out.append(_entry(cfg, f"gemv_m{m}{tag}", _timed(lambda: run.call("gemv", n, **kg), warm,
                                                         nrep), warm, _gbytes(n, k, bits, group, m),
                           2 * m * n * k))
+        _progress(out[-1])
     return out
+
+
+def _progress(e):
+    log(f"[oracle timing] {e['config']} {e['op']}: {e['warmups']}+{e['reps']} calls, "
+        f"median {e['median_us']:.0f} us")
 
 
 def cpu_legs(mode, plan, legs):
@@ -557,7 +642,7 @@ def _c4_leg(run, plan, leg):
         mats = mats[i::s]
     warm, nrep = plan["c4"]
     reps, nbytes = [0] * nrep, 0
-    for layer, tag, n, k, seed in mats:
+    for j, (layer, tag, n, k, seed) in enumerate(mats):
         w = inputs.weight(seed, n, k, inputs.C4["sigma"])
         kw = dict(bits=4, group=32, k=k, w=run.share(w), x=run.share(inputs.c4_x(k)))
         kw["payload"] = run.out("uint8", (n * k // 2,))
@@ -571,6 +656,8 @@ def _c4_leg(run, plan, leg):
             reps[r] += t
         nbytes += _qbytes(n, k, 4, 32) + _gbytes(n, k, 4, 32, 1)
         run.release()
+        if j % 8 == 7 or j == len(mats) - 1:
+            log(f"[oracle timing] {leg}: {j + 1}/{len(mats)} matrices")
     return _entry("c4", f"quantize_pack+gemv_m1 ({len(mats)} matrices)", reps, warm, nbytes,
                   matrices=len(mats), rep_us=[round(t / 1e3, 1) for t in reps])
 
@@ -591,7 +678,7 @@ def _c5_leg(run, plan):
     kw["out"] = run.out("float64", (c["m"], rows))
     run.call("quantize_pack", rows, **kw)
     warm, nrep = plan["c5"]
-    ts = _timed(lambda: run.call("gemm", rows, **kw), warm, nrep)
+    ts = _timed(lambda: run.call("gemm", rows, **kw), warm, nrep, what=f"c5 gemm, {rows} rows")
     return _entry("c5", f"gemm ({c['m']} x {rows} x {c['k']}, fp64)", ts, warm,
                   flops=2 * c["m"] * rows * c["k"], rows=rows)
 
@@ -610,18 +697,18 @@ def _run_cpu_child(mode, plan, legs, core=None, timeout=3600):
             env[v] = "1"
     spec = json.dumps({"mode": mode, "plan": plan, "legs": legs})
     pre = (lambda: os.sched_setaffinity(0, {core})) if core is not None else None
+    # the child's progress lines go straight to this process's stderr
     return subprocess.Popen([sys.executable, os.path.abspath(__file__), "--cpu-worker", spec],
-                            stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True, env=env,
+                            stdout=subprocess.PIPE, stderr=None, text=True, env=env,
                             preexec_fn=pre)
 
 
 def _collect(procs, timeout=3600):
     out = []
     for p in procs:
-        so, se = p.communicate(timeout=timeout)
+        so, _ = p.communicate(timeout=timeout)
         if p.returncode != 0:
-            log(se[-2000:])
-            raise RuntimeError("oracle timing child failed")
+            raise RuntimeError(f"oracle timing child failed (exit {p.returncode})")
         out += json.loads(so.strip().splitlines()[-1])
     return out
 
@@ -725,6 +812,9 @@ def main():
     if args.pmc_table:
         print(pmc_table(args.pmc_table))
         return
+    if args.trace_table:
+        print(trace_table(args.trace_table))
+        return
     if args.pmc_summary:
         print("```json\n" + json.dumps(pmc_summary(*args.pmc_summary, copy_mib=1024), indent=1)
               + "\n```")
@@ -817,6 +907,7 @@ def main():
             if st:
                 raise RuntimeError(f"qw_gemv failed: {st}")
 
+    prewarm(args, run_step)
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
@@ -1069,6 +1160,7 @@ def bench_chain(args, L, stream, mats, shapes, P, S, xs, gbytes):
             raise RuntimeError(f"qw_gemv_chain failed: {r}")
 
     def timed(fn, reps=max(3, args.steps)):
+        prewarm(args, fn)
         fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -1146,6 +1238,7 @@ def bench_context(args, stream):
     n = (2 << 30) // 4
     src = torch.rand(n, dtype=torch.float32, device=dev, generator=gen)
     dst = torch.empty_like(src)
+    prewarm(args, lambda: dst.copy_(src))
     t = _event_us(stream, lambda: dst.copy_(src), 10)
     med = statistics.median(t)
     out["device_copy_2GiB"] = {"bytes": 8 * n, "median_us": round(med, 1),
@@ -1154,6 +1247,7 @@ def bench_context(args, stream):
     del dst
     big = torch.cat([src, src])
     del src
+    prewarm(args, lambda: big.sum())
     t = _event_us(stream, lambda: big.sum(), 10)
     med = statistics.median(t)
     out["device_read_4GiB"] = {"bytes": 4 * big.numel(), "median_us": round(med, 1),
@@ -1168,6 +1262,7 @@ def bench_context(args, stream):
           ).to(torch.bfloat16)              # the weight's transpose, contiguous
     y = torch.empty((m, nn), dtype=torch.bfloat16, device=dev)
     mm = lambda: torch.matmul(x, wt, out=y)  # noqa: E731
+    prewarm(args, mm)
     t = _event_us(stream, mm, 20)
     med = statistics.median(t)
     tf = 2.0 * m * nn * k / (med * 1e-6) / 1e12
@@ -1220,6 +1315,7 @@ def bench_gemv_configs(args, L, stream):
                                   x.data_ptr(), y.data_ptr(), sp)
                     if r:
                         raise RuntimeError(f"qw_gemv failed: {r}")
+            prewarm(args, rnd)
             rnd()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -1272,6 +1368,7 @@ def bench_gemm(args, L, stream):
         if r:
             raise RuntimeError(f"qw_gemm failed: {r}")
 
+    prewarm(args, run)
     for _ in range(3):
         run()
     torch.cuda.synchronize()
@@ -1510,6 +1607,7 @@ def bench_gptq(args, L, stream):
     if not all(torch.equal(a, b) for a, b in zip(one_stream, outputs())):
         raise RuntimeError("GPTQ codes on four streams differ from those on one stream")
     # the layer with the four inputs' chains on four streams
+    prewarm(args, lambda: run(concurrent=True))
     conc = []
     for _ in range(args.gptq_reps):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
