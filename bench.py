@@ -740,12 +740,14 @@ def cpu_baselines(full=False):
     allc = _collect([_run_cpu_child("all_cores", plan, ["c2", "c3", "c4", "c5"])])
     c4a = next(e for e in one if e["config"] == "c4")
     c4b = next(e for e in allc if e["config"] == "c4")
-    sample = (f"{c4a['op']} of the 7B stack ({'all 32 layers' if plan['c4_layers'] == 32 else 'layer 0'}), "
-              f"weights generated outside the timing; median of {c4a['reps']} reps")
+    def sample(e):
+        return (f"{e['op']} of the 7B stack "
+                f"({'all 32 layers' if plan['c4_layers'] == 32 else 'layer 0'}), "
+                f"weights generated outside the timing; median of {e['reps']} reps")
     one_thread = {"value": c4a["GB/s"], "unit": "GB/s", "cores": 1, "kind": "oracle",
-                  "sample": sample, "median_us": c4a["median_us"], "p90_us": c4a["p90_us"]}
+                  "sample": sample(c4a), "median_us": c4a["median_us"], "p90_us": c4a["p90_us"]}
     all_cores = {"value": c4b["GB/s"], "unit": "GB/s", "cores": len(cores), "kind": "oracle",
-                 "sample": sample + "; row blocks over one process per core",
+                 "sample": sample(c4b) + "; row blocks over one process per core",
                  "median_us": c4b["median_us"], "p90_us": c4b["p90_us"]}
     configs = {"protocol": "full (the page's 20 warm-ups + 101 reps on c1-c3)" if full
                else "bounded (reps per entry)",
