@@ -71,8 +71,10 @@ enum qw_status {
     QW_OK = 0,
     QW_EBITS = -1,   /* bits is not 4 or 8                                   */
     QW_EGROUP = -2,  /* group < 1, or group does not divide n*k              */
-    QW_ESHAPE = -3,  /* n < 0, k < 0, n*k overflows, or int4 with odd n*k     */
-    QW_EM = -4,      /* m out of range (gemv: 0..8, gemm: >= 0)              */
+    QW_ESHAPE = -3,  /* n < 0, k < 0, a size above its limit (below), or     */
+                     /* int4 with odd n*k                                    */
+    QW_EM = -4,      /* m out of range (gemv: 0..8, gemm: >= 0) or m*n, m*k  */
+                     /* above QW_MAX_ELEMENTS                                */
     QW_ENULL = -5,   /* a required pointer is NULL                           */
     QW_EHIP = -6,    /* a HIP launch failed                                  */
     QW_ECOUNT = -7,  /* batched call: count < 0 or a descriptor is invalid   */
@@ -84,6 +86,17 @@ enum qw_status {
 /* Largest number of matrices the batched calls put into one kernel launch
  * (their descriptors travel as kernel arguments). */
 #define QW_BATCH_PER_LAUNCH 256
+
+/* Size limits.  One matrix holds at most QW_MAX_ELEMENTS weights: n, k and
+ * n*k are each at most that (2^31 fp32 weights are 8 GiB), and so are a
+ * product's m*k activations and m*n outputs.  Within them every kernel
+ * launch stays below the 2^32 work-items of one dispatch; beyond them a call
+ * returns QW_ESHAPE (QW_EM for m) and enqueues nothing.  The GPTQ calls also
+ * take k <= QW_GPTQ_MAX_K (H and U are k x k fp64: 8 GiB each at the limit),
+ * n <= QW_GPTQ_MAX_N and t*k <= QW_MAX_ELEMENTS. */
+#define QW_MAX_ELEMENTS (1ll << 31)
+#define QW_GPTQ_MAX_K 32768
+#define QW_GPTQ_MAX_N (1ll << 24)
 
 /* Bytes of packed codes for an n x k matrix: n*k*bits/8 (-1 if invalid). */
 int64_t qw_payload_bytes(int bits, int64_t n, int64_t k);

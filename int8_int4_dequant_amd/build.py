@@ -37,21 +37,27 @@ def _run(cmd):
     return err
 
 
-def build(verbose=False, save_temps=False):
-    os.makedirs(BUILD, exist_ok=True)
+def compile_objects(out_dir, extra=(), verbose=False):
+    """Compiles every source into out_dir with FLAGS plus `extra`; returns
+    the object paths."""
+    os.makedirs(out_dir, exist_ok=True)
     objs = []
     jobs = []
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         for src in SOURCES:
-            obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+            obj = os.path.join(out_dir, src.replace(".hip", ".o"))
             objs.append(obj)
-            extra = ["--save-temps"] if save_temps else []
             cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
             jobs.append(ex.submit(_run, cmd))
         for j in jobs:
             msg = j.result()
             if verbose and msg:
                 print(msg)
+    return objs
+
+
+def build(verbose=False, save_temps=False):
+    objs = compile_objects(BUILD, ["--save-temps"] if save_temps else [], verbose)
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB)

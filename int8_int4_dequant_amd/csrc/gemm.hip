@@ -29,6 +29,8 @@
 //     weight tile stays in that XCD's L2 while the M tiles reuse it).
 #include "qw_internal.h"
 
+#include <atomic>
+
 namespace qw {
 namespace {
 
@@ -646,24 +648,26 @@ __global__ __launch_bounds__(256) void round_bf16_kernel(const float* __restrict
 int gemm_path(const Mat& mt, const uint8_t* payload, const uint16_t* x) {
   const bool shape_ok = mt.k % BK == 0 && mt.n < (1ll << 30) && mt.k < (1ll << 30) &&
                         mt.n * mt.k * mt.bits / 8 < (1ll << 62);
-  const bool group_ok = (mt.k % mt.group == 0 && mt.group % 32 == 0) || (mt.group % mt.k == 0);
+  const bool group_ok = mt.k > 0 && ((mt.k % mt.group == 0 && mt.group % 32 == 0) ||
+                                      (mt.group % mt.k == 0));
   if (shape_ok && group_ok && aligned(payload, 16) && aligned(x, 16)) return PATH_FAST;
   return PATH_GENERIC;
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (cached per device; threads that
+// query a device for the first time at once store the same value).
 static int compute_units() {
-  static int cache[64] = {0};
+  static std::atomic<int> cache[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
         n <= 0)
       n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
 hipError_t launch_gemm(const Mat& mt, const uint8_t* payload, const float* scales, int64_t m,
@@ -704,7 +708,7 @@ hipError_t launch_gemm(const Mat& mt, const uint8_t* payload, const float* scale
       // still gives every compute unit a block
       const int nbw = tms * ((mt.n + 63) / 64) >= cus ? 2 : 1;
       const int64_t tns = (mt.n + 32 * nbw - 1) / (32 * nbw);
-      if (tms * tns >= (1ll << 31)) return hipErrorInvalidValue;
+      if (tms * tns >= (1ll << 24)) return hipErrorInvalidValue;  // < 2^32 work-items
       a.tiles_m = (int)tms;
       a.tiles_n = (int)tns;
       const unsigned grid = (unsigned)(tms * tns);
@@ -719,7 +723,7 @@ hipError_t launch_gemm(const Mat& mt, const uint8_t* payload, const float* scale
     }
     const int64_t tm = (m + BM - 1) / BM;
     const int64_t tn = (mt.n + BN - 1) / BN;
-    if (tm * tn >= (1ll << 31)) return hipErrorInvalidValue;
+    if (tm * tn >= (1ll << 23)) return hipErrorInvalidValue;  // grid <= 2 * tiles blocks
     a.tiles_m = (int)tm;
     a.tiles_n = (int)tn;
     a.xcd_map = (tn % 8 == 0) ? 1 : 0;
@@ -757,7 +761,7 @@ hipError_t launch_gemm(const Mat& mt, const uint8_t* payload, const float* scale
 
 hipError_t launch_round_bf16(const float* x, uint16_t* xb, int64_t count, hipStream_t st) {
   const int64_t threads = (count + 7) / 8;
-  if ((threads + 255) / 256 >= (1ll << 31)) return hipErrorInvalidValue;
+  if ((threads + 255) / 256 >= (1ll << 24)) return hipErrorInvalidValue;
   const int vec = aligned(x, 16) && aligned(xb, 16) ? 1 : 0;
   round_bf16_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(x, xb, count, vec);
   return hipGetLastError();

@@ -463,32 +463,34 @@ __global__ __launch_bounds__(256) void gemv8_split_kernel(const GemvBatch<NB> b)
 
 // --------------------------------------------------------- generic kernel
 
-// One wave per (row, m); any group dividing n*k and any alignment.
+// One wave per (row, m) at a time, the grid's waves striding over them; any
+// group dividing n*k and any alignment.
 template <int BITS>
 __global__ __launch_bounds__(256) void gemv_generic_kernel(
     const uint8_t* __restrict__ payload, const float* __restrict__ scales,
     const float* __restrict__ x, float* __restrict__ y, int64_t n, int64_t k, int m,
     int64_t group) {
-  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  if (wid >= n * m) return;
-  const int64_t row = wid % n;
-  const int64_t mm = wid / n;
-  float sum = 0.0f;
-  for (int64_t j = lane; j < k; j += 64) {
-    const int64_t e = row * k + j;
-    int q;
-    if (BITS == 4) {
-      const uint32_t b = payload[e >> 1];
-      q = (int)((e & 1) ? (b >> 4) : (b & 15u)) - 8;
-    } else {
-      q = (int)(int8_t)payload[e];
+  for (int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); wid < n * m;
+       wid += (int64_t)gridDim.x * 4) {
+    const int64_t row = wid % n;
+    const int64_t mm = wid / n;
+    float sum = 0.0f;
+    for (int64_t j = lane; j < k; j += 64) {
+      const int64_t e = row * k + j;
+      int q;
+      if (BITS == 4) {
+        const uint32_t b = payload[e >> 1];
+        q = (int)((e & 1) ? (b >> 4) : (b & 15u)) - 8;
+      } else {
+        q = (int)(int8_t)payload[e];
+      }
+      sum = __builtin_fmaf(x[mm * k + j], (float)q * scales[e / group], sum);
     }
-    sum = __builtin_fmaf(x[mm * k + j], (float)q * scales[e / group], sum);
-  }
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
-  if (lane == 0) y[mm * n + row] = sum;
+    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+    if (lane == 0) y[mm * n + row] = sum;
+  }
 }
 
 // Rows per wave of the streaming kernel: 16 at m = 1, 8 above (x reused
@@ -515,21 +517,37 @@ constexpr int64_t kSplitManyRows = 12288;
 constexpr int64_t kBigRowsMany = 16384;
 constexpr int64_t kBigRowsLone = 32768;
 
+// Work items one launch takes at most (2^22 blocks of 256 threads for the
+// split-K kernel, 2^20 for the streaming one: both far inside the 2^32
+// work-items of a dispatch).  A matrix has at most 2^28 rows on the fast path
+// (n * k <= 2^31 with k >= 8), so one always fits.
+constexpr int64_t kMaxItems = 1 << 22;
+
+// Fills `b` with descriptors ds[i..] (at most NB, at most kMaxItems work items
+// of R rows) and returns the index of the first descriptor left over.
+template <int R, int NB>
+int fill_batch(const GemvDesc* ds, int i, int count, GemvBatch<NB>& b) {
+  b = GemvBatch<NB>{};
+  int64_t items = 0;
+  for (; i < count && b.count < NB; ++i) {
+    const int64_t it = (ds[i].n + R - 1) / R;
+    if (b.count > 0 && items + it > kMaxItems) break;
+    b.d[b.count] = ds[i];
+    b.item0[b.count++] = (int)items;
+    items += it;
+  }
+  b.items = (int)items;
+  return i;
+}
+
 // Launches `count` descriptors (same bits, m), GEMV_NB per launch, R rows per
 // work item.
 template <int BITS, int M, int R, int NB>
 hipError_t launch_group(const GemvDesc* ds, int count, hipStream_t st) {
-  for (int base = 0; base < count; base += NB) {
-    GemvBatch<NB> b{};
-    b.count = count - base < NB ? count - base : NB;
-    int items = 0;
-    for (int i = 0; i < b.count; ++i) {
-      b.d[i] = ds[base + i];
-      b.item0[i] = items;
-      items += (b.d[i].n + R - 1) / R;
-    }
-    b.items = items;
-    gemv8_kernel<BITS, M, R, NB><<<(unsigned)((items + 3) / 4), 256, 0, st>>>(b);
+  for (int i = 0; i < count;) {
+    GemvBatch<NB> b;
+    i = fill_batch<R, NB>(ds, i, count, b);
+    gemv8_kernel<BITS, M, R, NB><<<(unsigned)((b.items + 3) / 4), 256, 0, st>>>(b);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -539,17 +557,10 @@ hipError_t launch_group(const GemvDesc* ds, int count, hipStream_t st) {
 // The same for the split-K kernel: one block per work item of R rows.
 template <int BITS, int M, int R, int NB>
 hipError_t launch_split_group(const GemvDesc* ds, int count, hipStream_t st) {
-  for (int base = 0; base < count; base += NB) {
-    GemvBatch<NB> b{};
-    b.count = count - base < NB ? count - base : NB;
-    int items = 0;
-    for (int i = 0; i < b.count; ++i) {
-      b.d[i] = ds[base + i];
-      b.item0[i] = items;
-      items += (b.d[i].n + R - 1) / R;
-    }
-    b.items = items;
-    gemv8_split_kernel<BITS, M, R, NB><<<(unsigned)items, 256, 0, st>>>(b);
+  for (int i = 0; i < count;) {
+    GemvBatch<NB> b;
+    i = fill_batch<R, NB>(ds, i, count, b);
+    gemv8_split_kernel<BITS, M, R, NB><<<(unsigned)b.items, 256, 0, st>>>(b);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -615,8 +626,9 @@ GemvDesc make_desc(const Mat& mt, const uint8_t* payload, const float* scales, c
 
 hipError_t launch_generic(const Mat& mt, const uint8_t* payload, const float* scales, int m,
                           const float* x, float* y, hipStream_t st) {
+  // at most 2^20 blocks (2^28 work-items); their waves stride over the rest
   const int64_t waves = mt.n * m;
-  const unsigned grid = (unsigned)((waves + 3) / 4);
+  const unsigned grid = (unsigned)std::min<int64_t>((waves + 3) / 4, 1 << 20);
   if (mt.bits == 4)
     gemv_generic_kernel<4><<<grid, 256, 0, st>>>(payload, scales, x, y, mt.n, mt.k, m, mt.group);
   else
@@ -630,7 +642,8 @@ int gemv_path(const Mat& mt, const uint8_t* payload, const float* x) {
   const int cpc = 8;  // codes per chunk
   const bool shape_ok = mt.k % cpc == 0 && mt.n < (1ll << 30) && mt.k < (1ll << 30) &&
                         (int64_t)mt.k * mt.bits / 8 < (1ll << 31);
-  const bool group_ok = (mt.k % mt.group == 0 && mt.group % cpc == 0) || (mt.group % mt.k == 0);
+  const bool group_ok = mt.k > 0 && ((mt.k % mt.group == 0 && mt.group % cpc == 0) ||
+                                      (mt.group % mt.k == 0));
   if (shape_ok && group_ok && aligned(payload, mt.bits == 4 ? 4 : 8) && aligned(x, 16))
     return PATH_FAST;
   return PATH_GENERIC;

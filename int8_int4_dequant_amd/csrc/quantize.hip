@@ -29,6 +29,7 @@
 //             per payload byte).
 #include "qw_internal.h"
 
+#include <algorithm>
 #include <vector>
 
 namespace qw {
@@ -340,18 +341,23 @@ __global__ __launch_bounds__(256) void scales_thread_kernel(
 // Scales, one block per group (large groups).
 template <int BITS>
 __global__ __launch_bounds__(256) void scales_block_kernel(
-    const float* __restrict__ w, float* __restrict__ scales, uint64_t group) {
+    const float* __restrict__ w, float* __restrict__ scales, uint64_t ngroups,
+    uint64_t group) {
   __shared__ float red[4];
-  const uint64_t g = blockIdx.x;
-  const float* p = w + g * group;
-  float m = 0.0f;
-  for (uint64_t i = threadIdx.x; i < group; i += 256) m = fmaxf(m, fabsf(p[i]));
+  // block-uniform loop over the groups (grid-stride): every thread reaches
+  // both barriers of every pass
+  for (uint64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
+    const float* p = w + g * group;
+    float m = 0.0f;
+    for (uint64_t i = threadIdx.x; i < group; i += 256) m = fmaxf(m, fabsf(p[i]));
 #pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0)
-    scales[g] = scale_of<BITS>(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0)
+      scales[g] = scale_of<BITS>(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+    __syncthreads();  // red is rewritten by the next pass
+  }
 }
 
 // Codes, one thread per payload byte.
@@ -520,7 +526,8 @@ hipError_t quantize_bits(const Mat& mt, const float* w, uint8_t* payload, float*
     if (group <= 64)
       scales_thread_kernel<BITS><<<blocks_for(ngroups), 256, 0, st>>>(w, scales, ngroups, group);
     else
-      scales_block_kernel<BITS><<<(unsigned)ngroups, 256, 0, st>>>(w, scales, group);
+      scales_block_kernel<BITS><<<(unsigned)std::min<uint64_t>(ngroups, 1u << 20), 256, 0, st>>>(
+          w, scales, ngroups, group);
     const uint64_t nbytes = count * BITS / 8;
     codes_generic_kernel<BITS><<<blocks_for(nbytes), 256, 0, st>>>(w, scales, payload, nbytes, group);
   }
@@ -561,9 +568,10 @@ int quantize_path(const Mat& mt, const float* w, const uint8_t* payload) {
   const uint64_t blocks_needed = (count / 4 + quant_block_vecs(mt.group) - 1) /
                                  quant_block_vecs(mt.group);
   const bool pow2 = (group & (group - 1)) == 0;
-  if (al && pow2 && group >= 8 && group <= 1024 && blocks_needed < (1ull << 31))
+  // (grids below 2^32 work-items: 2^24 blocks of at most 256 threads)
+  if (al && pow2 && group >= 8 && group <= 1024 && blocks_needed < (1ull << 24))
     return PATH_FAST;
-  if (al && group % 4 == 0 && group <= 256u * 4u * QB_J && count / group < (1ull << 31))
+  if (al && group % 4 == 0 && group <= 256u * 4u * QB_J && count / group < (1ull << 24))
     return PATH_BLOCK;
   return PATH_GENERIC;
 }
@@ -571,7 +579,7 @@ int quantize_path(const Mat& mt, const float* w, const uint8_t* payload) {
 int unpack_path(const Mat& mt, const uint8_t* payload, const float* w_out) {
   const uint64_t count = (uint64_t)mt.n * (uint64_t)mt.k;
   const bool al = aligned(w_out, 16) && aligned(payload, mt.bits == 4 ? 8 : 16);
-  if (al && mt.group % 4 == 0 && (count / 4 + 1023) / 1024 < (1ull << 31)) return PATH_FAST;
+  if (al && mt.group % 4 == 0 && (count / 4 + 1023) / 1024 < (1ull << 24)) return PATH_FAST;
   return PATH_GENERIC;
 }
 
@@ -632,8 +640,9 @@ hipError_t launch_quantize_pack_batched(const Mat* mts, const float* const* ws,
     }
     bk->idx.push_back(i);
   }
-  // a launch takes up to QUANT_NB matrices and fewer than 2^31 blocks
-  const uint64_t kMaxBlocks = (1ull << 31) - 1;
+  // a launch takes up to QUANT_NB matrices and at most 2^24 blocks (of 128
+  // threads: far inside the 2^32 work-items of a dispatch)
+  const uint64_t kMaxBlocks = 1ull << 24;
   for (const auto& bk : buckets) {
     size_t j = 0;
     while (j < bk.idx.size()) {
@@ -667,8 +676,8 @@ hipError_t launch_unpack_batched(const Mat* mts, const uint8_t* const* payloads,
                                  const float* const* scales, float* const* outs, int count,
                                  hipStream_t st) {
   // vector-path matrices of one bit width go out UNPACK_NB per launch (and
-  // fewer than 2^31 blocks); any other matrix takes the single call
-  const uint64_t kMaxBlocks = (1ull << 31) - 1;
+  // at most 2^23 blocks of 256 threads); any other matrix takes the single call
+  const uint64_t kMaxBlocks = 1ull << 23;
   for (int bits = 4; bits <= 8; bits += 4) {
     UnpackBatch b{};
     uint64_t blocks = 0;

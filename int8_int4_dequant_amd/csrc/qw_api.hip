@@ -19,14 +19,17 @@ int record(hipError_t e) {
   return QW_EHIP;
 }
 
-bool mul_overflows(int64_t a, int64_t b) {
-  return a != 0 && b > INT64_MAX / 4 / a;  // keep headroom for byte counts
+// 0 <= a, b and a * b <= QW_MAX_ELEMENTS (each factor bounded first, so the
+// product cannot overflow).
+bool within(int64_t a, int64_t b) {
+  const int64_t lim = QW_MAX_ELEMENTS;
+  return a >= 0 && b >= 0 && a <= lim && b <= lim && (a == 0 || b <= lim / a);
 }
 
 // Validates bits / group / shape; fills `mt` on success.
 int check_mat(int bits, int64_t group, int64_t n, int64_t k, qw::Mat* mt) {
   if (bits != 4 && bits != 8) return QW_EBITS;
-  if (n < 0 || k < 0 || mul_overflows(n, k)) return QW_ESHAPE;
+  if (!within(n, k)) return QW_ESHAPE;
   if (group < 1) return QW_EGROUP;
   const int64_t count = n * k;
   if (count % group != 0) return QW_EGROUP;
@@ -43,13 +46,13 @@ int check_mat(int bits, int64_t group, int64_t n, int64_t k, qw::Mat* mt) {
 extern "C" {
 
 int64_t qw_payload_bytes(int bits, int64_t n, int64_t k) {
-  if ((bits != 4 && bits != 8) || n < 0 || k < 0 || mul_overflows(n, k)) return -1;
+  if ((bits != 4 && bits != 8) || !within(n, k)) return -1;
   if (bits == 4 && (n * k) % 2 != 0) return -1;
   return n * k * bits / 8;
 }
 
 int64_t qw_num_scales(int64_t group, int64_t n, int64_t k) {
-  if (group < 1 || n < 0 || k < 0 || mul_overflows(n, k) || (n * k) % group != 0) return -1;
+  if (group < 1 || !within(n, k) || (n * k) % group != 0) return -1;
   return n * k / group;
 }
 
@@ -167,7 +170,7 @@ int qw_gemv(int bits, int64_t group, int64_t n, int64_t k, const uint8_t* payloa
   qw::Mat mt;
   int st = check_mat(bits, group, n, k, &mt);
   if (st != QW_OK) return st;
-  if (m < 0 || m > 8) return QW_EM;
+  if (m < 0 || m > 8 || !within(m, n) || !within(m, k)) return QW_EM;
   if (m == 0 || n == 0) return QW_OK;
   if (!y) return QW_ENULL;
   if (k == 0) return record(qw::launch_fill_zero(y, m * n, (hipStream_t)stream));
@@ -188,6 +191,7 @@ int qw_gemv_batched(int count, const qw_gemv_desc* descs, int64_t m, void* strea
     qw::Mat mt;
     int st = check_mat(d.bits, d.group, d.n, d.k, &mt);
     if (st != QW_OK) return st;
+    if (!within(m, d.n) || !within(m, d.k)) return QW_EM;
     if (d.n == 0) continue;
     if (!d.y) return QW_ENULL;
     if (d.k > 0 && (!d.payload || !d.scales || !d.x)) return QW_ENULL;
@@ -236,6 +240,7 @@ int qw_gemv_chain(int count, const qw_gemv_desc* descs, const int32_t* stage, in
     qw::Mat mt;
     int st = check_mat(d.bits, d.group, d.n, d.k, &mt);
     if (st != QW_OK) return st;
+    if (!within(m, d.n) || !within(m, d.k)) return QW_EM;
     if (d.n == 0) continue;
     if (!d.y) return QW_ENULL;
     if (d.k > 0 && (!d.payload || !d.scales || !d.x)) return QW_ENULL;
@@ -288,7 +293,7 @@ int qw_gemm(int bits, int64_t group, int64_t n, int64_t k, const uint8_t* payloa
   qw::Mat mt;
   int st = check_mat(bits, group, n, k, &mt);
   if (st != QW_OK) return st;
-  if (m < 0 || mul_overflows(m, n) || mul_overflows(m, k)) return QW_EM;
+  if (!within(m, n) || !within(m, k)) return QW_EM;
   if (m == 0 || n == 0) return QW_OK;
   if (!y) return QW_ENULL;
   if (k == 0) return record(qw::launch_fill_zero(y, m * n, (hipStream_t)stream));
@@ -297,7 +302,7 @@ int qw_gemm(int bits, int64_t group, int64_t n, int64_t k, const uint8_t* payloa
 }
 
 int64_t qw_matmul_work_bytes(int64_t m, int64_t k) {
-  if (m < 0 || k < 0 || mul_overflows(m, k)) return -1;
+  if (!within(m, k)) return -1;
   if (m <= QW_MATMUL_GEMV_MAX_M) return 0;
   return (m * k * 2 + 255) / 256 * 256;  // bf16 copy of x
 }
@@ -362,7 +367,7 @@ int qw_matmul(int bits, int64_t group, int64_t n, int64_t k, const uint8_t* payl
   qw::Mat mt;
   int st = check_mat(bits, group, n, k, &mt);
   if (st != QW_OK) return st;
-  if (m < 0 || mul_overflows(m, n) || mul_overflows(m, k)) return QW_EM;
+  if (!within(m, n) || !within(m, k)) return QW_EM;
   if (m <= QW_MATMUL_GEMV_MAX_M)
     return qw_gemv(bits, group, n, k, payload, scales, m, x, y, stream);
   if (n == 0) return QW_OK;
@@ -378,7 +383,7 @@ int qw_matmul_noalloc(int bits, int64_t group, int64_t n, int64_t k, const uint8
   qw::Mat mt;
   int st = check_mat(bits, group, n, k, &mt);
   if (st != QW_OK) return st;
-  if (m < 0 || mul_overflows(m, n) || mul_overflows(m, k)) return QW_EM;
+  if (!within(m, n) || !within(m, k)) return QW_EM;
   if (m <= QW_MATMUL_GEMV_MAX_M)
     return qw_gemv(bits, group, n, k, payload, scales, m, x, y, stream);
   if (n == 0) return QW_OK;
@@ -393,13 +398,13 @@ int qw_matmul_noalloc(int bits, int64_t group, int64_t n, int64_t k, const uint8
 }
 
 int64_t qw_gptq_hessian_work_bytes(int64_t k, int64_t t) {
-  if (k < 0 || t < 0 || mul_overflows(k, k)) return -1;
+  if (k < 0 || k > QW_GPTQ_MAX_K || !within(t, k)) return -1;
   return qw::gptq_hessian_work_bytes(k, t);
 }
 
 int qw_gptq_hessian(int64_t k, int64_t t, const float* x, double* h, void* work,
                     int64_t work_bytes, void* stream) {
-  if (k < 0 || t < 0 || mul_overflows(k, k) || mul_overflows(k, t)) return QW_ESHAPE;
+  if (k < 0 || k > QW_GPTQ_MAX_K || !within(t, k)) return QW_ESHAPE;
   if (k == 0 || t == 0) return QW_OK;
   if (!x || !h) return QW_ENULL;
   if (!work || work_bytes < qw::gptq_hessian_work_bytes(k, t)) return QW_EWORK;
@@ -407,13 +412,13 @@ int qw_gptq_hessian(int64_t k, int64_t t, const float* x, double* h, void* work,
 }
 
 int64_t qw_gptq_factor_work_bytes(int64_t k) {
-  if (k < 0 || mul_overflows(k + 64, k + 64)) return -1;
+  if (k < 0 || k > QW_GPTQ_MAX_K) return -1;
   return qw::gptq_factor_work_bytes(k);
 }
 
 int qw_gptq_factor(int64_t k, const double* h, double damp, double* u, int32_t* info,
                    void* work, int64_t work_bytes, void* stream) {
-  if (k < 0 || mul_overflows(k + 64, k + 64)) return QW_ESHAPE;
+  if (k < 0 || k > QW_GPTQ_MAX_K) return QW_ESHAPE;
   if (!(damp >= 0.0) || !(damp < 1e300)) return QW_EARG;
   if (k == 0) return QW_OK;
   if (!h || !u) return QW_ENULL;
@@ -422,7 +427,7 @@ int qw_gptq_factor(int64_t k, const double* h, double damp, double* u, int32_t* 
 }
 
 int64_t qw_gptq_quantize_work_bytes(int64_t n, int64_t k) {
-  if (n < 0 || k < 0 || mul_overflows(n, k + 64) || mul_overflows(k, k)) return -1;
+  if (!within(n, k) || n > QW_GPTQ_MAX_N || k > QW_GPTQ_MAX_K) return -1;
   return qw::gptq_quantize_work_bytes(n, k);
 }
 
@@ -432,7 +437,7 @@ int qw_gptq_quantize_pack(int bits, int64_t group, int64_t n, int64_t k, const f
   qw::Mat mt;
   int st = check_mat(bits, group, n, k, &mt);
   if (st != QW_OK) return st;
-  if (mul_overflows(n, k + 64) || mul_overflows(k, k)) return QW_ESHAPE;
+  if (n > QW_GPTQ_MAX_N || k > QW_GPTQ_MAX_K) return QW_ESHAPE;
   if (k > 0 && (k % group != 0 || (bits == 4 && group % 2 != 0))) return QW_EGROUP;
   if (n * k == 0) return QW_OK;
   if (!w || !u || !payload || !scales) return QW_ENULL;
