@@ -88,13 +88,14 @@ enum qw_status {
 #define QW_BATCH_PER_LAUNCH 256
 
 /* Size limits.  One matrix holds at most QW_MAX_ELEMENTS weights: n, k and
- * n*k are each at most that (2^31 fp32 weights are 8 GiB), and so are a
- * product's m*k activations and m*n outputs.  Within them every kernel
- * launch stays below the 2^32 work-items of one dispatch; beyond them a call
- * returns QW_ESHAPE (QW_EM for m) and enqueues nothing.  The GPTQ calls also
- * take k <= QW_GPTQ_MAX_K (H and U are k x k fp64: 8 GiB each at the limit),
- * n <= QW_GPTQ_MAX_N and t*k <= QW_MAX_ELEMENTS. */
-#define QW_MAX_ELEMENTS (1ll << 31)
+ * n*k are each at most that (2^36 fp32 weights are 256 GiB, more than one
+ * GPU's memory), and so are a product's m*k activations and m*n outputs.
+ * Beyond them a call returns QW_ESHAPE (QW_EM for m) and enqueues nothing.
+ * The GPTQ calls take smaller matrices: k <= QW_GPTQ_MAX_K (H and U are
+ * k x k fp64, 8 GiB each at the limit), n <= QW_GPTQ_MAX_N, and n*k and
+ * t*k at most QW_GPTQ_MAX_ELEMENTS. */
+#define QW_MAX_ELEMENTS (1ll << 36)
+#define QW_GPTQ_MAX_ELEMENTS (1ll << 31)
 #define QW_GPTQ_MAX_K 32768
 #define QW_GPTQ_MAX_N (1ll << 24)
 

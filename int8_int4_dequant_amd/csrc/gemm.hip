@@ -29,6 +29,7 @@
 //     weight tile stays in that XCD's L2 while the M tiles reuse it).
 #include "qw_internal.h"
 
+#include <algorithm>
 #include <atomic>
 
 namespace qw {
@@ -601,24 +602,25 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ payload,
     const float* __restrict__ scales, float* __restrict__ y, int64_t m, int64_t n, int64_t k,
     int64_t group) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= m * n) return;
-  const int64_t mm = t / n, nn = t % n;
-  float sum = 0.0f;
-  for (int64_t j = 0; j < k; ++j) {
-    const int64_t e = nn * k + j;
-    int q;
-    if (BITS == 4) {
-      const uint32_t b = payload[e >> 1];
-      q = (int)((e & 1) ? (b >> 4) : (b & 15u)) - 8;
-    } else {
-      q = (int)(int8_t)payload[e];
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < m * n;
+       t += (int64_t)gridDim.x * 256) {
+    const int64_t mm = t / n, nn = t % n;
+    float sum = 0.0f;
+    for (int64_t j = 0; j < k; ++j) {
+      const int64_t e = nn * k + j;
+      int q;
+      if (BITS == 4) {
+        const uint32_t b = payload[e >> 1];
+        q = (int)((e & 1) ? (b >> 4) : (b & 15u)) - 8;
+      } else {
+        q = (int)(int8_t)payload[e];
+      }
+      const float wf = (float)(__bf16)((float)q * scales[e / group]);
+      const float xf = __uint_as_float((uint32_t)x[mm * k + j] << 16);
+      sum = __builtin_fmaf(xf, wf, sum);
     }
-    const float wf = (float)(__bf16)((float)q * scales[e / group]);
-    const float xf = __uint_as_float((uint32_t)x[mm * k + j] << 16);
-    sum = __builtin_fmaf(xf, wf, sum);
+    y[mm * n + nn] = sum;
   }
-  y[mm * n + nn] = sum;
 }
 
 // ------------------------------------------------------ activation rounding
@@ -630,16 +632,17 @@ __global__ __launch_bounds__(256) void gemm_generic_kernel(
 __global__ __launch_bounds__(256) void round_bf16_kernel(const float* __restrict__ x,
                                                          uint16_t* __restrict__ xb, int64_t count,
                                                          int vec) {
-  const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
-  if (i0 >= count) return;
-  if (vec && i0 + 8 <= count) {
-    const float4 a = *reinterpret_cast<const float4*>(x + i0);
-    const float4 b = *reinterpret_cast<const float4*>(x + i0 + 4);
-    *reinterpret_cast<u32x4*>(xb + i0) = u32x4{pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w),
-                                               pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w)};
-  } else {
-    for (int64_t i = i0; i < count && i < i0 + 8; ++i)
-      xb[i] = (uint16_t)(pack_bf16x2(x[i], 0.0f) & 0xffffu);
+  for (int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8; i0 < count;
+       i0 += (int64_t)gridDim.x * 256 * 8) {
+    if (vec && i0 + 8 <= count) {
+      const float4 a = *reinterpret_cast<const float4*>(x + i0);
+      const float4 b = *reinterpret_cast<const float4*>(x + i0 + 4);
+      *reinterpret_cast<u32x4*>(xb + i0) = u32x4{pack_bf16x2(a.x, a.y), pack_bf16x2(a.z, a.w),
+                                                 pack_bf16x2(b.x, b.y), pack_bf16x2(b.z, b.w)};
+    } else {
+      for (int64_t i = i0; i < count && i < i0 + 8; ++i)
+        xb[i] = (uint16_t)(pack_bf16x2(x[i], 0.0f) & 0xffffu);
+    }
   }
 }
 
@@ -700,15 +703,16 @@ hipError_t launch_gemm(const Mat& mt, const uint8_t* payload, const float* scale
     }
     // one scale per `group` codes along a row (per-row groups), or per row
     a.scale_period = a.per_row_groups ? (mt.group % BK == 0 ? mt.group : 0) : mt.k;
-    if (m <= kSmallMaxM) {
-      // few rows: the small-M kernel, tile 32 x 32*NBW, K split over the block's waves
+    // few rows: the small-M kernel, tile 32 x 32*NBW, K split over the block's
+    // waves -- unless its grid (one block per tile) would pass 2^24 blocks; the
+    // 256-row tiles then take it
+    if (m <= kSmallMaxM && ((m + 31) / 32) * ((mt.n + 31) / 32) < (1ll << 24)) {
       const int cus = compute_units();
       const int64_t tms = (m + 31) / 32;
       // two column blocks per wave (half the A-fragment reads per weight) when that
       // still gives every compute unit a block
       const int nbw = tms * ((mt.n + 63) / 64) >= cus ? 2 : 1;
       const int64_t tns = (mt.n + 32 * nbw - 1) / (32 * nbw);
-      if (tms * tns >= (1ll << 24)) return hipErrorInvalidValue;  // < 2^32 work-items
       a.tiles_m = (int)tms;
       a.tiles_n = (int)tns;
       const unsigned grid = (unsigned)(tms * tns);
@@ -750,8 +754,9 @@ hipError_t launch_gemm(const Mat& mt, const uint8_t* payload, const float* scale
       gemm_kernel<8><<<grid, 256, 0, st>>>(a);
     return hipGetLastError();
   }
+  // at most 2^20 blocks, striding over the outputs
   const int64_t outs = m * mt.n;
-  const unsigned grid = (unsigned)((outs + 255) / 256);
+  const unsigned grid = (unsigned)std::min<int64_t>((outs + 255) / 256, 1 << 20);
   if (mt.bits == 4)
     gemm_generic_kernel<4><<<grid, 256, 0, st>>>(x, payload, scales, y, m, mt.n, mt.k, mt.group);
   else
@@ -761,9 +766,10 @@ hipError_t launch_gemm(const Mat& mt, const uint8_t* payload, const float* scale
 
 hipError_t launch_round_bf16(const float* x, uint16_t* xb, int64_t count, hipStream_t st) {
   const int64_t threads = (count + 7) / 8;
-  if ((threads + 255) / 256 >= (1ll << 24)) return hipErrorInvalidValue;
   const int vec = aligned(x, 16) && aligned(xb, 16) ? 1 : 0;
-  round_bf16_kernel<<<(unsigned)((threads + 255) / 256), 256, 0, st>>>(x, xb, count, vec);
+  // at most 2^20 blocks, striding over the rest
+  round_bf16_kernel<<<(unsigned)std::min<int64_t>((threads + 255) / 256, 1 << 20), 256, 0, st>>>(
+      x, xb, count, vec);
   return hipGetLastError();
 }
 

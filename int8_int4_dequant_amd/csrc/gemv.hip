@@ -517,11 +517,11 @@ constexpr int64_t kSplitManyRows = 12288;
 constexpr int64_t kBigRowsMany = 16384;
 constexpr int64_t kBigRowsLone = 32768;
 
-// Work items one launch takes at most (2^22 blocks of 256 threads for the
-// split-K kernel, 2^20 for the streaming one: both far inside the 2^32
-// work-items of a dispatch).  A matrix has at most 2^28 rows on the fast path
-// (n * k <= 2^31 with k >= 8), so one always fits.
-constexpr int64_t kMaxItems = 1 << 22;
+// Work items one launch takes at most (2^23 blocks of 256 threads for the
+// split-K kernel, 2^21 for the streaming one: both inside the 2^32
+// work-items of a dispatch).  A matrix on the fast path has at most 2^26
+// rows, at least 8 per item, so one always fits.
+constexpr int64_t kMaxItems = 1 << 23;
 
 // Fills `b` with descriptors ds[i..] (at most NB, at most kMaxItems work items
 // of R rows) and returns the index of the first descriptor left over.
@@ -640,7 +640,7 @@ hipError_t launch_generic(const Mat& mt, const uint8_t* payload, const float* sc
 
 int gemv_path(const Mat& mt, const uint8_t* payload, const float* x) {
   const int cpc = 8;  // codes per chunk
-  const bool shape_ok = mt.k % cpc == 0 && mt.n < (1ll << 30) && mt.k < (1ll << 30) &&
+  const bool shape_ok = mt.k % cpc == 0 && mt.n <= (1ll << 26) && mt.k < (1ll << 30) &&
                         (int64_t)mt.k * mt.bits / 8 < (1ll << 31);
   const bool group_ok = mt.k > 0 && ((mt.k % mt.group == 0 && mt.group % cpc == 0) ||
                                       (mt.group % mt.k == 0));
@@ -697,12 +697,15 @@ hipError_t launch_gemv_batched(const Mat* mts, const uint8_t* const* payloads,
 }
 
 __global__ void fill_zero_kernel(float* y, int64_t count) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i < count) y[i] = 0.0f;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < count;
+       i += (int64_t)gridDim.x * 256)
+    y[i] = 0.0f;
 }
 
 hipError_t launch_fill_zero(float* y, int64_t count, hipStream_t st) {
-  fill_zero_kernel<<<(unsigned)((count + 255) / 256), 256, 0, st>>>(y, count);
+  // at most 2^20 blocks, striding over the rest
+  fill_zero_kernel<<<(unsigned)std::min<int64_t>((count + 255) / 256, 1 << 20), 256, 0, st>>>(
+      y, count);
   return hipGetLastError();
 }
 

@@ -70,21 +70,26 @@ __device__ __forceinline__ float scale_of(float m) {
 // Rounded quotients rint(fl32(w[e] / s)) for the NE values of one lane,
 // all in one group (scale s), returned as exact small integers in fp32.
 //
-// Shortcut: with R = fl32(1/s) and t = fl32(w * R), |t - fl32(w / s)| <=
-// (3u + u^2) |w / s| < 3 * 2^-24 * 128 < 2^-15 (u = 2^-24, |w / s| <= qmax
-// up to one ulp), provided 1/s is a normal number.  rint is constant
-// between half-integers, so wherever t is farther than 2^-15 from a
-// half-integer rint(t) equals rint(fl32(w / s)) exactly.  Otherwise (a
-// near-tie, about 6e-5 of random codes) or when s is extreme, every value of
-// the lane is recomputed with the IEEE division.  Both paths are exact.
-template <int NE>
+// Shortcut: with R = v_rcp_f32(s) (the hardware reciprocal, within 1 ulp of
+// 1/s; 2 ulps are assumed below) and t = fl32(w * R),
+//   |t - fl32(w / s)| <= (2^-22 + 2^-24 + 2^-24 + O(2^-46)) |w / s|
+//                     <= 1.5 * 2^-22 * qmax * (1 + 2^-23)
+// (|w / s| <= qmax up to one ulp), i.e. below 2^-20 for int4 and 2^-16 for
+// int8, provided 1/s is a normal number.  rint is constant between
+// half-integers, so wherever t is farther than MARGIN (2^-17, resp. 2^-14)
+// from a half-integer, rint(t) equals rint(fl32(w / s)) exactly.  Otherwise
+// (a near-tie, about 2 * MARGIN of random codes) or when s is extreme, every
+// value of the lane is recomputed with the IEEE division.  Both paths are
+// exact.
+template <int BITS, int NE>
 __device__ __forceinline__ void rounded_quotients(const float (&w)[NE], float s, float (&r)[NE]) {
   // t must be the rounded product, and t - rint(t) a separate (exact)
   // subtraction: no contraction into an fma here.
 #pragma clang fp contract(off)
+  constexpr float kMargin = BITS == 4 ? 0x1p-17f : 0x1p-14f;
   bool fast = s >= 0x1p-125f && s <= 0x1p+125f;
   if (fast) {
-    const float rs = 1.0f / s;
+    const float rs = __builtin_amdgcn_rcpf(s);
     float dmax = 0.0f;
 #pragma unroll
     for (int e = 0; e < NE; ++e) {
@@ -93,7 +98,7 @@ __device__ __forceinline__ void rounded_quotients(const float (&w)[NE], float s,
       dmax = fmaxf(dmax, fabsf(t - rt));  // exact: t and rint(t) are close
       r[e] = rt;
     }
-    fast = dmax < 0.5f - 0x1p-15f;
+    fast = dmax < 0.5f - kMargin;
   }
   if (!fast) {
 #pragma unroll
@@ -105,21 +110,22 @@ __device__ __forceinline__ void rounded_quotients(const float (&w)[NE], float s,
 
 // Packs 4 rounded quotients (element order): int4 -> 16 bits, int8 -> 32 bits.
 // The quotients already lie in [-qmax, qmax] for finite inputs (|w / s|
-// exceeds qmax by at most one ulp), so no clip is needed; the masks keep
-// garbage from non-finite inputs inside its own field.  Adding 2^23 + 8
-// (int4) or 2^23 + 256 (int8) puts q + 8, resp. q mod 256, in the low
-// mantissa bits.
+// exceeds qmax by at most one ulp), so no clip is needed.  Each payload byte
+// is formed as an exact small integer in fp32 and converted with the
+// byte-inserting conversion (v_cvt_pk_u8_f32, which also clamps garbage from
+// non-finite inputs into its own byte): int4 byte = (q0 + 8) + 16 (q1 + 8)
+// = 16 q1 + q0 + 136 (one fma); int8 byte = q + 128, then the sign bit of
+// each byte is flipped to give q's two's complement.
 __device__ __forceinline__ uint32_t pack4_int4(const float* r) {
-  uint32_t v = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) v |= (__float_as_uint(r[i] + 8388616.0f) & 15u) << (4 * i);
-  return v;
+  const float b0 = __builtin_fmaf(r[1], 16.0f, r[0] + 136.0f);
+  const float b1 = __builtin_fmaf(r[3], 16.0f, r[2] + 136.0f);
+  return __builtin_amdgcn_cvt_pk_u8_f32(b1, 1, __builtin_amdgcn_cvt_pk_u8_f32(b0, 0, 0));
 }
 __device__ __forceinline__ uint32_t pack4_int8(const float* r) {
   uint32_t v = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) v |= (__float_as_uint(r[i] + 8388864.0f) & 255u) << (8 * i);
-  return v;
+  for (int i = 0; i < 4; ++i) v = __builtin_amdgcn_cvt_pk_u8_f32(r[i] + 128.0f, i, v);
+  return v ^ 0x80808080u;
 }
 
 constexpr int QV = 4;  // float4 vectors per lane in the unpack kernel
@@ -133,6 +139,10 @@ constexpr int QV = 4;  // float4 vectors per lane in the unpack kernel
 template <int G>
 constexpr int quant_qv() { return G <= 64 ? 2 : 4; }
 constexpr int QUANT_WAVES = 2;
+// Blocks per launch of the single-matrix fast kernels (of at most 256
+// threads: 2^32 work-items, the limit of one dispatch); a larger matrix takes
+// several launches, each with its first block index.
+constexpr uint64_t kMaxLaunchBlocks = 1ull << 24;
 // float4 vectors one block quantizes, for a group of `group` weights
 inline uint64_t quant_block_vecs(int64_t group) {
   return (uint64_t)64 * (group / 4 <= 64 ? 2 : 4) * QUANT_WAVES;
@@ -197,7 +207,7 @@ __device__ __forceinline__ void quant_subgroup_body(
     const float s = scale_of<BITS>(m[j]);
     if (vi % G == 0) stage_s[wv][vi / G] = s;
     float r[4];
-    rounded_quotients<4>(v[j], s, r);
+    rounded_quotients<BITS, 4>(v[j], s, r);
     if constexpr (BITS == 4)
       reinterpret_cast<uint16_t*>(stage_p[wv])[vi] = (uint16_t)pack4_int4(r);
     else
@@ -239,11 +249,13 @@ __device__ __forceinline__ void quant_subgroup_body(
   }
 }
 
+// One matrix; a launch covers blocks [block_base, block_base + gridDim.x)
+// (a matrix of more than 2^24 blocks takes several launches).
 template <int BITS, int G>
 __global__ __launch_bounds__(64 * QUANT_WAVES) void quant_subgroup_kernel(
     const float* __restrict__ w, uint8_t* __restrict__ payload,
-    float* __restrict__ scales, uint64_t nvec) {
-  quant_subgroup_body<BITS, G>(w, payload, scales, nvec, blockIdx.x);
+    float* __restrict__ scales, uint64_t nvec, uint64_t block_base) {
+  quant_subgroup_body<BITS, G>(w, payload, scales, nvec, block_base + blockIdx.x);
 }
 
 // Several matrices of the same bits and group in one launch: the matrices'
@@ -314,7 +326,7 @@ __global__ __launch_bounds__(256) void quant_block_kernel(
     const int c = tid + 256 * j;
     if (c < vpg) {
       float r[4];
-      rounded_quotients<4>(v[j], s, r);
+      rounded_quotients<BITS, 4>(v[j], s, r);
       if constexpr (BITS == 4)
         reinterpret_cast<uint16_t*>(payload)[base + c] = (uint16_t)pack4_int4(r);
       else
@@ -330,12 +342,13 @@ template <int BITS>
 __global__ __launch_bounds__(256) void scales_thread_kernel(
     const float* __restrict__ w, float* __restrict__ scales, uint64_t ngroups,
     uint64_t group) {
-  const uint64_t g = (uint64_t)blockIdx.x * 256u + threadIdx.x;
-  if (g >= ngroups) return;
-  const float* p = w + g * group;
-  float m = 0.0f;
-  for (uint64_t i = 0; i < group; ++i) m = fmaxf(m, fabsf(p[i]));
-  scales[g] = scale_of<BITS>(m);
+  for (uint64_t g = (uint64_t)blockIdx.x * 256u + threadIdx.x; g < ngroups;
+       g += (uint64_t)gridDim.x * 256u) {
+    const float* p = w + g * group;
+    float m = 0.0f;
+    for (uint64_t i = 0; i < group; ++i) m = fmaxf(m, fabsf(p[i]));
+    scales[g] = scale_of<BITS>(m);
+  }
 }
 
 // Scales, one block per group (large groups).
@@ -365,15 +378,16 @@ template <int BITS>
 __global__ __launch_bounds__(256) void codes_generic_kernel(
     const float* __restrict__ w, const float* __restrict__ scales,
     uint8_t* __restrict__ payload, uint64_t nbytes, uint64_t group) {
-  const uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x;
-  if (i >= nbytes) return;
-  if (BITS == 8) {
-    payload[i] = (uint8_t)(code_of<8>(w[i], scales[i / group]) & 255);
-  } else {
-    const uint64_t e0 = 2 * i, e1 = 2 * i + 1;
-    const int q0 = code_of<4>(w[e0], scales[e0 / group]);
-    const int q1 = code_of<4>(w[e1], scales[e1 / group]);
-    payload[i] = (uint8_t)(((q0 + 8) & 15) | (((q1 + 8) & 15) << 4));
+  for (uint64_t i = (uint64_t)blockIdx.x * 256u + threadIdx.x; i < nbytes;
+       i += (uint64_t)gridDim.x * 256u) {
+    if (BITS == 8) {
+      payload[i] = (uint8_t)(code_of<8>(w[i], scales[i / group]) & 255);
+    } else {
+      const uint64_t e0 = 2 * i, e1 = 2 * i + 1;
+      const int q0 = code_of<4>(w[e0], scales[e0 / group]);
+      const int q1 = code_of<4>(w[e1], scales[e1 / group]);
+      payload[i] = (uint8_t)(((q0 + 8) & 15) | (((q1 + 8) & 15) << 4));
+    }
   }
 }
 
@@ -441,8 +455,8 @@ __device__ __forceinline__ void unpack_vec_body(
 template <int BITS>
 __global__ __launch_bounds__(256) void unpack_vec_kernel(
     const uint8_t* __restrict__ payload, const float* __restrict__ scales,
-    float* __restrict__ out, uint64_t nvec, uint64_t vpg, int vshift) {
-  unpack_vec_body<BITS>(payload, scales, out, nvec, vpg, vshift, blockIdx.x);
+    float* __restrict__ out, uint64_t nvec, uint64_t vpg, int vshift, uint64_t block_base) {
+  unpack_vec_body<BITS>(payload, scales, out, nvec, vpg, vshift, block_base + blockIdx.x);
 }
 
 // Several matrices of one bit width in one launch (any groups the vector
@@ -484,19 +498,24 @@ template <int BITS>
 __global__ __launch_bounds__(256) void unpack_generic_kernel(
     const uint8_t* __restrict__ payload, const float* __restrict__ scales,
     float* __restrict__ out, uint64_t count, uint64_t group) {
-  const uint64_t e = (uint64_t)blockIdx.x * 256u + threadIdx.x;
-  if (e >= count) return;
-  int q;
-  if (BITS == 4) {
-    const uint32_t b = payload[e >> 1];
-    q = (int)((e & 1) ? (b >> 4) : (b & 15u)) - 8;
-  } else {
-    q = (int)(int8_t)payload[e];
+  for (uint64_t e = (uint64_t)blockIdx.x * 256u + threadIdx.x; e < count;
+       e += (uint64_t)gridDim.x * 256u) {
+    int q;
+    if (BITS == 4) {
+      const uint32_t b = payload[e >> 1];
+      q = (int)((e & 1) ? (b >> 4) : (b & 15u)) - 8;
+    } else {
+      q = (int)(int8_t)payload[e];
+    }
+    out[e] = (float)q * scales[e / group];
   }
-  out[e] = (float)q * scales[e / group];
 }
 
-inline unsigned blocks_for(uint64_t threads) { return (unsigned)((threads + 255) / 256); }
+// Blocks of 256 threads for a grid-stride kernel over `threads` items: at
+// most 2^20 (2^28 work-items, far inside one dispatch's 2^32).
+inline unsigned blocks_for(uint64_t threads) {
+  return (unsigned)std::min<uint64_t>((threads + 255) / 256, 1u << 20);
+}
 
 template <int BITS>
 hipError_t quantize_bits(const Mat& mt, const float* w, uint8_t* payload, float* scales,
@@ -507,16 +526,25 @@ hipError_t quantize_bits(const Mat& mt, const float* w, uint8_t* payload, float*
   if (path == PATH_FAST) {
     const uint64_t nvec = count / 4;
     const uint64_t bv = quant_block_vecs(mt.group);
-    const unsigned grid = (unsigned)((nvec + bv - 1) / bv);
-    switch (group / 4) {
-      case 2: quant_subgroup_kernel<BITS, 2><<<grid, 64 * QUANT_WAVES, 0, st>>>(w, payload, scales, nvec); break;
-      case 4: quant_subgroup_kernel<BITS, 4><<<grid, 64 * QUANT_WAVES, 0, st>>>(w, payload, scales, nvec); break;
-      case 8: quant_subgroup_kernel<BITS, 8><<<grid, 64 * QUANT_WAVES, 0, st>>>(w, payload, scales, nvec); break;
-      case 16: quant_subgroup_kernel<BITS, 16><<<grid, 64 * QUANT_WAVES, 0, st>>>(w, payload, scales, nvec); break;
-      case 32: quant_subgroup_kernel<BITS, 32><<<grid, 64 * QUANT_WAVES, 0, st>>>(w, payload, scales, nvec); break;
-      case 64: quant_subgroup_kernel<BITS, 64><<<grid, 64 * QUANT_WAVES, 0, st>>>(w, payload, scales, nvec); break;
-      case 128: quant_subgroup_kernel<BITS, 128><<<grid, 64 * QUANT_WAVES, 0, st>>>(w, payload, scales, nvec); break;
-      default: quant_subgroup_kernel<BITS, 256><<<grid, 64 * QUANT_WAVES, 0, st>>>(w, payload, scales, nvec); break;
+    const uint64_t blocks = (nvec + bv - 1) / bv;
+    // launches of at most kMaxLaunchBlocks blocks
+    for (uint64_t b0 = 0; b0 < blocks; b0 += kMaxLaunchBlocks) {
+      const unsigned grid = (unsigned)std::min<uint64_t>(blocks - b0, kMaxLaunchBlocks);
+#define QW_QSUB(Gv) \
+  quant_subgroup_kernel<BITS, Gv><<<grid, 64 * QUANT_WAVES, 0, st>>>(w, payload, scales, nvec, b0)
+      switch (group / 4) {
+        case 2: QW_QSUB(2); break;
+        case 4: QW_QSUB(4); break;
+        case 8: QW_QSUB(8); break;
+        case 16: QW_QSUB(16); break;
+        case 32: QW_QSUB(32); break;
+        case 64: QW_QSUB(64); break;
+        case 128: QW_QSUB(128); break;
+        default: QW_QSUB(256); break;
+      }
+#undef QW_QSUB
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
     }
   } else if (path == PATH_BLOCK) {
     const uint64_t ngroups = count / group;
@@ -549,10 +577,15 @@ hipError_t unpack_bits(const Mat& mt, const uint8_t* payload, const float* scale
   const uint64_t group = (uint64_t)mt.group;
   if (unpack_path(mt, payload, out) == PATH_FAST) {
     const uint64_t nvec = count / 4;
-    const unsigned grid = (unsigned)((nvec + 4 * 64 * QV - 1) / (4 * 64 * QV));
+    const uint64_t blocks = (nvec + 4 * 64 * QV - 1) / (4 * 64 * QV);
     const uint64_t vpg = group / 4;
     const int vshift = vec_shift(vpg);
-    unpack_vec_kernel<BITS><<<grid, 256, 0, st>>>(payload, scales, out, nvec, vpg, vshift);
+    for (uint64_t b0 = 0; b0 < blocks; b0 += kMaxLaunchBlocks) {
+      const unsigned grid = (unsigned)std::min<uint64_t>(blocks - b0, kMaxLaunchBlocks);
+      unpack_vec_kernel<BITS><<<grid, 256, 0, st>>>(payload, scales, out, nvec, vpg, vshift, b0);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   } else {
     unpack_generic_kernel<BITS><<<blocks_for(count), 256, 0, st>>>(payload, scales, out, count, group);
   }
@@ -565,21 +598,18 @@ int quantize_path(const Mat& mt, const float* w, const uint8_t* payload) {
   const uint64_t count = (uint64_t)mt.n * (uint64_t)mt.k;
   const uint64_t group = (uint64_t)mt.group;
   const bool al = aligned(w, 16) && aligned(payload, mt.bits == 4 ? 4 : 8);
-  const uint64_t blocks_needed = (count / 4 + quant_block_vecs(mt.group) - 1) /
-                                 quant_block_vecs(mt.group);
   const bool pow2 = (group & (group - 1)) == 0;
-  // (grids below 2^32 work-items: 2^24 blocks of at most 256 threads)
-  if (al && pow2 && group >= 8 && group <= 1024 && blocks_needed < (1ull << 24))
-    return PATH_FAST;
+  // (the block kernel takes one block per group: below 2^24 groups, every
+  // launch stays within the 2^32 work-items of one dispatch)
+  if (al && pow2 && group >= 8 && group <= 1024) return PATH_FAST;
   if (al && group % 4 == 0 && group <= 256u * 4u * QB_J && count / group < (1ull << 24))
     return PATH_BLOCK;
   return PATH_GENERIC;
 }
 
 int unpack_path(const Mat& mt, const uint8_t* payload, const float* w_out) {
-  const uint64_t count = (uint64_t)mt.n * (uint64_t)mt.k;
   const bool al = aligned(w_out, 16) && aligned(payload, mt.bits == 4 ? 8 : 16);
-  if (al && mt.group % 4 == 0 && (count / 4 + 1023) / 1024 < (1ull << 24)) return PATH_FAST;
+  if (al && mt.group % 4 == 0) return PATH_FAST;
   return PATH_GENERIC;
 }
 
@@ -653,7 +683,11 @@ hipError_t launch_quantize_pack_batched(const Mat* mts, const float* const* ws,
         const uint64_t nvec = (uint64_t)(mts[i].n * mts[i].k) / 4;
         const uint64_t bv = quant_block_vecs(bk.group);
         const uint64_t nblk = (nvec + bv - 1) / bv;
-        if (nblk > kMaxBlocks) return hipErrorInvalidValue;
+        if (nblk > kMaxBlocks) {  // too large for a shared launch: on its own
+          const hipError_t e = launch_quantize_pack(mts[i], ws[i], payloads[i], scales[i], st);
+          if (e != hipSuccess) return e;
+          continue;
+        }
         if (blocks + nblk > kMaxBlocks) break;  // next launch
         b.block0[b.count] = (uint32_t)blocks;
         QuantDesc& d = b.d[b.count++];
@@ -663,6 +697,7 @@ hipError_t launch_quantize_pack_batched(const Mat* mts, const float* const* ws,
         d.nvec = nvec;
         blocks += nblk;
       }
+      if (b.count == 0) continue;  // only matrices launched on their own
       b.blocks = (int)blocks;
       hipError_t e = bk.bits == 4 ? launch_quant_batch_g<4>(b, bk.group, st)
                                   : launch_quant_batch_g<8>(b, bk.group, st);
@@ -701,7 +736,11 @@ hipError_t launch_unpack_batched(const Mat* mts, const uint8_t* const* payloads,
       }
       const uint64_t nvec = (uint64_t)(mts[i].n * mts[i].k) / 4;
       const uint64_t nblk = (nvec + 4 * 64 * QV - 1) / (4 * 64 * QV);
-      if (nblk > kMaxBlocks) return hipErrorInvalidValue;
+      if (nblk > kMaxBlocks) {  // too large for a shared launch: on its own
+        hipError_t e = launch_unpack(mts[i], payloads[i], scales[i], outs[i], st);
+        if (e != hipSuccess) return e;
+        continue;
+      }
       if (b.count == UNPACK_NB || blocks + nblk > kMaxBlocks) {
         hipError_t e = flush();
         if (e != hipSuccess) return e;

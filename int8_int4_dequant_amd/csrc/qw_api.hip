@@ -19,10 +19,9 @@ int record(hipError_t e) {
   return QW_EHIP;
 }
 
-// 0 <= a, b and a * b <= QW_MAX_ELEMENTS (each factor bounded first, so the
-// product cannot overflow).
-bool within(int64_t a, int64_t b) {
-  const int64_t lim = QW_MAX_ELEMENTS;
+// 0 <= a, b and a * b <= lim (each factor bounded first, so the product
+// cannot overflow).
+bool within(int64_t a, int64_t b, int64_t lim = QW_MAX_ELEMENTS) {
   return a >= 0 && b >= 0 && a <= lim && b <= lim && (a == 0 || b <= lim / a);
 }
 
@@ -398,13 +397,13 @@ int qw_matmul_noalloc(int bits, int64_t group, int64_t n, int64_t k, const uint8
 }
 
 int64_t qw_gptq_hessian_work_bytes(int64_t k, int64_t t) {
-  if (k < 0 || k > QW_GPTQ_MAX_K || !within(t, k)) return -1;
+  if (k < 0 || k > QW_GPTQ_MAX_K || !within(t, k, QW_GPTQ_MAX_ELEMENTS)) return -1;
   return qw::gptq_hessian_work_bytes(k, t);
 }
 
 int qw_gptq_hessian(int64_t k, int64_t t, const float* x, double* h, void* work,
                     int64_t work_bytes, void* stream) {
-  if (k < 0 || k > QW_GPTQ_MAX_K || !within(t, k)) return QW_ESHAPE;
+  if (k < 0 || k > QW_GPTQ_MAX_K || !within(t, k, QW_GPTQ_MAX_ELEMENTS)) return QW_ESHAPE;
   if (k == 0 || t == 0) return QW_OK;
   if (!x || !h) return QW_ENULL;
   if (!work || work_bytes < qw::gptq_hessian_work_bytes(k, t)) return QW_EWORK;
@@ -427,7 +426,7 @@ int qw_gptq_factor(int64_t k, const double* h, double damp, double* u, int32_t* 
 }
 
 int64_t qw_gptq_quantize_work_bytes(int64_t n, int64_t k) {
-  if (!within(n, k) || n > QW_GPTQ_MAX_N || k > QW_GPTQ_MAX_K) return -1;
+  if (!within(n, k, QW_GPTQ_MAX_ELEMENTS) || n > QW_GPTQ_MAX_N || k > QW_GPTQ_MAX_K) return -1;
   return qw::gptq_quantize_work_bytes(n, k);
 }
 
@@ -437,7 +436,8 @@ int qw_gptq_quantize_pack(int bits, int64_t group, int64_t n, int64_t k, const f
   qw::Mat mt;
   int st = check_mat(bits, group, n, k, &mt);
   if (st != QW_OK) return st;
-  if (n > QW_GPTQ_MAX_N || k > QW_GPTQ_MAX_K) return QW_ESHAPE;
+  if (!within(n, k, QW_GPTQ_MAX_ELEMENTS) || n > QW_GPTQ_MAX_N || k > QW_GPTQ_MAX_K)
+    return QW_ESHAPE;
   if (k > 0 && (k % group != 0 || (bits == 4 && group % 2 != 0))) return QW_EGROUP;
   if (n * k == 0) return QW_OK;
   if (!w || !u || !payload || !scales) return QW_ENULL;

@@ -199,6 +199,17 @@ static void fixed_cases(int launches_ok) {
   EXPECT(qw_quantize_pack(8, 4, MAXE / 4, 4, PA, PA, PA, 0), QW_EHIP);  /* at the limit */
   EXPECT(qw_quantize_pack(8, 12, MAXE / 16, 12, PA, PA, PA, 0), QW_EHIP);
   EXPECT(qw_quantize_pack(8, 65, MAXE / 65, 65, P1, PA, PA, 0), QW_EHIP);
+  EXPECT(qw_quantize_pack(4, 32, MAXE / 32, 32, PA, PA, PA, 0), QW_EHIP); /* several launches */
+  {
+    qw_quant_desc big[2];
+    memset(big, 0, sizeof(big));
+    for (int i = 0; i < 2; ++i) {
+      big[i].bits = 4; big[i].group = 32; big[i].w = PA; big[i].payload = PA; big[i].scales = PA;
+    }
+    big[0].n = MAXE / 64; big[0].k = 64;  /* too large to share a launch */
+    big[1].n = 64; big[1].k = 64;
+    EXPECT(qw_quantize_pack_batched(2, big, 0), QW_EHIP);
+  }
   EXPECT(qw_unpack(4, 32, MAXE / 32, 32, PA, PA, PA, 0), QW_EHIP);
   EXPECT(qw_unpack(8, 7, MAXE / 7, 7, P1, PA, PA, 0), QW_EHIP);
   EXPECT(qw_gemv(4, 128, 11008, 4096, PA, PA, 4, PA, PA, 0), QW_EHIP);
