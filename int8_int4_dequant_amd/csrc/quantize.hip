@@ -52,6 +52,51 @@ __device__ __forceinline__ void stnt(float4* p, float4 v) {
 template <int BITS>
 __device__ __forceinline__ float qmax_f() { return BITS == 8 ? 127.0f : 7.0f; }
 
+// The value held by a partner lane in the other half of this lane's aligned
+// run of 2*H lanes.  Within 16-lane rows a DPP lane permutation does it with
+// no separate instruction (quad_perm [1,0,3,2] and [2,3,0,1] for H = 1, 2;
+// row_half_mirror and row_mirror, i <-> 7-i and i <-> 15-i, for H = 4, 8);
+// wider runs take a cross-lane shuffle.  Every lane must be active.
+template <int H>
+__device__ __forceinline__ float partner(float v) {
+  constexpr int ctrl = H == 1 ? 0xB1 : H == 2 ? 0x4E : H == 4 ? 0x141 : 0x140;
+  if constexpr (H <= 8)
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xF, 0xF, false));
+  else
+    return __shfl_xor(v, H);
+}
+
+// max of v with its partner's value (partner<H>) for v >= 0: non-negative
+// floats order like their bit patterns, so an unsigned integer max gives the
+// float max, and with 0 its identity the DPP move folds into the max
+// (v_max_u32 with a DPP operand: one instruction per step).
+template <int H>
+__device__ __forceinline__ float pair_max_nonneg(float v) {
+  const uint32_t u = __float_as_uint(v);
+  uint32_t p;
+  if constexpr (H <= 8) {
+    constexpr int ctrl = H == 1 ? 0xB1 : H == 2 ? 0x4E : H == 4 ? 0x141 : 0x140;
+    p = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, ctrl, 0xF, 0xF, false);
+  } else {
+    p = __float_as_uint(__shfl_xor(v, H));
+  }
+  return __uint_as_float(u > p ? u : p);
+}
+
+// max over an aligned run of R lanes (R a power of two <= 64) of values
+// >= 0 (the |w| maxima of finite weights): each step combines the two halves
+// of runs twice as long as the last.
+template <int R>
+__device__ __forceinline__ float run_max(float v) {
+  if constexpr (R >= 2) v = pair_max_nonneg<1>(v);
+  if constexpr (R >= 4) v = pair_max_nonneg<2>(v);
+  if constexpr (R >= 8) v = pair_max_nonneg<4>(v);
+  if constexpr (R >= 16) v = pair_max_nonneg<8>(v);
+  if constexpr (R >= 32) v = pair_max_nonneg<16>(v);
+  if constexpr (R >= 64) v = pair_max_nonneg<32>(v);
+  return v;
+}
+
 // One code: IEEE division, ties-to-even rounding, clip.  -0 becomes 0.
 template <int BITS>
 __device__ __forceinline__ int code_of(float w, float s) {
@@ -183,9 +228,7 @@ __device__ __forceinline__ void quant_subgroup_body(
   // (nvec is a multiple of G), so inactive lanes only meet inactive lanes.
   if constexpr (G <= 64) {
 #pragma unroll
-    for (int j = 0; j < QV; ++j)
-#pragma unroll
-      for (int off = G / 2; off >= 1; off >>= 1) m[j] = fmaxf(m[j], __shfl_xor(m[j], off));
+    for (int j = 0; j < QV; ++j) m[j] = run_max<G>(m[j]);
   } else {
     constexpr int J = G / 64;  // instructions per group: 2 or 4
 #pragma unroll
@@ -193,18 +236,33 @@ __device__ __forceinline__ void quant_subgroup_body(
       float t = m[j0];
 #pragma unroll
       for (int j = 1; j < J; ++j) t = fmaxf(t, m[j0 + j]);
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) t = fmaxf(t, __shfl_xor(t, off));
+      t = run_max<64>(t);
 #pragma unroll
       for (int j = 0; j < J; ++j) m[j0 + j] = t;
     }
+  }
+  // The scales (one IEEE division each).  With two vectors per lane and
+  // groups of G <= 64 lanes, every lane meets two groups; the lanes of a
+  // group's upper half divide for its second group, those of the lower half
+  // for its first, and partners in opposite halves swap results: one
+  // division per lane instead of two, on the same operands.
+  float sj[QV];
+  if constexpr (QV == 2 && G <= 64) {
+    const bool upper = (lane & (G / 2)) != 0;
+    const float mine = scale_of<BITS>(upper ? m[1] : m[0]);
+    const float other = partner<G / 2>(mine);
+    sj[0] = upper ? other : mine;
+    sj[1] = upper ? mine : other;
+  } else {
+#pragma unroll
+    for (int j = 0; j < QV; ++j) sj[j] = scale_of<BITS>(m[j]);
   }
   // codes and scales into this wave's LDS stage (wave-private: LDS accesses
   // of one wave complete in order, no barrier needed)
 #pragma unroll
   for (int j = 0; j < QV; ++j) {
     const int vi = lane + 64 * j;  // vector index within the wave
-    const float s = scale_of<BITS>(m[j]);
+    const float s = sj[j];
     if (vi % G == 0) stage_s[wv][vi / G] = s;
     float r[4];
     rounded_quotients<BITS, 4>(v[j], s, r);
@@ -314,8 +372,7 @@ __global__ __launch_bounds__(256) void quant_block_kernel(
     v[j][0] = f.x; v[j][1] = f.y; v[j][2] = f.z; v[j][3] = f.w;
     m = fmaxf(m, fmaxf(fmaxf(fabsf(f.x), fabsf(f.y)), fmaxf(fabsf(f.z), fabsf(f.w))));
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  m = run_max<64>(m);
   if ((tid & 63) == 0) red[tid >> 6] = m;
   __syncthreads();
   m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
