@@ -358,6 +358,28 @@ def test_gemm_small_m_waves_start_inside_a_group(bits, m, group, k):
     check_gemm(ref, rec, inputs.bf16_activations(m * 7 + group, m, k))
 
 
+# The int4 GEMM kernels decode a code with one FMA, fma(u * 2^-9, 512 * s, -8 * s),
+# which overflows for scales of 2^118 and above; a block that meets such a
+# scale redoes its tile with the two-step decode.  Weights of 2^119 to 2^122
+# give scales on both sides of that limit (2^122 / 7 > 2^118 > 2^119 / 7);
+# X is scaled by 2^-40 (exactly, in bf16) so that every sum stays finite.
+# m = 300 runs the 256-row kernel, m = 9 the small-M one.
+@pytest.mark.parametrize("m", [300, 9])
+def test_gemm_int4_scales_beyond_the_one_fma_decode(m):
+    n, k = 520, 512
+    w = inputs.weight(m + 40, n, k, 0.02)
+    w[5, 7] = 2.0 ** 122
+    w[300, 500] = -(2.0 ** 121)
+    w[519, 100] = 2.0 ** 119
+    ref, rec = quant_both(w, 4, 128)
+    assert ref["scales"].max() >= 2.0 ** 118 > np.sort(ref["scales"])[-3]
+    xf = oracle.bf16_bits_to_f32(inputs.bf16_activations(m + 41, m, k)) * np.float32(2.0 ** -40)
+    xb = (xf.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(oracle.bf16_bits_to_f32(xb), xf)
+    y = check_gemm(ref, rec, xb)
+    assert np.all(np.isfinite(y))
+
+
 def test_gemm_ignores_stale_output():
     # the split tiles accumulate into Y: stale contents (NaN) must not leak
     w = inputs.weight(21, 300, 512, 0.02)
