@@ -38,6 +38,14 @@ namespace {
 constexpr int QB_J = 16;  // float4 vectors per thread in the block kernel (group <= 16384)
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+// Word types for the LDS staging buffers, which a wave writes with one word
+// size and reads back with another: `may_alias` keeps the compiler from
+// assuming that accesses of different types never overlap (and so from
+// moving a read-back ahead of the writes it depends on).
+typedef uint16_t __attribute__((may_alias)) u16_la;
+typedef uint32_t __attribute__((may_alias)) u32_la;
+typedef uint32_t u32x2_la __attribute__((ext_vector_type(2), may_alias));
+typedef uint32_t u32x4_la __attribute__((ext_vector_type(4), may_alias));
 
 // Streaming (non-temporal) 16-byte load / store: each weight is touched once.
 __device__ __forceinline__ float4 ldnt(const float4* p) {
@@ -267,24 +275,24 @@ __device__ __forceinline__ void quant_subgroup_body(
     float r[4];
     rounded_quotients<BITS, 4>(v[j], s, r);
     if constexpr (BITS == 4)
-      reinterpret_cast<uint16_t*>(stage_p[wv])[vi] = (uint16_t)pack4_int4(r);
+      reinterpret_cast<u16_la*>(stage_p[wv])[vi] = (uint16_t)pack4_int4(r);
     else
-      reinterpret_cast<uint32_t*>(stage_p[wv])[vi] = pack4_int8(r);
+      reinterpret_cast<u32_la*>(stage_p[wv])[vi] = pack4_int8(r);
   }
   // lane L writes vectors [QV*L, QV*L + QV) of the wave: QV * PB contiguous bytes
   const uint64_t v0 = base + (uint64_t)QV * lane;
   if (v0 + QV <= nvec) {
     if constexpr (QV * PB == 4) {
-      __builtin_nontemporal_store(reinterpret_cast<const uint32_t*>(stage_p[wv])[lane],
+      __builtin_nontemporal_store((uint32_t)reinterpret_cast<const u32_la*>(stage_p[wv])[lane],
                                   reinterpret_cast<uint32_t*>(payload + v0 * PB));
     } else if constexpr (QV * PB == 8) {
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      __builtin_nontemporal_store(reinterpret_cast<const u32x2*>(stage_p[wv])[lane],
+      __builtin_nontemporal_store((u32x2)reinterpret_cast<const u32x2_la*>(stage_p[wv])[lane],
                                   reinterpret_cast<u32x2*>(payload + v0 * PB));
     } else {
       static_assert(QV * PB == 16, "QV * PB must be 4, 8 or 16");
       typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-      __builtin_nontemporal_store(reinterpret_cast<const u32x4*>(stage_p[wv])[lane],
+      __builtin_nontemporal_store((u32x4)reinterpret_cast<const u32x4_la*>(stage_p[wv])[lane],
                                   reinterpret_cast<u32x4*>(payload + v0 * PB));
     }
   } else {
@@ -476,12 +484,12 @@ __device__ __forceinline__ void unpack_vec_body(
   if (v0 + QV <= nvec) {
     if constexpr (QV * PB == 8) {
       typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-      reinterpret_cast<u32x2*>(stage[wv])[lane] =
+      reinterpret_cast<u32x2_la*>(stage[wv])[lane] =
           __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(payload + v0 * PB));
     } else {
       static_assert(QV * PB == 16, "QV * PB must be 8 or 16");
       typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-      reinterpret_cast<u32x4*>(stage[wv])[lane] =
+      reinterpret_cast<u32x4_la*>(stage[wv])[lane] =
           __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(payload + v0 * PB));
     }
   } else {
@@ -497,11 +505,11 @@ __device__ __forceinline__ void unpack_vec_body(
     const float s = scales[vshift >= 0 ? (idx >> vshift) : idx / vpg];
     float v[4];
     if constexpr (BITS == 4) {
-      const uint32_t p = reinterpret_cast<const uint16_t*>(stage[wv])[vi];
+      const uint32_t p = reinterpret_cast<const u16_la*>(stage[wv])[vi];
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = (float)((int)((p >> (4 * i)) & 15u) - 8) * s;
     } else {
-      const uint32_t p = reinterpret_cast<const uint32_t*>(stage[wv])[vi];
+      const uint32_t p = reinterpret_cast<const u32_la*>(stage[wv])[vi];
 #pragma unroll
       for (int i = 0; i < 4; ++i) v[i] = (float)(int)(int8_t)(p >> (8 * i)) * s;
     }
