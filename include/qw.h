@@ -33,7 +33,10 @@
  *   qw_gemm : prefill product, bf16 activations; the weights are dequantized
  *             to bf16 (round to nearest even of w_hat) and multiplied on the
  *             matrix cores with fp32 accumulation; m >= 1.
- *             Error <= 8e-3 * sum_j |x[m][j] * w_hat[i][j]|.
+ *             Error <= 8e-3 * sum_j |x[m][j] * w_hat[i][j]| for weights that
+ *             are zero or at least 2^-126 in magnitude; below that bf16
+ *             keeps fewer bits than the 8 this bound assumes, though the
+ *             matrix cores still multiply subnormal bf16 values exactly.
  *
  * Conventions shared by every entry point:
  *   - All buffers are DEVICE pointers owned by the caller.  The library never

@@ -380,6 +380,35 @@ def test_gemm_int4_scales_beyond_the_one_fma_decode(m):
     assert np.all(np.isfinite(y))
 
 
+# Dequantized weights below 2^-126 are subnormal in fp32 and in bf16, and the
+# matrix cores must take the bf16 ones as they are.  (bf16 keeps fewer bits
+# there, so bf16(w_hat) itself may be further from w_hat than 2^-9 of it: the
+# 8e-3 bar of the GEMM contract assumes normal weights.)  Weights of about
+# 2^-128 -- most w_hat subnormal -- against x of about 2^10, so every product
+# and sum is a normal fp32 number; the result is compared with the exact
+# products of x and bf16(w_hat) (oracle bf16 rounding, fp64 sums) at the bar
+# of the fp32 accumulation alone.  A flushed subnormal input would be off by
+# its whole term.  m = 300 runs the 256-row kernel, m = 9 the small-M one.
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("m", [300, 9])
+def test_gemm_subnormal_dequantized_weights(bits, m):
+    n, k = 260, 512
+    w = (inputs.weight(m + bits + 70, n, k, 1.0) * np.float32(2.0 ** -128)).astype(np.float32)
+    ref, rec = quant_both(w, bits, 128)
+    w_hat = oracle.unpack(ref)
+    assert np.mean((w_hat != 0) & (np.abs(w_hat) < 2.0 ** -126)) > 0.5
+    wb = oracle.bf16_bits_to_f32(oracle.bf16_round(w_hat)).astype(np.float64)
+    assert np.mean((wb != 0) & (np.abs(wb) < 2.0 ** -126)) > 0.5
+    xf = oracle.bf16_bits_to_f32(inputs.bf16_activations(m + 71, m, k)) * np.float32(2.0 ** 10)
+    xb = (xf.view(np.uint32) >> 16).astype(np.uint16)
+    y = host(qw.gemm(rec, dev(xb.view(np.int16))))
+    x64 = xf.astype(np.float64)
+    yr = x64 @ wb.T
+    B = np.abs(x64) @ np.abs(wb).T
+    err = np.abs(y.astype(np.float64) - yr)
+    assert np.all(err <= 1e-5 * B), f"max err/B = {np.max(err / np.maximum(B, 1e-300))}"
+
+
 def test_gemm_ignores_stale_output():
     # the split tiles accumulate into Y: stale contents (NaN) must not leak
     w = inputs.weight(21, 300, 512, 0.02)
