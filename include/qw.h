@@ -37,6 +37,8 @@
  *             are zero or at least 2^-126 in magnitude; below that bf16
  *             keeps fewer bits than the 8 this bound assumes, though the
  *             matrix cores still multiply subnormal bf16 values exactly.
+ *   Both bounds are relative ones and, as for any fp32 arithmetic, assume
+ *   that the products and partial sums do not underflow below 2^-126.
  *
  * Conventions shared by every entry point:
  *   - All buffers are DEVICE pointers owned by the caller.  The library never
