@@ -380,6 +380,36 @@ def test_gemm_int4_scales_beyond_the_one_fma_decode(m):
     assert np.all(np.isfinite(y))
 
 
+# The GEMM's weight operand, bit for bit: with X the identity (bf16 1.0 on the
+# diagonal) every output is one product, y[i][j] = bf16(w_hat[j][i]), exact in
+# fp32 (the other terms are zeros, and the split tiles add two halves into
+# zeroed memory).  This pins the decoders themselves, which the 8e-3 bar
+# cannot see one weight at a time: int4 through its one-FMA decode, the
+# two-step fallback (a group of weights near 2^121, scales past 2^118) and
+# int8; k = 256 rows of X run the 256-row kernel (k / 64 = 4 k-steps, split
+# tiles at the end), k = 32 the small-M kernel.
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("k", [256, 32])
+def test_gemm_weight_operand_is_bf16_of_w_hat(bits, k):
+    if k == 32:
+        k_rows, k = 32, 256   # 32 rows of the identity, the first 32 columns of w
+    else:
+        k_rows = k
+    n = 520
+    w = inputs.weight(k + bits + 90, n, k, 0.02)
+    w[7, 0:128] *= np.float32(2.0 ** 126)   # one group of weights near 2^121
+    group = 128
+    ref, rec = quant_both(w, bits, group)
+    if bits == 4:
+        assert ref["scales"].max() >= 2.0 ** 118
+    eye = np.zeros((k_rows, k), np.float32)
+    eye[np.arange(k_rows), np.arange(k_rows)] = 1.0
+    xb = (eye.view(np.uint32) >> 16).astype(np.uint16)
+    y = host(qw.gemm(rec, dev(xb.view(np.int16))))
+    want = oracle.bf16_bits_to_f32(oracle.bf16_round(oracle.unpack(ref)))[:, :k_rows].T
+    assert same_bits(y, np.ascontiguousarray(want))
+
+
 # Dequantized weights below 2^-126 are subnormal in fp32 and in bf16, and the
 # matrix cores must take the bf16 ones as they are.  (bf16 keeps fewer bits
 # there, so bf16(w_hat) itself may be further from w_hat than 2^-9 of it: the
