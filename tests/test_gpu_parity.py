@@ -197,6 +197,24 @@ def test_gemv_split_and_stream_kernels(bits, group, n, k):
         check_gemv(ref, rec, inputs.activations(m + n, m, k))
 
 
+# The GEMV's decode, bit for bit: with one-hot rows of x every output is one
+# code times its scale, which the kernels form exactly as fl32(q * S) (int4
+# codes carry a factor 16, a power of two, removed at the end), so y must equal
+# the unpacked weight.  8 rows of x pick 8 columns; 300 weight rows take the
+# split-K kernel, 32768 + 7 the row-streaming one.
+@pytest.mark.parametrize("bits,group", [(4, 32), (4, 128), (8, 64)])
+@pytest.mark.parametrize("n", [300, 32768 + 7])
+def test_gemv_decode_reads_back_w_hat(bits, group, n):
+    k = 512
+    w = inputs.weight(n + group + bits, n, k, 0.02)
+    ref, rec = quant_both(w, bits, group)
+    cols = np.array([0, 1, 31, 32, 100, 255, 256, 511])
+    x = np.zeros((8, k), np.float32)
+    x[np.arange(8), cols] = 1.0
+    y = host(qw.gemv(rec, dev(x)))
+    assert same_bits(y, np.ascontiguousarray(oracle.unpack(ref)[:, cols].T))
+
+
 def test_gemv_k_zero_and_empty():
     rec = dict(bits=4, group=32, shape=[5, 0],
                payload=torch.empty(0, dtype=torch.uint8, device="cuda"),
