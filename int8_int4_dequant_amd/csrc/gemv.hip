@@ -409,43 +409,100 @@ __global__ __launch_bounds__(256) void gemv8_split_kernel(const GemvBatch<NB> b)
     step_g = fastdiv(64u, a.cpg);
     step_r = 64u - step_g * cpg;
   }
-  for (int c = cbeg + lane; c < cend; c += 64) {
-    const uint32_t poff = (uint32_t)c * (4u * PW), soff = gc * 4u, xoff = (uint32_t)c * 32u;
-    uint32_t p[R][PW];
-    float s[R];
+  // The chunk loop below; at M = 1, when no lane of the wave has more than two
+  // chunks, both chunks' loads are issued before either is used (one trip to
+  // memory instead of two; the same sums in the same order).  The second load
+  // of a lane with one chunk is clamped to the row's last chunk and dropped.
+  if (M == 1 && cend - cbeg <= 128 && cend > cbeg) {
+    const int c0 = cbeg + lane, c1 = c0 + 64;
+    const int l0 = c0 < nch ? c0 : nch - 1, l1 = c1 < nch ? c1 : nch - 1;
+    const uint32_t glast = a.per_row ? (uint32_t)(a.gpr - 1) : 0u;
+    uint32_t p0[R][PW], p1[R][PW];
+    float s0[R], s1[R];
+    const uint32_t g0 = gc < glast ? gc : glast;
+    uint32_t g1 = gc;
+    if (cpg) {
+      g1 += step_g;
+      if (rem + step_r >= cpg) ++g1;
+    }
+    g1 = g1 < glast ? g1 : glast;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      load_chunk<PW>(prsrc[r], poff, p[r]);
-      s[r] = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(srow[r]) + soff);
+      load_chunk<PW>(prsrc[r], (uint32_t)l0 * (4u * PW), p0[r]);
+      load_chunk<PW>(prsrc[r], (uint32_t)l1 * (4u * PW), p1[r]);
+      s0[r] = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(srow[r]) + g0 * 4u);
+      s1[r] = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(srow[r]) + g1 * 4u);
     }
-    float xv[M][8];
+    float xv0[M][8], xv1[M][8];
 #pragma unroll
     for (int m = 0; m < M; ++m) {
-      const float4* xp = reinterpret_cast<const float4*>(
-          reinterpret_cast<const uint8_t*>(a.x + (int64_t)m * a.k) + xoff);
-      const float4 x0 = xp[0], x1 = xp[1];
-      xv[m][0] = x0.x; xv[m][1] = x0.y; xv[m][2] = x0.z; xv[m][3] = x0.w;
-      xv[m][4] = x1.x; xv[m][5] = x1.y; xv[m][6] = x1.z; xv[m][7] = x1.w;
+      const float4* xp0 = reinterpret_cast<const float4*>(a.x + (int64_t)m * a.k + 8 * (int64_t)l0);
+      const float4* xp1 = reinterpret_cast<const float4*>(a.x + (int64_t)m * a.k + 8 * (int64_t)l1);
+      const float4 x00 = xp0[0], x01 = xp0[1], x10 = xp1[0], x11 = xp1[1];
+      xv0[m][0] = x00.x; xv0[m][1] = x00.y; xv0[m][2] = x00.z; xv0[m][3] = x00.w;
+      xv0[m][4] = x01.x; xv0[m][5] = x01.y; xv0[m][6] = x01.z; xv0[m][7] = x01.w;
+      xv1[m][0] = x10.x; xv1[m][1] = x10.y; xv1[m][2] = x10.z; xv1[m][3] = x10.w;
+      xv1[m][4] = x11.x; xv1[m][5] = x11.y; xv1[m][6] = x11.z; xv1[m][7] = x11.w;
     }
+    auto use = [&](const uint32_t (&p)[R][PW], const float (&sc)[R], const float (&xv)[M][8])
+        __attribute__((always_inline)) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      float q8[8];
-      if constexpr (BITS == 4) {
-        decode8_int4_x16(p[r][0], q8);
-      } else {
-        float q0[4], q1[4];
-        decode4_int8(p[r][0], q0);
-        decode4_int8(p[r][PW - 1], q1);
+      for (int r = 0; r < R; ++r) {
+        float q8[8];
+        if constexpr (BITS == 4) {
+          decode8_int4_x16(p[r][0], q8);
+        } else {
+          float q0[4], q1[4];
+          decode4_int8(p[r][0], q0);
+          decode4_int8(p[r][PW - 1], q1);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { q8[e] = q0[e]; q8[4 + e] = q1[e]; }
+          for (int e = 0; e < 4; ++e) { q8[e] = q0[e]; q8[4 + e] = q1[e]; }
+        }
+#pragma unroll
+        for (int m = 0; m < M; ++m) chunk_dot<M>(xv[m], q8, sc[r], acc[r * M + m]);
       }
-#pragma unroll
-      for (int m = 0; m < M; ++m) chunk_dot<M>(xv[m], q8, s[r], acc[r * M + m]);
-    }
-    if (cpg) {
-      gc += step_g;
-      rem += step_r;
-      if (rem >= cpg) { rem -= cpg; ++gc; }
+    };
+    if (c0 < cend) use(p0, s0, xv0);
+    if (c1 < cend) use(p1, s1, xv1);
+  } else {
+    for (int c = cbeg + lane; c < cend; c += 64) {
+      const uint32_t poff = (uint32_t)c * (4u * PW), soff = gc * 4u, xoff = (uint32_t)c * 32u;
+      uint32_t p[R][PW];
+      float s[R];
+  #pragma unroll
+      for (int r = 0; r < R; ++r) {
+        load_chunk<PW>(prsrc[r], poff, p[r]);
+        s[r] = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(srow[r]) + soff);
+      }
+      float xv[M][8];
+  #pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const float4* xp = reinterpret_cast<const float4*>(
+            reinterpret_cast<const uint8_t*>(a.x + (int64_t)m * a.k) + xoff);
+        const float4 x0 = xp[0], x1 = xp[1];
+        xv[m][0] = x0.x; xv[m][1] = x0.y; xv[m][2] = x0.z; xv[m][3] = x0.w;
+        xv[m][4] = x1.x; xv[m][5] = x1.y; xv[m][6] = x1.z; xv[m][7] = x1.w;
+      }
+  #pragma unroll
+      for (int r = 0; r < R; ++r) {
+        float q8[8];
+        if constexpr (BITS == 4) {
+          decode8_int4_x16(p[r][0], q8);
+        } else {
+          float q0[4], q1[4];
+          decode4_int8(p[r][0], q0);
+          decode4_int8(p[r][PW - 1], q1);
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) { q8[e] = q0[e]; q8[4 + e] = q1[e]; }
+        }
+  #pragma unroll
+        for (int m = 0; m < M; ++m) chunk_dot<M>(xv[m], q8, s[r], acc[r * M + m]);
+      }
+      if (cpg) {
+        gc += step_g;
+        rem += step_r;
+        if (rem >= cpg) { rem -= cpg; ++gc; }
+      }
     }
   }
 
