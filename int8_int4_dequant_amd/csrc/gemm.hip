@@ -506,13 +506,33 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
   const int ks0 = min(nk, wave * q);
   const int ks1 = min(nk, ks0 + q);
 
-  // weights: lane's row for column block nb, k range [32g, 32g+32) of a step
-  const uint8_t* prow[NBW];
+  // Weights.  A super-step is the k-steps whose codes fill 128 bytes of a row
+  // (4 int4 k-steps, 2 int8 ones).  The wave loads a super-step's weights
+  // row-contiguously -- lane L takes the 16 bytes at 16*(L%8) of rows L/8,
+  // L/8 + 8, L/8 + 16, L/8 + 24 of each 32-row column block, 8 whole rows
+  // per load instruction -- one super-step ahead, stages them in its own LDS
+  // region and reads back its MFMA fragments there (lane l: row l%32, k range
+  // [32g, 32g+32) of each k-step).  Loading the fragments straight from
+  // memory touched 32 rows per instruction.  A piece past the end of its row
+  // (a short row, or a super-step past the last k-step) is clamped onto the
+  // row's last 16 bytes; such pieces are never read back.
+  constexpr int SS = 128 / (BK * BITS / 8);       // k-steps per super-step
+  constexpr int SP = 128 + 16;                    // LDS row pitch (bank spread)
+  constexpr int FB = 16 * (BITS / 4);             // fragment bytes per lane and k-step
+  __shared__ __attribute__((aligned(16))) uint8_t wst[4][NBW][32 * SP];
+  const int prow_bytes = a.row_stride_b;
+  const uint8_t* lrow[NBW][4];                    // rows this lane loads
+#pragma unroll
+  for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int nn = min(n0 + 32 * nb + (lane >> 3) + 8 * j, a.n - 1);
+      lrow[nb][j] = a.payload + (int64_t)nn * prow_bytes;
+    }
   const float* srow[NBW];
 #pragma unroll
   for (int nb = 0; nb < NBW; ++nb) {
     const int nn = min(n0 + 32 * nb + l32, a.n - 1);
-    prow[nb] = a.payload + (int64_t)nn * a.row_stride_b + 16 * g * (BITS / 4);
     srow[nb] = a.scales + (a.per_row_groups ? (int64_t)nn * a.groups_per_row
                                             : ((int64_t)nn * a.k) / a.group);
   }
@@ -542,7 +562,9 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
       if (kin >= a.scale_period) kin -= a.scale_period;
     }
   };
-  auto load_w = [&](BRegs<BITS> (&br)[NBW], int k0) __attribute__((always_inline)) {
+  // the scales of k-step ks (loaded only when it starts a group)
+  auto load_s = [&](float (&sv)[NBW], int ks) __attribute__((always_inline)) {
+    int k0 = ks * BK;
     k0 = k0 < klast ? k0 : klast;
     const uint32_t kk = (uint32_t)(k0 + 32 * g);
     const uint32_t t = __umulhi(kk, a.gdiv_mul);
@@ -551,12 +573,32 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
     first_load = false;
     advance(kin_load);
 #pragma unroll
-    for (int nb = 0; nb < NBW; ++nb) {
-      const uint8_t* src = prow[nb] + (int64_t)k0 * BITS / 8;
-      br[nb].p[0] = *reinterpret_cast<const u32x4*>(src);
-      if constexpr (BITS == 8) br[nb].p[1] = *reinterpret_cast<const u32x4*>(src + 16);
-      if (need_s) br[nb].s = srow[nb][gi];
-    }
+    for (int nb = 0; nb < NBW; ++nb)
+      if (need_s) sv[nb] = srow[nb][gi];
+  };
+  // a super-step's weights, row-contiguous (16 bytes per lane and row piece)
+  auto load_super = [&](u32x4 (&raw)[NBW][4], int kb) __attribute__((always_inline)) {
+    const int off0 = kb * (BK * BITS / 8) + 16 * (lane & 7);
+    const int off = off0 < prow_bytes - 16 ? off0 : prow_bytes - 16;
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        raw[nb][j] = *reinterpret_cast<const u32x4*>(lrow[nb][j] + off);
+  };
+  auto store_super = [&](const u32x4 (&raw)[NBW][4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<u32x4*>(&wst[wave][nb][((lane >> 3) + 8 * j) * SP + 16 * (lane & 7)]) =
+            raw[nb][j];
+  };
+  // the lane's fragment of k-step s of the staged super-step
+  auto read_frag = [&](BRegs<BITS>& br, int nb, int s) __attribute__((always_inline)) {
+    const uint8_t* src = &wst[wave][nb][l32 * SP + s * (BK * BITS / 8) + FB * g];
+    br.p[0] = *reinterpret_cast<const u32x4*>(src);
+    if constexpr (BITS == 8) br.p[1] = *reinterpret_cast<const u32x4*>(src + 16);
   };
   auto load_a = [&](u32x4 (&af)[MB][4], int k0) __attribute__((always_inline)) {
     k0 = k0 < klast ? k0 : klast;
@@ -590,42 +632,64 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  // k-step ks: weights loaded two steps ahead, A fragments one step ahead
-  BRegs<BITS> brE[NBW], brO[NBW];
+  // super-step weights one super-step ahead, A fragments one k-step ahead
+  u32x4 raw[NBW][4];
+  float scur[SS][NBW], snxt[SS][NBW];
+#pragma unroll
+  for (int t = 0; t < SS; ++t)
+#pragma unroll
+    for (int nb = 0; nb < NBW; ++nb) scur[t][nb] = snxt[t][nb] = 0.0f;
   u32x4 afE[MB][4], afO[MB][4];
-  load_w(brE, ks0 * BK);
-  load_w(brO, (ks0 + 1) * BK);
+  load_super(raw, ks0);
+#pragma unroll
+  for (int t = 0; t < SS; ++t) load_s(scur[t], ks0 + t);
   load_a(afE, ks0 * BK);
-  auto kstep = [&](int ks, BRegs<BITS> (&br)[NBW], const u32x4 (&af)[MB][4],
+  // k-step ks (s-th of its super-step): its fragment br, A fragments af
+  auto kstep = [&](int ks, int s, const BRegs<BITS> (&br)[NBW], const u32x4 (&af)[MB][4],
                    u32x4 (&af_nxt)[MB][4]) __attribute__((always_inline)) {
-    // this step's scales: loaded with its codes when it starts a group
     const bool new_s = a.scale_period == 0 || kin_use == 0 || first_use;
     first_use = false;
     advance(kin_use);
     u32x4 bq[NBW][4];
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
-      if (new_s) s_cur[nb] = br[nb].s;
+      if (new_s) s_cur[nb] = scur[s][nb];
       dequant(br[nb], s_cur[nb], bq[nb]);
     }
-    load_w(br, (ks + 2) * BK);
     load_a(af_nxt, (ks + 1) * BK);
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+    for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8, af[mb][s]), __builtin_bit_cast(bf16x8, bq[nb][s]),
+              __builtin_bit_cast(bf16x8, af[mb][q4]), __builtin_bit_cast(bf16x8, bq[nb][q4]),
               acc[mb][nb], 0, 0, 0);
   };
-  int ks = ks0;
-  for (; ks + 1 < ks1; ks += 2) {
-    kstep(ks, brE, afE, afO);
-    kstep(ks + 1, brO, afO, afE);
+  for (int kb = ks0; kb < ks1; kb += SS) {
+    // stage this super-step (the wave's own LDS region: its LDS accesses
+    // complete in order, so the reads below see these writes and the next
+    // super-step's writes come after these reads), then load the next one
+    store_super(raw);
+    BRegs<BITS> br[SS][NBW];
+#pragma unroll
+    for (int t = 0; t < SS; ++t)
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) read_frag(br[t][nb], nb, t);
+    load_super(raw, kb + SS);
+#pragma unroll
+    for (int t = 0; t < SS; ++t) load_s(snxt[t], kb + SS + t);
+#pragma unroll
+    for (int t = 0; t < SS; t += 2) {
+      if (kb + t < ks1) kstep(kb + t, t, br[t], afE, afO);
+      if (kb + t + 1 < ks1) kstep(kb + t + 1, t + 1, br[t + 1], afO, afE);
+    }
+#pragma unroll
+    for (int t = 0; t < SS; ++t)
+#pragma unroll
+      for (int nb = 0; nb < NBW; ++nb) scur[t][nb] = snxt[t][nb];
   }
-  if (ks < ks1) kstep(ks, brE, afE, afO);
 
   // ---- partial tiles of waves 1..3 into LDS (register layout), then every
   // thread adds the four partials of its outputs in wave order and stores
