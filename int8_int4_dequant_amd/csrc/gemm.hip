@@ -43,9 +43,16 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int BM = 256, BN = 256, BK = 64;
-// Rows of X up to which the small-M kernel runs (measured: it beats the
-// 256-row tiles up to M = 32 on the 7B and 70B MLP shapes, loses from 64).
-constexpr int kSmallMaxM = 32;
+// Rows of X up to which the small-M kernel runs: up to kSmallMaxM always, up
+// to kSmallMaxMNarrow when the weight has at most kNarrowN rows (output
+// columns), where the 256 x 256 tiles leave most compute units idle.
+// Measured (us, 256-row tiles / small-M kernel, int4 g128): 28672 x 8192 at
+// M = 64 121 / 93, 80 124 / 125, 96 126 / 135; 16384 x 8192 at M = 96
+// 102 / 73, 128 104 / 94; 11008 x 4096 at M = 128 61 / 41; 4096 x 11008 at
+// M = 128 120 / 38.
+constexpr int kSmallMaxM = 64;
+constexpr int kSmallMaxMNarrow = 128;
+constexpr int64_t kNarrowN = 16384;
 // LDS row stride of the X tile: 128 bytes of data + 16 bytes of padding, so
 // that 16 consecutive rows (one 16-lane phase of a ds_read_b128) start 36
 // dwords apart and cover 16 distinct 4-bank groups of the 64 banks.
@@ -834,7 +841,8 @@ hipError_t launch_gemm(const Mat& mt, const uint8_t* payload, const float* scale
     // few rows: the small-M kernel, tile 32 x 32*NBW, K split over the block's
     // waves -- unless its grid (one block per tile) would pass 2^24 blocks; the
     // 256-row tiles then take it
-    if (m <= kSmallMaxM && ((m + 31) / 32) * ((mt.n + 31) / 32) < (1ll << 24)) {
+    const bool few_rows = m <= kSmallMaxM || (m <= kSmallMaxMNarrow && mt.n <= kNarrowN);
+    if (few_rows && ((m + 31) / 32) * ((mt.n + 31) / 32) < (1ll << 24)) {
       const int cus = compute_units();
       const int64_t tms = (m + 31) / 32;
       // two column blocks per wave (half the A-fragment reads per weight) when that

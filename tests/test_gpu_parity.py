@@ -346,14 +346,20 @@ def test_gemm_split_tail(bits, group, m, n, k):
     check_gemm(ref, rec, inputs.bf16_activations(m + 7, m, k))
 
 
-# Up to 32 rows of X the small-M kernel runs: a 32-row tile of 32 or 64
-# columns per block, K split over the block's four waves (some idle when
-# k / 64 < 4), partial tiles added in LDS.  Ragged columns, per-tensor
-# groups, int8, and a width that selects 64-column tiles (n >= 16384).
+# Up to 64 rows of X (128 when the weight has at most 16384 rows) the small-M
+# kernel runs: 32-row tiles of 32 or 64 columns per block, K split over the
+# block's four waves (some idle when k / 64 < 4), partial tiles added in LDS,
+# the weights of 4 (int4) or 2 (int8) k-steps staged through LDS at a time
+# (rows of 64 to 192 codes are shorter than that: their last pieces are
+# clamped).  Ragged columns, per-tensor groups, int8, a width that selects
+# 64-column tiles (n >= 16384), several row tiles (m = 33, 64, 100, 128 with
+# n <= 16384); m = 65 and 100 with n = 16448 take the 256-row kernel.
 @pytest.mark.parametrize("bits,group,m,n,k", [
     (4, 128, 1, 300, 512), (4, 32, 2, 77, 64), (8, 64, 17, 130, 192), (4, 32, 31, 96, 128),
     (8, 128, 32, 257, 1024), (4, 96 * 2, 5, 40, 96 * 2), (4, 256, 3, 16448, 256),
-    (4, 1024 * 3, 7, 3, 1024),
+    (4, 1024 * 3, 7, 3, 1024), (4, 128, 33, 300, 640), (8, 64, 64, 200, 320),
+    (4, 64, 100, 520, 192), (8, 128, 128, 96, 256), (4, 128, 65, 16448, 256),
+    (4, 32, 100, 16448, 128),
 ])
 def test_gemm_small_m(bits, group, m, n, k):
     w = inputs.weight(m + n + k + 5, n, k, 0.02)
