@@ -279,9 +279,12 @@ int qw_gemm(int bits, int64_t group, int64_t n, int64_t k,
  *   qw_gemm on it: the weights are dequantized in registers, not kept as a
  *   second copy.  Error <= 8e-3 * sum_j |x[m][j] * w_hat[i][j]| (rounding
  *   x adds at most 2^-9 of it to the GEMM's own bound).
- * The bound is the fastest side of the measured crossover on MI355X
- * (4096- to 28672-row int4 matrices: the GEMV wins up to 4 rows, the GEMM
- * from 8).  `work`: a device buffer of at least qw_matmul_work_bytes(m, k)
+ * The bound sits at the measured crossover on MI355X (int4 g128, 4096- to
+ * 28672-row matrices: the GEMV is faster up to 3 rows on each, up to 6 on
+ * the 4096-row one, the GEMM from 8 on each; at 4 rows the two are within
+ * 10% on the wider matrices and the GEMV 22% faster on the 4096-row one, so
+ * 4 rows stay on the more precise product).
+ * `work`: a device buffer of at least qw_matmul_work_bytes(m, k)
  * bytes (may be NULL when that is 0); after the call it holds the bf16 bit
  * patterns of x, row-major.  QW_EWORK when it is missing or too small;
  * other validation as in qw_gemv / qw_gemm.
