@@ -844,19 +844,39 @@ hipError_t launch_gemm(const Mat& mt, const uint8_t* payload, const float* scale
     const bool few_rows = m <= kSmallMaxM || (m <= kSmallMaxMNarrow && mt.n <= kNarrowN);
     if (few_rows && ((m + 31) / 32) * ((mt.n + 31) / 32) < (1ll << 24)) {
       const int cus = compute_units();
-      const int64_t tms = (m + 31) / 32;
-      // two column blocks per wave (half the A-fragment reads per weight) when that
-      // still gives every compute unit a block
-      const int nbw = tms * ((mt.n + 63) / 64) >= cus ? 2 : 1;
-      const int64_t tns = (mt.n + 32 * nbw - 1) / (32 * nbw);
+      // Two column blocks per wave (half the A-fragment reads per weight) when that
+      // still gives every compute unit a block.  Above 32 rows of X, 64-row tiles
+      // (the weights read once per 64 rows) when their grid still gives every
+      // compute unit 1.5 blocks: measured (us, 32- / 64-row tiles) 28672 x 8192
+      // at M = 48 92 / 73, 64 93 / 84; 16384 x 8192 at M = 128 94 / 86; with
+      // fewer blocks they lose (11008 x 4096 at M = 64 28 / 39, 4096 x 11008
+      // 30 / 47).
+      auto shape = [&](int mbv, int64_t& tmv, int& nbv, int64_t& tnv) {
+        tmv = (m + 32 * mbv - 1) / (32 * mbv);
+        nbv = tmv * ((mt.n + 63) / 64) >= cus ? 2 : 1;
+        tnv = (mt.n + 32 * nbv - 1) / (32 * nbv);
+      };
+      int64_t tms, tns;
+      int nbw;
+      shape(2, tms, nbw, tns);
+      const int mbk = m > 32 && 2 * tms * tns >= 3 * (int64_t)cus ? 2 : 1;
+      if (mbk == 1) shape(1, tms, nbw, tns);
       a.tiles_m = (int)tms;
       a.tiles_n = (int)tns;
       const unsigned grid = (unsigned)(tms * tns);
-#define QW_SMALL(B, NBv) gemm_small_kernel<B, 1, NBv><<<grid, 256, 0, st>>>(a)
+#define QW_SMALL(B, MBv, NBv) gemm_small_kernel<B, MBv, NBv><<<grid, 256, 0, st>>>(a)
       if (mt.bits == 4) {
-        if (nbw == 1) QW_SMALL(4, 1); else QW_SMALL(4, 2);
+        if (mbk == 1) {
+          if (nbw == 1) QW_SMALL(4, 1, 1); else QW_SMALL(4, 1, 2);
+        } else {
+          if (nbw == 1) QW_SMALL(4, 2, 1); else QW_SMALL(4, 2, 2);
+        }
       } else {
-        if (nbw == 1) QW_SMALL(8, 1); else QW_SMALL(8, 2);
+        if (mbk == 1) {
+          if (nbw == 1) QW_SMALL(8, 1, 1); else QW_SMALL(8, 1, 2);
+        } else {
+          if (nbw == 1) QW_SMALL(8, 2, 1); else QW_SMALL(8, 2, 2);
+        }
       }
 #undef QW_SMALL
       return hipGetLastError();

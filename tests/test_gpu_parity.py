@@ -353,13 +353,14 @@ def test_gemm_split_tail(bits, group, m, n, k):
 # (rows of 64 to 192 codes are shorter than that: their last pieces are
 # clamped).  Ragged columns, per-tensor groups, int8, a width that selects
 # 64-column tiles (n >= 16384), several row tiles (m = 33, 64, 100, 128 with
-# n <= 16384); m = 65 and 100 with n = 16448 take the 256-row kernel.
+# n <= 16384), 64-row tiles (m > 32 on a wide weight, n = 24640: enough blocks
+# for them); m = 65 and 100 with n = 16448 take the 256-row kernel.
 @pytest.mark.parametrize("bits,group,m,n,k", [
     (4, 128, 1, 300, 512), (4, 32, 2, 77, 64), (8, 64, 17, 130, 192), (4, 32, 31, 96, 128),
     (8, 128, 32, 257, 1024), (4, 96 * 2, 5, 40, 96 * 2), (4, 256, 3, 16448, 256),
     (4, 1024 * 3, 7, 3, 1024), (4, 128, 33, 300, 640), (8, 64, 64, 200, 320),
     (4, 64, 100, 520, 192), (8, 128, 128, 96, 256), (4, 128, 65, 16448, 256),
-    (4, 32, 100, 16448, 128),
+    (4, 32, 100, 16448, 128), (4, 128, 40, 24640, 256), (8, 64, 64, 24640 + 7, 128),
 ])
 def test_gemm_small_m(bits, group, m, n, k):
     w = inputs.weight(m + n + k + 5, n, k, 0.02)
@@ -411,15 +412,18 @@ def test_gemm_int4_scales_beyond_the_one_fma_decode(m):
 # cannot see one weight at a time: int4 through its one-FMA decode, the
 # two-step fallback (a group of weights near 2^121, scales past 2^118) and
 # int8; k = 256 rows of X run the 256-row kernel (k / 64 = 4 k-steps, split
-# tiles at the end), k = 32 the small-M kernel.
+# tiles at the end), 32 the small-M kernel, 64 (on a wide weight) its 64-row
+# tiles.
 @pytest.mark.parametrize("bits", [4, 8])
-@pytest.mark.parametrize("k", [256, 32])
+@pytest.mark.parametrize("k", [256, 32, 64])
 def test_gemm_weight_operand_is_bf16_of_w_hat(bits, k):
-    if k == 32:
-        k_rows, k = 32, 256   # 32 rows of the identity, the first 32 columns of w
+    n = 520
+    if k in (32, 64):
+        k_rows, k = k, 256   # k rows of the identity, the first k columns of w
+        if k_rows == 64:
+            n = 24640        # wide enough for the small-M kernel's 64-row tiles
     else:
         k_rows = k
-    n = 520
     w = inputs.weight(k + bits + 90, n, k, 0.02)
     w[7, 0:128] *= np.float32(2.0 ** 126)   # one group of weights near 2^121
     group = 128
