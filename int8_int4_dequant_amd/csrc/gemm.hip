@@ -614,30 +614,22 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
 #pragma unroll
       for (int s = 0; s < 4; ++s) af[mb][s] = *reinterpret_cast<const u32x4*>(xrow[mb] + k0 + 8 * s);
   };
-  auto dequant = [&](const BRegs<BITS>& br, float sc, u32x4 (&bq)[4])
-      __attribute__((always_inline)) {
-    if constexpr (BITS == 4) {
-      const u32x4 p = br.p[0];
-      bq[0] = dequant8_int4(p.x, sc);
-      bq[1] = dequant8_int4(p.y, sc);
-      bq[2] = dequant8_int4(p.z, sc);
-      bq[3] = dequant8_int4(p.w, sc);
-    } else {
-      const u32x4 p0 = br.p[0], p1 = br.p[1];
-      bq[0] = dequant8_int8(p0.x, p0.y, sc);
-      bq[1] = dequant8_int8(p0.z, p0.w, sc);
-      bq[2] = dequant8_int8(p1.x, p1.y, sc);
-      bq[3] = dequant8_int8(p1.z, p1.w, sc);
-    }
-  };
-
   f32x16 acc[MB][NBW];
+  // Largest |scale| this wave decoded with the one-FMA int4 decoder.
+  float smax = 0.0f;
+
+  // The wave's k-steps, with the one-FMA int4 decoder (fma = true) or the
+  // two-step decoders.
+  auto run = [&](auto fma) __attribute__((always_inline)) {
+  constexpr bool F = decltype(fma)::value;
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int j = 0; j < NBW; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  kin_load = kin_use = kin0;
+  first_load = first_use = true;
 
   // super-step weights one super-step ahead, A fragments one k-step ahead
   u32x4 raw[NBW][4];
@@ -661,7 +653,8 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
 #pragma unroll
     for (int nb = 0; nb < NBW; ++nb) {
       if (new_s) s_cur[nb] = scur[s][nb];
-      dequant(br[nb], s_cur[nb], bq[nb]);
+      if constexpr (F) smax = fmaxf(smax, fabsf(s_cur[nb]));
+      dequant32<BITS, F>(br[nb], s_cur[nb], bq[nb]);
     }
     load_a(af_nxt, (ks + 1) * BK);
 #pragma unroll
@@ -696,6 +689,15 @@ __global__ __launch_bounds__(256) void gemm_small_kernel(GemmArgs a) {
     for (int t = 0; t < SS; ++t)
 #pragma unroll
       for (int nb = 0; nb < NBW; ++nb) scur[t][nb] = snxt[t][nb];
+  }
+  };
+  if constexpr (BITS == 4) {
+    run(std::true_type{});
+    // a scale too large for the one-FMA decoder: the wave redoes its k-steps
+    // with the two-step decoder (its LDS stage is its own; no other wave waits)
+    if (__builtin_amdgcn_ballot_w64(smax >= kFmaScaleLimit)) run(std::false_type{});
+  } else {
+    run(std::false_type{});
   }
 
   // ---- partial tiles of waves 1..3 into LDS (register layout), then every
