@@ -177,6 +177,42 @@ void gemm64_kernel(G64 g) {
 #pragma unroll
     for (int bj = 0; bj < WB; ++bj) acc[bi][bj] = (d4){0.0, 0.0, 0.0, 0.0};
 
+  // D of v_mfma_f64_16x16x4f64: register r of lane l is row 4r + l/16,
+  // column l%16 of the 16x16 block.  With beta != 0 the old values of C
+  // are needed at the end; on the 64-wide tiles (registers to spare) they
+  // are read here, in flight with the first stage's operands, since the
+  // short reductions this shape serves (the Cholesky and code updates)
+  // would otherwise wait for them after their few MFMAs.  Clamped
+  // addresses as for the operands.
+  const bool use_beta = g.beta != 0.0;
+  double old[WB][WB][4];
+  auto load_old = [&](int bi) {
+#pragma unroll
+    for (int bj = 0; bj < WB; ++bj)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int64_t gi = i0 + wi * 16 * WB + bi * 16 + 4 * r + (lane >> 4);
+        const int64_t gj = j0 + wj * 16 * WB + bj * 16 + (lane & 15);
+        const bool ok = use_beta && gi < g.m && gj < g.n;
+        const double v = *(ok ? pc + gi * g.c_sm + gj * g.c_sn : pc);
+        old[bi][bj][r] = ok ? v : 0.0;
+      }
+  };
+  if constexpr (WB == 2) {
+    if (use_beta) {
+#pragma unroll
+      for (int bi = 0; bi < WB; ++bi) load_old(bi);
+    } else {
+      // beta == 0: C is never read (and may hold anything, even NaN)
+#pragma unroll
+      for (int bi = 0; bi < WB; ++bi)
+#pragma unroll
+        for (int bj = 0; bj < WB; ++bj)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) old[bi][bj][r] = 0.0;
+    }
+  }
+
   const int64_t nstage = (kred + kS - 1) / kS;
   if (nstage > 0) {
     load_stage(0);
@@ -204,24 +240,11 @@ void gemm64_kernel(G64 g) {
     __syncthreads();
   }
 
-  // D of v_mfma_f64_16x16x4f64: register r of lane l is row 4r + l/16,
-  // column l%16 of the 16x16 block.  With beta != 0 the old values of C are
-  // read first, one row of blocks at a time (clamped addresses as for the
-  // operands, so the reads are in flight together).
-  const bool use_beta = g.beta != 0.0;
+  // On the 128-wide tiles the old values of C are read here, one row of
+  // blocks at a time (the reads of a row in flight together).
 #pragma unroll
   for (int bi = 0; bi < WB; ++bi) {
-    double old[WB][4];
-#pragma unroll
-    for (int bj = 0; bj < WB; ++bj)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t gi = i0 + wi * 16 * WB + bi * 16 + 4 * r + (lane >> 4);
-        const int64_t gj = j0 + wj * 16 * WB + bj * 16 + (lane & 15);
-        const bool ok = use_beta && gi < g.m && gj < g.n;
-        const double v = *(ok ? pc + gi * g.c_sm + gj * g.c_sn : pc);
-        old[bj][r] = ok ? v : 0.0;
-      }
+    if constexpr (WB != 2) load_old(bi);
 #pragma unroll
     for (int bj = 0; bj < WB; ++bj)
 #pragma unroll
@@ -229,7 +252,7 @@ void gemm64_kernel(G64 g) {
         const int64_t gi = i0 + wi * 16 * WB + bi * 16 + 4 * r + (lane >> 4);
         const int64_t gj = j0 + wj * 16 * WB + bj * 16 + (lane & 15);
         if (gi < g.m && gj < g.n)
-          pc[gi * g.c_sm + gj * g.c_sn] = g.alpha * acc[bi][bj][r] + g.beta * old[bj][r];
+          pc[gi * g.c_sm + gj * g.c_sn] = g.alpha * acc[bi][bj][r] + g.beta * old[bi][bj][r];
       }
   }
 }
@@ -432,6 +455,49 @@ __device__ inline double readlane_f64(double v, int lane) {
   return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
 }
 
+// Orders a wave's own LDS accesses: a read after this sees the wave's
+// earlier writes (one wave's LDS operations run in issue order; this keeps
+// the compiler from moving them).
+__device__ inline void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// x[s] = fma(-xc, row[s], x[s]) for s0 <= s < kNb, in order of s, where
+// row is a row of an LDS array that every lane reads at the same address.
+// The values are read in chunks of 8 and each chunk's reads are issued
+// before the previous chunk's FMAs, so the LDS latency is paid about once
+// per row (left to itself the compiler waited for every pair of values
+// before using it, one LDS round trip per two FMAs).  s0 must be a
+// constant after unrolling.
+__device__ inline void lds_axpy(double (&x)[kNb], double xc, const double* row, int s0) {
+  constexpr int kC = 8;
+  double buf[2][kC];
+#pragma unroll
+  for (int i = 0; i < kC; ++i)
+    if (s0 + i < kNb) buf[0][i] = row[s0 + i];
+#pragma unroll
+  for (int ch = 0; ch < kNb / kC; ++ch) {
+    if (s0 + ch * kC < kNb) {
+      if (s0 + (ch + 1) * kC < kNb) {
+#pragma unroll
+        for (int i = 0; i < kC; ++i) {
+          const int s = s0 + (ch + 1) * kC + i;
+          if (s < kNb) buf[(ch + 1) & 1][i] = row[s];
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < kC; ++i) {
+        const int s = s0 + ch * kC + i;
+        if (s < kNb) x[s] = fma(-xc, buf[ch & 1][i], x[s]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
 // The small kernels below run 64 dependent steps.  An fp64 operation takes
 // about 36 cycles to produce its result and a division or square root is a
 // chain of about ten of them, so the steps use reciprocals computed off the
@@ -442,30 +508,75 @@ __device__ inline double readlane_f64(double v, int lane) {
 // dependent chain of 64 pivots.
 
 // The whole panel of block column p in one launch: the diagonal block and
-// every row below it, column by column.  A work-group holds the 64 rows of
-// the diagonal block (wave 0, recomputed by every work-group) and up to
-// kPanelOther rows below it, one row per thread in registers.  For each
-// column c: wave 0 takes the pivot from lane c (readlane), scales its
-// column by rsqrt(pivot) and publishes the column in LDS (double-buffered);
-// after one barrier every thread scales its own entry of column c and
-// updates its later columns with the published values.  Every work-group
-// writes its own rows of the panel; work-group 0 writes the factored
-// diagonal block to l11 (64 x 64, row-major, zero above the diagonal), not
-// back into a: the other work-groups read the unfactored block from a when
-// they start, and nothing orders that read after work-group 0 finishes.
-// info = 1 when a pivot is not positive.
+// every row below it.  A work-group holds the 64 rows of the diagonal block
+// (wave 0, recomputed by every work-group) and up to kPanelOther rows below
+// it, one row per thread in registers.
+//
+// Wave 0 factors the diagonal block alone, column by column: the pivot of
+// column c from lane c (readlane), the column scaled by rsqrt(pivot) and
+// written to LDS as row c of lt (lt[c][s] = L[s][c]), then the later
+// columns of every row updated.  The next pivot's column is updated first,
+// with L[c+1][c] read from lane c + 1 (readlane), so the chain from one
+// pivot to the next holds no LDS round trip; the other updates read lt.
+// No barrier sits on that chain: the rows below follow one stage of
+// kPanelStage columns behind, each thread scaling its entry of column c by
+// the staged rsqrt and updating its later columns with lt[c], and one
+// barrier per stage hands the columns over.  Every row sees the same
+// operations in the same order as in the plain column loop.  Every
+// work-group writes its own rows of the panel; work-group 0 writes the
+// factored diagonal block to l11 (64 x 64, row-major, zero above the
+// diagonal), not back into a: the other work-groups read the unfactored
+// block from a when they start, and nothing orders that read after
+// work-group 0 finishes.  info = 1 when a pivot is not positive.
 constexpr int kPanelThreads = 256;
 constexpr int kPanelOther = kPanelThreads - kNb;
+constexpr int kPanelStage = 16;
+static_assert(kNb % kPanelStage == 0, "whole stages");
+
+// Stage ST of the diagonal block (wave 0): columns [ST*S, (ST+1)*S).
+template <int ST>
+__device__ inline void panel_diag_stage(double (&x)[kNb], double (*lt)[kNb], double* rps, int t,
+                                        bool& bad) {
+#pragma unroll
+  for (int c = ST * kPanelStage; c < (ST + 1) * kPanelStage; ++c) {
+    const double d = readlane_f64(x[c], c);
+    bad = bad || !(d > 0.0);
+    const double rp = rsqrt(d);
+    x[c] = (t == c) ? d * rp : x[c] * rp;
+    lt[c][t] = x[c];
+    if (t == 0) rps[c] = rp;
+    if (c + 1 < kNb) {
+      x[c + 1] = fma(-x[c], readlane_f64(x[c], c + 1), x[c + 1]);
+      wave_lds_sync();
+      lds_axpy(x, x[c], lt[c], c + 2);
+    }
+  }
+}
+
+// Stage ST of a row below the diagonal block, once its columns are in lt.
+template <int ST>
+__device__ inline void panel_row_stage(double (&x)[kNb], const double (*lt)[kNb],
+                                       const double* rps) {
+  double r[kPanelStage];
+#pragma unroll
+  for (int i = 0; i < kPanelStage; ++i) r[i] = rps[ST * kPanelStage + i];
+#pragma unroll
+  for (int i = 0; i < kPanelStage; ++i) {
+    const int c = ST * kPanelStage + i;
+    x[c] *= r[i];
+    lds_axpy(x, x[c], lt[c], c + 1);
+  }
+}
 
 __global__ __launch_bounds__(kPanelThreads) void panel_factor_kernel(double* a, int64_t kp,
                                                                      int64_t p0,
                                                                      double* __restrict__ l11,
                                                                      int32_t* __restrict__ info) {
-  __shared__ __align__(16) double col[2][kNb];
-  __shared__ double rps[2];
+  static_assert(kNb / kPanelStage == 4, "the stages below are spelled out");
+  __shared__ __align__(16) double lt[kNb][kNb];
+  __shared__ double rps[kNb];
   const int t = threadIdx.x;
   const bool diag = t < kNb;
-  const int64_t rest = kp - p0 - kNb;
   const int64_t row = diag ? p0 + t : p0 + kNb + (int64_t)blockIdx.x * kPanelOther + (t - kNb);
   const bool active = diag || (row < kp);
   double x[kNb];
@@ -476,51 +587,55 @@ __global__ __launch_bounds__(kPanelThreads) void panel_factor_kernel(double* a, 
     x[c] = (active && (!diag || c <= t)) ? v : 0.0;
   }
   bool bad = false;
-#pragma unroll
-  for (int c = 0; c < kNb; ++c) {
-    const int b = c & 1;
-    if (diag) {
-      // wave 0: the pivot and column c of the diagonal block
-      const double d = readlane_f64(x[c], c);
-      bad = bad || !(d > 0.0);
-      const double rp = rsqrt(d);
-      x[c] = (t == c) ? d * rp : x[c] * rp;
-      col[b][t] = x[c];
-      if (t == 0) rps[b] = rp;
-    }
-    __syncthreads();
-    if (!diag) x[c] *= rps[b];
-#pragma unroll
-    for (int s2 = c + 1; s2 < kNb; ++s2) x[s2] = fma(-x[c], col[b][s2], x[s2]);
-  }
+  if (diag) panel_diag_stage<0>(x, lt, rps, t, bad);
+  __syncthreads();
+  if (diag) panel_diag_stage<1>(x, lt, rps, t, bad);
+  else panel_row_stage<0>(x, lt, rps);
+  __syncthreads();
+  if (diag) panel_diag_stage<2>(x, lt, rps, t, bad);
+  else panel_row_stage<1>(x, lt, rps);
+  __syncthreads();
+  if (diag) panel_diag_stage<3>(x, lt, rps, t, bad);
+  else panel_row_stage<2>(x, lt, rps);
+  __syncthreads();
+  if (!diag) panel_row_stage<3>(x, lt, rps);
   if (active && (!diag || blockIdx.x == 0)) {
     double* aw = diag ? l11 + t * kNb : a + row * kp + p0;
 #pragma unroll
     for (int c = 0; c < kNb; ++c) aw[c] = (!diag || c <= t) ? x[c] : 0.0;
   }
   if (diag && bad && t == 0 && blockIdx.x == 0 && info) *info = 1;
-  (void)rest;
 }
 
 // A lower triangular 64 x 64 block L (row-major, leading dimension 64)
-// staged for the row solves: lt[c][s] = L[s][c] (zero for s < c),
-// rd[c] = 1 / L[c][c].
+// staged for the row solves by a work-group of 64 threads: lt[c][s] =
+// L[s][c] (zero for s < c), rd[c] = 1 / L[c][c].  Thread s reads row s
+// whole, so its 64 loads are in flight together.
 __device__ inline void load_lt(double (*lt)[kNb], double* rd, const double* l) {
-  for (int e = threadIdx.x; e < kNb * kNb; e += blockDim.x) {
-    const int s = e / kNb, c = e % kNb;  // L[s][c], read along the row
-    lt[c][s] = (s >= c) ? l[s * kNb + c] : 0.0;
-  }
-  for (int c = threadIdx.x; c < kNb; c += blockDim.x) rd[c] = 1.0 / l[c * kNb + c];
+  const int s = threadIdx.x;
+  double v[kNb];
+#pragma unroll
+  for (int c = 0; c < kNb; ++c) v[c] = l[s * kNb + c];
+#pragma unroll
+  for (int c = 0; c < kNb; ++c) lt[c][s] = (s >= c) ? v[c] : 0.0;
+  rd[s] = 1.0 / l[s * kNb + s];
 }
 
 // x L^T = x0 for one row x: x_c *= 1/L[c][c], then x_s -= x_c L[s][c] for
 // s > c.
 __device__ inline void solve_lt(double (&x)[kNb], const double (*lt)[kNb], const double* rd) {
+  constexpr int kG = 16;  // reciprocals read together
 #pragma unroll
-  for (int c = 0; c < kNb; ++c) {
-    x[c] = x[c] * rd[c];
+  for (int g = 0; g < kNb; g += kG) {
+    double r[kG];
 #pragma unroll
-    for (int s = c + 1; s < kNb; ++s) x[s] = fma(-x[c], lt[c][s], x[s]);
+    for (int i = 0; i < kG; ++i) r[i] = rd[g + i];
+#pragma unroll
+    for (int i = 0; i < kG; ++i) {
+      const int c = g + i;
+      x[c] = x[c] * r[i];
+      lds_axpy(x, x[c], lt[c], c + 1);
+    }
   }
 }
 
@@ -596,9 +711,24 @@ __global__ __launch_bounds__(256) void gptq_block_kernel(
     uint8_t* __restrict__ payload, float* __restrict__ scales) {
   __shared__ double ub[64][64];
   const int t = threadIdx.x;
-  for (int e = t; e < 64 * 64; e += 256) {
-    const int s = e >> 6, j = e & 63;
-    ub[s][j] = (s < bsz && j < bsz) ? v[(k0 + s) * k + (k0 + j)] : 0.0;
+  {
+    // 16 values per thread, every load issued before the first store (an
+    // element outside the block reads v[0] and stores 0)
+    constexpr int kPer = 64 * 64 / 256;
+    double tv[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = t + 256 * i;
+      const int s = e >> 6, j = e & 63;
+      const bool ok = s < bsz && j < bsz;
+      tv[i] = v[ok ? (k0 + s) * k + (k0 + j) : 0];
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = t + 256 * i;
+      const int s = e >> 6, j = e & 63;
+      ub[s][j] = (s < bsz && j < bsz) ? tv[i] : 0.0;
+    }
   }
   __syncthreads();
   const int lane = t & 63;

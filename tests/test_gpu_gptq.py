@@ -48,9 +48,10 @@ def _say(*a):
 # ----------------------------------------------------------------- H
 
 
-# (1368, 2048): the tokens cut into 7 full chunks and a short eighth
+# (1368, 2048): the tokens cut into 7 full chunks and a short eighth;
+# (512, 8192): a calibration batch of the small model's 512-input maps
 @pytest.mark.parametrize("k,t", [(1, 7), (64, 64), (65, 3000), (130, 255), (200, 1000),
-                                 (512, 4096), (1368, 2048)])
+                                 (512, 4096), (512, 8192), (1368, 2048)])
 def test_hessian_parity(k, t):
     _say("gptq_hessian", k, t)
     x0 = inputs.calibration_activations([8, 1, k], 33, k)
@@ -63,6 +64,27 @@ def test_hessian_parity(k, t):
     bound = (t + 33 + 2) * 2.0 ** -52 * (xa.T @ xa)
     assert np.all(np.abs(got - want) <= bound)
     assert np.array_equal(got, got.T)
+
+
+@pytest.mark.parametrize("k,t", [(512, 8192), (1368, 2048)])
+def test_hessian_ignores_stale_work(k, t):
+    """The partial sums are written, never read before being written: a work
+    buffer full of NaN gives the same h, bit for bit, as a zeroed one (the
+    64-wide and the 128-wide tiles)."""
+    _say("gptq_hessian stale work", k, t)
+    L = qw.lib()
+    x = dev(inputs.calibration_activations([8, 4, k], t, k))
+    nb = L.qw_gptq_hessian_work_bytes(k, t)
+    out = []
+    for fill in (0x00, 0xFF):   # 0xFF.. is a NaN in every fp64 lane
+        work = torch.full((nb,), fill, dtype=torch.uint8, device="cuda")
+        h = torch.zeros((k, k), dtype=torch.float64, device="cuda")
+        rc = L.qw_gptq_hessian(k, t, x.data_ptr(), h.data_ptr(), work.data_ptr(), nb,
+                               torch.cuda.current_stream().cuda_stream)
+        assert rc == 0
+        out.append(host(h))
+    assert np.all(np.isfinite(out[0]))
+    assert np.array_equal(out[0], out[1])
 
 
 def test_hessian_is_deterministic():
