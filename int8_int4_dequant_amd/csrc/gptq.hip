@@ -756,15 +756,10 @@ __global__ __launch_bounds__(256) void gptq_block_kernel(
   }
   int code = 0;
   double ev = 0.0;
-  for (int s = 0; s < bsz; ++s) {
+  // Component s: its code from the current weight of lane s, its rounding
+  // error, and that error carried to the later lanes.
+  auto step = [&](int s) {
     const double us = ub[s][lane];
-    if (group <= bsz && ((k0 + s) % group) == 0) {
-      const float aw = (lane >= s && lane < s + group) ? fabsf((float)w) : 0.0f;
-      const float m = wave_max(aw);
-      sc = m / qmax;
-      if (sc == 0.0f) sc = 1.0f;
-      if (lane == 0) scales[row * ngroups + (k0 + s) / group] = sc;
-    }
     const double ws = readlane_f64(w, s);
     const float r = (float)ws / sc;
     const float c = fminf(fmaxf(rintf(r), -qmax), qmax);
@@ -775,6 +770,21 @@ __global__ __launch_bounds__(256) void gptq_block_kernel(
       ev = err;
     }
     if (lane > s) w = fma(-err, us, w);
+  };
+  if (group <= bsz) {
+    // Whole groups, starting at the multiples of group (k0 and bsz are
+    // multiples of group here): each group's scale from the current weights
+    // of its components, then its components, with no test in the loop.
+    for (int g0 = 0; g0 < bsz; g0 += (int)group) {
+      const float aw = (lane >= g0 && lane < g0 + group) ? fabsf((float)w) : 0.0f;
+      const float m = wave_max(aw);
+      sc = m / qmax;
+      if (sc == 0.0f) sc = 1.0f;
+      if (lane == 0) scales[row * ngroups + (k0 + g0) / group] = sc;
+      for (int s = g0; s < g0 + (int)group; ++s) step(s);
+    }
+  } else {
+    for (int s = 0; s < bsz; ++s) step(s);
   }
   if (lane < bsz) e_out[row * 64 + lane] = ev;
   if (BITS == 8) {
