@@ -216,6 +216,51 @@ def test_diagonal_h_gives_the_plain_codes(bits, group):
     assert torch.equal(rec["scales"], plain["scales"])
 
 
+def _tie_weights(bits, group, n, k, seed):
+    """Rows of quotients on half-integers: in every group one weight is
+    qmax * S (so the scale is S, a power of two) and the others are
+    (j + 1/2) * S.  Rows 0-3 are ties everywhere with S = 2^-8, rows 4-5 in
+    their last 64 components only, row 6 everywhere with S = 2^-135 (a
+    subnormal scale, outside the range the reciprocal shortcut takes), the
+    other rows are random."""
+    qmax = 7 if bits == 4 else 127
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
+
+    def ties(scale_exp, cols):
+        v = (rng.integers(-qmax, qmax, size=cols) + 0.5) * 2.0 ** scale_exp
+        v[::group] = qmax * 2.0 ** scale_exp
+        return v.astype(np.float32)
+
+    for r in range(4):
+        w[r] = ties(-8, k)
+    for r in (4, 5):
+        w[r, k - 64:] = ties(-8, 64)
+        w[r, :k - 64] = w[r, :k - 64] * 0.25  # below the tie row's scale
+    w[6] = ties(-135, k)
+    return w
+
+
+@pytest.mark.parametrize("bits,group,k", [(4, 64, 192), (4, 128, 384), (8, 96, 384),
+                                          (4, 16, 192), (8, 64, 192)])
+def test_ties_and_tiny_scales_take_the_division(bits, group, k):
+    """Quotients exactly on half-integers, and a subnormal scale, must give
+    the codes of the IEEE division (ties to even), however the kernel reaches
+    them.  With U = I nothing is carried, so the codes are the plain
+    quantizer's: equal to the oracle's plain codes and to qw_quantize_pack."""
+    n = 12
+    _say("gptq ties", bits, group, n, k)
+    w = _tie_weights(bits, group, n, k, 93)
+    u = np.eye(k)
+    rec = qw.gptq_quantize_pack(dev(w), dev(u), bits, group)
+    want = oracle.quantize_pack(w, bits, group)
+    assert np.array_equal(host(rec["payload"]), want["payload"])
+    assert np.array_equal(host(rec["scales"]).view(np.uint32), want["scales"].view(np.uint32))
+    plain = qw.quantize_pack(dev(w), bits, group)
+    assert torch.equal(rec["payload"], plain["payload"])
+    assert torch.equal(rec["scales"], plain["scales"])
+
+
 def test_unpack_and_gemv_take_gptq_records():
     n, k = 96, 256
     x = inputs.calibration_activations([8, 10], 1024, k)
