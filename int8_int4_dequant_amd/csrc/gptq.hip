@@ -377,28 +377,44 @@ __global__ __launch_bounds__(256) void hess_reduce_kernel(const double* __restri
   const int64_t bj = x - bi * (bi + 1) / 2;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;  // 32 x 8
   const int64_t kk2 = k * k;
-  for (int yy = ty; yy < 32; yy += 8) {
+  // Each thread sums 4 entries (rows ty, ty + 8, ty + 16, ty + 24 of the
+  // tile), adding the partial sums in chunk order; the loads of 8 chunks
+  // of all 4 entries are issued before their additions (a chunk past the
+  // last reads chunk 0 and is not added).
+  const double* pp[4];
+  bool ok[4];
+  double s[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int64_t i = bi * 32 + ty + 8 * r, j = bj * 32 + tx;
+    ok[r] = i < k && j < k && i >= j;
+    pp[r] = part + (ok[r] ? i * k + j : 0);
+    s[r] = 0.0;
+  }
+  for (int64_t p = 0; p < splits; p += 8) {
+    double v[4][8];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[r][q] = pp[r][(p + q < splits ? p + q : 0) * kk2];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (p + q < splits) s[r] += v[r][q];
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int yy = ty + 8 * r;
     const int64_t i = bi * 32 + yy, j = bj * 32 + tx;
-    const bool ok = i < k && j < k && i >= j;
-    const double* pp = part + (ok ? i * k + j : 0);
-    // partial sums added in chunk order; the loads of eight chunks are
-    // issued before their additions
-    double s = 0.0;
-    int64_t p = 0;
-    for (; p + 8 <= splits; p += 8) {
-      double v[8];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = pp[(p + q) * kk2];
-#pragma unroll
-      for (int q = 0; q < 8; ++q) s += v[q];
-    }
-    for (; p < splits; ++p) s += pp[p * kk2];
-    tile[yy][tx] = s;
-    if (ok) h[i * k + j] += s;
+    tile[yy][tx] = s[r];
+    if (ok[r]) h[i * k + j] += s[r];
   }
   __syncthreads();
   // mirrored half: h[j][i] += s(i, j) for i > j, read transposed from LDS
-  for (int yy = ty; yy < 32; yy += 8) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int yy = ty + 8 * r;
     const int64_t j = bj * 32 + yy, i = bi * 32 + tx;
     if (i < k && j < k && i > j) h[j * k + i] += tile[tx][yy];
   }
