@@ -37,6 +37,16 @@ def _run(cmd):
     return err
 
 
+# Flags of one source only.  gptq.hip: its fp64 MFMA GEMM keeps the
+# accumulators in VGPRs (the VGPR form of v_mfma_f64_16x16x4f64); left to
+# its heuristics the compiler put the 64-wide tiles' accumulators in AGPRs
+# and copied them to and from VGPRs around every reduction stage, so every
+# stage waited for the matrix pipeline to drain.
+SOURCE_FLAGS = {
+    "gptq.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def compile_objects(out_dir, extra=(), verbose=False):
     """Compiles every source into out_dir with FLAGS plus `extra`; returns
     the object paths."""
@@ -47,7 +57,8 @@ def compile_objects(out_dir, extra=(), verbose=False):
         for src in SOURCES:
             obj = os.path.join(out_dir, src.replace(".hip", ".o"))
             objs.append(obj)
-            cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [HIPCC, *FLAGS, *SOURCE_FLAGS.get(src, []), *extra, "-c",
+                   os.path.join(CSRC, src), "-o", obj]
             jobs.append(ex.submit(_run, cmd))
         for j in jobs:
             msg = j.result()
