@@ -28,8 +28,13 @@
  *
  *   y[m][i] = sum_j x[m][j] * w_hat[i][j]
  *
- *   qw_gemv : decode-time product, fp32 activations, fp32 arithmetic,
- *             1 <= m <= 8.  Error <= 1e-5 * sum_j |x[m][j] * w_hat[i][j]|.
+ *   qw_gemv : decode-time product, fp32 activations, 1 <= m <= 8; every
+ *             product exact or singly rounded, sums in fp32.  From 2 rows of
+ *             x on, the products run on the bf16 matrix cores: each x value
+ *             is cut into three bf16 pieces that add up to it exactly, and
+ *             each piece times a code (an integer, exact in bf16) is exact in
+ *             the fp32 accumulator.
+ *             Error <= 1e-5 * sum_j |x[m][j] * w_hat[i][j]|.
  *   qw_gemm : prefill product, bf16 activations; the weights are dequantized
  *             to bf16 (round to nearest even of w_hat) and multiplied on the
  *             matrix cores with fp32 accumulation; m >= 1.
@@ -38,7 +43,9 @@
  *             keeps fewer bits than the 8 this bound assumes, though the
  *             matrix cores still multiply subnormal bf16 values exactly.
  *   Both bounds are relative ones and, as for any fp32 arithmetic, assume
- *   that the products and partial sums do not underflow below 2^-126.
+ *   that the products and partial sums do not underflow below 2^-126 (for
+ *   the three-piece GEMV: x values of magnitude 2^-110 or more, whose
+ *   smallest piece is still a normal number).
  *
  * Conventions shared by every entry point:
  *   - All buffers are DEVICE pointers owned by the caller.  The library never
@@ -200,7 +207,11 @@ int qw_unpack_batched(int count, const qw_unpack_desc* descs, void* stream);
  *   x  fp32 [m][k]  (read),   y  fp32 [m][n]  (written),   0 <= m <= 8.
  * Any group dividing n*k is accepted; with k % 8 == 0 and either
  * k % group == 0 with group % 8 == 0, or group % k == 0, the streaming
- * kernel runs.
+ * kernels run.  At 2..8 rows of x, rows of whole 128-code steps
+ * (k % 128 == 0), groups of whole steps (group % 128 == 0) or of whole rows
+ * (group % k == 0), a 16-byte aligned payload and an 8-byte aligned x take
+ * the matrix-core kernel.  Outputs are deterministic: the same call gives
+ * the same bits.
  */
 int qw_gemv(int bits, int64_t group, int64_t n, int64_t k,
             const uint8_t* payload, const float* scales,
@@ -399,9 +410,11 @@ int qw_gptq_quantize_pack(int bits, int64_t group, int64_t n, int64_t k,
 /*
  * Diagnostic: which kernel family a call with these arguments would take
  * (1 = streaming/tiled fast kernel, 2 = block-per-group kernel, 3 = generic
- * kernel) or a negative status for invalid arguments.  `op`: 0 quantize_pack
- * (a = w, b = payload), 1 unpack (a = payload, b = w_out), 2 gemv (a =
- * payload, b = x), 3 gemm (a = payload, b = x_bf16).  Enqueues nothing.
+ * kernel, 4 = matrix-core GEMV) or a negative status for invalid arguments.
+ * `op`: 0 quantize_pack (a = w, b = payload), 1 unpack (a = payload, b =
+ * w_out), 2 gemv at one row of x (a = payload, b = x), 3 gemm (a = payload,
+ * b = x_bf16), 4 gemv at 2..8 rows of x (a = payload, b = x).  Enqueues
+ * nothing.
  */
 int qw_debug_path(int op, int bits, int64_t group, int64_t n, int64_t k,
                   const void* a, const void* b);

@@ -518,6 +518,258 @@ __global__ __launch_bounds__(256) void gemv8_split_kernel(const GemvBatch<NB> b)
   }
 }
 
+// ------------------------------------------- matrix-core GEMV (M = 2 .. 8)
+//
+// With several x rows the fp32 kernels above spend 8*M products and M scale
+// FMAs per 8 codes on top of the decode, and the wave reductions of R*M
+// partial sums; at M = 4 and 8 they are bound by VALU issue and latency, not
+// by HBM.  Here the dot products run on the bf16 matrix cores
+// (v_mfma_f32_16x16x32_bf16) without giving up fp32 accuracy:
+//   * the codes are small integers, exact in bf16 (int4 as 16*q, int8 as q);
+//   * every x value is cut into three bf16 pieces, x = p0 + p1 + p2 exactly:
+//     p0 is x with the low 16 bits of its encoding cleared, p1 the same of
+//     x - p0, and p2 = x - p0 - p1 keeps at most 8 significant bits; both
+//     subtractions are exact (the operands agree in sign and exponent range)
+//     as long as nothing underflows;
+//   * a product of a piece and a code is exact in the fp32 accumulator, so
+//     the only roundings are the accumulator's additions, as on the fp32
+//     path, and the 1e-5 * sum|x * w_hat| bound keeps a wide margin.
+// Layout: the A operand is the x pieces (16 rows: x row m, rows past M
+// repeat the last one and their outputs are dropped), the B operand the
+// weights (16 columns = 16 weight rows), so each lane's four outputs belong
+// to one weight row and need one scale per group.
+// Work split: a block takes R tiles of 16 weight rows over the whole row
+// length; its W waves split the row into super-steps of 128 codes (a lane
+// reads a row-contiguous 32-code slab per super-step: 16 B int4, 32 B int8,
+// four lanes cover a 128 B line of a row), and their partial sums meet in
+// LDS in wave order, so the result is deterministic.  Each super-step a wave
+// cuts the 128*M x values once, two per lane, into pieces stored in its own
+// LDS region, reads them back in the A layout, and uses them for its R
+// tiles.  A super-step lies inside one group (groups are multiples of 128
+// codes), and its sum is multiplied by the group's scale into an fp32
+// accumulator (one FMA per output).
+
+typedef __bf16 mx_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float mx_f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t mx_u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kMxRowBytes = 272;  // one x row of one piece in LDS: 128 bf16 + 16 B pad
+constexpr int kMxCodes = 128;     // codes per super-step
+constexpr int kMxAhead = 4;       // super-steps of payload in flight per wave
+
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 h = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+// 8 int4 codes (one dword, element order) -> 8 bf16 values 16*q (exact).
+__device__ __forceinline__ mx_u32x4 bf16x8_int4_x16(uint32_t w) {
+  float q[8];
+  decode8_int4_x16(w, q);
+  return mx_u32x4{bf16_pair(q[0], q[1]), bf16_pair(q[2], q[3]), bf16_pair(q[4], q[5]),
+                  bf16_pair(q[6], q[7])};
+}
+
+// 8 int8 codes (two dwords, element order) -> 8 bf16 values q (exact).
+__device__ __forceinline__ mx_u32x4 bf16x8_int8(uint32_t w0, uint32_t w1) {
+  float a[4], b[4];
+  decode4_int8(w0, a);
+  decode4_int8(w1, b);
+  return mx_u32x4{bf16_pair(a[0], a[1]), bf16_pair(a[2], a[3]), bf16_pair(b[0], b[1]),
+                  bf16_pair(b[2], b[3])};
+}
+
+// The three bf16 pieces of x values a (low half) and b (high half), packed.
+__device__ __forceinline__ void split3_pair(float a, float b, uint32_t& p0, uint32_t& p1,
+                                            uint32_t& p2) {
+  const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+  const float a1 = a - __uint_as_float(ua & 0xffff0000u);
+  const float b1 = b - __uint_as_float(ub & 0xffff0000u);
+  const uint32_t ua1 = __float_as_uint(a1), ub1 = __float_as_uint(b1);
+  const float a2 = a1 - __uint_as_float(ua1 & 0xffff0000u);
+  const float b2 = b1 - __uint_as_float(ub1 & 0xffff0000u);
+  // high halves of (a, b) -> one dword: a's bf16 low, b's high
+  p0 = __builtin_amdgcn_perm(ub, ua, 0x07060302u);
+  p1 = __builtin_amdgcn_perm(ub1, ua1, 0x07060302u);
+  p2 = __builtin_amdgcn_perm(__float_as_uint(b2), __float_as_uint(a2), 0x07060302u);
+}
+
+template <int BITS, int M, int R, int W, int P>
+__global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const GemvDesc a, int ss_per_group) {
+  static_assert(M >= 2 && M <= 8 && R >= 1 && P >= 1, "shape of the matrix-core GEMV");
+  constexpr int PB = BITS == 4 ? 4 : 8;           // payload dwords per lane per super-step
+  constexpr int NR = 3 * M;                       // A rows: (piece, x row), piece-major
+  constexpr int NS = (NR + 15) / 16;              // 16-row MFMA sets
+  // a wave's LDS region: the pieces of one super-step (NR rows of 128 bf16),
+  // and after the loop its partial sums (R tiles x NS sets x 16 x 16 fp32)
+  constexpr int XBYTES = NR * kMxRowBytes, PBYTES = R * NS * 1024;
+  constexpr int REGION = XBYTES > PBYTES ? XBYTES : PBYTES;
+  static_assert(R * M * 16 <= 64 * W, "one thread per output in the final sum");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[W][REGION];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15, kb = lane >> 4;      // B column (weight row of the tile), k block
+  const int tile0 = blockIdx.x * R;
+  const int ks = a.k / kMxCodes;                  // super-steps per row
+  const int qs = (ks + W - 1) / W;
+  const int ss0 = min(ks, wave * qs), ss1 = min(ks, ss0 + qs);
+
+  // One buffer resource per tile (wave-uniform, so it stays in scalar
+  // registers), bounded at the matrix's last row: a lane's rows past it
+  // read zeros, and their outputs are dropped.
+  __amdgpu_buffer_rsrc_t rs[R];
+  const float* srow[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int trow = (tile0 + r) * 16;
+    const int rows = max(0, min(16, a.n - trow));
+    // (readfirstlane: the clamp is computed in vector registers, and a
+    // resource there would cost a loop over the lanes' values at every load)
+    rs[r] = row_rsrc(a.payload + (int64_t)min(trow, a.n - 1) * a.row_stride_b,
+                     __builtin_amdgcn_readfirstlane(rows * a.row_stride_b));
+    const int row = min(trow + col, a.n - 1);
+    srow[r] = a.scales + (a.per_row ? (int64_t)row * a.gpr : ((int64_t)row * a.k) / a.group);
+  }
+  const int lane_off = col * a.row_stride_b + kb * (PB * 4);
+  uint8_t* const xw = lds[wave];
+  // this lane's A-operand rows, one per set (rows past NR repeat the last)
+  uint32_t aoff[NS];
+#pragma unroll
+  for (int t = 0; t < NS; ++t)
+    aoff[t] = (uint32_t)(min(16 * t + col, NR - 1) * kMxRowBytes + kb * 64);
+
+  mx_f32x4 acc[R][NS];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int t = 0; t < NS; ++t) acc[r][t] = mx_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  // The payload, scales and x of the next P super-steps are always in
+  // flight (a ring of P register slots, refilled as each is used).  Loads
+  // complete in issue order, so x goes out with its super-step's payload:
+  // fetched a step ahead instead, waiting for it would also wait for the
+  // payload issued before it.  The group of the next super-step to load is
+  // tracked without a division.
+  int lg = 0, lr = 0;  // group of the next super-step to load, and its place in it
+  if (a.per_row) {
+    lg = ss0 / ss_per_group;
+    lr = ss0 - lg * ss_per_group;
+  }
+  uint32_t pw[P][R][PB];
+  float sc[P][R];
+  f32x2 xv[P][M];
+  auto load_slot = [&](int ss, uint32_t (&p)[R][PB], float (&sv)[R], f32x2 (&xx)[M])
+      __attribute__((always_inline)) {
+    constexpr int kNT = 2;  // non-temporal: every weight is read once
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+      xx[m] = *reinterpret_cast<const f32x2*>(a.x + (int64_t)m * a.k + (int64_t)ss * kMxCodes +
+                                              2 * lane);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int off = lane_off + ss * (kMxCodes * BITS / 8);
+#pragma unroll
+      for (int h = 0; h < PB / 4; ++h) {
+        const mx_u32x4 v = __builtin_bit_cast(
+            mx_u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs[r], off + 16 * h, 0, kNT));
+        p[r][4 * h] = v.x; p[r][4 * h + 1] = v.y; p[r][4 * h + 2] = v.z; p[r][4 * h + 3] = v.w;
+      }
+      sv[r] = srow[r][lg];
+    }
+    if (a.per_row && ++lr == ss_per_group) { lr = 0; ++lg; }
+  };
+#pragma unroll
+  for (int j = 0; j < P; ++j)
+    if (ss0 + j < ss1) load_slot(ss0 + j, pw[j], sc[j], xv[j]);
+
+  for (int base = ss0; base < ss1; base += P) {
+#pragma unroll
+    for (int j = 0; j < P; ++j) {
+      const int ss = base + j;
+      if (ss >= ss1) break;
+
+      // x pieces of this super-step into the wave's LDS region (row
+      // piece * M + m) ...
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        uint32_t p0, p1, p2;
+        split3_pair(xv[j][m].x, xv[j][m].y, p0, p1, p2);
+        uint8_t* d = xw + m * kMxRowBytes + 4 * lane;
+        *reinterpret_cast<uint32_t*>(d) = p0;
+        *reinterpret_cast<uint32_t*>(d + M * kMxRowBytes) = p1;
+        *reinterpret_cast<uint32_t*>(d + 2 * M * kMxRowBytes) = p2;
+      }
+      __builtin_amdgcn_wave_barrier();
+      // ... and back in the A-operand layout (a wave's LDS accesses complete
+      // in order, so the region needs no barrier)
+      mx_u32x4 av[NS][4];
+#pragma unroll
+      for (int t = 0; t < NS; ++t)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+          av[t][s] = *reinterpret_cast<const mx_u32x4*>(xw + aoff[t] + 16 * s);
+      __builtin_amdgcn_wave_barrier();
+
+      // Every output (piece, x row, weight row) sums its own products: the
+      // pieces are added only at the end, so the big piece's roundings are
+      // not mixed with the small ones'.
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        mx_f32x4 d[NS];
+#pragma unroll
+        for (int t = 0; t < NS; ++t) d[t] = mx_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const mx_u32x4 bv = BITS == 4 ? bf16x8_int4_x16(pw[j][r][s])
+                                        : bf16x8_int8(pw[j][r][2 * s], pw[j][r][2 * s + 1]);
+#pragma unroll
+          for (int t = 0; t < NS; ++t)
+            d[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(mx_bf16x8, av[t][s]), __builtin_bit_cast(mx_bf16x8, bv),
+                d[t], 0, 0, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < NS; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            acc[r][t][i] = __builtin_fmaf(d[t][i], sc[j][r], acc[r][t][i]);
+      }
+      // refill this slot with the super-step P ahead
+      if (ss + P < ss1) load_slot(ss + P, pw[j], sc[j], xv[j]);
+    }
+  }
+
+  // Partial sums into the wave's region as [tile][A row][column] ...
+  float* const part = reinterpret_cast<float*>(xw);
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int t = 0; t < NS; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        part[(r * NS * 16 + 16 * t + 4 * kb + i) * 16 + col] = acc[r][t][i];
+  __syncthreads();
+  // ... then one thread per output adds the waves' sums in wave order, per
+  // piece, and the pieces.
+  const int o = threadIdx.x;
+  if (o < R * M * 16) {
+    const int r = o / (M * 16), m = (o / 16) % M, c = o % 16;
+    const int row = (tile0 + r) * 16 + c;
+    float sp[3];
+#pragma unroll
+    for (int pc = 0; pc < 3; ++pc) {
+      const int idx = (r * NS * 16 + pc * M + m) * 16 + c;
+      float v = reinterpret_cast<const float*>(lds[0])[idx];
+#pragma unroll
+      for (int w = 1; w < W; ++w) v += reinterpret_cast<const float*>(lds[w])[idx];
+      sp[pc] = v;
+    }
+    if (row < a.n) a.y[(int64_t)m * a.n + row] = (sp[0] + (sp[1] + sp[2])) * code_unscale<BITS>();
+  }
+}
+
 // --------------------------------------------------------- generic kernel
 
 // One wave per (row, m) at a time, the grid's waves striding over them; any
@@ -693,7 +945,59 @@ hipError_t launch_generic(const Mat& mt, const uint8_t* payload, const float* sc
   return hipGetLastError();
 }
 
+// Whether the matrix-core kernel can take a lone matrix (at 2..8 x rows):
+// rows of whole super-steps, groups of whole super-steps (or of whole rows),
+// 16-byte aligned payload rows and 8-byte aligned x rows, and the payload of
+// 16 rows addressable with 32-bit offsets.
+bool mfma_ok(const Mat& mt, const uint8_t* payload, const float* x) {
+  return mt.k > 0 && mt.k % kMxCodes == 0 && mt.n <= (1ll << 26) &&
+         16 * ((int64_t)mt.k * mt.bits / 8) < (1ll << 31) &&
+         ((mt.k % mt.group == 0 && mt.group % kMxCodes == 0) || mt.group % mt.k == 0) &&
+         aligned(payload, 16) && aligned(x, 8);
+}
+
+template <int BITS, int M, int R, int W>
+hipError_t launch_mfma_rw(const GemvDesc& d, hipStream_t st) {
+  const int64_t blocks = ((d.n + 15) / 16 + R - 1) / R;  // at most 2^22
+  const int spg = d.per_row ? (int)(d.group / kMxCodes) : 1;
+  constexpr int P = M <= 4 ? kMxAhead : kMxAhead / 2;  // x slots cost 2*M registers each
+  gemv_mfma_kernel<BITS, M, R, W, P><<<(unsigned)blocks, 64 * W, 0, st>>>(d, spg);
+  return hipGetLastError();
+}
+
+// Work split by shape (measured on int4 group 128 and int8 per-channel
+// weights, M = 2..8): tall matrices take two tiles per block over four waves,
+// the others one tile per block, over 16 waves when few tiles would leave the
+// GPU short of waves, else over 8 (4 for rows of fewer than 8 super-steps).
+// 11008 x 4096 (688 tiles) runs best on 8 waves, 4096 x 11008 and 4096 x 4096
+// (256 tiles) on 16, 28672 x 8192 (1792 tiles) on two tiles by four waves.
+template <int BITS, int M>
+hipError_t launch_mfma_m(const GemvDesc& d, hipStream_t st) {
+  const int64_t tiles = (d.n + 15) / 16, ks = d.k / kMxCodes;
+  if (tiles >= 1024) return launch_mfma_rw<BITS, M, 2, 4>(d, st);
+  if (tiles <= 384 && ks >= 32) return launch_mfma_rw<BITS, M, 1, 16>(d, st);
+  if (ks >= 8) return launch_mfma_rw<BITS, M, 1, 8>(d, st);
+  return launch_mfma_rw<BITS, M, 1, 4>(d, st);
+}
+
+template <int BITS>
+hipError_t launch_mfma_bits(const GemvDesc& d, int m, hipStream_t st) {
+  switch (m) {
+    case 2: return launch_mfma_m<BITS, 2>(d, st);
+    case 3: return launch_mfma_m<BITS, 3>(d, st);
+    case 4: return launch_mfma_m<BITS, 4>(d, st);
+    case 5: return launch_mfma_m<BITS, 5>(d, st);
+    case 6: return launch_mfma_m<BITS, 6>(d, st);
+    case 7: return launch_mfma_m<BITS, 7>(d, st);
+    default: return launch_mfma_m<BITS, 8>(d, st);
+  }
+}
+
 }  // namespace
+
+int gemv_mfma_path(const Mat& mt, const uint8_t* payload, const float* x) {
+  return mfma_ok(mt, payload, x) ? PATH_MATRIX : gemv_path(mt, payload, x);
+}
 
 int gemv_path(const Mat& mt, const uint8_t* payload, const float* x) {
   const int cpc = 8;  // codes per chunk
@@ -708,6 +1012,10 @@ int gemv_path(const Mat& mt, const uint8_t* payload, const float* x) {
 
 hipError_t launch_gemv(const Mat& mt, const uint8_t* payload, const float* scales, int m,
                        const float* x, float* y, hipStream_t st) {
+  if (m >= 2 && mfma_ok(mt, payload, x)) {
+    const GemvDesc d = make_desc(mt, payload, scales, x, y);
+    return mt.bits == 4 ? launch_mfma_bits<4>(d, m, st) : launch_mfma_bits<8>(d, m, st);
+  }
   if (gemv_path(mt, payload, x) == PATH_FAST) {
     const GemvDesc d = make_desc(mt, payload, scales, x, y);
     return mt.bits == 4 ? launch_bits<4>(&d, 1, m, st) : launch_bits<8>(&d, 1, m, st);

@@ -447,8 +447,8 @@ int qw_gptq_quantize_pack(int bits, int64_t group, int64_t n, int64_t k, const f
 }
 
 // Which kernel family a call with these arguments would take (1 = fast,
-// 2 = block, 3 = generic; negative = invalid arguments).  Used by the tests
-// to make sure every family is exercised.
+// 2 = block, 3 = generic, 4 = matrix-core GEMV; negative = invalid
+// arguments).  Used by the tests to make sure every family is exercised.
 int qw_debug_path(int op, int bits, int64_t group, int64_t n, int64_t k, const void* a,
                   const void* b) {
   qw::Mat mt;
@@ -459,6 +459,7 @@ int qw_debug_path(int op, int bits, int64_t group, int64_t n, int64_t k, const v
     case 1: return qw::unpack_path(mt, (const uint8_t*)a, (const float*)b);
     case 2: return qw::gemv_path(mt, (const uint8_t*)a, (const float*)b);
     case 3: return qw::gemm_path(mt, (const uint8_t*)a, (const uint16_t*)b);
+    case 4: return qw::gemv_mfma_path(mt, (const uint8_t*)a, (const float*)b);
     default: return QW_ECOUNT;
   }
 }

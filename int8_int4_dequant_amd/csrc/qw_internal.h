@@ -59,10 +59,12 @@ hipError_t launch_gptq_quantize_pack(const Mat& mt, const float* w, const double
                                      hipStream_t stream);
 
 // Which kernel family a call takes (exposed for tests through qw_debug_path).
-enum Path { PATH_NONE = 0, PATH_FAST = 1, PATH_BLOCK = 2, PATH_GENERIC = 3 };
+enum Path { PATH_NONE = 0, PATH_FAST = 1, PATH_BLOCK = 2, PATH_GENERIC = 3, PATH_MATRIX = 4 };
 int quantize_path(const Mat& mt, const float* w, const uint8_t* payload);
 int unpack_path(const Mat& mt, const uint8_t* payload, const float* w_out);
 int gemv_path(const Mat& mt, const uint8_t* payload, const float* x);
+// The kernel family of a lone GEMV at 2..8 x rows (PATH_MATRIX: matrix cores).
+int gemv_mfma_path(const Mat& mt, const uint8_t* payload, const float* x);
 int gemm_path(const Mat& mt, const uint8_t* payload, const uint16_t* x);
 
 }  // namespace qw

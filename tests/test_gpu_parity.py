@@ -202,7 +202,7 @@ def test_gemv_split_and_stream_kernels(bits, group, n, k):
 # codes carry a factor 16, a power of two, removed at the end), so y must equal
 # the unpacked weight.  8 rows of x pick 8 columns; 300 weight rows take the
 # split-K kernel, 32768 + 7 the row-streaming one.
-@pytest.mark.parametrize("bits,group", [(4, 32), (4, 128), (8, 64)])
+@pytest.mark.parametrize("bits,group", [(4, 32), (4, 128), (8, 64), (8, 128)])
 @pytest.mark.parametrize("n", [300, 32768 + 7])
 def test_gemv_decode_reads_back_w_hat(bits, group, n):
     k = 512
@@ -213,6 +213,64 @@ def test_gemv_decode_reads_back_w_hat(bits, group, n):
     x[np.arange(8), cols] = 1.0
     y = host(qw.gemv(rec, dev(x)))
     assert same_bits(y, np.ascontiguousarray(oracle.unpack(ref)[:, cols].T))
+
+
+# A lone matrix at 2..8 rows of x whose rows and groups are whole 128-code
+# super-steps takes the matrix-core kernel (x cut into three bf16 pieces).
+# The 7B MLP up/down shapes, int8 per output channel, groups of 128 to 512
+# codes, groups spanning whole rows (48 rows sharing one scale; pairs of rows),
+# rows that are not a multiple of the 16-row tile, one super-step per row
+# (most of a block's waves idle), and row counts that take each work split.
+MX_CASES = [
+    (4, 128, 11008, 4096), (4, 128, 4096, 11008), (8, 4096, 4096, 4096),
+    (4, 256, 300, 1024), (8, 128, 77, 640), (4, 384, 33, 768), (8, 128, 16, 128),
+    (4, 128, 1, 128), (4, 128, 17, 256), (8, 512, 1000, 512), (4, 128 * 48, 48, 128),
+    (8, 1280, 78, 640), (4, 128, 16384 + 9, 256), (8, 256, 9000, 2048),
+]
+
+
+@pytest.mark.parametrize("bits,group,n,k", MX_CASES)
+def test_gemv_matrix_cores(bits, group, n, k):
+    w = inputs.weight(n * 3 + k + bits, n, k, 0.02)
+    ref, rec = quant_both(w, bits, group)
+    for m in range(2, 9):
+        x = inputs.activations(m * 7 + n + k, m, k)
+        xd = dev(x)
+        assert qw.qw_debug_path(4, bits, group, n, k, rec["payload"], xd) == 4
+        y = host(qw.gemv(rec, xd))
+        yr = oracle.gemv_ref(ref, x)
+        B = oracle.error_base(ref, x)
+        assert np.all(np.abs(y.astype(np.float64) - yr) <= GEMV_TOL * B), (m, np.max(
+            np.abs(y - yr) / np.maximum(B, 1e-300)))
+
+
+# x over a wide range of magnitudes (2^-40 .. 2^40, a third of it zero, signs
+# mixed): every value needs all three bf16 pieces, and rows mixing huge and
+# tiny terms check that no piece is lost.  The matrix-core kernel stays
+# within the fp32 bound everywhere.
+@pytest.mark.parametrize("bits,group", [(4, 128), (8, 256)])
+def test_gemv_matrix_cores_wide_range_x(bits, group):
+    n, k = 333, 2048
+    w = inputs.weight(5 + bits, n, k, 0.02)
+    ref, rec = quant_both(w, bits, group)
+    rng = np.random.default_rng(11 + bits)
+    for m in (2, 5, 8):
+        x = inputs.activations(m + bits, m, k)
+        x = (x * np.exp2(rng.integers(-40, 41, size=x.shape))).astype(np.float32)
+        x[rng.random(x.shape) < 0.33] = 0.0
+        check_gemv(ref, rec, x)
+
+
+# Not on the matrix-core kernel: rows or groups that are not whole
+# super-steps, and payload rows not 16-byte aligned.
+def test_gemv_matrix_cores_not_taken():
+    n, k = 64, 256
+    x = dev(inputs.activations(1, 4, k))
+    p = torch.empty(n * k, dtype=torch.uint8, device="cuda")
+    assert qw.qw_debug_path(4, 4, 128, n, k, p, x) == 4
+    assert qw.qw_debug_path(4, 4, 64, n, k, p, x) == 1
+    assert qw.qw_debug_path(4, 4, 32, n, 96, p, x) == 1
+    assert qw.qw_debug_path(4, 4, 128, n, k, p[4:], x) != 4
 
 
 def test_gemv_k_zero_and_empty():
