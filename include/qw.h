@@ -29,7 +29,7 @@
  *   y[m][i] = sum_j x[m][j] * w_hat[i][j]
  *
  *   qw_gemv : decode-time product, fp32 activations, 1 <= m <= 8; every
- *             product exact or singly rounded, sums in fp32.  From 2 rows of
+ *             product exact or singly rounded, sums in fp32.  From 3 rows of
  *             x on, the products run on the bf16 matrix cores: each x value
  *             is cut into three bf16 pieces that add up to it exactly, and
  *             each piece times a code (an integer, exact in bf16) is exact in
@@ -207,7 +207,8 @@ int qw_unpack_batched(int count, const qw_unpack_desc* descs, void* stream);
  *   x  fp32 [m][k]  (read),   y  fp32 [m][n]  (written),   0 <= m <= 8.
  * Any group dividing n*k is accepted; with k % 8 == 0 and either
  * k % group == 0 with group % 8 == 0, or group % k == 0, the streaming
- * kernels run.  At 2..8 rows of x, rows of whole 128-code steps
+ * kernels run.  At 3..8 rows of x (5..8 for matrices of 16384 rows or
+ * more), rows of whole 128-code steps
  * (k % 128 == 0), groups of whole steps (group % 128 == 0) or of whole rows
  * (group % k == 0), a 16-byte aligned payload and an 8-byte aligned x take
  * the matrix-core kernel.  Outputs are deterministic: the same call gives
@@ -413,7 +414,8 @@ int qw_gptq_quantize_pack(int bits, int64_t group, int64_t n, int64_t k,
  * kernel, 4 = matrix-core GEMV) or a negative status for invalid arguments.
  * `op`: 0 quantize_pack (a = w, b = payload), 1 unpack (a = payload, b =
  * w_out), 2 gemv at one row of x (a = payload, b = x), 3 gemm (a = payload,
- * b = x_bf16), 4 gemv at 2..8 rows of x (a = payload, b = x).  Enqueues
+ * b = x_bf16), 4 gemv at 8 rows of x (a = payload, b = x; at fewer rows the
+ * matrix-core kernel runs from the row counts qw_gemv states).  Enqueues
  * nothing.
  */
 int qw_debug_path(int op, int bits, int64_t group, int64_t n, int64_t k,

@@ -518,7 +518,7 @@ __global__ __launch_bounds__(256) void gemv8_split_kernel(const GemvBatch<NB> b)
   }
 }
 
-// ------------------------------------------- matrix-core GEMV (M = 2 .. 8)
+// ------------------------------------------- matrix-core GEMV (M = 3 .. 8)
 //
 // With several x rows the fp32 kernels above spend 8*M products and M scale
 // FMAs per 8 codes on top of the decode, and the wave reductions of R*M
@@ -529,15 +529,24 @@ __global__ __launch_bounds__(256) void gemv8_split_kernel(const GemvBatch<NB> b)
 //   * every x value is cut into three bf16 pieces, x = p0 + p1 + p2 exactly:
 //     p0 is x with the low 16 bits of its encoding cleared, p1 the same of
 //     x - p0, and p2 = x - p0 - p1 keeps at most 8 significant bits; both
-//     subtractions are exact (the operands agree in sign and exponent range)
-//     as long as nothing underflows;
-//   * a product of a piece and a code is exact in the fp32 accumulator, so
-//     the only roundings are the accumulator's additions, as on the fp32
-//     path, and the 1e-5 * sum|x * w_hat| bound keeps a wide margin.
-// Layout: the A operand is the x pieces (16 rows: x row m, rows past M
-// repeat the last one and their outputs are dropped), the B operand the
-// weights (16 columns = 16 weight rows), so each lane's four outputs belong
-// to one weight row and need one scale per group.
+//     subtractions are exact (x - p0 only drops bits p0 already holds) as
+//     long as nothing underflows (|x| >= 2^-110);
+//   * a product of a piece and a code has at most 12 significant bits, so
+//     it is exact in the fp32 accumulator, and the only roundings are the
+//     accumulator's additions.  Measured on this part, one instruction adds
+//     its 32 products and the accumulator with a few roundings near fp32's
+//     own (products are aligned to the largest before they are added, in
+//     blocks of 8, with the bits below 2^-24 of it dropped, and the block
+//     sums rounded as they meet): a handful of 2^-24 relative errors per
+//     instruction, as a chain of fp32 additions of the same terms would.
+// Layout: the A operand is the x pieces, one row per (piece, x row), piece
+// major: 3*M rows in one (M <= 5) or two 16-row sets; rows past 3*M repeat
+// the last one and their outputs are dropped.  The B operand is the weights
+// (16 columns = 16 weight rows), so each lane's outputs belong to one weight
+// row and need one scale per group.  Each (piece, x row, weight row) output
+// keeps its own sum; the three pieces are added only in the final sum, so
+// the big piece's roundings are not mixed with the small ones' (theirs are
+// 2^-8 and 2^-16 smaller).
 // Work split: a block takes R tiles of 16 weight rows over the whole row
 // length; its W waves split the row into super-steps of 128 codes (a lane
 // reads a row-contiguous 32-code slab per super-step: 16 B int4, 32 B int8,
@@ -546,8 +555,13 @@ __global__ __launch_bounds__(256) void gemv8_split_kernel(const GemvBatch<NB> b)
 // cuts the 128*M x values once, two per lane, into pieces stored in its own
 // LDS region, reads them back in the A layout, and uses them for its R
 // tiles.  A super-step lies inside one group (groups are multiples of 128
-// codes), and its sum is multiplied by the group's scale into an fp32
-// accumulator (one FMA per output).
+// codes), and its sums are multiplied by the group's scale into fp32
+// accumulators (one FMA per output).
+// Error chain of one output, in units of 2^-24 * sum|x * w_hat|: 4
+// instructions per super-step on the big piece, one scale FMA, one addition
+// per super-step of the wave (row length / 128 / W), W - 1 additions across
+// waves and 2 for the pieces -- about 50 for the shapes here, 3e-6, inside
+// the 1e-5 bound.
 
 typedef __bf16 mx_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float mx_f32x4 __attribute__((ext_vector_type(4)));
@@ -555,7 +569,10 @@ typedef uint32_t mx_u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMxRowBytes = 272;  // one x row of one piece in LDS: 128 bf16 + 16 B pad
 constexpr int kMxCodes = 128;     // codes per super-step
-constexpr int kMxAhead = 4;       // super-steps of payload in flight per wave
+// Super-steps of payload, scales and x in flight per wave (measured on the
+// 7B MLP shapes: 2 was as fast as 4 or faster, with 76 instead of 104
+// registers at 4 rows of x)
+constexpr int kMxAhead = 2;
 
 __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -597,7 +614,7 @@ __device__ __forceinline__ void split3_pair(float a, float b, uint32_t& p0, uint
 
 template <int BITS, int M, int R, int W, int P>
 __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const GemvDesc a, int ss_per_group) {
-  static_assert(M >= 2 && M <= 8 && R >= 1 && P >= 1, "shape of the matrix-core GEMV");
+  static_assert(M >= 3 && M <= 8 && R >= 1 && P >= 1, "shape of the matrix-core GEMV");
   constexpr int PB = BITS == 4 ? 4 : 8;           // payload dwords per lane per super-step
   constexpr int NR = 3 * M;                       // A rows: (piece, x row), piece-major
   constexpr int NS = (NR + 15) / 16;              // 16-row MFMA sets
@@ -945,7 +962,7 @@ hipError_t launch_generic(const Mat& mt, const uint8_t* payload, const float* sc
   return hipGetLastError();
 }
 
-// Whether the matrix-core kernel can take a lone matrix (at 2..8 x rows):
+// Whether the matrix-core kernel can take a lone matrix (at 3..8 x rows):
 // rows of whole super-steps, groups of whole super-steps (or of whole rows),
 // 16-byte aligned payload rows and 8-byte aligned x rows, and the payload of
 // 16 rows addressable with 32-bit offsets.
@@ -956,17 +973,22 @@ bool mfma_ok(const Mat& mt, const uint8_t* payload, const float* x) {
          aligned(payload, 16) && aligned(x, 8);
 }
 
+// Rows of x from which the matrix-core kernel beats the fp32 kernels
+// (measured, int4 group 128: 11008 x 4096 at m = 2 9.9 against 10.3 us, at
+// m = 3 12.2 against 11.1; 28672 x 8192 at m = 4 50.8 against 52.9 us, at
+// m = 8 83 against 63).
+int mfma_min_rows(const Mat& mt) { return mt.n >= 16384 ? 5 : 3; }
+
 template <int BITS, int M, int R, int W>
 hipError_t launch_mfma_rw(const GemvDesc& d, hipStream_t st) {
   const int64_t blocks = ((d.n + 15) / 16 + R - 1) / R;  // at most 2^22
   const int spg = d.per_row ? (int)(d.group / kMxCodes) : 1;
-  constexpr int P = M <= 4 ? kMxAhead : kMxAhead / 2;  // x slots cost 2*M registers each
-  gemv_mfma_kernel<BITS, M, R, W, P><<<(unsigned)blocks, 64 * W, 0, st>>>(d, spg);
+  gemv_mfma_kernel<BITS, M, R, W, kMxAhead><<<(unsigned)blocks, 64 * W, 0, st>>>(d, spg);
   return hipGetLastError();
 }
 
 // Work split by shape (measured on int4 group 128 and int8 per-channel
-// weights, M = 2..8): tall matrices take two tiles per block over four waves,
+// weights, M = 3..8): tall matrices take two tiles per block over four waves,
 // the others one tile per block, over 16 waves when few tiles would leave the
 // GPU short of waves, else over 8 (4 for rows of fewer than 8 super-steps).
 // 11008 x 4096 (688 tiles) runs best on 8 waves, 4096 x 11008 and 4096 x 4096
@@ -983,7 +1005,6 @@ hipError_t launch_mfma_m(const GemvDesc& d, hipStream_t st) {
 template <int BITS>
 hipError_t launch_mfma_bits(const GemvDesc& d, int m, hipStream_t st) {
   switch (m) {
-    case 2: return launch_mfma_m<BITS, 2>(d, st);
     case 3: return launch_mfma_m<BITS, 3>(d, st);
     case 4: return launch_mfma_m<BITS, 4>(d, st);
     case 5: return launch_mfma_m<BITS, 5>(d, st);
@@ -1012,7 +1033,7 @@ int gemv_path(const Mat& mt, const uint8_t* payload, const float* x) {
 
 hipError_t launch_gemv(const Mat& mt, const uint8_t* payload, const float* scales, int m,
                        const float* x, float* y, hipStream_t st) {
-  if (m >= 2 && mfma_ok(mt, payload, x)) {
+  if (m >= mfma_min_rows(mt) && mfma_ok(mt, payload, x)) {
     const GemvDesc d = make_desc(mt, payload, scales, x, y);
     return mt.bits == 4 ? launch_mfma_bits<4>(d, m, st) : launch_mfma_bits<8>(d, m, st);
   }

@@ -63,7 +63,7 @@ enum Path { PATH_NONE = 0, PATH_FAST = 1, PATH_BLOCK = 2, PATH_GENERIC = 3, PATH
 int quantize_path(const Mat& mt, const float* w, const uint8_t* payload);
 int unpack_path(const Mat& mt, const uint8_t* payload, const float* w_out);
 int gemv_path(const Mat& mt, const uint8_t* payload, const float* x);
-// The kernel family of a lone GEMV at 2..8 x rows (PATH_MATRIX: matrix cores).
+// The kernel family of a lone GEMV at 8 rows of x (PATH_MATRIX: matrix cores).
 int gemv_mfma_path(const Mat& mt, const uint8_t* payload, const float* x);
 int gemm_path(const Mat& mt, const uint8_t* payload, const uint16_t* x);
 

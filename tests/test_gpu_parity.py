@@ -215,8 +215,9 @@ def test_gemv_decode_reads_back_w_hat(bits, group, n):
     assert same_bits(y, np.ascontiguousarray(oracle.unpack(ref)[:, cols].T))
 
 
-# A lone matrix at 2..8 rows of x whose rows and groups are whole 128-code
-# super-steps takes the matrix-core kernel (x cut into three bf16 pieces).
+# A lone matrix at 3..8 rows of x (5..8 from 16384 rows) whose rows and
+# groups are whole 128-code super-steps takes the matrix-core kernel (x cut
+# into three bf16 pieces); m = 2 checks the fp32 kernel on the same shapes.
 # The 7B MLP up/down shapes, int8 per output channel, groups of 128 to 512
 # codes, groups spanning whole rows (48 rows sharing one scale; pairs of rows),
 # rows that are not a multiple of the 16-row tile, one super-step per row
@@ -237,7 +238,7 @@ def test_gemv_matrix_cores(bits, group, n, k):
         x = inputs.activations(m * 7 + n + k, m, k)
         xd = dev(x)
         assert qw.qw_debug_path(4, bits, group, n, k, rec["payload"], xd) == 4
-        y = host(qw.gemv(rec, xd))
+        y = host(qw.gemv(rec, xd))  # the matrix-core kernel from m = 3 (m = 5 from 16384 rows)
         yr = oracle.gemv_ref(ref, x)
         B = oracle.error_base(ref, x)
         assert np.all(np.abs(y.astype(np.float64) - yr) <= GEMV_TOL * B), (m, np.max(
