@@ -268,10 +268,10 @@ PMC_TABLE_KERNELS = [
     ("c4 decode pass (qw_gemv_batched, M=1, 224 matrices)", "gemv8_kernel<4, 1, 16, 256>",
      21248 * 256),
     ("c3 up 11008x4096 M=1 (qw_gemv)", "gemv8_split_kernel<4, 1, 4, 1>", 2752 * 256),
-    ("c3 up 11008x4096 M=4", "gemv8_split_kernel<4, 4, 8, 1>", 1376 * 256),
-    ("c3 down 4096x11008 M=4", "gemv8_split_kernel<4, 4, 8, 1>", 512 * 256),
-    ("c3 up 11008x4096 M=8", "gemv8_split_kernel<4, 8, 8, 1>", 1376 * 256),
-    ("c3 down 4096x11008 M=8", "gemv8_split_kernel<4, 8, 8, 1>", 512 * 256),
+    ("c3 up 11008x4096 M=4 (matrix cores)", "gemv_mfma_kernel<4, 4, 1, 8, 2>", 688 * 512),
+    ("c3 down 4096x11008 M=4 (matrix cores)", "gemv_mfma_kernel<4, 4, 1, 16, 2>", 256 * 1024),
+    ("c3 up 11008x4096 M=8 (matrix cores)", "gemv_mfma_kernel<4, 8, 1, 8, 2>", 688 * 512),
+    ("c3 down 4096x11008 M=8 (matrix cores)", "gemv_mfma_kernel<4, 8, 1, 16, 2>", 256 * 1024),
     ("c5 prefill GEMM 2048x28672x8192", "gemm_kernel<4>", 262144),
     ("c4 quantize pass (qw_quantize_pack_batched)", "quant_subgroup_batched_kernel<4, 8>", None),
 ]
