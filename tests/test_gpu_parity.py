@@ -262,6 +262,26 @@ def test_gemv_matrix_cores_wide_range_x(bits, group):
         check_gemv(ref, rec, x)
 
 
+# x built against the matrix core's own additions: in every 8-element block of
+# a row one value of 1 and seven just under 2^-24 of it (the instruction
+# drops bits below 2^-24 of a block's largest term before adding), signs
+# alternating by block so that partial sums cancel; constant weights make
+# every code +-7.  The outputs stay within the fp32 bound.
+@pytest.mark.parametrize("bits", [4, 8])
+def test_gemv_matrix_cores_small_terms_beside_large(bits):
+    n, k, group = 48, 1024, 128
+    w = np.full((n, k), 0.03, np.float32)
+    w[1::2] *= -1.0
+    ref, rec = quant_both(w, bits, group)
+    x = np.full((4, k), np.float32(0.9 * 2.0 ** -24), np.float32)
+    x[:, ::8] = 1.0
+    x[:, (np.arange(k) // 8) % 2 == 1] *= -1.0
+    x[1] *= np.float32(3.0)
+    x[2, ::2] = 0.0
+    x[3] = x[3][::-1]
+    check_gemv(ref, rec, x)
+
+
 # Not on the matrix-core kernel: rows or groups that are not whole
 # super-steps, and payload rows not 16-byte aligned.
 def test_gemv_matrix_cores_not_taken():
