@@ -238,7 +238,9 @@ typedef struct qw_gemv_desc {
  * Batched dequantizing GEMV: `count` independent products y_i = x_i * W_i^T
  * with a common m (0 <= m <= 8), each within qw_gemv's error bound (the
  * kernel, and so the summation order, follows the rows of the whole launch:
- * a product may differ from a lone qw_gemv call in its last bits), and
+ * a product may differ from a lone qw_gemv call in its last bits; the
+ * matrix-core kernel takes the matrices qw_gemv would give it, from the row
+ * counts of x that qw_gemv states for the batch's total weight rows), and
  * enqueued as a few launches (up to QW_BATCH_PER_LAUNCH matrices of one bit
  * width each) that stream the weights back to back instead of one launch
  * per matrix (the fixed cost of many short kernels is what

@@ -612,8 +612,9 @@ __device__ __forceinline__ void split3_pair(float a, float b, uint32_t& p0, uint
   p2 = __builtin_amdgcn_perm(__float_as_uint(b2), __float_as_uint(a2), 0x07060302u);
 }
 
+// One block: R tiles of 16 weight rows from row 16 * tile0 of matrix `a`.
 template <int BITS, int M, int R, int W, int P>
-__global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const GemvDesc a, int ss_per_group) {
+__device__ __forceinline__ void gemv_mfma_body(const GemvDesc& a, int ss_per_group, int tile0) {
   static_assert(M >= 3 && M <= 8 && R >= 1 && P >= 1, "shape of the matrix-core GEMV");
   constexpr int PB = BITS == 4 ? 4 : 8;           // payload dwords per lane per super-step
   constexpr int NR = 3 * M;                       // A rows: (piece, x row), piece-major
@@ -627,7 +628,6 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const GemvDesc a, int
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int col = lane & 15, kb = lane >> 4;      // B column (weight row of the tile), k block
-  const int tile0 = blockIdx.x * R;
   const int ks = a.k / kMxCodes;                  // super-steps per row
   const int qs = (ks + W - 1) / W;
   const int ss0 = min(ks, wave * qs), ss1 = min(ks, ss0 + qs);
@@ -785,6 +785,25 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const GemvDesc a, int
     }
     if (row < a.n) a.y[(int64_t)m * a.n + row] = (sp[0] + (sp[1] + sp[2])) * code_unscale<BITS>();
   }
+}
+
+template <int BITS, int M, int R, int W, int P>
+__global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const GemvDesc a, int ss_per_group) {
+  gemv_mfma_body<BITS, M, R, W, P>(a, ss_per_group, blockIdx.x * R);
+}
+
+// Several matrices in one launch: one block per work item of R tiles, the
+// matrix found by the binary search over the items' first indices.
+template <int BITS, int M, int R, int W, int P, int NB>
+__global__ __launch_bounds__(64 * W) void gemv_mfma_batched_kernel(const GemvBatch<NB> b) {
+  const int item = blockIdx.x;
+  if (item >= b.items) return;
+  const int di = find_desc(b, item);
+  const GemvDesc a = load_desc<NB>(di);
+  typedef const __attribute__((address_space(4))) GemvBatch<NB>* KArg;
+  const int tile0 = (item - ((KArg)__builtin_amdgcn_kernarg_segment_ptr())->item0[di]) * R;
+  const int spg = a.per_row ? (int)(a.group / kMxCodes) : 1;
+  gemv_mfma_body<BITS, M, R, W, P>(a, spg, tile0);
 }
 
 // --------------------------------------------------------- generic kernel
@@ -973,11 +992,12 @@ bool mfma_ok(const Mat& mt, const uint8_t* payload, const float* x) {
          aligned(payload, 16) && aligned(x, 8);
 }
 
-// Rows of x from which the matrix-core kernel beats the fp32 kernels
+// Rows of x from which the matrix-core kernel beats the fp32 kernels, for a
+// matrix (or batch) of `rows` weight rows
 // (measured, int4 group 128: 11008 x 4096 at m = 2 9.9 against 10.3 us, at
 // m = 3 12.2 against 11.1; 28672 x 8192 at m = 4 50.8 against 52.9 us, at
 // m = 8 83 against 63).
-int mfma_min_rows(const Mat& mt) { return mt.n >= 16384 ? 5 : 3; }
+int mfma_min_rows(int64_t rows) { return rows >= 16384 ? 5 : 3; }
 
 template <int BITS, int M, int R, int W>
 hipError_t launch_mfma_rw(const GemvDesc& d, hipStream_t st) {
@@ -1014,6 +1034,45 @@ hipError_t launch_mfma_bits(const GemvDesc& d, int m, hipStream_t st) {
   }
 }
 
+// The same over a batch: one launch per QW_BATCH_PER_LAUNCH matrices, work
+// items of R tiles.
+template <int BITS, int M, int R, int W>
+hipError_t launch_mfma_batched_rw(const GemvDesc* ds, int count, hipStream_t st) {
+  for (int i = 0; i < count;) {
+    GemvBatch<GEMV_NB> b;
+    i = fill_batch<16 * R, GEMV_NB>(ds, i, count, b);
+    gemv_mfma_batched_kernel<BITS, M, R, W, kMxAhead, GEMV_NB>
+        <<<(unsigned)b.items, 64 * W, 0, st>>>(b);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int BITS, int M>
+hipError_t launch_mfma_batched_m(const GemvDesc* ds, int count, hipStream_t st) {
+  int64_t tiles = 0, ks = INT64_MAX;
+  for (int i = 0; i < count; ++i) {
+    tiles += (ds[i].n + 15) / 16;
+    ks = std::min<int64_t>(ks, ds[i].k / kMxCodes);
+  }
+  if (tiles >= 1024) return launch_mfma_batched_rw<BITS, M, 2, 4>(ds, count, st);
+  if (ks >= 8) return launch_mfma_batched_rw<BITS, M, 1, 8>(ds, count, st);
+  return launch_mfma_batched_rw<BITS, M, 1, 4>(ds, count, st);
+}
+
+template <int BITS>
+hipError_t launch_mfma_batched_bits(const GemvDesc* ds, int count, int m, hipStream_t st) {
+  switch (m) {
+    case 3: return launch_mfma_batched_m<BITS, 3>(ds, count, st);
+    case 4: return launch_mfma_batched_m<BITS, 4>(ds, count, st);
+    case 5: return launch_mfma_batched_m<BITS, 5>(ds, count, st);
+    case 6: return launch_mfma_batched_m<BITS, 6>(ds, count, st);
+    case 7: return launch_mfma_batched_m<BITS, 7>(ds, count, st);
+    default: return launch_mfma_batched_m<BITS, 8>(ds, count, st);
+  }
+}
+
 }  // namespace
 
 int gemv_mfma_path(const Mat& mt, const uint8_t* payload, const float* x) {
@@ -1033,7 +1092,7 @@ int gemv_path(const Mat& mt, const uint8_t* payload, const float* x) {
 
 hipError_t launch_gemv(const Mat& mt, const uint8_t* payload, const float* scales, int m,
                        const float* x, float* y, hipStream_t st) {
-  if (m >= mfma_min_rows(mt) && mfma_ok(mt, payload, x)) {
+  if (m >= mfma_min_rows(mt.n) && mfma_ok(mt, payload, x)) {
     const GemvDesc d = make_desc(mt, payload, scales, x, y);
     return mt.bits == 4 ? launch_mfma_bits<4>(d, m, st) : launch_mfma_bits<8>(d, m, st);
   }
@@ -1058,20 +1117,35 @@ hipError_t launch_gemv_batched(const Mat* mts, const uint8_t* const* payloads,
   for (int i = 0; i < count; ++i) order[i] = i;
   std::stable_sort(order.begin(), order.end(),
                    [&](int a, int b) { return mts[a].k > mts[b].k; });
+  // The matrix-core kernel takes the batch's eligible matrices from the row
+  // counts a lone matrix of the batch's total rows would take it (measured
+  // on 16 layers of the 7B stack at int4 group 128, graph-replayed: m = 3
+  // 507 us on the fp32 kernels against 560, m = 4 607 against 591, m = 5 722
+  // against 645, m = 8 1027 against 720).
+  int64_t rows = 0;
+  for (int i = 0; i < count; ++i) rows += mts[i].n;
+  const bool mx_rows = m >= mfma_min_rows(rows);
   for (int bits = 4; bits <= 8; bits += 4) {
-    GemvDesc ds[GEMV_NB];
-    int nd = 0;
+    GemvDesc ds[GEMV_NB], dx[GEMV_NB];
+    int nd = 0, nx = 0;
     for (int oi = 0; oi <= count; ++oi) {
-      const bool flush = (oi == count) || nd == GEMV_NB;
-      if (flush && nd) {
+      if (((oi == count) || nd == GEMV_NB) && nd) {
         hipError_t e = bits == 4 ? launch_bits<4>(ds, nd, m, st) : launch_bits<8>(ds, nd, m, st);
         if (e != hipSuccess) return e;
         nd = 0;
       }
+      if (((oi == count) || nx == GEMV_NB) && nx) {
+        hipError_t e = bits == 4 ? launch_mfma_batched_bits<4>(dx, nx, m, st)
+                                 : launch_mfma_batched_bits<8>(dx, nx, m, st);
+        if (e != hipSuccess) return e;
+        nx = 0;
+      }
       if (oi == count) break;
       const int i = order[oi];
       if (mts[i].bits != bits || mts[i].n * mts[i].k == 0) continue;
-      if (gemv_path(mts[i], payloads[i], xs[i]) == PATH_FAST) {
+      if (mx_rows && mfma_ok(mts[i], payloads[i], xs[i])) {
+        dx[nx++] = make_desc(mts[i], payloads[i], scales[i], xs[i], ys[i]);
+      } else if (gemv_path(mts[i], payloads[i], xs[i]) == PATH_FAST) {
         ds[nd++] = make_desc(mts[i], payloads[i], scales[i], xs[i], ys[i]);
       } else {
         hipError_t e = launch_generic(mts[i], payloads[i], scales[i], m, xs[i], ys[i], st);

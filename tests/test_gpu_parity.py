@@ -751,6 +751,33 @@ def test_gemv_batched_mixed(m):
         assert np.all(np.abs(host(y) - yr) <= GEMV_TOL * B)
 
 
+# More matrices for the matrix-core kernel than one launch holds
+# (QW_BATCH_PER_LAUNCH), of mixed row counts, row lengths and groups, at 3, 4
+# and 8 rows of x, beside int8 ones and fp32-kernel ones (group 64).
+@pytest.mark.parametrize("m", [3, 4, 8])
+def test_gemv_batched_matrix_cores_many(m):
+    specs = []
+    for i in range(qw.BATCH_PER_LAUNCH + 45):
+        n = [1, 16, 17, 130][i % 4]
+        k = [128, 384, 1024][(i // 4) % 3]
+        bits = 8 if i % 7 == 0 else 4
+        group = [128, k, 64][(i // 12) % 3]
+        specs.append((bits, group, n, k))
+    refs, recs, xs, xds = [], [], [], []
+    for j, (bits, group, n, k) in enumerate(specs):
+        w = inputs.weight(1300 + j, n, k, 0.05)
+        ref = oracle.quantize_pack(w, bits, group)
+        refs.append(ref)
+        recs.append(qw.quantize_pack(dev(w), bits, group))
+        x = inputs.activations(1700 + j, m, k)
+        xs.append(x)
+        xds.append(dev(x))
+    ys = qw.gemv_batched(recs, xds)
+    for ref, x, y in zip(refs, xs, ys):
+        B = oracle.error_base(ref, x)
+        assert np.all(np.abs(host(y) - oracle.gemv_ref(ref, x)) <= GEMV_TOL * B)
+
+
 def test_quantize_pack_batched_mixed():
     # several (bits, group) classes, a generic-path group, an empty matrix and
     # more matrices than one launch holds; every output bit-identical
