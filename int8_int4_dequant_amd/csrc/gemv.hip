@@ -612,10 +612,29 @@ __device__ __forceinline__ void split3_pair(float a, float b, uint32_t& p0, uint
   p2 = __builtin_amdgcn_perm(__float_as_uint(b2), __float_as_uint(a2), 0x07060302u);
 }
 
+// 4 x 4 transpose between the four 16-lane rows of a wave and four
+// registers: afterwards register s of a lane in row kb holds what register
+// kb held in row s (same lane within the row).  Two swap stages, 32 then 16
+// lanes apart.
+__device__ __forceinline__ void xpose4_rows(uint32_t& w0, uint32_t& w1, uint32_t& w2,
+                                            uint32_t& w3) {
+  const auto a = __builtin_amdgcn_permlane32_swap(w0, w2, false, false);
+  const auto b = __builtin_amdgcn_permlane32_swap(w1, w3, false, false);
+  const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+  const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+  w0 = c[0]; w1 = c[1]; w2 = d[0]; w3 = d[1];
+}
+
 // One block: R tiles of 16 weight rows from row 16 * tile0 of matrix `a`.
-template <int BITS, int M, int R, int W, int P>
+// G32: groups of 32 codes (four per super-step).  A lane still reads its
+// row-contiguous slab, one group; a transpose across the four lane blocks
+// then gives MFMA step s the 32 codes of group s (8 per lane block), the A
+// operand reads x in that order, and each step's sums take their group's
+// scale.
+template <int BITS, int M, int R, int W, int P, bool G32>
 __device__ __forceinline__ void gemv_mfma_body(const GemvDesc& a, int ss_per_group, int tile0) {
   static_assert(M >= 3 && M <= 8 && R >= 1 && P >= 1, "shape of the matrix-core GEMV");
+  constexpr int GS = G32 ? 4 : 1;                 // groups (scales) per super-step
   constexpr int PB = BITS == 4 ? 4 : 8;           // payload dwords per lane per super-step
   constexpr int NR = 3 * M;                       // A rows: (piece, x row), piece-major
   constexpr int NS = (NR + 15) / 16;              // 16-row MFMA sets
@@ -654,7 +673,8 @@ __device__ __forceinline__ void gemv_mfma_body(const GemvDesc& a, int ss_per_gro
   uint32_t aoff[NS];
 #pragma unroll
   for (int t = 0; t < NS; ++t)
-    aoff[t] = (uint32_t)(min(16 * t + col, NR - 1) * kMxRowBytes + kb * 64);
+    aoff[t] = (uint32_t)(min(16 * t + col, NR - 1) * kMxRowBytes + kb * (G32 ? 16 : 64));
+  constexpr int SSTEP = G32 ? 64 : 16;  // LDS bytes between MFMA steps' x
 
   mx_f32x4 acc[R][NS];
 #pragma unroll
@@ -669,14 +689,14 @@ __device__ __forceinline__ void gemv_mfma_body(const GemvDesc& a, int ss_per_gro
   // payload issued before it.  The group of the next super-step to load is
   // tracked without a division.
   int lg = 0, lr = 0;  // group of the next super-step to load, and its place in it
-  if (a.per_row) {
+  if (!G32 && a.per_row) {
     lg = ss0 / ss_per_group;
     lr = ss0 - lg * ss_per_group;
   }
   uint32_t pw[P][R][PB];
-  float sc[P][R];
+  float sc[P][R][GS];
   f32x2 xv[P][M];
-  auto load_slot = [&](int ss, uint32_t (&p)[R][PB], float (&sv)[R], f32x2 (&xx)[M])
+  auto load_slot = [&](int ss, uint32_t (&p)[R][PB], float (&sv)[R][GS], f32x2 (&xx)[M])
       __attribute__((always_inline)) {
     constexpr int kNT = 2;  // non-temporal: every weight is read once
 #pragma unroll
@@ -692,9 +712,14 @@ __device__ __forceinline__ void gemv_mfma_body(const GemvDesc& a, int ss_per_gro
             mx_u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs[r], off + 16 * h, 0, kNT));
         p[r][4 * h] = v.x; p[r][4 * h + 1] = v.y; p[r][4 * h + 2] = v.z; p[r][4 * h + 3] = v.w;
       }
-      sv[r] = srow[r][lg];
+      if constexpr (G32) {
+#pragma unroll
+        for (int g = 0; g < GS; ++g) sv[r][g] = srow[r][GS * ss + g];
+      } else {
+        sv[r][0] = srow[r][lg];
+      }
     }
-    if (a.per_row && ++lr == ss_per_group) { lr = 0; ++lg; }
+    if (!G32 && a.per_row && ++lr == ss_per_group) { lr = 0; ++lg; }
   };
 #pragma unroll
   for (int j = 0; j < P; ++j)
@@ -725,7 +750,7 @@ __device__ __forceinline__ void gemv_mfma_body(const GemvDesc& a, int ss_per_gro
       for (int t = 0; t < NS; ++t)
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-          av[t][s] = *reinterpret_cast<const mx_u32x4*>(xw + aoff[t] + 16 * s);
+          av[t][s] = *reinterpret_cast<const mx_u32x4*>(xw + aoff[t] + SSTEP * s);
       __builtin_amdgcn_wave_barrier();
 
       // Every output (piece, x row, weight row) sums its own products: the
@@ -733,24 +758,45 @@ __device__ __forceinline__ void gemv_mfma_body(const GemvDesc& a, int ss_per_gro
       // not mixed with the small ones'.
 #pragma unroll
       for (int r = 0; r < R; ++r) {
+        uint32_t w[PB];
+#pragma unroll
+        for (int e = 0; e < PB; ++e) w[e] = pw[j][r][e];
+        if constexpr (G32) {
+          if constexpr (BITS == 4) {
+            xpose4_rows(w[0], w[1], w[2], w[3]);
+          } else {  // the two dwords of a step transposed as two sets
+            xpose4_rows(w[0], w[2], w[4], w[6]);
+            xpose4_rows(w[1], w[3], w[5], w[7]);
+          }
+        }
         mx_f32x4 d[NS];
 #pragma unroll
         for (int t = 0; t < NS; ++t) d[t] = mx_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const mx_u32x4 bv = BITS == 4 ? bf16x8_int4_x16(pw[j][r][s])
-                                        : bf16x8_int8(pw[j][r][2 * s], pw[j][r][2 * s + 1]);
+          const mx_u32x4 bv = BITS == 4 ? bf16x8_int4_x16(w[s]) : bf16x8_int8(w[2 * s], w[2 * s + 1]);
 #pragma unroll
           for (int t = 0; t < NS; ++t)
             d[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                 __builtin_bit_cast(mx_bf16x8, av[t][s]), __builtin_bit_cast(mx_bf16x8, bv),
                 d[t], 0, 0, 0);
+          if constexpr (G32) {  // step s is group s: its sums take its scale
+#pragma unroll
+            for (int t = 0; t < NS; ++t) {
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                acc[r][t][i] = __builtin_fmaf(d[t][i], sc[j][r][s], acc[r][t][i]);
+              d[t] = mx_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            }
+          }
         }
+        if constexpr (!G32) {
 #pragma unroll
-        for (int t = 0; t < NS; ++t)
+          for (int t = 0; t < NS; ++t)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            acc[r][t][i] = __builtin_fmaf(d[t][i], sc[j][r], acc[r][t][i]);
+            for (int i = 0; i < 4; ++i)
+              acc[r][t][i] = __builtin_fmaf(d[t][i], sc[j][r][0], acc[r][t][i]);
+        }
       }
       // refill this slot with the super-step P ahead
       if (ss + P < ss1) load_slot(ss + P, pw[j], sc[j], xv[j]);
@@ -787,14 +833,14 @@ __device__ __forceinline__ void gemv_mfma_body(const GemvDesc& a, int ss_per_gro
   }
 }
 
-template <int BITS, int M, int R, int W, int P>
+template <int BITS, int M, int R, int W, int P, bool G32>
 __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const GemvDesc a, int ss_per_group) {
-  gemv_mfma_body<BITS, M, R, W, P>(a, ss_per_group, blockIdx.x * R);
+  gemv_mfma_body<BITS, M, R, W, P, G32>(a, ss_per_group, blockIdx.x * R);
 }
 
 // Several matrices in one launch: one block per work item of R tiles, the
 // matrix found by the binary search over the items' first indices.
-template <int BITS, int M, int R, int W, int P, int NB>
+template <int BITS, int M, int R, int W, int P, bool G32, int NB>
 __global__ __launch_bounds__(64 * W) void gemv_mfma_batched_kernel(const GemvBatch<NB> b) {
   const int item = blockIdx.x;
   if (item >= b.items) return;
@@ -802,8 +848,8 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_batched_kernel(const GemvBat
   const GemvDesc a = load_desc<NB>(di);
   typedef const __attribute__((address_space(4))) GemvBatch<NB>* KArg;
   const int tile0 = (item - ((KArg)__builtin_amdgcn_kernarg_segment_ptr())->item0[di]) * R;
-  const int spg = a.per_row ? (int)(a.group / kMxCodes) : 1;
-  gemv_mfma_body<BITS, M, R, W, P>(a, spg, tile0);
+  const int spg = (!G32 && a.per_row) ? (int)(a.group / kMxCodes) : 1;
+  gemv_mfma_body<BITS, M, R, W, P, G32>(a, spg, tile0);
 }
 
 // --------------------------------------------------------- generic kernel
@@ -982,13 +1028,15 @@ hipError_t launch_generic(const Mat& mt, const uint8_t* payload, const float* sc
 }
 
 // Whether the matrix-core kernel can take a lone matrix (at 3..8 x rows):
-// rows of whole super-steps, groups of whole super-steps (or of whole rows),
+// rows of whole super-steps, groups of whole super-steps, of 32 codes, or of
+// whole rows,
 // 16-byte aligned payload rows and 8-byte aligned x rows, and the payload of
 // 16 rows addressable with 32-bit offsets.
 bool mfma_ok(const Mat& mt, const uint8_t* payload, const float* x) {
   return mt.k > 0 && mt.k % kMxCodes == 0 && mt.n <= (1ll << 26) &&
          16 * ((int64_t)mt.k * mt.bits / 8) < (1ll << 31) &&
-         ((mt.k % mt.group == 0 && mt.group % kMxCodes == 0) || mt.group % mt.k == 0) &&
+         ((mt.k % mt.group == 0 && (mt.group % kMxCodes == 0 || mt.group == 32)) ||
+          mt.group % mt.k == 0) &&
          aligned(payload, 16) && aligned(x, 8);
 }
 
@@ -1002,8 +1050,12 @@ int mfma_min_rows(int64_t rows) { return rows >= 16384 ? 5 : 3; }
 template <int BITS, int M, int R, int W>
 hipError_t launch_mfma_rw(const GemvDesc& d, hipStream_t st) {
   const int64_t blocks = ((d.n + 15) / 16 + R - 1) / R;  // at most 2^22
-  const int spg = d.per_row ? (int)(d.group / kMxCodes) : 1;
-  gemv_mfma_kernel<BITS, M, R, W, kMxAhead><<<(unsigned)blocks, 64 * W, 0, st>>>(d, spg);
+  if (d.per_row && d.group == 32) {
+    gemv_mfma_kernel<BITS, M, R, W, kMxAhead, true><<<(unsigned)blocks, 64 * W, 0, st>>>(d, 1);
+  } else {
+    const int spg = d.per_row ? (int)(d.group / kMxCodes) : 1;
+    gemv_mfma_kernel<BITS, M, R, W, kMxAhead, false><<<(unsigned)blocks, 64 * W, 0, st>>>(d, spg);
+  }
   return hipGetLastError();
 }
 
@@ -1036,12 +1088,12 @@ hipError_t launch_mfma_bits(const GemvDesc& d, int m, hipStream_t st) {
 
 // The same over a batch: one launch per QW_BATCH_PER_LAUNCH matrices, work
 // items of R tiles.
-template <int BITS, int M, int R, int W>
+template <int BITS, int M, int R, int W, bool G32>
 hipError_t launch_mfma_batched_rw(const GemvDesc* ds, int count, hipStream_t st) {
   for (int i = 0; i < count;) {
     GemvBatch<GEMV_NB> b;
     i = fill_batch<16 * R, GEMV_NB>(ds, i, count, b);
-    gemv_mfma_batched_kernel<BITS, M, R, W, kMxAhead, GEMV_NB>
+    gemv_mfma_batched_kernel<BITS, M, R, W, kMxAhead, G32, GEMV_NB>
         <<<(unsigned)b.items, 64 * W, 0, st>>>(b);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1049,28 +1101,36 @@ hipError_t launch_mfma_batched_rw(const GemvDesc* ds, int count, hipStream_t st)
   return hipSuccess;
 }
 
-template <int BITS, int M>
+template <int BITS, int M, bool G32>
 hipError_t launch_mfma_batched_m(const GemvDesc* ds, int count, hipStream_t st) {
   int64_t tiles = 0, ks = INT64_MAX;
   for (int i = 0; i < count; ++i) {
     tiles += (ds[i].n + 15) / 16;
     ks = std::min<int64_t>(ks, ds[i].k / kMxCodes);
   }
-  if (tiles >= 1024) return launch_mfma_batched_rw<BITS, M, 2, 4>(ds, count, st);
-  if (ks >= 8) return launch_mfma_batched_rw<BITS, M, 1, 8>(ds, count, st);
-  return launch_mfma_batched_rw<BITS, M, 1, 4>(ds, count, st);
+  if (tiles >= 1024) return launch_mfma_batched_rw<BITS, M, 2, 4, G32>(ds, count, st);
+  if (ks >= 8) return launch_mfma_batched_rw<BITS, M, 1, 8, G32>(ds, count, st);
+  return launch_mfma_batched_rw<BITS, M, 1, 4, G32>(ds, count, st);
 }
 
-template <int BITS>
-hipError_t launch_mfma_batched_bits(const GemvDesc* ds, int count, int m, hipStream_t st) {
+template <int BITS, bool G32>
+hipError_t launch_mfma_batched_g(const GemvDesc* ds, int count, int m, hipStream_t st) {
   switch (m) {
-    case 3: return launch_mfma_batched_m<BITS, 3>(ds, count, st);
-    case 4: return launch_mfma_batched_m<BITS, 4>(ds, count, st);
-    case 5: return launch_mfma_batched_m<BITS, 5>(ds, count, st);
-    case 6: return launch_mfma_batched_m<BITS, 6>(ds, count, st);
-    case 7: return launch_mfma_batched_m<BITS, 7>(ds, count, st);
-    default: return launch_mfma_batched_m<BITS, 8>(ds, count, st);
+    case 3: return launch_mfma_batched_m<BITS, 3, G32>(ds, count, st);
+    case 4: return launch_mfma_batched_m<BITS, 4, G32>(ds, count, st);
+    case 5: return launch_mfma_batched_m<BITS, 5, G32>(ds, count, st);
+    case 6: return launch_mfma_batched_m<BITS, 6, G32>(ds, count, st);
+    case 7: return launch_mfma_batched_m<BITS, 7, G32>(ds, count, st);
+    default: return launch_mfma_batched_m<BITS, 8, G32>(ds, count, st);
   }
+}
+
+// One launch family per layout: groups of 32 codes (g32) or not.
+template <int BITS>
+hipError_t launch_mfma_batched_bits(const GemvDesc* ds, int count, int m, bool g32,
+                                    hipStream_t st) {
+  return g32 ? launch_mfma_batched_g<BITS, true>(ds, count, m, st)
+             : launch_mfma_batched_g<BITS, false>(ds, count, m, st);
 }
 
 }  // namespace
@@ -1126,25 +1186,28 @@ hipError_t launch_gemv_batched(const Mat* mts, const uint8_t* const* payloads,
   for (int i = 0; i < count; ++i) rows += mts[i].n;
   const bool mx_rows = m >= mfma_min_rows(rows);
   for (int bits = 4; bits <= 8; bits += 4) {
-    GemvDesc ds[GEMV_NB], dx[GEMV_NB];
-    int nd = 0, nx = 0;
+    GemvDesc ds[GEMV_NB], dx[2][GEMV_NB];  // dx[1]: groups of 32 codes
+    int nd = 0, nx[2] = {0, 0};
     for (int oi = 0; oi <= count; ++oi) {
       if (((oi == count) || nd == GEMV_NB) && nd) {
         hipError_t e = bits == 4 ? launch_bits<4>(ds, nd, m, st) : launch_bits<8>(ds, nd, m, st);
         if (e != hipSuccess) return e;
         nd = 0;
       }
-      if (((oi == count) || nx == GEMV_NB) && nx) {
-        hipError_t e = bits == 4 ? launch_mfma_batched_bits<4>(dx, nx, m, st)
-                                 : launch_mfma_batched_bits<8>(dx, nx, m, st);
-        if (e != hipSuccess) return e;
-        nx = 0;
+      for (int g = 0; g < 2; ++g) {
+        if (((oi == count) || nx[g] == GEMV_NB) && nx[g]) {
+          hipError_t e = bits == 4 ? launch_mfma_batched_bits<4>(dx[g], nx[g], m, g == 1, st)
+                                   : launch_mfma_batched_bits<8>(dx[g], nx[g], m, g == 1, st);
+          if (e != hipSuccess) return e;
+          nx[g] = 0;
+        }
       }
       if (oi == count) break;
       const int i = order[oi];
       if (mts[i].bits != bits || mts[i].n * mts[i].k == 0) continue;
       if (mx_rows && mfma_ok(mts[i], payloads[i], xs[i])) {
-        dx[nx++] = make_desc(mts[i], payloads[i], scales[i], xs[i], ys[i]);
+        const int g = mts[i].k % mts[i].group == 0 && mts[i].group == 32 ? 1 : 0;
+        dx[g][nx[g]++] = make_desc(mts[i], payloads[i], scales[i], xs[i], ys[i]);
       } else if (gemv_path(mts[i], payloads[i], xs[i]) == PATH_FAST) {
         ds[nd++] = make_desc(mts[i], payloads[i], scales[i], xs[i], ys[i]);
       } else {

@@ -215,9 +215,10 @@ def test_gemv_decode_reads_back_w_hat(bits, group, n):
     assert same_bits(y, np.ascontiguousarray(oracle.unpack(ref)[:, cols].T))
 
 
-# A lone matrix at 3..8 rows of x (5..8 from 16384 rows) whose rows and
-# groups are whole 128-code super-steps takes the matrix-core kernel (x cut
-# into three bf16 pieces); m = 2 checks the fp32 kernel on the same shapes.
+# A lone matrix at 3..8 rows of x (5..8 from 16384 rows) whose rows are
+# whole 128-code super-steps, with groups of whole super-steps, of 32 codes
+# or of whole rows, takes the matrix-core kernel (x cut into three bf16
+# pieces); m = 2 checks the fp32 kernel on the same shapes.
 # The 7B MLP up/down shapes, int8 per output channel, groups of 128 to 512
 # codes, groups spanning whole rows (48 rows sharing one scale; pairs of rows),
 # rows that are not a multiple of the 16-row tile, one super-step per row
@@ -227,6 +228,8 @@ MX_CASES = [
     (4, 256, 300, 1024), (8, 128, 77, 640), (4, 384, 33, 768), (8, 128, 16, 128),
     (4, 128, 1, 128), (4, 128, 17, 256), (8, 512, 1000, 512), (4, 128 * 48, 48, 128),
     (8, 1280, 78, 640), (4, 128, 16384 + 9, 256), (8, 256, 9000, 2048),
+    # groups of 32 codes: four per super-step, the lane blocks transposed
+    (4, 32, 11008, 4096), (8, 32, 300, 1024), (4, 32, 17, 128), (8, 32, 16384 + 5, 256),
 ]
 
 
@@ -752,8 +755,9 @@ def test_gemv_batched_mixed(m):
 
 
 # More matrices for the matrix-core kernel than one launch holds
-# (QW_BATCH_PER_LAUNCH), of mixed row counts, row lengths and groups, at 3, 4
-# and 8 rows of x, beside int8 ones and fp32-kernel ones (group 64).
+# (QW_BATCH_PER_LAUNCH), of mixed row counts, row lengths and groups (both
+# layouts: groups of whole super-steps and of 32 codes), at 3, 4 and 8 rows of
+# x, beside int8 ones and fp32-kernel ones (group 64).
 @pytest.mark.parametrize("m", [3, 4, 8])
 def test_gemv_batched_matrix_cores_many(m):
     specs = []
@@ -761,7 +765,7 @@ def test_gemv_batched_matrix_cores_many(m):
         n = [1, 16, 17, 130][i % 4]
         k = [128, 384, 1024][(i // 4) % 3]
         bits = 8 if i % 7 == 0 else 4
-        group = [128, k, 64][(i // 12) % 3]
+        group = [128, k, 64, 32][(i // 12) % 4]
         specs.append((bits, group, n, k))
     refs, recs, xs, xds = [], [], [], []
     for j, (bits, group, n, k) in enumerate(specs):
