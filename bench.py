@@ -999,6 +999,23 @@ def main():
 
     unpack_us = timed(unpack_pass)
     unpack_single_us = timed(unpack_single_pass)
+
+    # the same decode pass at 8 rows of x (several sequences at once): one
+    # batched call, which takes the matrix-core kernel
+    x8 = {k: torch.from_numpy(inputs.activations(808 + k, 8, k)).to(dev) for k in (4096, 11008)}
+    Y8 = [torch.empty((8, n), dtype=torch.float32, device=dev) for n, k in shapes]
+    d8, n8 = qw.make_gemv_descs(
+        (4, 32, n, k, P[i], S[i], x8[k], Y8[i]) for i, (n, k) in enumerate(shapes))
+
+    def m8_pass():
+        st = L.qw_gemv_batched(n8, d8, 8, sptr)
+        if st:
+            raise RuntimeError(f"qw_gemv_batched (m = 8) failed: {st}")
+
+    prewarm(args, m8_pass)
+    m8_us = timed(m8_pass)
+    gbytes8 = sum(gemv_bytes(n, k, m=8) for n, k in shapes)
+    del Y8, d8
     ubytes = sum(n * k * 4 + n * k // 2 + 4 * (n * k // 32) for n, k in shapes)
     del wouts, udescs
     q_gbs = qbytes * args.steps / (q_ms * 1e-3) / 1e9
@@ -1012,7 +1029,7 @@ def main():
         f"{single_graph_us if single_graph_us is None else round(single_graph_us, 1)} us); "
         f"unpack pass {unpack_us:.1f} us "
         f"({ubytes / (unpack_us * 1e-6) / 1e9:.0f} GB/s, 1 batched call; one launch per matrix: "
-        f"{unpack_single_us:.1f} us)")
+        f"{unpack_single_us:.1f} us); pass at 8 rows of x {m8_us:.1f} us")
 
     chain = bench_chain(args, L, stream, mats, shapes, P, S, xs, gbytes)
 
@@ -1058,6 +1075,10 @@ def main():
             "pass_us": round(unpack_single_us, 1),
             "GB/s": round(ubytes / (unpack_single_us * 1e-6) / 1e9, 1)},
         "decode_chain_m1": chain,
+        "decode_gemv_m8": {"entry": "qw_gemv_batched (matrix cores)", "m": 8,
+                           "pass_us": round(m8_us, 1), "bytes_per_pass": gbytes8,
+                           "GB/s": round(gbytes8 / (m8_us * 1e-6) / 1e9, 1),
+                           "TFLOP/s": round(2.0 * 8 * weights / (m8_us * 1e-6) / 1e12, 2)},
         "decode_gemv_m1_one_launch_per_matrix": {
             "pass_us": round(single_us, 1),
             "GB/s": round(gbytes / (single_us * 1e-6) / 1e9, 1),
