@@ -642,7 +642,6 @@ __device__ __forceinline__ void gemv_mfma_body(const GemvDesc& a, int ss_per_gro
   // and after the loop its partial sums (R tiles x NS sets x 16 x 16 fp32)
   constexpr int XBYTES = NR * kMxRowBytes, PBYTES = R * NS * 1024;
   constexpr int REGION = XBYTES > PBYTES ? XBYTES : PBYTES;
-  static_assert(R * M * 16 <= 64 * W, "one thread per output in the final sum");
   __shared__ __attribute__((aligned(16))) uint8_t lds[W][REGION];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -814,10 +813,9 @@ __device__ __forceinline__ void gemv_mfma_body(const GemvDesc& a, int ss_per_gro
       for (int i = 0; i < 4; ++i)
         part[(r * NS * 16 + 16 * t + 4 * kb + i) * 16 + col] = acc[r][t][i];
   __syncthreads();
-  // ... then one thread per output adds the waves' sums in wave order, per
-  // piece, and the pieces.
-  const int o = threadIdx.x;
-  if (o < R * M * 16) {
+  // ... then the block's threads, one output each at a time, add the waves'
+  // sums in wave order, per piece, and the pieces.
+  for (int o = threadIdx.x; o < R * M * 16; o += 64 * W) {
     const int r = o / (M * 16), m = (o / 16) % M, c = o % 16;
     const int row = (tile0 + r) * 16 + c;
     float sp[3];
