@@ -30,7 +30,8 @@
  *
  *   qw_gemv : decode-time product, fp32 activations, 1 <= m <= 8; every
  *             product exact or singly rounded, sums in fp32.  From 3 rows of
- *             x on, the products run on the bf16 matrix cores: each x value
+ *             x on (for the shapes qw_gemv lists), the products run on the
+ *             bf16 matrix cores: each x value
  *             is cut into three bf16 pieces that add up to it exactly, and
  *             each piece times a code (an integer, exact in bf16) is exact in
  *             the fp32 accumulator.
