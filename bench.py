@@ -268,15 +268,15 @@ PMC_TABLE_KERNELS = [
     ("c4 decode pass (qw_gemv_batched, M=1, 224 matrices)", "gemv8_kernel<4, 1, 16, 256>",
      21248 * 256),
     ("c3 up 11008x4096 M=1 (qw_gemv)", "gemv8_split_kernel<4, 1, 4, 1>", 2752 * 256),
-    ("c3 up 11008x4096 M=4 (matrix cores)", "gemv_mfma_kernel<4, 4, 1, 8, 2, false>",
+    ("c3 up 11008x4096 M=4 (matrix cores)", "gemv_mfma_kernel<4, 4, 1, 8, 2, 1>",
      688 * 512),
-    ("c3 down 4096x11008 M=4 (matrix cores)", "gemv_mfma_kernel<4, 4, 1, 16, 2, false>",
+    ("c3 down 4096x11008 M=4 (matrix cores)", "gemv_mfma_kernel<4, 4, 1, 16, 2, 1>",
      256 * 1024),
-    ("c3 up 11008x4096 M=8 (matrix cores)", "gemv_mfma_kernel<4, 8, 1, 8, 2, false>", 688 * 512),
-    ("c3 down 4096x11008 M=8 (matrix cores)", "gemv_mfma_kernel<4, 8, 1, 16, 2, false>",
+    ("c3 up 11008x4096 M=8 (matrix cores)", "gemv_mfma_kernel<4, 8, 1, 8, 2, 1>", 688 * 512),
+    ("c3 down 4096x11008 M=8 (matrix cores)", "gemv_mfma_kernel<4, 8, 1, 16, 2, 1>",
      256 * 1024),
     ("c4 decode pass at M=8 (qw_gemv_batched, matrix cores, groups of 32)",
-     "gemv_mfma_batched_kernel<4, 8, 2, 4, 2, true, 256>", None),
+     "gemv_mfma_batched_kernel<4, 8, 2, 4, 2, 4, 256>", None),
     ("c5 prefill GEMM 2048x28672x8192", "gemm_kernel<4>", 262144),
     ("c4 quantize pass (qw_quantize_pack_batched)", "quant_subgroup_batched_kernel<4, 8>", None),
 ]

@@ -210,9 +210,9 @@ int qw_unpack_batched(int count, const qw_unpack_desc* descs, void* stream);
  * k % group == 0 with group % 8 == 0, or group % k == 0, the streaming
  * kernels run.  At 3..8 rows of x (5..8 for matrices of 16384 rows or
  * more), rows of whole 128-code steps
- * (k % 128 == 0), groups of whole steps (group % 128 == 0), of 32 codes or
- * of whole rows (group % k == 0), a 16-byte aligned payload and an 8-byte
- * aligned x take
+ * (k % 128 == 0), groups of whole steps (group % 128 == 0), of 32 or 64
+ * codes, or of whole rows (group % k == 0), a 16-byte aligned payload and an
+ * 8-byte aligned x take
  * the matrix-core kernel.  Outputs are deterministic: the same call gives
  * the same bits.
  */

@@ -626,15 +626,18 @@ __device__ __forceinline__ void xpose4_rows(uint32_t& w0, uint32_t& w1, uint32_t
 }
 
 // One block: R tiles of 16 weight rows from row 16 * tile0 of matrix `a`.
-// G32: groups of 32 codes (four per super-step).  A lane still reads its
-// row-contiguous slab, one group; a transpose across the four lane blocks
-// then gives MFMA step s the 32 codes of group s (8 per lane block), the A
-// operand reads x in that order, and each step's sums take their group's
-// scale.
-template <int BITS, int M, int R, int W, int P, bool G32>
+// GS: groups per super-step -- 1 for groups of whole super-steps (or whole
+// rows), 4 for groups of 32 codes, 2 for 64.  With GS > 1 a lane still reads
+// its row-contiguous 32-code slab; a transpose across the four lane blocks
+// then gives MFMA step s the 32 codes s*32 .. s*32+31 of the super-step (8
+// per lane block), the A operand reads x in that order, and the sums of a
+// group's steps take that group's scale.
+template <int BITS, int M, int R, int W, int P, int GS>
 __device__ __forceinline__ void gemv_mfma_body(const GemvDesc& a, int ss_per_group, int tile0) {
-  static_assert(M >= 3 && M <= 8 && R >= 1 && P >= 1, "shape of the matrix-core GEMV");
-  constexpr int GS = G32 ? 4 : 1;                 // groups (scales) per super-step
+  static_assert(M >= 3 && M <= 8 && R >= 1 && P >= 1 && (GS == 1 || GS == 2 || GS == 4),
+                "shape of the matrix-core GEMV");
+  constexpr bool XP = GS > 1;                     // transposed layout
+  constexpr int SPG = 4 / GS;                     // MFMA steps per group (GS > 1)
   constexpr int PB = BITS == 4 ? 4 : 8;           // payload dwords per lane per super-step
   constexpr int NR = 3 * M;                       // A rows: (piece, x row), piece-major
   constexpr int NS = (NR + 15) / 16;              // 16-row MFMA sets
@@ -672,8 +675,8 @@ __device__ __forceinline__ void gemv_mfma_body(const GemvDesc& a, int ss_per_gro
   uint32_t aoff[NS];
 #pragma unroll
   for (int t = 0; t < NS; ++t)
-    aoff[t] = (uint32_t)(min(16 * t + col, NR - 1) * kMxRowBytes + kb * (G32 ? 16 : 64));
-  constexpr int SSTEP = G32 ? 64 : 16;  // LDS bytes between MFMA steps' x
+    aoff[t] = (uint32_t)(min(16 * t + col, NR - 1) * kMxRowBytes + kb * (XP ? 16 : 64));
+  constexpr int SSTEP = XP ? 64 : 16;  // LDS bytes between MFMA steps' x
 
   mx_f32x4 acc[R][NS];
 #pragma unroll
@@ -688,7 +691,7 @@ __device__ __forceinline__ void gemv_mfma_body(const GemvDesc& a, int ss_per_gro
   // payload issued before it.  The group of the next super-step to load is
   // tracked without a division.
   int lg = 0, lr = 0;  // group of the next super-step to load, and its place in it
-  if (!G32 && a.per_row) {
+  if (!XP && a.per_row) {
     lg = ss0 / ss_per_group;
     lr = ss0 - lg * ss_per_group;
   }
@@ -711,14 +714,14 @@ __device__ __forceinline__ void gemv_mfma_body(const GemvDesc& a, int ss_per_gro
             mx_u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs[r], off + 16 * h, 0, kNT));
         p[r][4 * h] = v.x; p[r][4 * h + 1] = v.y; p[r][4 * h + 2] = v.z; p[r][4 * h + 3] = v.w;
       }
-      if constexpr (G32) {
+      if constexpr (XP) {
 #pragma unroll
         for (int g = 0; g < GS; ++g) sv[r][g] = srow[r][GS * ss + g];
       } else {
         sv[r][0] = srow[r][lg];
       }
     }
-    if (!G32 && a.per_row && ++lr == ss_per_group) { lr = 0; ++lg; }
+    if (!XP && a.per_row && ++lr == ss_per_group) { lr = 0; ++lg; }
   };
 #pragma unroll
   for (int j = 0; j < P; ++j)
@@ -760,7 +763,7 @@ __device__ __forceinline__ void gemv_mfma_body(const GemvDesc& a, int ss_per_gro
         uint32_t w[PB];
 #pragma unroll
         for (int e = 0; e < PB; ++e) w[e] = pw[j][r][e];
-        if constexpr (G32) {
+        if constexpr (XP) {
           if constexpr (BITS == 4) {
             xpose4_rows(w[0], w[1], w[2], w[3]);
           } else {  // the two dwords of a step transposed as two sets
@@ -779,17 +782,19 @@ __device__ __forceinline__ void gemv_mfma_body(const GemvDesc& a, int ss_per_gro
             d[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                 __builtin_bit_cast(mx_bf16x8, av[t][s]), __builtin_bit_cast(mx_bf16x8, bv),
                 d[t], 0, 0, 0);
-          if constexpr (G32) {  // step s is group s: its sums take its scale
+          if constexpr (XP) {  // a group's last step: its sums take its scale
+            if ((s + 1) % SPG == 0) {
 #pragma unroll
-            for (int t = 0; t < NS; ++t) {
+              for (int t = 0; t < NS; ++t) {
 #pragma unroll
-              for (int i = 0; i < 4; ++i)
-                acc[r][t][i] = __builtin_fmaf(d[t][i], sc[j][r][s], acc[r][t][i]);
-              d[t] = mx_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                for (int i = 0; i < 4; ++i)
+                  acc[r][t][i] = __builtin_fmaf(d[t][i], sc[j][r][s / SPG], acc[r][t][i]);
+                d[t] = mx_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+              }
             }
           }
         }
-        if constexpr (!G32) {
+        if constexpr (!XP) {
 #pragma unroll
           for (int t = 0; t < NS; ++t)
 #pragma unroll
@@ -831,14 +836,14 @@ __device__ __forceinline__ void gemv_mfma_body(const GemvDesc& a, int ss_per_gro
   }
 }
 
-template <int BITS, int M, int R, int W, int P, bool G32>
+template <int BITS, int M, int R, int W, int P, int GS>
 __global__ __launch_bounds__(64 * W) void gemv_mfma_kernel(const GemvDesc a, int ss_per_group) {
-  gemv_mfma_body<BITS, M, R, W, P, G32>(a, ss_per_group, blockIdx.x * R);
+  gemv_mfma_body<BITS, M, R, W, P, GS>(a, ss_per_group, blockIdx.x * R);
 }
 
 // Several matrices in one launch: one block per work item of R tiles, the
 // matrix found by the binary search over the items' first indices.
-template <int BITS, int M, int R, int W, int P, bool G32, int NB>
+template <int BITS, int M, int R, int W, int P, int GS, int NB>
 __global__ __launch_bounds__(64 * W) void gemv_mfma_batched_kernel(const GemvBatch<NB> b) {
   const int item = blockIdx.x;
   if (item >= b.items) return;
@@ -846,8 +851,8 @@ __global__ __launch_bounds__(64 * W) void gemv_mfma_batched_kernel(const GemvBat
   const GemvDesc a = load_desc<NB>(di);
   typedef const __attribute__((address_space(4))) GemvBatch<NB>* KArg;
   const int tile0 = (item - ((KArg)__builtin_amdgcn_kernarg_segment_ptr())->item0[di]) * R;
-  const int spg = (!G32 && a.per_row) ? (int)(a.group / kMxCodes) : 1;
-  gemv_mfma_body<BITS, M, R, W, P, G32>(a, spg, tile0);
+  const int spg = (GS == 1 && a.per_row) ? (int)(a.group / kMxCodes) : 1;
+  gemv_mfma_body<BITS, M, R, W, P, GS>(a, spg, tile0);
 }
 
 // --------------------------------------------------------- generic kernel
@@ -1026,14 +1031,15 @@ hipError_t launch_generic(const Mat& mt, const uint8_t* payload, const float* sc
 }
 
 // Whether the matrix-core kernel can take a lone matrix (at 3..8 x rows):
-// rows of whole super-steps, groups of whole super-steps, of 32 codes, or of
-// whole rows,
+// rows of whole super-steps, groups of whole super-steps, of 32 or 64 codes,
+// or of whole rows,
 // 16-byte aligned payload rows and 8-byte aligned x rows, and the payload of
 // 16 rows addressable with 32-bit offsets.
 bool mfma_ok(const Mat& mt, const uint8_t* payload, const float* x) {
   return mt.k > 0 && mt.k % kMxCodes == 0 && mt.n <= (1ll << 26) &&
          16 * ((int64_t)mt.k * mt.bits / 8) < (1ll << 31) &&
-         ((mt.k % mt.group == 0 && (mt.group % kMxCodes == 0 || mt.group == 32)) ||
+         ((mt.k % mt.group == 0 &&
+           (mt.group % kMxCodes == 0 || mt.group == 32 || mt.group == 64)) ||
           mt.group % mt.k == 0) &&
          aligned(payload, 16) && aligned(x, 8);
 }
@@ -1049,10 +1055,12 @@ template <int BITS, int M, int R, int W>
 hipError_t launch_mfma_rw(const GemvDesc& d, hipStream_t st) {
   const int64_t blocks = ((d.n + 15) / 16 + R - 1) / R;  // at most 2^22
   if (d.per_row && d.group == 32) {
-    gemv_mfma_kernel<BITS, M, R, W, kMxAhead, true><<<(unsigned)blocks, 64 * W, 0, st>>>(d, 1);
+    gemv_mfma_kernel<BITS, M, R, W, kMxAhead, 4><<<(unsigned)blocks, 64 * W, 0, st>>>(d, 1);
+  } else if (d.per_row && d.group == 64) {
+    gemv_mfma_kernel<BITS, M, R, W, kMxAhead, 2><<<(unsigned)blocks, 64 * W, 0, st>>>(d, 1);
   } else {
     const int spg = d.per_row ? (int)(d.group / kMxCodes) : 1;
-    gemv_mfma_kernel<BITS, M, R, W, kMxAhead, false><<<(unsigned)blocks, 64 * W, 0, st>>>(d, spg);
+    gemv_mfma_kernel<BITS, M, R, W, kMxAhead, 1><<<(unsigned)blocks, 64 * W, 0, st>>>(d, spg);
   }
   return hipGetLastError();
 }
@@ -1086,12 +1094,12 @@ hipError_t launch_mfma_bits(const GemvDesc& d, int m, hipStream_t st) {
 
 // The same over a batch: one launch per QW_BATCH_PER_LAUNCH matrices, work
 // items of R tiles.
-template <int BITS, int M, int R, int W, bool G32>
+template <int BITS, int M, int R, int W, int GS>
 hipError_t launch_mfma_batched_rw(const GemvDesc* ds, int count, hipStream_t st) {
   for (int i = 0; i < count;) {
     GemvBatch<GEMV_NB> b;
     i = fill_batch<16 * R, GEMV_NB>(ds, i, count, b);
-    gemv_mfma_batched_kernel<BITS, M, R, W, kMxAhead, G32, GEMV_NB>
+    gemv_mfma_batched_kernel<BITS, M, R, W, kMxAhead, GS, GEMV_NB>
         <<<(unsigned)b.items, 64 * W, 0, st>>>(b);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1099,36 +1107,37 @@ hipError_t launch_mfma_batched_rw(const GemvDesc* ds, int count, hipStream_t st)
   return hipSuccess;
 }
 
-template <int BITS, int M, bool G32>
+template <int BITS, int M, int GS>
 hipError_t launch_mfma_batched_m(const GemvDesc* ds, int count, hipStream_t st) {
   int64_t tiles = 0, ks = INT64_MAX;
   for (int i = 0; i < count; ++i) {
     tiles += (ds[i].n + 15) / 16;
     ks = std::min<int64_t>(ks, ds[i].k / kMxCodes);
   }
-  if (tiles >= 1024) return launch_mfma_batched_rw<BITS, M, 2, 4, G32>(ds, count, st);
-  if (ks >= 8) return launch_mfma_batched_rw<BITS, M, 1, 8, G32>(ds, count, st);
-  return launch_mfma_batched_rw<BITS, M, 1, 4, G32>(ds, count, st);
+  if (tiles >= 1024) return launch_mfma_batched_rw<BITS, M, 2, 4, GS>(ds, count, st);
+  if (ks >= 8) return launch_mfma_batched_rw<BITS, M, 1, 8, GS>(ds, count, st);
+  return launch_mfma_batched_rw<BITS, M, 1, 4, GS>(ds, count, st);
 }
 
-template <int BITS, bool G32>
+template <int BITS, int GS>
 hipError_t launch_mfma_batched_g(const GemvDesc* ds, int count, int m, hipStream_t st) {
   switch (m) {
-    case 3: return launch_mfma_batched_m<BITS, 3, G32>(ds, count, st);
-    case 4: return launch_mfma_batched_m<BITS, 4, G32>(ds, count, st);
-    case 5: return launch_mfma_batched_m<BITS, 5, G32>(ds, count, st);
-    case 6: return launch_mfma_batched_m<BITS, 6, G32>(ds, count, st);
-    case 7: return launch_mfma_batched_m<BITS, 7, G32>(ds, count, st);
-    default: return launch_mfma_batched_m<BITS, 8, G32>(ds, count, st);
+    case 3: return launch_mfma_batched_m<BITS, 3, GS>(ds, count, st);
+    case 4: return launch_mfma_batched_m<BITS, 4, GS>(ds, count, st);
+    case 5: return launch_mfma_batched_m<BITS, 5, GS>(ds, count, st);
+    case 6: return launch_mfma_batched_m<BITS, 6, GS>(ds, count, st);
+    case 7: return launch_mfma_batched_m<BITS, 7, GS>(ds, count, st);
+    default: return launch_mfma_batched_m<BITS, 8, GS>(ds, count, st);
   }
 }
 
-// One launch family per layout: groups of 32 codes (g32) or not.
+// One launch family per layout: gs groups per super-step (1, 2 or 4).
 template <int BITS>
-hipError_t launch_mfma_batched_bits(const GemvDesc* ds, int count, int m, bool g32,
+hipError_t launch_mfma_batched_bits(const GemvDesc* ds, int count, int m, int gs,
                                     hipStream_t st) {
-  return g32 ? launch_mfma_batched_g<BITS, true>(ds, count, m, st)
-             : launch_mfma_batched_g<BITS, false>(ds, count, m, st);
+  return gs == 4 ? launch_mfma_batched_g<BITS, 4>(ds, count, m, st)
+       : gs == 2 ? launch_mfma_batched_g<BITS, 2>(ds, count, m, st)
+                 : launch_mfma_batched_g<BITS, 1>(ds, count, m, st);
 }
 
 }  // namespace
@@ -1184,18 +1193,18 @@ hipError_t launch_gemv_batched(const Mat* mts, const uint8_t* const* payloads,
   for (int i = 0; i < count; ++i) rows += mts[i].n;
   const bool mx_rows = m >= mfma_min_rows(rows);
   for (int bits = 4; bits <= 8; bits += 4) {
-    GemvDesc ds[GEMV_NB], dx[2][GEMV_NB];  // dx[1]: groups of 32 codes
-    int nd = 0, nx[2] = {0, 0};
+    GemvDesc ds[GEMV_NB], dx[3][GEMV_NB];  // by layout: 1, 2 or 4 groups per super-step
+    int nd = 0, nx[3] = {0, 0, 0};
     for (int oi = 0; oi <= count; ++oi) {
       if (((oi == count) || nd == GEMV_NB) && nd) {
         hipError_t e = bits == 4 ? launch_bits<4>(ds, nd, m, st) : launch_bits<8>(ds, nd, m, st);
         if (e != hipSuccess) return e;
         nd = 0;
       }
-      for (int g = 0; g < 2; ++g) {
+      for (int g = 0; g < 3; ++g) {
         if (((oi == count) || nx[g] == GEMV_NB) && nx[g]) {
-          hipError_t e = bits == 4 ? launch_mfma_batched_bits<4>(dx[g], nx[g], m, g == 1, st)
-                                   : launch_mfma_batched_bits<8>(dx[g], nx[g], m, g == 1, st);
+          hipError_t e = bits == 4 ? launch_mfma_batched_bits<4>(dx[g], nx[g], m, 1 << g, st)
+                                   : launch_mfma_batched_bits<8>(dx[g], nx[g], m, 1 << g, st);
           if (e != hipSuccess) return e;
           nx[g] = 0;
         }
@@ -1204,7 +1213,8 @@ hipError_t launch_gemv_batched(const Mat* mts, const uint8_t* const* payloads,
       const int i = order[oi];
       if (mts[i].bits != bits || mts[i].n * mts[i].k == 0) continue;
       if (mx_rows && mfma_ok(mts[i], payloads[i], xs[i])) {
-        const int g = mts[i].k % mts[i].group == 0 && mts[i].group == 32 ? 1 : 0;
+        const bool pr = mts[i].k % mts[i].group == 0;
+        const int g = pr && mts[i].group == 32 ? 2 : pr && mts[i].group == 64 ? 1 : 0;
         dx[g][nx[g]++] = make_desc(mts[i], payloads[i], scales[i], xs[i], ys[i]);
       } else if (gemv_path(mts[i], payloads[i], xs[i]) == PATH_FAST) {
         ds[nd++] = make_desc(mts[i], payloads[i], scales[i], xs[i], ys[i]);

@@ -209,10 +209,10 @@ def test_quantize_dispatch(bits, group, n, k, al, expect):
     (3, 4, 128, 28672, 8192, 1), (3, 8, 32, 64, 256, 1), (3, 4, 16, 64, 256, 3),
     (3, 4, 32, 64, 96, 3),
     # 3..8 rows of x: the matrix-core GEMV for rows of whole 128-code steps
-    # with groups of whole steps, of 32 codes or of whole rows, else the fp32
-    # kernels
+    # with groups of whole steps, of 32 or 64 codes or of whole rows, else the
+    # fp32 kernels
     (4, 4, 128, 11008, 4096, 4), (4, 4, 128, 4096, 11008, 4), (4, 8, 4096, 4096, 4096, 4),
-    (4, 4, 4096 * 8, 8, 4096, 4), (4, 8, 256, 2, 128, 4), (4, 4, 64, 64, 256, 1),
+    (4, 4, 4096 * 8, 8, 4096, 4), (4, 8, 256, 2, 128, 4), (4, 4, 64, 64, 256, 4), (4, 4, 96, 64, 384, 1),
     (4, 4, 32, 11008, 4096, 4), (4, 8, 32, 300, 1024, 4), (4, 4, 128, 64, 384 + 8, 3),
     (4, 4, 8, 64, 96, 1),
     (4, 4, 3, 8, 48, 3), (4, 4, 128, 64, 0, 3),

@@ -216,8 +216,8 @@ def test_gemv_decode_reads_back_w_hat(bits, group, n):
 
 
 # A lone matrix at 3..8 rows of x (5..8 from 16384 rows) whose rows are
-# whole 128-code super-steps, with groups of whole super-steps, of 32 codes
-# or of whole rows, takes the matrix-core kernel (x cut into three bf16
+# whole 128-code super-steps, with groups of whole super-steps, of 32 or 64
+# codes or of whole rows, takes the matrix-core kernel (x cut into three bf16
 # pieces); m = 2 checks the fp32 kernel on the same shapes.
 # The 7B MLP up/down shapes, int8 per output channel, groups of 128 to 512
 # codes, groups spanning whole rows (48 rows sharing one scale; pairs of rows),
@@ -230,6 +230,8 @@ MX_CASES = [
     (8, 1280, 78, 640), (4, 128, 16384 + 9, 256), (8, 256, 9000, 2048),
     # groups of 32 codes: four per super-step, the lane blocks transposed
     (4, 32, 11008, 4096), (8, 32, 300, 1024), (4, 32, 17, 128), (8, 32, 16384 + 5, 256),
+    # groups of 64 codes: two per super-step
+    (4, 64, 300, 1024), (8, 64, 33, 384), (4, 64, 4096, 4096),
 ]
 
 
@@ -285,14 +287,16 @@ def test_gemv_matrix_cores_small_terms_beside_large(bits):
     check_gemv(ref, rec, x)
 
 
-# Not on the matrix-core kernel: rows or groups that are not whole
-# super-steps, and payload rows not 16-byte aligned.
+# Not on the matrix-core kernel: rows that are not whole super-steps, groups
+# that are neither whole super-steps nor 32 or 64 codes, and payload rows not
+# 16-byte aligned.
 def test_gemv_matrix_cores_not_taken():
     n, k = 64, 256
     x = dev(inputs.activations(1, 4, k))
     p = torch.empty(n * k, dtype=torch.uint8, device="cuda")
     assert qw.qw_debug_path(4, 4, 128, n, k, p, x) == 4
-    assert qw.qw_debug_path(4, 4, 64, n, k, p, x) == 1
+    assert qw.qw_debug_path(4, 4, 64, n, k, p, x) == 4
+    assert qw.qw_debug_path(4, 4, 96, n, 384, p, dev(inputs.activations(1, 4, 384))) == 1
     assert qw.qw_debug_path(4, 4, 32, n, 96, p, x) == 1
     assert qw.qw_debug_path(4, 4, 128, n, k, p[4:], x) != 4
 
@@ -756,8 +760,8 @@ def test_gemv_batched_mixed(m):
 
 # More matrices for the matrix-core kernel than one launch holds
 # (QW_BATCH_PER_LAUNCH), of mixed row counts, row lengths and groups (both
-# layouts: groups of whole super-steps and of 32 codes), at 3, 4 and 8 rows of
-# x, beside int8 ones and fp32-kernel ones (group 64).
+# layouts: groups of whole super-steps, of 32 and of 64 codes), at 3, 4 and 8
+# rows of x, beside int8 ones and fp32-kernel ones (group 16).
 @pytest.mark.parametrize("m", [3, 4, 8])
 def test_gemv_batched_matrix_cores_many(m):
     specs = []
@@ -765,7 +769,7 @@ def test_gemv_batched_matrix_cores_many(m):
         n = [1, 16, 17, 130][i % 4]
         k = [128, 384, 1024][(i // 4) % 3]
         bits = 8 if i % 7 == 0 else 4
-        group = [128, k, 64, 32][(i // 12) % 4]
+        group = [128, k, 64, 32, 16][(i // 12) % 5]
         specs.append((bits, group, n, k))
     refs, recs, xs, xds = [], [], [], []
     for j, (bits, group, n, k) in enumerate(specs):
