@@ -554,9 +554,10 @@ __global__ __launch_bounds__(256) void gemv8_split_kernel(const GemvBatch<NB> b)
 // LDS in wave order, so the result is deterministic.  Each super-step a wave
 // cuts the 128*M x values once, two per lane, into pieces stored in its own
 // LDS region, reads them back in the A layout, and uses them for its R
-// tiles.  A super-step lies inside one group (groups are multiples of 128
-// codes), and its sums are multiplied by the group's scale into fp32
-// accumulators (one FMA per output).
+// tiles.  With groups of whole super-steps (multiples of 128 codes) a
+// super-step's sums are multiplied by its group's scale into fp32
+// accumulators (one FMA per output); groups of 32 or 64 codes take a
+// transposed layout (see gemv_mfma_body) with one scale per group.
 // Error chain of one output, in units of 2^-24 * sum|x * w_hat|: 4
 // instructions per super-step on the big piece, one scale FMA, one addition
 // per super-step of the wave (row length / 128 / W), W - 1 additions across
