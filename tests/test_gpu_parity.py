@@ -232,6 +232,8 @@ MX_CASES = [
     (4, 32, 11008, 4096), (8, 32, 300, 1024), (4, 32, 17, 128), (8, 32, 16384 + 5, 256),
     # groups of 64 codes: two per super-step
     (4, 64, 300, 1024), (8, 64, 33, 384), (4, 64, 4096, 4096),
+    # long rows: 256 super-steps, 16 per wave through the prefetch ring
+    (4, 128, 200, 32768), (8, 32, 40, 32768),
 ]
 
 
