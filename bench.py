@@ -1007,7 +1007,7 @@ def main():
 
     # the same decode pass at 8 rows of x (several sequences at once): one
     # batched call, which takes the matrix-core kernel
-    x8 = {k: torch.from_numpy(inputs.activations(808 + k, 8, k)).to(dev) for k in (4096, 11008)}
+    x8 = {k: torch.from_numpy(inputs.c4_x8(k)).to(dev) for k in (4096, 11008)}
     Y8 = [torch.empty((8, n), dtype=torch.float32, device=dev) for n, k in shapes]
     d8, n8 = qw.make_gemv_descs(
         (4, 32, n, k, P[i], S[i], x8[k], Y8[i]) for i, (n, k) in enumerate(shapes))

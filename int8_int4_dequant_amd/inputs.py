@@ -147,6 +147,12 @@ def c4_x(k):
     return activations([4, 0 if k == 4096 else 1, 100], 1, k)
 
 
+def c4_x8(k):
+    """8 rows of x of length k for a decode pass through the stack at 8 rows
+    (several sequences at once): fp32 N(0, 1)."""
+    return activations(808 + k, 8, k)
+
+
 def c4_weights_parallel(callback, threads=None):
     """Generate the 224 c4 matrices on a thread pool (numpy releases the GIL
     while filling) and call ``callback(index, layer, tag, w)`` for each, in

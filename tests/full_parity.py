@@ -48,5 +48,13 @@ def c4_check(job):
         bad = err > GEMV_TOL * base
         out[name + "_bad"] = int(np.count_nonzero(bad))
         worst = max(worst, float(np.max(err / np.maximum(base, 1e-300))))
+    x8 = inputs.c4_x8(k)
+    yr8 = oracle.gemv_ref(ref, x8)
+    base8 = oracle.error_base(ref, x8)
+    y8 = np.memmap(files["y8"], np.float32, "r", 4 * 8 * off["rows"], 8 * n).reshape(8, n)
+    err8 = np.abs(y8.astype(np.float64) - yr8)
+    out["y8_bad"] = int(np.count_nonzero(err8 > GEMV_TOL * base8))
+    worst = max(worst, float(np.max(err8 / np.maximum(base8, 1e-300))))
     out["gemv_worst_err_over_base"] = worst
     return out
+

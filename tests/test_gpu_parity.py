@@ -601,8 +601,9 @@ def _pool_workers():
 def test_config4_full_stack():
     """The whole 7B stack (224 matrices, 6.48e9 weights) in the launch
     configuration the benchmark times: one batched quantize launch, one
-    batched M = 1 GEMV launch, one batched unpack launch, and every matrix
-    also as a lone qw_gemv call.  Every payload byte, every scale and every
+    batched M = 1 GEMV launch, one batched unpack launch, one batched GEMV
+    launch at 8 rows of x (the matrix-core kernel), and every matrix also as
+    a lone qw_gemv call.  Every payload byte, every scale and every
     GEMV output of every matrix is compared with the oracle (worker
     processes regenerate each seeded weight and run the oracle on it); the
     unpacked weights are compared through exact per-row checksums of their
@@ -628,12 +629,14 @@ def test_config4_full_stack():
     xin = [xs[m[3]] for m in mats]
     ys = qw.gemv_batched(recs, xin)
     y1 = [qw.gemv(r, x) for r, x in zip(recs, xin)]
+    x8 = {k: dev(inputs.c4_x8(k)) for k in (4096, 11008)}
+    y8 = qw.gemv_batched(recs, [x8[m[3]] for m in mats])
     w_hats = qw.unpack_batched(recs)
     torch.cuda.synchronize()
     print("c4 full: GPU passes done", flush=True)
     with tempfile.TemporaryDirectory(dir="/dev/shm" if os.path.isdir("/dev/shm") else None) as d:
         files = {name: os.path.join(d, name) for name in
-                 ("payload", "scales", "y_batched", "y_single", "unpack_ck")}
+                 ("payload", "scales", "y_batched", "y_single", "y8", "unpack_ck")}
         tot_p = sum(n * k // 2 for _, _, n, k, _ in mats)
         tot_s = sum(n * k // 32 for _, _, n, k, _ in mats)
         tot_r = sum(n for _, _, n, k, _ in mats)
@@ -641,6 +644,7 @@ def test_config4_full_stack():
               "scales": np.memmap(files["scales"], np.float32, "w+", shape=(tot_s,)),
               "y_batched": np.memmap(files["y_batched"], np.float32, "w+", shape=(tot_r,)),
               "y_single": np.memmap(files["y_single"], np.float32, "w+", shape=(tot_r,)),
+              "y8": np.memmap(files["y8"], np.float32, "w+", shape=(8 * tot_r,)),
               "unpack_ck": np.memmap(files["unpack_ck"], np.int64, "w+", shape=(tot_r,))}
         jobs, op, os_, orow = [], 0, 0, 0
         for i, ((layer, tag, n, k, _seed), rec) in enumerate(zip(mats, recs)):
@@ -648,6 +652,7 @@ def test_config4_full_stack():
             mm["scales"][os_:os_ + n * k // 32] = host(rec["scales"])
             mm["y_batched"][orow:orow + n] = host(ys[i]).reshape(-1)
             mm["y_single"][orow:orow + n] = host(y1[i]).reshape(-1)
+            mm["y8"][8 * orow:8 * (orow + n)] = host(y8[i]).reshape(-1)
             bitsv = w_hats[i].view(torch.int32).view(n, k).to(torch.int64)
             wk = torch.arange(1, k + 1, dtype=torch.int64, device="cuda")
             mm["unpack_ck"][orow:orow + n] = host((bitsv * wk).sum(dim=1))
@@ -687,7 +692,7 @@ def test_config4_full_stack():
     for r in results:
         assert r["payload_diff"] == 0 and r["scales_diff"] == 0, r
         assert r["unpack_rows_diff"] == 0, r
-        assert r["y_batched_bad"] == 0 and r["y_single_bad"] == 0, r
+        assert r["y_batched_bad"] == 0 and r["y_single_bad"] == 0 and r["y8_bad"] == 0, r
 
 
 @pytest.mark.parametrize("bits", [4, 8])
