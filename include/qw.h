@@ -291,18 +291,21 @@ int qw_gemm(int bits, int64_t group, int64_t n, int64_t k,
  *   x  fp32 [m][k]  (read),   y  fp32 [m][n]  (written),   m >= 0.
  * m <= QW_MATMUL_GEMV_MAX_M is qw_gemv itself: fp32 arithmetic on the codes,
  *   error <= 1e-5 * sum_j |x[m][j] * w_hat[i][j]|; no work buffer is needed.
- * Larger m rounds x to bf16 (round to nearest even) into `work` and runs
- *   qw_gemm on it: the weights are dequantized in registers, not kept as a
- *   second copy.  Error <= 8e-3 * sum_j |x[m][j] * w_hat[i][j]| (rounding
- *   x adds at most 2^-9 of it to the GEMM's own bound).
+ * 5 <= m <= 8 is also qw_gemv when the matrix has at most 8192 rows and
+ *   qw_gemv's matrix-core kernel takes it (measured faster there than the
+ *   GEMM, and more precise); `work` is then left untouched.
+ * Otherwise x is rounded to bf16 (round to nearest even) into `work` and
+ *   qw_gemm runs on it: the weights are dequantized in registers, not kept
+ *   as a second copy.  Error <= 8e-3 * sum_j |x[m][j] * w_hat[i][j]|
+ *   (rounding x adds at most 2^-9 of it to the GEMM's own bound).
  * The bound sits at the measured crossover on MI355X (int4 g128, 4096- to
  * 28672-row matrices: the GEMV is faster up to 3 rows on each, up to 6 on
  * the 4096-row one, the GEMM from 8 on each; at 4 rows the two are within
  * 10% on the wider matrices and the GEMV 22% faster on the 4096-row one, so
  * 4 rows stay on the more precise product).
  * `work`: a device buffer of at least qw_matmul_work_bytes(m, k)
- * bytes (may be NULL when that is 0); after the call it holds the bf16 bit
- * patterns of x, row-major.  QW_EWORK when it is missing or too small;
+ * bytes (may be NULL when that is 0); after a GEMM call it holds the bf16
+ * bit patterns of x, row-major.  QW_EWORK when it is missing or too small;
  * other validation as in qw_gemv / qw_gemm.
  */
 #define QW_MATMUL_GEMV_MAX_M 4
@@ -419,8 +422,9 @@ int qw_gptq_quantize_pack(int bits, int64_t group, int64_t n, int64_t k,
  * `op`: 0 quantize_pack (a = w, b = payload), 1 unpack (a = payload, b =
  * w_out), 2 gemv at one row of x (a = payload, b = x), 3 gemm (a = payload,
  * b = x_bf16), 4 gemv at 8 rows of x (a = payload, b = x; at fewer rows the
- * matrix-core kernel runs from the row counts qw_gemv states).  Enqueues
- * nothing.
+ * matrix-core kernel runs from the row counts qw_gemv states), 5 qw_matmul
+ * at 5..8 rows of x (a = payload, b = x): 1 = it runs qw_gemv, 2 = the
+ * GEMM.  Enqueues nothing.
  */
 int qw_debug_path(int op, int bits, int64_t group, int64_t n, int64_t k,
                   const void* a, const void* b);

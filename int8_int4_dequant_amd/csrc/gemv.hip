@@ -1143,6 +1143,13 @@ hipError_t launch_mfma_batched_bits(const GemvDesc* ds, int count, int m, int gs
 
 }  // namespace
 
+bool matmul_prefers_gemv(const Mat& mt, const uint8_t* payload, const float* x) {
+  // measured at 5..8 rows, int4 g128 and int8 per channel: the matrix-core
+  // GEMV beats the bf16 GEMM on 4096-row matrices by 20-50% and is within
+  // a few percent of it at 11008 rows; from 14336 rows the GEMM leads
+  return mt.n <= 8192 && mfma_ok(mt, payload, x);
+}
+
 int gemv_mfma_path(const Mat& mt, const uint8_t* payload, const float* x) {
   return mfma_ok(mt, payload, x) ? PATH_MATRIX : gemv_path(mt, payload, x);
 }

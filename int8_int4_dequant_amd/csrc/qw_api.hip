@@ -367,7 +367,7 @@ int qw_matmul(int bits, int64_t group, int64_t n, int64_t k, const uint8_t* payl
   int st = check_mat(bits, group, n, k, &mt);
   if (st != QW_OK) return st;
   if (!within(m, n) || !within(m, k)) return QW_EM;
-  if (m <= QW_MATMUL_GEMV_MAX_M)
+  if (m <= QW_MATMUL_GEMV_MAX_M || (m <= 8 && qw::matmul_prefers_gemv(mt, payload, x)))
     return qw_gemv(bits, group, n, k, payload, scales, m, x, y, stream);
   if (n == 0) return QW_OK;
   if (!y) return QW_ENULL;
@@ -383,7 +383,7 @@ int qw_matmul_noalloc(int bits, int64_t group, int64_t n, int64_t k, const uint8
   int st = check_mat(bits, group, n, k, &mt);
   if (st != QW_OK) return st;
   if (!within(m, n) || !within(m, k)) return QW_EM;
-  if (m <= QW_MATMUL_GEMV_MAX_M)
+  if (m <= QW_MATMUL_GEMV_MAX_M || (m <= 8 && qw::matmul_prefers_gemv(mt, payload, x)))
     return qw_gemv(bits, group, n, k, payload, scales, m, x, y, stream);
   if (n == 0) return QW_OK;
   if (qw_matmul_work_bytes(m, k) > QW_MATMUL_NOALLOC_MAX_BYTES) return QW_ESCRATCH;
@@ -447,8 +447,9 @@ int qw_gptq_quantize_pack(int bits, int64_t group, int64_t n, int64_t k, const f
 }
 
 // Which kernel family a call with these arguments would take (1 = fast,
-// 2 = block, 3 = generic, 4 = matrix-core GEMV; negative = invalid
-// arguments).  Used by the tests to make sure every family is exercised.
+// 2 = block, 3 = generic, 4 = matrix-core GEMV; for op 5, 1 = GEMV and
+// 2 = GEMM; negative = invalid arguments).  Used by the tests to make sure
+// every family is exercised.
 int qw_debug_path(int op, int bits, int64_t group, int64_t n, int64_t k, const void* a,
                   const void* b) {
   qw::Mat mt;
@@ -460,6 +461,7 @@ int qw_debug_path(int op, int bits, int64_t group, int64_t n, int64_t k, const v
     case 2: return qw::gemv_path(mt, (const uint8_t*)a, (const float*)b);
     case 3: return qw::gemm_path(mt, (const uint8_t*)a, (const uint16_t*)b);
     case 4: return qw::gemv_mfma_path(mt, (const uint8_t*)a, (const float*)b);
+    case 5: return qw::matmul_prefers_gemv(mt, (const uint8_t*)a, (const float*)b) ? 1 : 2;
     default: return QW_ECOUNT;
   }
 }

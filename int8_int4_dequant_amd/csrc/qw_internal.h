@@ -65,6 +65,8 @@ int unpack_path(const Mat& mt, const uint8_t* payload, const float* w_out);
 int gemv_path(const Mat& mt, const uint8_t* payload, const float* x);
 // The kernel family of a lone GEMV at 8 rows of x (PATH_MATRIX: matrix cores).
 int gemv_mfma_path(const Mat& mt, const uint8_t* payload, const float* x);
+// Whether qw_matmul runs the GEMV instead of the GEMM at 5..8 rows of x.
+bool matmul_prefers_gemv(const Mat& mt, const uint8_t* payload, const float* x);
 int gemm_path(const Mat& mt, const uint8_t* payload, const uint16_t* x);
 
 }  // namespace qw

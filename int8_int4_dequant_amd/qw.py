@@ -478,9 +478,10 @@ def gemm(rec, x_bf16, out=None, stream=None):
 
 def matmul(rec, x, out=None, work=None, stream=None):
     """QuantizedMatmul: fp32 x [m][k] (any m) times the quantized weight;
-    returns fp32 y [m][n].  Up to QW_MATMUL_GEMV_MAX_M rows this is the codes
-    GEMV; beyond, x is rounded to bf16 into ``work`` (allocated here when not
-    given) and the matrix-core GEMM runs."""
+    returns fp32 y [m][n].  Up to QW_MATMUL_GEMV_MAX_M rows (and up to 8 for
+    matrices of at most 8192 rows the matrix-core GEMV takes) this is the
+    codes GEMV; beyond, x is rounded to bf16 into ``work`` (allocated here
+    when not given) and the matrix-core GEMM runs."""
     n, k = _check_rec(rec)
     if not isinstance(x, torch.Tensor) or x.dim() != 2 or x.shape[1] != k:
         raise ValueError("x must be a contiguous float32 [m][k] tensor")

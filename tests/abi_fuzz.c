@@ -340,7 +340,7 @@ static void fuzz(long iters, int launches_ok) {
         else st = qw_gemv_chain(count, gd, stage, launches_ok ? m : (mm > 0 ? mm : 1), 0);
         break;
       }
-      default: st = qw_debug_path((int)(rnd() % 6), bits, group, n, k, ptr(1), ptr(1)); break;
+      default: st = qw_debug_path((int)(rnd() % 7), bits, group, n, k, ptr(1), ptr(1)); break;
     }
     if (op == 13) {
       ++g_calls;

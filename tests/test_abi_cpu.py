@@ -216,6 +216,10 @@ def test_quantize_dispatch(bits, group, n, k, al, expect):
     (4, 4, 32, 11008, 4096, 4), (4, 8, 32, 300, 1024, 4), (4, 4, 128, 64, 384 + 8, 3),
     (4, 4, 8, 64, 96, 1),
     (4, 4, 3, 8, 48, 3), (4, 4, 128, 64, 0, 3),
+    # qw_matmul at 5..8 rows: the GEMV (1) for matrices of up to 8192 rows the
+    # matrix-core GEMV takes, else the GEMM (2)
+    (5, 4, 128, 4096, 11008, 1), (5, 8, 4096, 8192, 4096, 1), (5, 4, 128, 8193, 4096, 2),
+    (5, 4, 128, 11008, 4096, 2), (5, 4, 16, 64, 256, 2), (5, 4, 32, 64, 96, 2),
 ])
 def test_product_dispatch(op, bits, group, n, k, expect):
     base = 1 << 20

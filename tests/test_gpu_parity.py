@@ -365,15 +365,18 @@ def test_codes_path_agrees_with_dequantized_path():
                                            (4, 128, 520, 256)])
 def test_matmul_dispatch_across_m(bits, group, n, k):
     """qw_matmul (QuantizedMatmul) at the Smallem test rows 1, 9, 40, 300 and
-    around the crossover: up to MATMUL_GEMV_MAX_M rows it is the codes GEMV
-    (bit for bit, and within the GEMV bar); above, the work buffer holds
-    exactly the oracle's bf16 rounding of x, the result equals qw_gemm on
-    those bits, and it is within the GEMM bar of the fp32-x product."""
+    around the crossover: up to MATMUL_GEMV_MAX_M rows, and up to 8 rows for
+    matrices the matrix-core GEMV takes with at most 8192 rows, it is the
+    codes GEMV (bit for bit, and within the GEMV bar); above, the work buffer
+    holds exactly the oracle's bf16 rounding of x, the result equals qw_gemm
+    on those bits, and it is within the GEMM bar of the fp32-x product."""
     w = inputs.weight(n + k + bits, n, k, 0.02)
     ref, rec = quant_both(w, bits, group)
-    for m in (1, 4, 5, 9, 40, 300):
+    for m in (1, 4, 5, 8, 9, 40, 300):
         x = inputs.activations(900 + m, m, k)
         xd = dev(x)
+        gemv_rows = m <= qw.MATMUL_GEMV_MAX_M or (
+            m <= 8 and qw.qw_debug_path(5, bits, group, n, k, rec["payload"], xd) == 1)
         nb = qw.qw_matmul_work_bytes(m, k)
         assert (nb == 0) == (m <= qw.MATMUL_GEMV_MAX_M)
         work = torch.zeros(max(nb, 1), dtype=torch.uint8, device="cuda")
@@ -384,7 +387,7 @@ def test_matmul_dispatch_across_m(bits, group, n, k):
         yr = oracle.gemv_ref(ref, x)
         B = oracle.error_base(ref, x)
         err = np.abs(yh.astype(np.float64) - yr)
-        if m <= qw.MATMUL_GEMV_MAX_M:
+        if gemv_rows:
             assert same_bits(yh, host(qw.gemv(rec, xd)))
             assert np.all(err <= GEMV_TOL * B)
         else:
