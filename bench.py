@@ -440,7 +440,7 @@ CPU_FULL = {"c1": (20, 101), "c2": (20, 101), "c3": (20, 101), "c4": (0, 3), "c5
 def _stats(ts_ns):
     t = sorted(ts_ns)
     return {"median_us": round(statistics.median(t) / 1e3, 1),
-            "p90_us": round(t[int(0.9 * (len(t) - 1))] / 1e3, 1)}
+            "p90_us": round(t[-(-9 * len(t) // 10) - 1] / 1e3, 1)}
 
 
 def _entry(cfg, op, ts_ns, warm, nbytes=None, flops=None, **extra):
@@ -938,7 +938,7 @@ def main():
     def med_p90_us(pairs):
         t = sorted(1e3 * e0.elapsed_time(e1) for e0, e1 in pairs)
         return {"median_us": round(statistics.median(t), 1),
-                "p90_us": round(t[int(0.9 * (len(t) - 1))], 1)}
+                "p90_us": round(t[-(-9 * len(t) // 10) - 1], 1)}
 
     q_spread = med_p90_us([(evs[s][0][0], evs[s][1][0]) for s in range(args.steps)])
     g_spread = med_p90_us([(evs[s][2][0], evs[s][3][0]) for s in range(args.steps)])
@@ -1295,7 +1295,7 @@ def bench_context(args, stream):
     med = statistics.median(t)
     tf = 2.0 * m * nn * k / (med * 1e-6) / 1e12
     out["torch_matmul_bf16_2048x28672x8192"] = {
-        "median_us": round(med, 1), "p90_us": round(t[int(0.9 * (len(t) - 1))], 1),
+        "median_us": round(med, 1), "p90_us": round(t[-(-9 * len(t) // 10) - 1], 1),
         "TFLOP/s": round(tf, 1), "frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4),
         "gpu_clock_sustained": sustained_clock(args, mm)}
     del x, wt, y
@@ -1476,7 +1476,7 @@ def bench_gemm(args, L, stream):
            f"{clock['socket_w_median']} W ({clock['samples']} samples)"))
     return {"workload": "c5: M=2048 bf16 x (28672 x 8192) int4 group 128, fp32 accumulate",
             "m_sweep_same_weight": sweep,
-            "median_us": round(med * 1e3, 2), "p90_us": round(times[int(0.9 * (len(times) - 1))] * 1e3, 2),
+            "median_us": round(med * 1e3, 2), "p90_us": round(times[-(-9 * len(times) // 10) - 1] * 1e3, 2),
             "rep_us_sorted": [round(t_ * 1e3, 1) for t_ in times],
             "TFLOP/s": round(tf, 2), "gpu_clock_sustained": clock,
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_PEAK_TFLOPS,
